@@ -1,0 +1,196 @@
+/*
+ * kvc.h -- C ABI of the compressed-KV-cache hot path for AMD MI355X (gfx950).
+ *
+ * The path (one transformer layer per call):
+ *   kvc_select      SnapKV/PyramidKV selection: the last W prompt queries score
+ *                   every earlier prompt position, the scores are max-pooled and
+ *                   the top-k positions per KV head are kept.
+ *   kvc_quantize    KIVI/MiniKV group quantization of the kept tokens (keys per
+ *                   channel, values per token, group 32, 2 or 4 bits, fp16
+ *                   scale and zero-point) into a packed cache plus a bf16
+ *                   residual of the most recent tokens.
+ *   kvc_decode_attn one decode step: append the new token, flush a full group of
+ *                   the residual into the packed history, then single-query
+ *                   attention over packed history (dequantized on the fly) and
+ *                   residual under one softmax.
+ *   kvc_budget      host-only per-layer budgets (uniform or pyramid) and the
+ *                   cache footprint.
+ *
+ * Conventions shared by every call
+ *   Memory:   every device buffer is allocated and owned by the caller; the
+ *             library allocates no device memory and keeps no global mutable
+ *             state besides a thread-local last-HIP-error code.  Scratch space
+ *             comes from a caller workspace: pass ws == NULL to have the
+ *             required size written to *ws_bytes (nothing is launched).
+ *   Streams:  device work is only enqueued on `stream` (a hipStream_t passed as
+ *             void*, NULL = default stream); no call synchronizes.  kvc_budget
+ *             runs on the host and returns when done.
+ *   Errors:   every call returns a kvc_status and never aborts or throws.  All
+ *             argument checks happen before any launch, so a validation error
+ *             leaves caller memory untouched.  KVC_ERR_HIP means a launch
+ *             failed (kvc_last_hip_error() gives the hipError_t); cache contents
+ *             are then undefined.  Faults inside kernels surface at the caller's
+ *             next synchronization, as with any HIP work.
+ *   Dtypes:   q/k/v inputs are float32 or bfloat16 (kvc_dtype); the residual is
+ *             bfloat16 (round to nearest even from float32 inputs); attention
+ *             output is float32.
+ *   Shapes:   1 <= D <= 256 with D % 32 == 0; Hq % Hkv == 0; Hq/Hkv <= 16.
+ *
+ * Cache layout (one layer; C-contiguous, capacities are the strides):
+ *   k_codes [B][Hkv][q_cap][D*bits/32]  uint32: word w of token t holds
+ *                                       channel (32/bits)*w+i at bits bits*i
+ *   k_meta  [B][Hkv][q_cap/32][D]       uint32: group g = tokens 32g..32g+31,
+ *                                       channel c
+ *   v_codes [B][Hkv][q_cap*bits/32][D]  uint32: word row w, channel c holds
+ *                                       token (32/bits)*w+i at bits bits*i
+ *   v_meta  [B][Hkv][q_cap][D/32]       uint32: token t, channels 32j..32j+31
+ *   meta word = fp16 scale bits | (fp16 zero-point bits << 16)
+ *   k_res, v_res [B][Hkv][r_cap][D]     uint16 bfloat16 bits, oldest first
+ * Codes are LSB-first (MiniKV Sec. 4.4: 16 INT2 values shifted into one INT32).
+ * Dequantized value = zero + code * scale.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_NULL = 1,      /* a required pointer is NULL                         */
+  KVC_ERR_SHAPE = 2,     /* inconsistent or unsupported sizes                  */
+  KVC_ERR_DTYPE = 3,     /* unknown kvc_dtype                                  */
+  KVC_ERR_BITS = 4,      /* bits not in {2,4} (or group/meta invalid)          */
+  KVC_ERR_CAPACITY = 5,  /* q_cap / r_cap too small, or cache not empty        */
+  KVC_ERR_WORKSPACE = 6, /* *ws_bytes smaller than required                    */
+  KVC_ERR_HIP = 7        /* a HIP launch or runtime call failed                */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* One layer's compressed cache.  Host struct of caller-owned device pointers.
+ * The library updates q_len and r_len when it enqueues work, so the host view
+ * is the state after the enqueued work completes (stream order). */
+typedef struct {
+  int32_t batch, kv_heads, head_dim; /* B, Hkv, D                              */
+  int32_t bits;                      /* 2 or 4; group size is fixed at 32      */
+  int32_t residual;                  /* R: recent tokens kept in bf16          */
+  int32_t q_cap, q_len;              /* packed history, tokens (multiples of 32)*/
+  int32_t r_cap, r_len;              /* bf16 residual, tokens; r_cap >= R + 32 */
+  uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
+  uint16_t *k_res, *v_res;
+} kvc_cache;
+
+/* Byte sizes of the six cache arrays for given capacities (host-only helper):
+ * out[0..5] = k_codes, k_meta, v_codes, v_meta, k_res, v_res.
+ * q_cap must be a multiple of 32. */
+kvc_status kvc_cache_sizes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t bits,
+                           int32_t q_cap, int32_t r_cap, size_t out[6]);
+
+/* ------------------------------------------------------------------ budget
+ * Per-layer selection budgets and footprint, on the host.
+ * Uniform: every layer keeps avg_budget (MiniKV Sec. 4.2 "Uniform").
+ * Pyramid: PyramidKV "Proposed Method" (budget allocation: top layer gets
+ *   total/(beta*m), an arithmetic sequence between bottom and top) read with
+ *   MiniKV Sec. 4.2's mean-preserving endpoints: top = avg/beta,
+ *   bottom = 2*avg - avg/beta, linear in between, layer 0 largest; integerized
+ *   exactly (floor, then +1 to the largest fractional parts, ties to the lower
+ *   layer) so the budgets sum to layers*avg.  Each budget is then capped at
+ *   prompt_len - window.  avg_budget < 0 means no eviction (all n-W kept).
+ * The budget counts selected tokens, excluding the window.
+ * Footprint (blog "The budget"; MiniKV "KV Cache compression ratio analysis"):
+ *   bits_per_element = 16 if bits == 16 else bits + 2*meta_bits/group;
+ *   bytes_per_prompt_token = 2*L*Hkv*D*bits_per_element/8 * kept fraction;
+ *   bytes_total = 2*Hkv*D*bits_per_element/8 * sum over layers of
+ *                 (kept + gen_len) tokens;
+ *   bytes_layout = exact bytes of this library's packed layout right after
+ *                 kvc_quantize for one sequence (codes + meta + bf16 residual).
+ * layer_budget: host array [layers] (required).  fp may be NULL.
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE (layers < 1, window or prompt invalid,
+ *   beta < 1 or not finite for pyramid), KVC_ERR_BITS (bits not in {2,4,8,16},
+ *   group not in {16,32}, meta_bits not in {8,16,32}). */
+typedef struct {
+  int32_t layers, kv_heads, head_dim, prompt_len, window, gen_len;
+  int32_t avg_budget; /* selected tokens per head per layer; < 0: keep all   */
+  int32_t pyramid;    /* 0 uniform, 1 arithmetic pyramid                     */
+  double beta;        /* pyramid shape: top layer = avg/beta                  */
+  int32_t bits, group, meta_bits, residual; /* bits == 16: unquantized      */
+} kvc_budget_args;
+
+typedef struct {
+  double bits_per_element, bytes_per_prompt_token, bytes_total, bytes_layout;
+} kvc_footprint;
+
+kvc_status kvc_budget(const kvc_budget_args *args, int32_t *layer_budget, kvc_footprint *fp);
+
+/* ------------------------------------------------------------------ select
+ * Observation-window token selection for one layer (blog "Eviction": SnapKV;
+ * PyramidKV "KV Cache Selection").  For KV head j and each of its G query
+ * heads, window row r (absolute position p = n-W+r) attends causally to keys
+ * 0..p with logits q.k/sqrt(D); the softmax probabilities are summed over the
+ * W rows and the G heads for every candidate c < n-W, max-pooled with an odd
+ * kernel `pool` (stride 1, edges clipped), and the k' = min(budget, n-W)
+ * largest are selected (ties to the lower position), written in ascending
+ * order.  The window [n-W, n) is always kept and is not part of idx.
+ *   q_win  [B][Hq][W][D]   the last W prompt queries (post-RoPE), dtype
+ *   k      [B][Hkv][n][D]  prompt keys (post-RoPE), dtype
+ *   idx    [B][Hkv][k']    int32 output, ascending, in [0, n-W) (may be NULL if k' == 0)
+ *   scores [B][Hkv][n-W]   float32 output of the pooled scores, or NULL
+ *   budget < 0 keeps every candidate.
+ * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_SHAPE (W < 1, W > n, pool even
+ *   or < 1, shapes above), KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
+kvc_status kvc_select(const void *q_win, const void *k, kvc_dtype dtype, int32_t B, int32_t Hq,
+                      int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool, int32_t budget,
+                      int32_t *idx, float *scores, void *ws, size_t *ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ quantize
+ * Prompt compression into an empty cache (MiniKV Alg. 1 prefill: heavy
+ * hitters, then Quant; Sec. 4.4 INT2 quantization kernel; blog
+ * "Quantization": keys per channel, values per token, recent tokens in full
+ * precision until a group fills).  The kept tokens of each (b, KV head) are
+ * idx[b][j][0..k_sel) followed by the window n-W..n-1 (T = k_sel + W), or all n
+ * prompt tokens when idx == NULL (T = n).  The oldest Q = 32*floor(max(T-R,0)/32)
+ * are quantized: per group of 32 values, lo/hi -> scale = fp16((hi-lo)/(2^b-1)),
+ * zero = fp16(lo), code = clamp(rint((x - zero) * (1/scale)), 0, 2^b-1) in IEEE
+ * float32 (scale 0 -> codes 0); the last T-Q go to the residual as bf16.
+ *   k, v [B][Hkv][n][D] dtype; idx [B][Hkv][k_sel] int32 (ascending, < n-W) or
+ *   NULL; cache: batch/kv_heads/head_dim/bits/residual/capacities/pointers set,
+ *   q_len == r_len == 0.  On success cache->q_len = Q, cache->r_len = T-Q.
+ * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_BITS, KVC_ERR_SHAPE,
+ *   KVC_ERR_CAPACITY (cache not empty, Q > q_cap, T-Q > r_cap or
+ *   r_cap < R+32), KVC_ERR_HIP. */
+kvc_status kvc_quantize(const void *k, const void *v, kvc_dtype dtype, int32_t n, const int32_t *idx,
+                        int32_t k_sel, int32_t W, kvc_cache *cache, void *stream);
+
+/* ------------------------------------------------------------------ decode
+ * One decode step (MiniKV Eq. 1 and Alg. 1 decoding; blog attention hook):
+ * k_new/v_new are appended to the bf16 residual; if the residual then holds
+ * R+32 tokens its oldest 32 are quantized (same arithmetic as kvc_quantize)
+ * and appended to the packed history; then for every query head h (KV head
+ * h / (Hq/Hkv)) out = softmax(q K^T / sqrt(D)) V over the q_len dequantized
+ * history tokens and the r_len residual tokens, one softmax over both.
+ *   q [B][Hq][D], k_new, v_new [B][Hkv][D] in dtype; out [B][Hq][D] float32.
+ * Workspace: *ws_bytes (ws == NULL query) is sized for q_len == q_cap, so one
+ *   buffer serves every step of this cache.
+ * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_BITS, KVC_ERR_SHAPE,
+ *   KVC_ERR_CAPACITY (r_len+1 > r_cap, or a flush with q_len+32 > q_cap),
+ *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
+kvc_status kvc_decode_attn(kvc_cache *cache, const void *q, const void *k_new, const void *v_new,
+                           kvc_dtype dtype, int32_t Hq, float *out, void *ws, size_t *ws_bytes,
+                           void *stream);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int kvc_last_hip_error(void);
+
+/* Static text for a status code. */
+const char *kvc_status_string(kvc_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,224 @@
+"""ctypes binding of libkvc.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; PyTorch supplies device
+memory and the current stream.  Importing this module raises if the library has
+not been built (there is no fallback implementation).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+KVC_F32, KVC_BF16 = 0, 1
+STATUS = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_BITS",
+          5: "KVC_ERR_CAPACITY", 6: "KVC_ERR_WORKSPACE", 7: "KVC_ERR_HIP"}
+EXPORTS = ("kvc_budget", "kvc_select", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
+           "kvc_last_hip_error", "kvc_status_string")
+
+
+class KvcError(RuntimeError):
+    def __init__(self, fn, status, hip=0):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}" + (f" (hipError {hip})" if hip else ""))
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("residual", ctypes.c_int32),
+                ("q_cap", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("r_cap", ctypes.c_int32), ("r_len", ctypes.c_int32),
+                ("k_codes", ctypes.c_void_p), ("k_meta", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
+                ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p)]
+
+
+class BudgetArgs(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("prompt_len", ctypes.c_int32), ("window", ctypes.c_int32), ("gen_len", ctypes.c_int32),
+                ("avg_budget", ctypes.c_int32), ("pyramid", ctypes.c_int32), ("beta", ctypes.c_double),
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("meta_bits", ctypes.c_int32),
+                ("residual", ctypes.c_int32)]
+
+
+class Footprint(ctypes.Structure):
+    _fields_ = [("bits_per_element", ctypes.c_double), ("bytes_per_prompt_token", ctypes.c_double),
+                ("bytes_total", ctypes.c_double), ("bytes_layout", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_compression_snapkv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)
+    lib.kvc_budget.argtypes = [ctypes.POINTER(BudgetArgs), ctypes.POINTER(I32), ctypes.POINTER(Footprint)]
+    lib.kvc_select.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    lib.kvc_quantize.argtypes = [P, P, I32, I32, P, I32, I32, ctypes.POINTER(CacheStruct), P]
+    lib.kvc_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P, SZ, P]
+    lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvc_status_string.argtypes = [I32]
+    lib.kvc_status_string.restype = ctypes.c_char_p
+    for f in ("kvc_budget", "kvc_select", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
+              "kvc_last_hip_error"):
+        getattr(lib, f).restype = I32
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise KvcError(fn, status, lib.kvc_last_hip_error() if status == 7 else 0)
+
+
+def _dtype(t):
+    if t.dtype == torch.float32:
+        return KVC_F32
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ---------------------------------------------------------------- budget
+def kvc_budget(layers, kv_heads, head_dim, prompt_len, window, gen_len, avg_budget, pyramid=False,
+               beta=1.0, bits=2, group=32, meta_bits=16, residual=0):
+    a = BudgetArgs(layers, kv_heads, head_dim, prompt_len, window, gen_len, avg_budget, int(bool(pyramid)),
+                   float(beta), bits, group, meta_bits, residual)
+    out = (ctypes.c_int32 * layers)()
+    fp = Footprint()
+    _check("kvc_budget", lib.kvc_budget(ctypes.byref(a), out, ctypes.byref(fp)))
+    return list(out), {"bits_per_element": fp.bits_per_element,
+                       "bytes_per_prompt_token": fp.bytes_per_prompt_token,
+                       "bytes_total": fp.bytes_total, "bytes_layout": fp.bytes_layout}
+
+
+# ---------------------------------------------------------------- select
+def select_ws_bytes(dtype, B, Hq, Hkv, n, D, W, pool, budget):
+    need = ctypes.c_size_t(0)
+    _check("kvc_select", lib.kvc_select(None, None, dtype, B, Hq, Hkv, n, D, W, pool, budget, None, None,
+                                        None, ctypes.byref(need), None))
+    return need.value
+
+
+def kvc_select(q_win, k, W, pool, budget, want_scores=False, ws=None, idx=None, scores=None, stream=None):
+    """Returns idx [B][Hkv][k'] int32 (and pooled scores [B][Hkv][n-W] if asked)."""
+    _contig(q_win, k)
+    B, Hq, Wq, D = q_win.shape
+    _, Hkv, n, _ = k.shape
+    if Wq != W or k.dtype != q_win.dtype:
+        raise ValueError("q_win must be [B][Hq][W][D] with the dtype of k")
+    dt = _dtype(k)
+    N = n - W
+    kk = N if budget < 0 else min(budget, N)
+    need = select_ws_bytes(dt, B, Hq, Hkv, n, D, W, pool, budget)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    if idx is None:
+        idx = torch.empty(B, Hkv, kk, dtype=torch.int32, device=k.device)
+    if want_scores and scores is None:
+        scores = torch.empty(B, Hkv, N, dtype=torch.float32, device=k.device)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("kvc_select", lib.kvc_select(_ptr(q_win), _ptr(k), dt, B, Hq, Hkv, n, D, W, pool, budget,
+                                        _ptr(idx), _ptr(scores) if want_scores else None, _ptr(ws),
+                                        ctypes.byref(wsb), _stream(stream)))
+    return (idx, scores) if want_scores else idx
+
+
+# ---------------------------------------------------------------- cache
+class Cache:
+    """One layer's compressed cache: caller-owned torch buffers + the C struct."""
+
+    def __init__(self, batch, kv_heads, head_dim, bits, residual, q_cap, r_cap=None, device="cuda"):
+        if r_cap is None:
+            r_cap = residual + 32
+        q_cap = 32 * ((q_cap + 31) // 32)
+        sizes = (ctypes.c_size_t * 6)()
+        _check("kvc_cache_sizes", lib.kvc_cache_sizes(batch, kv_heads, head_dim, bits, q_cap, r_cap, sizes))
+        u32 = lambda nbytes: torch.zeros(max(nbytes // 4, 1), dtype=torch.int32, device=device)
+        u16 = lambda nbytes: torch.zeros(max(nbytes // 2, 1), dtype=torch.int16, device=device)
+        self.k_codes, self.k_meta = u32(sizes[0]), u32(sizes[1])
+        self.v_codes, self.v_meta = u32(sizes[2]), u32(sizes[3])
+        self.k_res, self.v_res = u16(sizes[4]), u16(sizes[5])
+        self.s = CacheStruct(batch, kv_heads, head_dim, bits, residual, q_cap, 0, r_cap, 0,
+                             self.k_codes.data_ptr(), self.k_meta.data_ptr(), self.v_codes.data_ptr(),
+                             self.v_meta.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr())
+        self._ws = None
+
+    @property
+    def q_len(self):
+        return self.s.q_len
+
+    @property
+    def r_len(self):
+        return self.s.r_len
+
+    def reset(self):
+        """Mark the cache empty (buffers are kept; the next kvc_quantize refills them)."""
+        self.s.q_len = 0
+        self.s.r_len = 0
+
+    def views(self):
+        """Logical views of the stored state (for tests): codes/meta/residual per (b, j)."""
+        s = self.s
+        B, H, D, b = s.batch, s.kv_heads, s.head_dim, s.bits
+        qc, rc = s.q_cap, s.r_cap
+        return {
+            "k_codes": self.k_codes.view(B, H, qc, D * b // 32)[:, :, : s.q_len],
+            "k_meta": self.k_meta.view(B, H, qc // 32, D)[:, :, : s.q_len // 32],
+            "v_codes": self.v_codes.view(B, H, qc * b // 32, D)[:, :, : s.q_len * b // 32],
+            "v_meta": self.v_meta.view(B, H, qc, D // 32)[:, :, : s.q_len],
+            "k_res": self.k_res.view(B, H, rc, D)[:, :, : s.r_len],
+            "v_res": self.v_res.view(B, H, rc, D)[:, :, : s.r_len],
+        }
+
+
+def kvc_quantize(k, v, cache, idx=None, W=0, stream=None):
+    _contig(k, v, idx)
+    B, Hkv, n, D = k.shape
+    k_sel = idx.shape[-1] if idx is not None else 0
+    _check("kvc_quantize", lib.kvc_quantize(_ptr(k), _ptr(v), _dtype(k), n, _ptr(idx), k_sel, W,
+                                            ctypes.byref(cache.s), _stream(stream)))
+    return cache
+
+
+def decode_ws_bytes(cache, Hq):
+    need = ctypes.c_size_t(0)
+    _check("kvc_decode_attn", lib.kvc_decode_attn(ctypes.byref(cache.s), None, None, None, KVC_BF16, Hq,
+                                                  None, None, ctypes.byref(need), None))
+    return need.value
+
+
+def kvc_decode_attn(cache, q, k_new, v_new, out=None, ws=None, stream=None):
+    """One decode step; returns out [B][Hq][D] float32."""
+    _contig(q, k_new, v_new)
+    B, Hq, D = q.shape
+    if ws is None:
+        if cache._ws is None:
+            cache._ws = torch.empty(decode_ws_bytes(cache, Hq), dtype=torch.uint8, device=q.device)
+        ws = cache._ws
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("kvc_decode_attn", lib.kvc_decode_attn(ctypes.byref(cache.s), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                  _dtype(q), Hq, _ptr(out), _ptr(ws), ctypes.byref(wsb),
+                                                  _stream(stream)))
+    return out

@@ -1,0 +1,342 @@
+// Group quantization + bit packing of kept tokens (prompt compression) and the
+// residual flush of a decode step.
+//
+// MiniKV Sec. 4.4 (INT2 quantization kernel: codes bit-shifted into INT32,
+// keys along channels' token groups, values per token, fp16 scale/zero) and
+// Alg. 1 (prefill Quant; decoding flush of the streaming residual); blog
+// "Quantization" (KIVI grouping; recent tokens kept exact until a group fills).
+//
+// One workgroup owns one 32-token block of one (batch, KV head): the block's
+// gathered keys and values are staged in LDS as float32, the per-channel key
+// groups and per-token value groups get their fp16 scale/zero, and the codes
+// are packed: keys along channels (a word holds 32/b channels of one token),
+// values along tokens (a word holds 32/b tokens of one channel).
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxD = 256;
+
+struct QuantLds {
+  float k[kGroup][kMaxD + 1];
+  float v[kGroup][kMaxD + 1];
+  float kz[kMaxD], kinv[kMaxD];
+  float vz[kGroup][kMaxD / kGroup], vinv[kGroup][kMaxD / kGroup];
+  uint8_t kok[kMaxD];
+  uint8_t vok[kGroup][kMaxD / kGroup];
+};
+
+// Quantize the 32 tokens staged in L and write them at token offset q0 of the
+// (batch, KV head) slice whose base pointers are given.
+template <int BITS>
+__device__ void quantize_block(QuantLds& L, int D, int q0, uint32_t* k_codes, uint32_t* k_meta,
+                               uint32_t* v_codes, uint32_t* v_meta) {
+  const int tid = threadIdx.x;
+  const float qmax = static_cast<float>((1 << BITS) - 1);
+  const int ngv = D / kGroup;
+  // key groups: one channel over the 32 tokens
+  for (int c = tid; c < D; c += kThreads) {
+    float lo = L.k[0][c], hi = lo;
+    for (int t = 1; t < kGroup; ++t) {
+      lo = fminf(lo, L.k[t][c]);
+      hi = fmaxf(hi, L.k[t][c]);
+    }
+    const GroupQ g = make_group(lo, hi, qmax);
+    L.kz[c] = g.z;
+    L.kinv[c] = g.inv;
+    L.kok[c] = g.ok;
+    k_meta[static_cast<size_t>(q0 / kGroup) * D + c] = g.meta;
+  }
+  // value groups: one token over 32 channels
+  for (int e = tid; e < kGroup * ngv; e += kThreads) {
+    const int t = e / ngv, j = e % ngv;
+    float lo = L.v[t][j * kGroup], hi = lo;
+    for (int i = 1; i < kGroup; ++i) {
+      lo = fminf(lo, L.v[t][j * kGroup + i]);
+      hi = fmaxf(hi, L.v[t][j * kGroup + i]);
+    }
+    const GroupQ g = make_group(lo, hi, qmax);
+    L.vz[t][j] = g.z;
+    L.vinv[t][j] = g.inv;
+    L.vok[t][j] = g.ok;
+    v_meta[static_cast<size_t>(q0 + t) * ngv + j] = g.meta;
+  }
+  __syncthreads();
+  constexpr int per = 32 / BITS;
+  const int nw = D / per;  // key words per token
+  for (int e = tid; e < kGroup * nw; e += kThreads) {
+    const int t = e / nw, w = e % nw;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int c = w * per + i;
+      word |= code_of(L.k[t][c], L.kz[c], L.kinv[c], L.kok[c], qmax) << (BITS * i);
+    }
+    k_codes[static_cast<size_t>(q0 + t) * nw + w] = word;
+  }
+  constexpr int rows = kGroup / per;  // value word rows per block
+  for (int e = tid; e < rows * D; e += kThreads) {
+    const int r = e / D, c = e % D, j = c / kGroup;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int t = r * per + i;
+      word |= code_of(L.v[t][c], L.vz[t][j], L.vinv[t][j], L.vok[t][j], qmax) << (BITS * i);
+    }
+    v_codes[(static_cast<size_t>(q0) / per + r) * D + c] = word;
+  }
+}
+
+struct QuantArgs {
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  int n, D, Hkv, k_sel, W, Q, T, q_cap, r_cap;
+  uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
+  uint16_t *k_res, *v_res;
+};
+
+// Kept position t of (b, j): selected ascending, then the window; clamped into
+// the prompt so that a malformed idx cannot address outside k/v.
+__device__ __forceinline__ int kept_pos(const QuantArgs& a, int bj, int t) {
+  int p;
+  if (a.idx == nullptr) {
+    p = t;
+  } else if (t < a.k_sel) {
+    p = a.idx[static_cast<size_t>(bj) * a.k_sel + t];
+  } else {
+    p = a.n - a.W + (t - a.k_sel);
+  }
+  return min(max(p, 0), a.n - 1);
+}
+
+template <typename T, int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ QuantLds L;
+  const int blk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int bj = b * a.Hkv + j;
+  const int D = a.D;
+  const int tid = threadIdx.x;
+  const T* k = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
+  const T* v = static_cast<const T*>(a.v) + static_cast<size_t>(bj) * a.n * D;
+  const int nqb = a.Q / kGroup;
+  if (blk < nqb) {
+    const int t0 = blk * kGroup;
+    for (int e = tid; e < kGroup * D; e += kThreads) {
+      const int t = e / D, c = e % D;
+      const size_t src = static_cast<size_t>(kept_pos(a, bj, t0 + t)) * D + c;
+      L.k[t][c] = load_f32(k, src);
+      L.v[t][c] = load_f32(v, src);
+    }
+    __syncthreads();
+    const size_t qc = a.q_cap;
+    quantize_block<BITS>(L, D, t0, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
+                         a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D,
+                         a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
+                         a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
+  } else {
+    // residual: kept tokens [Q, T) -> bf16 rows 0..T-Q-1
+    const int r0 = (blk - nqb) * kGroup;
+    const int nr = min(kGroup, a.T - a.Q - r0);
+    uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;
+    uint16_t* vr = a.v_res + static_cast<size_t>(bj) * a.r_cap * D;
+    for (int e = tid; e < nr * D; e += kThreads) {
+      const int t = e / D, c = e % D;
+      const size_t src = static_cast<size_t>(kept_pos(a, bj, a.Q + r0 + t)) * D + c;
+      const size_t dst = static_cast<size_t>(r0 + t) * D + c;
+      kr[dst] = f32_to_bf16(load_f32(k, src));
+      vr[dst] = f32_to_bf16(load_f32(v, src));
+    }
+  }
+}
+
+struct FlushArgs {
+  const void* k_new;
+  const void* v_new;
+  int D, Hkv, R, r_old, q_len, q_cap, r_cap;
+  uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
+  uint16_t *k_res, *v_res;
+};
+
+// Decode-step flush: the residual held r_old = R+31 tokens; the new token makes
+// it R+32.  Quantize the oldest 32 (the new token is among them only when R==0),
+// append them at q_len, and shift the remaining R tokens (ending with the new
+// one) to the front of the residual.
+template <typename T, int BITS>
+__global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
+  __shared__ QuantLds L;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int bj = b * a.Hkv + j;
+  const int D = a.D;
+  const int tid = threadIdx.x;
+  const T* kn = static_cast<const T*>(a.k_new) + static_cast<size_t>(bj) * D;
+  const T* vn = static_cast<const T*>(a.v_new) + static_cast<size_t>(bj) * D;
+  uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;
+  uint16_t* vr = a.v_res + static_cast<size_t>(bj) * a.r_cap * D;
+  for (int e = tid; e < kGroup * D; e += kThreads) {
+    const int t = e / D, c = e % D;
+    uint16_t kb, vb;
+    if (t < a.r_old) {
+      kb = kr[static_cast<size_t>(t) * D + c];
+      vb = vr[static_cast<size_t>(t) * D + c];
+    } else {
+      kb = f32_to_bf16(load_f32(kn, c));
+      vb = f32_to_bf16(load_f32(vn, c));
+    }
+    L.k[t][c] = bf16_to_f32(kb);
+    L.v[t][c] = bf16_to_f32(vb);
+  }
+  __syncthreads();
+  const size_t qc = a.q_cap;
+  quantize_block<BITS>(L, D, a.q_len, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
+                       a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D,
+                       a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
+                       a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
+  // shift rows [32, R+32) -> [0, R) in chunks of 8 rows; each chunk is read in
+  // full before it is written, and a chunk only overwrites rows already read.
+  constexpr int kRows = 8;
+  constexpr int kPer = kRows * kMaxD / kThreads;
+  for (int r0 = 0; r0 < a.R; r0 += kRows) {
+    const int nr = min(kRows, a.R - r0);
+    uint16_t kb[kPer], vb[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < nr * D) {
+        const int t = r0 + e / D + kGroup, c = e % D;
+        if (t < a.r_old) {
+          kb[u] = kr[static_cast<size_t>(t) * D + c];
+          vb[u] = vr[static_cast<size_t>(t) * D + c];
+        } else {
+          kb[u] = f32_to_bf16(load_f32(kn, c));
+          vb[u] = f32_to_bf16(load_f32(vn, c));
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < nr * D) {
+        const size_t dst = static_cast<size_t>(r0 + e / D) * D + e % D;
+        kr[dst] = kb[u];
+        vr[dst] = vb[u];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T>
+kvc_status launch_quantize(const QuantArgs& a, int bits, int B, hipStream_t st) {
+  const int nblk = a.Q / kGroup + (a.T - a.Q + kGroup - 1) / kGroup;
+  if (nblk == 0) return KVC_OK;
+  dim3 grid(nblk, a.Hkv, B);
+  if (bits == 2)
+    hipLaunchKernelGGL((quantize_kernel<T, 2>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((quantize_kernel<T, 4>), grid, dim3(kThreads), 0, st, a);
+  return check_launch();
+}
+
+}  // namespace
+
+kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new, kvc_dtype dt,
+                        hipStream_t st) {
+  FlushArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.D = c->head_dim;
+  a.Hkv = c->kv_heads;
+  a.R = c->residual;
+  a.r_old = c->r_len;
+  a.q_len = c->q_len;
+  a.q_cap = c->q_cap;
+  a.r_cap = c->r_cap;
+  a.k_codes = c->k_codes;
+  a.k_meta = c->k_meta;
+  a.v_codes = c->v_codes;
+  a.v_meta = c->v_meta;
+  a.k_res = c->k_res;
+  a.v_res = c->v_res;
+  dim3 grid(c->kv_heads, c->batch);
+  if (dt == KVC_F32) {
+    if (c->bits == 2)
+      hipLaunchKernelGGL((flush_kernel<float, 2>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((flush_kernel<float, 4>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (c->bits == 2)
+      hipLaunchKernelGGL((flush_kernel<uint16_t, 2>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((flush_kernel<uint16_t, 4>), grid, dim3(kThreads), 0, st, a);
+  }
+  return check_launch();
+}
+
+bool cache_ok(const kvc_cache* c) {
+  return c && c->k_codes && c->k_meta && c->v_codes && c->v_meta && c->k_res && c->v_res;
+}
+
+kvc_status cache_shape_status(const kvc_cache* c) {
+  if (c->bits != 2 && c->bits != 4) return KVC_ERR_BITS;
+  if (c->batch < 1 || c->kv_heads < 1 || !head_dim_ok(c->head_dim) || c->residual < 0 ||
+      c->q_cap < 0 || c->q_cap % kGroup != 0 || c->r_cap < 0 || c->q_len < 0 || c->r_len < 0 ||
+      c->q_len % kGroup != 0)
+    return KVC_ERR_SHAPE;
+  if (c->q_len > c->q_cap || c->r_len > c->r_cap || c->r_cap < c->residual + kGroup)
+    return KVC_ERR_CAPACITY;
+  return KVC_OK;
+}
+
+}  // namespace kvc
+
+extern "C" kvc_status kvc_quantize(const void* k, const void* v, kvc_dtype dtype, int32_t n,
+                                   const int32_t* idx, int32_t k_sel, int32_t W, kvc_cache* cache,
+                                   void* stream) {
+  using namespace kvc;
+  if (!k || !v || !cache_ok(cache)) return KVC_ERR_NULL;
+  if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
+  kvc_status s = cache_shape_status(cache);
+  if (s != KVC_OK) return s;
+  if (n < 1) return KVC_ERR_SHAPE;
+  int T;
+  if (idx) {
+    if (W < 1 || W > n || k_sel < 0 || k_sel > n - W) return KVC_ERR_SHAPE;
+    T = k_sel + W;
+  } else {
+    T = n;
+  }
+  if (cache->q_len != 0 || cache->r_len != 0) return KVC_ERR_CAPACITY;
+  const int R = cache->residual;
+  const int Q = kGroup * (std::max(T - R, 0) / kGroup);
+  if (Q > cache->q_cap || T - Q > cache->r_cap) return KVC_ERR_CAPACITY;
+  QuantArgs a;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.n = n;
+  a.D = cache->head_dim;
+  a.Hkv = cache->kv_heads;
+  a.k_sel = idx ? k_sel : 0;
+  a.W = idx ? W : 0;
+  a.Q = Q;
+  a.T = T;
+  a.q_cap = cache->q_cap;
+  a.r_cap = cache->r_cap;
+  a.k_codes = cache->k_codes;
+  a.k_meta = cache->k_meta;
+  a.v_codes = cache->v_codes;
+  a.v_meta = cache->v_meta;
+  a.k_res = cache->k_res;
+  a.v_res = cache->v_res;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = dtype == KVC_F32 ? launch_quantize<float>(a, cache->bits, cache->batch, st)
+                       : launch_quantize<uint16_t>(a, cache->bits, cache->batch, st);
+  if (s != KVC_OK) return s;
+  cache->q_len = Q;
+  cache->r_len = T - Q;
+  return KVC_OK;
+}

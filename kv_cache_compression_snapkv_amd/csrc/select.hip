@@ -1,0 +1,442 @@
+// SnapKV/PyramidKV observation-window selection (blog "Eviction": SnapKV;
+// PyramidKV "KV Cache Selection").
+//
+// For KV head j the R = G*W window rows (G query heads x W last prompt queries)
+// attend causally to the prompt.  The scorer is a dense contraction
+// Q_w[R][D] x K[n][D]^T on MFMA (bf16 inputs: v_mfma_f32_16x16x32_bf16; fp32
+// inputs: v_mfma_f32_16x16x4_f32), in two passes over K:
+//   pass 1: per 128-column chunk, each row's max and sum of 2^(x - max)
+//           (x = logit * log2(e)/sqrt(D), causal mask), merged per row by a
+//           small kernel into (M_r, 1/L_r);
+//   pass 2: column sums of 2^(x - M_r)/L_r over the rows for candidates
+//           c < n-W, written in fixed order (deterministic).
+// Then one workgroup per (b, j) max-pools the scores, maps them to
+// order-preserving uint32 keys and finds the k'-th largest by a 4x8-bit radix
+// select; an index-order scan emits every key above the threshold plus the
+// lowest-index ties, so idx comes out ascending with ties to the lower index.
+#include <algorithm>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowBlock = 128;  // rows per pass over the staged chunk (8 tiles, 2 per wave)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+struct ScoreArgs {
+  const void* q_win;  // [B][Hq][W][D]
+  const void* k;      // [B][Hkv][n][D]
+  float2* stats;      // pass 1: [B][Hkv][nc1][R] (max, sum) in log2 units
+  float2* rowstat;    // [B][Hkv][R] (M, 1/L)
+  float* raw;         // [B][Hkv][N] column sums
+  int Hq, Hkv, G, n, W, R, N, nc1;
+  float scale2;
+};
+
+// Fragment of 8 consecutive channels for one lane, and the MFMA that consumes it.
+template <typename T> struct Frag;
+template <> struct Frag<uint16_t> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void zero() {
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<__bf16>(0.0f);
+  }
+};
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void load(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void zero() {
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+};
+
+// acc[row = 4*(lane/16)+i][col = lane%16] += sum_k A[row][k] B[k][col] over one
+// 32-channel step; lane (r, q) supplies channels 32s+8q..+7 of its row/column.
+__device__ __forceinline__ f32x4 mma(const Frag<uint16_t>& a, const Frag<uint16_t>& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 acc) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[u], b.v[u], acc, 0, 0, 0);
+  return acc;
+}
+
+template <typename T> struct ChunkCols { static constexpr int value = 128; };
+template <> struct ChunkCols<float> { static constexpr int value = 64; };
+
+// Reduce (max, sum) pairs across the 16 lanes that share a row group.
+__device__ __forceinline__ void merge16(float& m, float& l) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const float l2 = __shfl_xor(l, o);
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) {
+      l = 0.0f;
+    } else {
+      l = l * exp2f(m - M) + l2 * exp2f(m2 - M);
+    }
+    m = M;
+  }
+}
+
+template <typename T, int KS, int PASS>
+__global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
+  constexpr int CH = ChunkCols<T>::value;
+  constexpr int D = KS * 32;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int LD = D + PAD;  // padded LDS row (elements)
+  constexpr int CT = CH / 16;  // column tiles per chunk
+  __shared__ __attribute__((aligned(16))) T ks[CH * LD];
+  __shared__ float colred[4][CH];
+
+  const int chunk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int bj = b * a.Hkv + j;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ln = lane & 15, lq = lane >> 4;
+  const int c0 = chunk * CH;
+  const int ncol_valid = (PASS == 1) ? a.n : a.N;
+
+  // stage the key chunk (zero-filled beyond the valid columns)
+  const T* kp = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
+  constexpr int VEC = 16 / sizeof(T);
+  for (int e = tid; e < CH * D / VEC; e += kThreads) {
+    const int c = e / (D / VEC), d = (e % (D / VEC)) * VEC;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (c0 + c < ncol_valid) val = *reinterpret_cast<const uint4*>(kp + static_cast<size_t>(c0 + c) * D + d);
+    *reinterpret_cast<uint4*>(&ks[c * LD + d]) = val;
+  }
+  __syncthreads();
+
+  const T* qbase = static_cast<const T*>(a.q_win) + static_cast<size_t>(b * a.Hq + j * a.G) * a.W * D;
+  float colacc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) colacc[ct] = 0.0f;
+
+  for (int rb = 0; rb < a.R; rb += kRowBlock) {
+    Frag<T> qf[2][KS];
+    int row0[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      row0[u] = rb + (wave + 4 * u) * 16;  // first row of this wave's tile u
+      const int r = row0[u] + ln;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (r < a.R) qf[u][s].load(qbase + static_cast<size_t>(r) * D + 32 * s + 8 * lq);
+        else qf[u][s].zero();
+      }
+    }
+    const bool active0 = row0[0] < a.R, active1 = row0[1] < a.R;
+    if (!active0) continue;  // wave-uniform
+
+    f32x4 acc[2][CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      acc[0][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Frag<T> kf;
+        kf.load(&ks[(ct * 16 + ln) * LD + 32 * s + 8 * lq]);
+        acc[0][ct] = mma(qf[0][s], kf, acc[0][ct]);
+        if (active1) acc[1][ct] = mma(qf[1][s], kf, acc[1][ct]);
+      }
+    }
+
+    if (PASS == 1) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (u == 1 && !active1) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0[u] + 4 * lq + i;
+          const int lim = a.n - a.W + (r % a.W);  // last key this row may see
+          float m = -INFINITY;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int c = c0 + ct * 16 + ln;
+            const float x = acc[u][ct][i] * a.scale2;
+            if (c <= lim && c < a.n) m = fmaxf(m, x);
+          }
+          float l = 0.0f;
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              const int c = c0 + ct * 16 + ln;
+              const float x = acc[u][ct][i] * a.scale2;
+              if (c <= lim && c < a.n) l += exp2f(x - m);
+            }
+          }
+          merge16(m, l);
+          if (ln == 0 && r < a.R)
+            a.stats[(static_cast<size_t>(bj) * a.nc1 + chunk) * a.R + r] = make_float2(m, l);
+        }
+      }
+    } else {
+      float2 st[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0[u] + 4 * lq + i;
+          st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float v = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = row0[u] + 4 * lq + i;
+            if (r < a.R) v += exp2f(acc[u][ct][i] * a.scale2 - st[u][i].x) * st[u][i].y;
+          }
+        }
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        colacc[ct] += v;
+      }
+    }
+  }
+
+  if (PASS == 2) {
+    if (lq == 0) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) colred[wave][ct * 16 + ln] = colacc[ct];
+    }
+    __syncthreads();
+    for (int c = tid; c < CH; c += kThreads) {
+      const float v = ((colred[0][c] + colred[1][c]) + colred[2][c]) + colred[3][c];
+      if (c0 + c < a.N) a.raw[static_cast<size_t>(bj) * a.N + c0 + c] = v;
+    }
+  }
+}
+
+// Per row: M = max over chunks, 1/L with L = sum l_k 2^(m_k - M).
+__global__ __launch_bounds__(kThreads) void rowstat_kernel(ScoreArgs a) {
+  const int r = blockIdx.x * kThreads + threadIdx.x;
+  const int j = blockIdx.y, b = blockIdx.z;
+  if (r >= a.R) return;
+  const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
+  float M = -INFINITY;
+  for (int c = 0; c < a.nc1; ++c) M = fmaxf(M, a.stats[(bj * a.nc1 + c) * a.R + r].x);
+  float L = 0.0f;
+  for (int c = 0; c < a.nc1; ++c) {
+    const float2 ml = a.stats[(bj * a.nc1 + c) * a.R + r];
+    if (ml.x != -INFINITY) L += ml.y * exp2f(ml.x - M);
+  }
+  a.rowstat[bj * a.R + r] = make_float2(M, 1.0f / L);
+}
+
+constexpr int kTopThreads = 1024;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f == 0.0f) f = 0.0f;  // -0 ranks as +0
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive prefix sum of one int per thread; *total gets the sum.
+__device__ int block_exclusive_scan(int x, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < kTopThreads / 64; ++i) {
+      const int t = sh[i];
+      sh[i] = run;
+      run += t;
+    }
+    sh[kTopThreads / 64] = run;
+  }
+  __syncthreads();
+  const int res = sh[w] + inc - x;
+  *total = sh[kTopThreads / 64];
+  __syncthreads();
+  return res;
+}
+
+struct TopArgs {
+  const float* raw;  // [B][Hkv][N]
+  uint32_t* keys;    // [B][Hkv][N]
+  float* scores;     // pooled scores out, or null
+  int32_t* idx;      // [B][Hkv][kk]
+  int Hkv, N, kk, pool;
+};
+
+__global__ __launch_bounds__(kTopThreads) void pool_topk_kernel(TopArgs a) {
+  __shared__ int hist[kTopThreads / 64][256];
+  __shared__ int scan_sh[kTopThreads / 64 + 1];
+  __shared__ uint32_t sel_sh[2];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int N = a.N, h = a.pool / 2;
+  const float* raw = a.raw + bj * N;
+  uint32_t* keys = a.keys + bj * N;
+  int32_t* idx = a.idx + bj * a.kk;
+  for (int c = tid; c < N; c += kTopThreads) {
+    float m = raw[c];
+    const int lo = max(0, c - h), hi = min(N - 1, c + h);
+    for (int d = lo; d <= hi; ++d) m = fmaxf(m, raw[d]);
+    keys[c] = order_key(m);
+    if (a.scores) a.scores[bj * N + c] = m;
+  }
+  if (a.kk == 0) return;
+  if (a.kk == N) {
+    for (int c = tid; c < N; c += kTopThreads) idx[c] = c;
+    return;
+  }
+  __syncthreads();
+  uint32_t prefix = 0, pmask = 0;
+  int krem = a.kk;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    for (int c = tid; c < N; c += kTopThreads) {
+      const uint32_t key = keys[c];
+      if ((key & pmask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int s = 0;
+      for (int i = 0; i < kTopThreads / 64; ++i) s += hist[i][tid];
+      hist[0][tid] = s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (acc + hist[0][d] >= krem) break;
+        acc += hist[0][d];
+      }
+      sel_sh[0] = static_cast<uint32_t>(d);
+      sel_sh[1] = static_cast<uint32_t>(krem - acc);
+    }
+    __syncthreads();
+    prefix |= sel_sh[0] << shift;
+    pmask |= 255u << shift;
+    krem = static_cast<int>(sel_sh[1]);
+    __syncthreads();
+  }
+  // prefix is the k'-th largest key; krem ties at that key are taken, lowest index first
+  int out_pos = 0, eq_seen = 0;
+  for (int base = 0; base < N; base += kTopThreads) {
+    const int c = base + tid;
+    const uint32_t key = c < N ? keys[c] : 0u;
+    const int is_eq = (c < N && key == prefix) ? 1 : 0;
+    int eq_total;
+    const int eq_rank = block_exclusive_scan(is_eq, scan_sh, &eq_total) + eq_seen;
+    const int take = (c < N && (key > prefix || (is_eq && eq_rank < krem))) ? 1 : 0;
+    int take_total;
+    const int pos = block_exclusive_scan(take, scan_sh, &take_total) + out_pos;
+    if (take && pos < a.kk) idx[pos] = c;
+    eq_seen += eq_total;
+    out_pos += take_total;
+  }
+}
+
+template <typename T, int PASS>
+kvc_status launch_score(const ScoreArgs& a, int KS, dim3 grid, hipStream_t st) {
+  switch (KS) {
+#define KVC_CASE(k)                                                                     \
+  case k:                                                                               \
+    hipLaunchKernelGGL((score_kernel<T, k, PASS>), grid, dim3(kThreads), 0, st, a); \
+    break;
+    KVC_CASE(1) KVC_CASE(2) KVC_CASE(3) KVC_CASE(4) KVC_CASE(5) KVC_CASE(6) KVC_CASE(7) KVC_CASE(8)
+#undef KVC_CASE
+    default: return KVC_ERR_SHAPE;
+  }
+  return check_launch();
+}
+
+template <typename T>
+kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t st) {
+  constexpr int CH = ChunkCols<T>::value;
+  kvc_status s = launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
+  if (s != KVC_OK) return s;
+  hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kThreads - 1) / kThreads, a.Hkv, B), dim3(kThreads), 0, st, a);
+  if ((s = check_launch()) != KVC_OK) return s;
+  s = launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
+  if (s != KVC_OK) return s;
+  hipLaunchKernelGGL(pool_topk_kernel, dim3(a.Hkv, B), dim3(kTopThreads), 0, st, t);
+  return check_launch();
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dtype, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool, int32_t budget,
+                                 int32_t* idx, float* scores, void* ws, size_t* ws_bytes, void* stream) {
+  using namespace kvc;
+  if (!ws_bytes) return KVC_ERR_NULL;
+  if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
+  if (B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || n < 1 || W < 1 || W > n ||
+      pool < 1 || pool % 2 == 0)
+    return KVC_ERR_SHAPE;
+  const int G = Hq / Hkv;
+  const int N = n - W;
+  const int R = G * W;
+  const int CH = dtype == KVC_F32 ? ChunkCols<float>::value : ChunkCols<uint16_t>::value;
+  const int nc1 = (n + CH - 1) / CH;
+  const size_t units = static_cast<size_t>(B) * Hkv;
+  const size_t sz_stats = align_up(units * nc1 * R * sizeof(float2), 256);
+  const size_t sz_row = align_up(units * R * sizeof(float2), 256);
+  const size_t sz_raw = align_up(units * N * sizeof(float), 256);
+  const size_t need = sz_stats + sz_row + 2 * sz_raw;
+  if (!ws) {
+    *ws_bytes = need;
+    return KVC_OK;
+  }
+  const int kk = budget < 0 ? N : std::min(budget, N);
+  if (!q_win || !k || (kk > 0 && !idx)) return KVC_ERR_NULL;
+  if (*ws_bytes < need) return KVC_ERR_WORKSPACE;
+  if (N == 0) return KVC_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  ScoreArgs a;
+  a.q_win = q_win;
+  a.k = k;
+  a.stats = reinterpret_cast<float2*>(w);
+  a.rowstat = reinterpret_cast<float2*>(w + sz_stats);
+  a.raw = reinterpret_cast<float*>(w + sz_stats + sz_row);
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.n = n;
+  a.W = W;
+  a.R = R;
+  a.N = N;
+  a.nc1 = nc1;
+  a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  TopArgs t;
+  t.raw = a.raw;
+  t.keys = reinterpret_cast<uint32_t*>(w + sz_stats + sz_row + sz_raw);
+  t.scores = scores;
+  t.idx = idx;
+  t.Hkv = Hkv;
+  t.N = N;
+  t.kk = kk;
+  t.pool = pool;
+  return dtype == KVC_F32 ? run_select<float>(a, D / 32, B, t, st)
+                          : run_select<uint16_t>(a, D / 32, B, t, st);
+}

@@ -1,0 +1,171 @@
+"""GPU parity of each stage, through the C ABI, against the oracle on the same
+seeded inputs: bit-exact codes, scales, residual and indices; decode outputs
+within 2e-3.  Sizes span several tiles with ragged tails."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import decode as odecode
+from oracle import quant as oquant
+from oracle import select as oselect
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _kvc():
+    gu.need_gpu()
+    import kv_cache_compression_snapkv_amd as kvc
+    return kvc
+
+
+def _case(seed, B, Hkv, n, D, dtype, outliers=True):
+    scale = None
+    if outliers:
+        g = torch.Generator().manual_seed(seed)
+        scale = torch.exp(0.5 * torch.randn(D, generator=g))
+        scale[torch.randperm(D, generator=g)[:2]] *= 8
+    k, v = synth.random_case(seed, B, Hkv, Hkv, D, n, dtype, key_scale=scale)
+    return k.cuda(), v.cuda()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("with_idx", [True, False])
+def test_quantize_parity(dtype, bits, D, with_idx):
+    kvc = _kvc()
+    B, Hkv, n, W, R = 2, 3, 300, 8, 16
+    k, v = _case(1, B, Hkv, n, D, dtype)
+    idx = None
+    k_sel = 0
+    if with_idx:
+        g = torch.Generator().manual_seed(2)
+        k_sel = 100
+        idx = torch.stack([torch.stack([torch.sort(torch.randperm(n - W, generator=g)[:k_sel]).values
+                                        for _ in range(Hkv)]) for _ in range(B)]).to(torch.int32).cuda()
+    T = k_sel + W if with_idx else n
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=T + 64, device="cuda")
+    kvc.kvc_quantize(k, v, cache, idx=idx, W=W)
+    torch.cuda.synchronize()
+    kf, vf = gu.as_f32(k), gu.as_f32(v)
+    for b in range(B):
+        for j in range(Hkv):
+            kept = oquant.kept_positions(n, W, idx[b, j].cpu().numpy() if with_idx else None)
+            ref = oquant.build_head_cache(kf[b, j], vf[b, j], kept, R, bits)
+            gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref, f"b{b} j{j}")
+
+
+@pytest.mark.parametrize("dtype,bits,G,D,R,n", [
+    ("bf16", 2, 4, 128, 16, 300), ("bf16", 4, 1, 128, 16, 300), ("f32", 2, 1, 64, 16, 250),
+    ("bf16", 2, 2, 64, 0, 200), ("bf16", 4, 8, 32, 40, 160), ("f32", 4, 3, 256, 24, 130),
+    ("bf16", 2, 16, 64, 16, 100)])
+def test_decode_parity_multi_step(dtype, bits, G, D, R, n):
+    kvc = _kvc()
+    B, Hkv = 2, 2
+    Hq = Hkv * G
+    steps = 40
+    k, v = _case(3, B, Hkv, n, D, dtype)
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=n + steps + 32, device="cuda")
+    kvc.kvc_quantize(k, v, cache)
+    kf, vf = gu.as_f32(k), gu.as_f32(v)
+    ref = [[oquant.build_head_cache(kf[b, j], vf[b, j], np.arange(n), R, bits) for j in range(Hkv)]
+           for b in range(B)]
+    worst = 0.0
+    flushes = 0
+    for s in range(steps):
+        q = synth.random_tensor(100 + s, (B, Hq, D), dtype, tag="q").cuda()
+        kn = synth.random_tensor(200 + s, (B, Hkv, D), dtype, tag="kn").cuda()
+        vn = synth.random_tensor(300 + s, (B, Hkv, D), dtype, tag="vn").cuda()
+        ql = cache.q_len
+        out = kvc.kvc_decode_attn(cache, q, kn, vn).cpu().numpy()
+        flushes += cache.q_len != ql
+        qf = gu.as_f32(q).astype(np.float64)
+        knb, vnb = gu.bf16_bits(kn), gu.bf16_bits(vn)
+        for b in range(B):
+            o_ref, ref[b] = odecode.decode_step(ref[b], qf[b], knb[b], vnb[b], R, bits)
+            worst = max(worst, gu.assert_decode_close(out[b], o_ref, f"step {s} b{b}"))
+    torch.cuda.synchronize()
+    for b in range(B):
+        for j in range(Hkv):
+            gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[b][j], f"after steps b{b} j{j}")
+    assert flushes >= 1
+
+
+@pytest.mark.parametrize("dtype,B,G,Hkv,n,D,W,pool,budget", [
+    ("bf16", 2, 4, 2, 700, 128, 16, 7, 100), ("f32", 1, 1, 4, 512, 64, 8, 5, 64),
+    ("bf16", 1, 2, 3, 333, 64, 5, 3, 40), ("bf16", 1, 8, 1, 1000, 256, 32, 7, 200),
+    ("f32", 2, 3, 1, 257, 32, 13, 1, 30), ("bf16", 1, 4, 2, 300, 128, 300, 7, 10),
+    ("bf16", 1, 4, 2, 300, 128, 20, 7, 0), ("bf16", 1, 4, 2, 300, 128, 20, 7, 5000),
+    ("bf16", 1, 4, 2, 300, 128, 20, 7, -1), ("bf16", 1, 1, 1, 2000, 128, 150, 9, 333)])
+def test_select_parity(dtype, B, G, Hkv, n, D, W, pool, budget):
+    kvc = _kvc()
+    Hq = G * Hkv
+    k, _ = _case(5, B, Hkv, n, D, dtype)
+    q_win = synth.random_tensor(6, (B, Hq, W, D), dtype, tag="qw").cuda()
+    idx, scores = kvc.kvc_select(q_win, k, W, pool, budget, want_scores=True)
+    torch.cuda.synchronize()
+    N = n - W
+    assert idx.shape == (B, Hkv, N if budget < 0 else min(budget, N))
+    if N == 0:
+        return
+    pooled = oselect.max_pool(oselect.window_scores(gu.as_f32(q_win), gu.as_f32(k), W), pool)
+    sc = scores.cpu().numpy()
+    ix = idx.cpu().numpy()
+    for b in range(B):
+        for j in range(Hkv):
+            gu.check_selection(ix[b, j], sc[b, j], pooled[b, j], budget)
+
+
+def test_select_planted_and_dense_special_case():
+    """Budget >= n-W keeps everything and the step equals dense attention."""
+    kvc = _kvc()
+    B, Hkv, G, n, D, W = 1, 2, 2, 200, 64, 8
+    k, v = _case(9, B, Hkv, n, D, "bf16")
+    q_win = synth.random_tensor(10, (B, Hkv * G, W, D), "bf16", tag="qw").cuda()
+    idx = kvc.kvc_select(q_win, k, W, 5, n)
+    assert torch.equal(idx[0, 0].cpu(), torch.arange(n - W, dtype=torch.int32))
+    cache = kvc.Cache(B, Hkv, D, 2, residual=n + 1, q_cap=32, r_cap=n + 64, device="cuda")
+    kvc.kvc_quantize(k, v, cache, idx=idx, W=W)
+    assert cache.q_len == 0 and cache.r_len == n
+    q = synth.random_tensor(11, (B, Hkv * G, D), "bf16", tag="q").cuda()
+    kn = synth.random_tensor(12, (B, Hkv, D), "bf16", tag="kn").cuda()
+    vn = synth.random_tensor(13, (B, Hkv, D), "bf16", tag="vn").cuda()
+    out = kvc.kvc_decode_attn(cache, q, kn, vn).cpu().numpy()
+    K = torch.cat([k, kn[:, :, None]], 2).double().cpu().repeat_interleave(G, 1)
+    V = torch.cat([v, vn[:, :, None]], 2).double().cpu().repeat_interleave(G, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q.double().cpu()[:, :, None], K, V)[:, :, 0]
+    gu.assert_decode_close(out[0], ref[0].numpy(), "dense")
+
+
+def test_tiny_config_end_to_end():
+    """The tiny workload through all stages, stage-wise and end to end."""
+    kvc = _kvc()
+    cfg = synth.CONFIGS["tiny"]
+    p = synth.prompt_layer(cfg, 0, "cpu")
+    d = synth.decode_inputs(cfg, 0, 0, "cpu")
+    q_win, k, v = p["q_win"].cuda(), p["k"].cuda(), p["v"].cuda()
+    idx, scores = kvc.kvc_select(q_win, k, cfg.window, cfg.pool, cfg.budget, want_scores=True)
+    bits = cfg.bits[0]
+    T = cfg.budget + cfg.window
+    cache = kvc.Cache(cfg.batch, cfg.kv_heads, cfg.head_dim, bits, cfg.residual, q_cap=T + 32, device="cuda")
+    kvc.kvc_quantize(k, v, cache, idx=idx, W=cfg.window)
+    out = kvc.kvc_decode_attn(cache, d["q"].cuda(), d["k_new"].cuda(), d["v_new"].cuda()).cpu().numpy()
+    assert (cache.q_len, cache.r_len) == (32, 41)
+    qw, kf, vf = gu.as_f32(p["q_win"]), gu.as_f32(p["k"]), gu.as_f32(p["v"])
+    oidx, pooled = oselect.select(qw, kf, cfg.window, cfg.pool, cfg.budget)
+    swaps = gu.check_selection(idx[0, 0].cpu().numpy(), scores[0, 0].cpu().numpy(), pooled[0, 0], cfg.budget)
+    for j in range(1, cfg.kv_heads):
+        swaps += gu.check_selection(idx[0, j].cpu().numpy(), scores[0, j].cpu().numpy(), pooled[0, j], cfg.budget)
+    assert swaps == 0
+    n, W = cfg.prompt, cfg.window
+    ref = [oquant.build_head_cache(kf[0, j], vf[0, j], oquant.kept_positions(n, W, oidx[0, j]),
+                                   cfg.residual, bits) for j in range(cfg.kv_heads)]
+    qf = gu.as_f32(d["q"]).astype(np.float64)
+    o_ref, ref = odecode.decode_step(ref, qf[0], gu.bf16_bits(d["k_new"])[0], gu.bf16_bits(d["v_new"])[0],
+                                     cfg.residual, bits)
+    for j in range(cfg.kv_heads):
+        gu.assert_cache_equal(gu.gpu_head_cache(cache, 0, j), ref[j], f"j{j}")
+    gu.assert_decode_close(out[0], o_ref, "tiny end-to-end")
