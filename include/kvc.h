@@ -45,7 +45,11 @@
  *                                       token (32/bits)*w+i at bits bits*i
  *   v_meta  [B][Hkv][q_cap][D/32]       uint32: token t, channels 32j..32j+31
  *   meta word = fp16 scale bits | (fp16 zero-point bits << 16)
- *   k_res, v_res [B][Hkv][r_cap][D]     uint16 bfloat16 bits, oldest first
+ *   k_res [B][Hkv][r_cap][D]            uint16 bfloat16 keys, token-major,
+ *                                       oldest first
+ *   v_res [B][Hkv][D][r_cap]            uint16 bfloat16 values, channel-major
+ *                                       (a decode step reads 8 consecutive
+ *                                       tokens of one channel per load)
  * Codes are LSB-first (MiniKV Sec. 4.4: 16 INT2 values shifted into one INT32).
  * Dequantized value = zero + code * scale.
  */
@@ -80,7 +84,8 @@ typedef struct {
   int32_t bits;                      /* 2 or 4; group size is fixed at 32      */
   int32_t residual;                  /* R: recent tokens kept in bf16          */
   int32_t q_cap, q_len;              /* packed history, tokens (multiples of 32)*/
-  int32_t r_cap, r_len;              /* bf16 residual, tokens; r_cap >= R + 32 */
+  int32_t r_cap, r_len;              /* bf16 residual, tokens; r_cap >= R + 32,
+                                        r_cap a multiple of 8                  */
   uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;
 } kvc_cache;

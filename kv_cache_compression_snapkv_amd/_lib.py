@@ -150,6 +150,7 @@ class Cache:
     def __init__(self, batch, kv_heads, head_dim, bits, residual, q_cap, r_cap=None, device="cuda"):
         if r_cap is None:
             r_cap = residual + 32
+        r_cap = 8 * ((r_cap + 7) // 8)
         q_cap = 32 * ((q_cap + 31) // 32)
         sizes = (ctypes.c_size_t * 6)()
         _check("kvc_cache_sizes", lib.kvc_cache_sizes(batch, kv_heads, head_dim, bits, q_cap, r_cap, sizes))
@@ -187,7 +188,7 @@ class Cache:
             "v_codes": self.v_codes.view(B, H, qc * b // 32, D)[:, :, : s.q_len * b // 32],
             "v_meta": self.v_meta.view(B, H, qc, D // 32)[:, :, : s.q_len],
             "k_res": self.k_res.view(B, H, rc, D)[:, :, : s.r_len],
-            "v_res": self.v_res.view(B, H, rc, D)[:, :, : s.r_len],
+            "v_res": self.v_res.view(B, H, D, rc)[:, :, :, : s.r_len].transpose(-1, -2),
         }
 
 
@@ -213,7 +214,7 @@ def kvc_decode_attn(cache, q, k_new, v_new, out=None, ws=None, stream=None):
     B, Hq, D = q.shape
     if ws is None:
         if cache._ws is None:
-            cache._ws = torch.empty(decode_ws_bytes(cache, Hq), dtype=torch.uint8, device=q.device)
+            cache._ws = torch.zeros(decode_ws_bytes(cache, Hq), dtype=torch.uint8, device=q.device)
         ws = cache._ws
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)

@@ -140,14 +140,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     // residual: kept tokens [Q, T) -> bf16 rows 0..T-Q-1
     const int r0 = (blk - nqb) * kGroup;
     const int nr = min(kGroup, a.T - a.Q - r0);
-    uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;
-    uint16_t* vr = a.v_res + static_cast<size_t>(bj) * a.r_cap * D;
+    uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
+    uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
     for (int e = tid; e < nr * D; e += kThreads) {
       const int t = e / D, c = e % D;
       const size_t src = static_cast<size_t>(kept_pos(a, bj, a.Q + r0 + t)) * D + c;
-      const size_t dst = static_cast<size_t>(r0 + t) * D + c;
-      kr[dst] = f32_to_bf16(load_f32(k, src));
-      vr[dst] = f32_to_bf16(load_f32(v, src));
+      kr[static_cast<size_t>(r0 + t) * D + c] = f32_to_bf16(load_f32(k, src));
+    }
+    // values are channel-major: consecutive threads take consecutive tokens
+    for (int e = tid; e < nr * D; e += kThreads) {
+      const int c = e / nr, t = e % nr;
+      const size_t src = static_cast<size_t>(kept_pos(a, bj, a.Q + r0 + t)) * D + c;
+      vr[static_cast<size_t>(c) * a.r_cap + r0 + t] = f32_to_bf16(load_f32(v, src));
     }
   }
 }
@@ -173,20 +177,15 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   const int tid = threadIdx.x;
   const T* kn = static_cast<const T*>(a.k_new) + static_cast<size_t>(bj) * D;
   const T* vn = static_cast<const T*>(a.v_new) + static_cast<size_t>(bj) * D;
-  uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;
-  uint16_t* vr = a.v_res + static_cast<size_t>(bj) * a.r_cap * D;
+  uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
+  uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
   for (int e = tid; e < kGroup * D; e += kThreads) {
-    const int t = e / D, c = e % D;
-    uint16_t kb, vb;
-    if (t < a.r_old) {
-      kb = kr[static_cast<size_t>(t) * D + c];
-      vb = vr[static_cast<size_t>(t) * D + c];
-    } else {
-      kb = f32_to_bf16(load_f32(kn, c));
-      vb = f32_to_bf16(load_f32(vn, c));
-    }
+    const int t = e / D, c = e % D;  // keys: token-major
+    const uint16_t kb = t < a.r_old ? kr[static_cast<size_t>(t) * D + c] : f32_to_bf16(load_f32(kn, c));
     L.k[t][c] = bf16_to_f32(kb);
-    L.v[t][c] = bf16_to_f32(vb);
+    const int cv = e / kGroup, tv = e % kGroup;  // values: channel-major
+    const uint16_t vb = tv < a.r_old ? vr[static_cast<size_t>(cv) * a.r_cap + tv] : f32_to_bf16(load_f32(vn, cv));
+    L.v[tv][cv] = bf16_to_f32(vb);
   }
   __syncthreads();
   const size_t qc = a.q_cap;
@@ -194,25 +193,21 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
                        a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D,
                        a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
                        a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
-  // shift rows [32, R+32) -> [0, R) in chunks of 8 rows; each chunk is read in
-  // full before it is written, and a chunk only overwrites rows already read.
-  constexpr int kRows = 8;
-  constexpr int kPer = kRows * kMaxD / kThreads;
-  for (int r0 = 0; r0 < a.R; r0 += kRows) {
-    const int nr = min(kRows, a.R - r0);
+  // shift tokens [32, R+32) -> [0, R) in chunks of 32 tokens: each chunk is read
+  // in full before it is written, and it overwrites only the previous chunk's
+  // (already read) source tokens.  Token r_old is the appended one.
+  constexpr int kPer = kGroup * kMaxD / kThreads;
+  for (int r0 = 0; r0 < a.R; r0 += kGroup) {
+    const int nr = min(kGroup, a.R - r0);
     uint16_t kb[kPer], vb[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = tid + u * kThreads;
       if (e < nr * D) {
-        const int t = r0 + e / D + kGroup, c = e % D;
-        if (t < a.r_old) {
-          kb[u] = kr[static_cast<size_t>(t) * D + c];
-          vb[u] = vr[static_cast<size_t>(t) * D + c];
-        } else {
-          kb[u] = f32_to_bf16(load_f32(kn, c));
-          vb[u] = f32_to_bf16(load_f32(vn, c));
-        }
+        const int t = r0 + e / D + kGroup, c = e % D;  // keys: token-major
+        kb[u] = t < a.r_old ? kr[static_cast<size_t>(t) * D + c] : f32_to_bf16(load_f32(kn, c));
+        const int cv = e / nr, tv = r0 + e % nr + kGroup;  // values: channel-major
+        vb[u] = tv < a.r_old ? vr[static_cast<size_t>(cv) * a.r_cap + tv] : f32_to_bf16(load_f32(vn, cv));
       }
     }
     __syncthreads();
@@ -220,9 +215,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     for (int u = 0; u < kPer; ++u) {
       const int e = tid + u * kThreads;
       if (e < nr * D) {
-        const size_t dst = static_cast<size_t>(r0 + e / D) * D + e % D;
-        kr[dst] = kb[u];
-        vr[dst] = vb[u];
+        kr[static_cast<size_t>(r0 + e / D) * D + e % D] = kb[u];
+        vr[static_cast<size_t>(e / nr) * a.r_cap + r0 + e % nr] = vb[u];
       }
     }
     __syncthreads();
@@ -283,7 +277,7 @@ bool cache_ok(const kvc_cache* c) {
 kvc_status cache_shape_status(const kvc_cache* c) {
   if (c->bits != 2 && c->bits != 4) return KVC_ERR_BITS;
   if (c->batch < 1 || c->kv_heads < 1 || !head_dim_ok(c->head_dim) || c->residual < 0 ||
-      c->q_cap < 0 || c->q_cap % kGroup != 0 || c->r_cap < 0 || c->q_len < 0 || c->r_len < 0 ||
+      c->q_cap < 0 || c->q_cap % kGroup != 0 || c->r_cap < 0 || c->r_cap % 8 != 0 || c->q_len < 0 || c->r_len < 0 ||
       c->q_len % kGroup != 0)
     return KVC_ERR_SHAPE;
   if (c->q_len > c->q_cap || c->r_len > c->r_cap || c->r_cap < c->residual + kGroup)

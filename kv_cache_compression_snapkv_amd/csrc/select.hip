@@ -227,12 +227,23 @@ __global__ __launch_bounds__(kThreads) void rowstat_kernel(ScoreArgs a) {
   const int j = blockIdx.y, b = blockIdx.z;
   if (r >= a.R) return;
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
-  float M = -INFINITY;
-  for (int c = 0; c < a.nc1; ++c) M = fmaxf(M, a.stats[(bj * a.nc1 + c) * a.R + r].x);
-  float L = 0.0f;
-  for (int c = 0; c < a.nc1; ++c) {
-    const float2 ml = a.stats[(bj * a.nc1 + c) * a.R + r];
-    if (ml.x != -INFINITY) L += ml.y * exp2f(ml.x - M);
+  const float2* st = a.stats + bj * a.nc1 * a.R + r;
+  // online (max, sum) merge; blocks of 8 independent loads keep them in flight
+  float M = -INFINITY, L = 0.0f;
+  for (int c0 = 0; c0 < a.nc1; c0 += 8) {
+    float2 ml[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      ml[u] = (c0 + u < a.nc1) ? st[static_cast<size_t>(c0 + u) * a.R] : make_float2(-INFINITY, 0.0f);
+    float m8 = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m8 = fmaxf(m8, ml[u].x);
+    if (m8 == -INFINITY) continue;
+    L = (M == -INFINITY) ? 0.0f : L * exp2f(M - m8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (ml[u].x != -INFINITY) L += ml[u].y * exp2f(ml[u].x - m8);
+    M = m8;
   }
   a.rowstat[bj * a.R + r] = make_float2(M, 1.0f / L);
 }

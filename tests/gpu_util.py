@@ -29,11 +29,11 @@ def bf16_bits(t):
 
 
 def u32(t):
-    return t.detach().cpu().numpy().view(np.uint32)
+    return t.detach().contiguous().cpu().numpy().view(np.uint32)
 
 
 def u16(t):
-    return t.detach().cpu().numpy().view(np.uint16)
+    return t.detach().contiguous().cpu().numpy().view(np.uint16)
 
 
 def gpu_head_cache(cache, b, j):

@@ -116,8 +116,9 @@ def test_quantize_and_decode_validation():
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(q_len=32)), None) == 5    # not empty
     assert q(P, P, 1, 200, None, 0, 0, ctypes.byref(_cache()), None) == 5           # Q > q_cap
     assert q(P, P, 1, 64, P, 100, 8, ctypes.byref(_cache()), None) == 2             # k_sel > n-W
-    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_cap=20)), None) == 5    # r_cap < R+32
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_cap=24)), None) == 5    # r_cap < R+32
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(q_cap=40)), None) == 2    # q_cap % 32
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_cap=52)), None) == 2    # r_cap % 8
     d = L.lib.kvc_decode_attn
     need = ctypes.c_size_t(0)
     assert d(ctypes.byref(_cache()), None, None, None, 1, 4, None, None, ctypes.byref(need), None) == 0
