@@ -5,11 +5,15 @@ for every layer, kvc_select (window scorer + pool + top-k) and kvc_quantize
 (prompt compression), then `decode_steps` decode steps, each running
 kvc_decode_attn (append, flush, attention) on every layer.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--bits B]
+                    [--no-cpu-baseline] [--no-hbm-stress]
 
 Prints one JSON line.  value = decode-attention tokens/s (batch * decode steps /
 time of the decode part); the selection+quantization time per prompt is
 reported beside it.  Inputs are generated on the GPU before timing (seeded).
+By default the line also carries `hbm_stress`: the decode-only, no-eviction
+Llama-2-13B-shaped case (40 layers x 0.5 GB of packed cache per step), the one
+large enough to be bound by HBM rather than by launch latency.
 """
 
 import argparse
@@ -32,6 +36,9 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--bits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-stress", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches (for counter collection)")
+    ap.add_argument("--layers", type=int, default=None, help="run only the first N layers")
     return ap.parse_args()
 
 
@@ -97,24 +104,20 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=20.0):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by (batch, KV head); see DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
+def run(cfg, bits, steps, warmup, graph=True, layers=None):
+    """Time `steps` graph-replayed steps of the whole path on one workload."""
     import torch
 
     import kv_cache_compression_snapkv_amd as kvc
     import synth
 
-    cfg = synth.CONFIGS[args.workload]
-    bits = args.bits or cfg.bits[0]
     dev = "cuda"
     L, B, Hq, Hkv, D, n, W = cfg.layers, cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.prompt, cfg.window
     budgets, fp = kvc.kvc_budget(L, Hkv, D, n, W, cfg.decode_steps, cfg.budget, cfg.pyramid, cfg.beta,
                                  bits=bits, group=32, meta_bits=16, residual=cfg.residual)
     in_bytes = 4 if cfg.dtype == "f32" else 2
+    if layers is not None:
+        L = min(L, layers)
 
     # inputs resident in HBM before timing
     prompts = [synth.prompt_layer(cfg, l, dev) for l in range(L)]
@@ -152,73 +155,103 @@ def main():
     # eager pass, then capture one step into two HIP graphs (prompt compression;
     # all decode steps of all layers) so the timed replays run without host gaps
     prefill()
-    decode_all()
-    torch.cuda.synchronize()
-    g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_pre):
-        prefill()
     call_bytes = []
-    with torch.cuda.graph(g_dec):
-        decode_all(call_bytes)
+    decode_all(call_bytes)
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        g_pre.replay()
-        g_dec.replay()
+    if graph:
+        g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pre):
+            prefill()
+        with torch.cuda.graph(g_dec):
+            decode_all()
+        torch.cuda.synchronize()
+        run_pre, run_dec = g_pre.replay, g_dec.replay
+    else:
+        g_pre = g_dec = None
+        run_pre, run_dec = prefill, decode_all
+    for _ in range(warmup):
+        run_pre()
+        run_dec()
     torch.cuda.synchronize()
     recs = []
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record(stream)
-        g_pre.replay()
+        run_pre()
         e1.record(stream)
-        g_dec.replay()
+        run_dec()
         e2.record(stream)
         recs.append((e0, e1, e2))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    pre_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in recs) / args.steps
-    dec_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in recs) / args.steps
-    step_ms = sum(e0.elapsed_time(e2) for e0, _, e2 in recs) / args.steps
+    pre_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in recs) / steps
+    dec_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in recs) / steps
+    step_ms = sum(e0.elapsed_time(e2) for e0, _, e2 in recs) / steps
     ncalls = len(call_bytes)
-    call_ms = dec_ms / ncalls
     achieved = sum(call_bytes) / (dec_ms * 1e-3) / 1e9
-    tokens_per_s = B * cfg.decode_steps / (dec_ms * 1e-3)
+    desc = (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
+            f"prompt {n}, {cfg.dtype} inputs, W={W}, pool {cfg.pool}, budget "
+            f"{'all' if cfg.budget < 0 else ('pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
+            f"{bits}-bit g32 fp16 scale/zero, residual {cfg.residual}, {cfg.decode_steps} decode steps")
+    res = {
+        "desc": desc, "budgets": budgets, "footprint": fp,
+        "tokens_per_s": B * cfg.decode_steps / (dec_ms * 1e-3),
+        "step_ms": step_ms, "pre_ms": pre_ms, "dec_ms": dec_ms, "wall": wall,
+        "roofline": {
+            "kernel": "decode_kernel (+ merge_kernel; flush_kernel on 1 step in 32), per kvc_decode_attn call",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "avg_call_us": dec_ms * 1e3 / ncalls, "algorithmic_bytes_per_call": sum(call_bytes) / ncalls,
+        },
+    }
+    del prompts, dec, caches, idxs, sel_ws, dec_ws, g_pre, g_dec
+    torch.cuda.empty_cache()
+    return res
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (batch, KV head); see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    bits = args.bits or cfg.bits[0]
+    r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers)
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s (% peak); select+quantize ms/prompt",
-        "value": tokens_per_s,
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_ms,
+        "ms_per_step": r["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
-                         f"prompt {n}, {cfg.dtype} inputs, W={W}, pool {cfg.pool}, budget "
-                         f"{'all' if cfg.budget < 0 else ('pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
-                         f"{bits}-bit g32 fp16 scale/zero, residual {cfg.residual}, {cfg.decode_steps} decode steps"),
-            "batch": B, "prompt": n, "layers": L, "bits": bits, "decode_steps": cfg.decode_steps,
-        },
-        "select_quantize_ms_per_prompt": pre_ms / B,
-        "decode_ms_per_token_all_layers": dec_ms / cfg.decode_steps,
-        "decode_hbm_GBs": achieved,
-        "roofline": {
-            "kernel": "kvc_decode_attn (decode_kernel; flush kernel on 1 step in 32), graph-replayed",
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "avg_call_us": call_ms * 1e3, "algorithmic_bytes_per_call": sum(call_bytes) / ncalls,
-        },
-        "wall_s_timed": wall,
-        "footprint_bytes_per_prompt_token": fp["bytes_per_prompt_token"],
+        "config": {"workload": r["desc"], "batch": cfg.batch, "prompt": cfg.prompt, "layers": cfg.layers,
+                   "bits": bits, "decode_steps": cfg.decode_steps},
+        "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
+        "decode_ms_per_token_all_layers": r["dec_ms"] / cfg.decode_steps,
+        "decode_hbm_GBs": r["roofline"]["achieved"],
+        "roofline": r["roofline"],
+        "wall_s_timed": r["wall"],
+        "footprint_bytes_per_prompt_token": r["footprint"]["bytes_per_prompt_token"],
     }
+    if not args.no_hbm_stress and args.workload != "llama2_13b_mha":
+        # the HBM-bound decode case: no eviction, full 32k cache of 40 layers
+        hc = synth.CONFIGS["llama2_13b_mha"]
+        h = run(hc, 2, 2, 1)
+        res["hbm_stress"] = {"workload": h["desc"], "decode_tokens_per_s": h["tokens_per_s"],
+                             "quantize_ms_per_prompt": h["pre_ms"] / hc.batch, "steps": 2, "warmup": 1,
+                             "roofline": h["roofline"]}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, bits, budgets)
+        res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"])
     print(json.dumps(res))
 
 

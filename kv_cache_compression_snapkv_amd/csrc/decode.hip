@@ -41,7 +41,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kHB = 8;              // query heads per head block (2 MFMA rows each)
-constexpr int kTargetWaves = 2048;  // split-planning target (8 waves per CU)
+constexpr int kPrefetch = 2;        // history tiles in flight per wave
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -159,14 +159,23 @@ __device__ __forceinline__ uint32_t load_bf16_pair(const T* p, int i) {
          (static_cast<uint32_t>(f32_to_bf16(load_f32(p, i + 1))) << 16);
 }
 
+// All-reduce over the 16 lanes of a DPP row: swap neighbours, swap pairs,
+// mirror within 8, mirror within 16.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float max16(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp<0x140>(x));  // row_mirror
   return x;
 }
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
   return x;
 }
 __device__ __forceinline__ void wave_sync() {
@@ -176,7 +185,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 template <typename T, int BITS, int KS>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode_kernel(DecArgs a) {
   constexpr int D = 32 * KS;
   constexpr int NGV = KS;  // value channel groups
   constexpr int NW = D * BITS / 32;  // key words per token
@@ -246,21 +255,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
   // lane l owns positions l + 64u and loops over the heads, so its meta loads do
   // not depend on the head and can be issued a tile ahead.
   constexpr int NP = (D / 2 + 63) / 64;
+  constexpr int NKW = (BITS == 2) ? KS / 2 + (KS & 1) : KS;  // key words a lane reads per token
   struct HistRegs {
-    uint32_t kw[2][KS];  // key code words, per column tile and k-step
+    uint32_t kw[2][NKW];  // key code words, per column tile
     uint32_t km[NP][2];  // key meta of the lane's channel pairs
     uint32_t vm[NP][2];  // value meta of the lane's token pairs
     u32x2 vw[NGV];       // value code words, per channel group
   };
   auto load_hist = [&](int tile, HistRegs& r) {
     const int t0 = tile * kGroup;
+    const int w_first = (BITS == 2) ? ((lq * KS) >> 1) : lq * KS;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const uint32_t* row = kc + static_cast<size_t>(t0 + col_token(ct, ln)) * NW;
+      const uint32_t* row = kc + (t0 + col_token(ct, ln)) * NW + w_first;
+      if constexpr (NKW == 4) {
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(row);
+        r.kw[ct][0] = w4.x; r.kw[ct][1] = w4.y; r.kw[ct][2] = w4.z; r.kw[ct][3] = w4.w;
+      } else if constexpr (NKW == 2) {
+        const u32x2 w2 = *reinterpret_cast<const u32x2*>(row);
+        r.kw[ct][0] = w2.x; r.kw[ct][1] = w2.y;
+      } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) r.kw[ct][s] = (BITS == 2) ? row[(lq * KS + s) >> 1] : row[lq * KS + s];
+        for (int i = 0; i < NKW; ++i) r.kw[ct][i] = (w_first + i < NW) ? row[i] : 0u;
+      }
     }
-    const uint32_t* kmg = km + static_cast<size_t>(tile) * D;
+    const uint32_t* kmg = km + tile * D;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int pi = lane + 64 * u;
@@ -270,125 +289,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         r.km[u][0] = kmg[key_channel<BITS, KS>(s, q4, jj, 0)];
         r.km[u][1] = kmg[key_channel<BITS, KS>(s, q4, jj, 1)];
         const int g = pi >> 4, pr = pi & 15;
-        r.vm[u][0] = vm[static_cast<size_t>(t0 + value_token<BITS>(pr >> 2, pr & 3, 0)) * NGV + g];
-        r.vm[u][1] = vm[static_cast<size_t>(t0 + value_token<BITS>(pr >> 2, pr & 3, 1)) * NGV + g];
+        r.vm[u][0] = vm[(t0 + value_token<BITS>(pr >> 2, pr & 3, 0)) * NGV + g];
+        r.vm[u][1] = vm[(t0 + value_token<BITS>(pr >> 2, pr & 3, 1)) * NGV + g];
       }
     }
     const int wrow = (BITS == 2) ? (t0 / 16 + (lq >> 1)) : (t0 / 8 + lq);
-    const uint32_t* vrow = vc + static_cast<size_t>(wrow) * D;
+    const uint32_t* vrow = vc + wrow * D;
 #pragma unroll
     for (int g = 0; g < NGV; ++g) r.vw[g] = *reinterpret_cast<const u32x2*>(vrow + 32 * g + 2 * ln);
   };
 
-  HistRegs cur, nxt;
-  const int th_end = min(te, NTh);  // this wave's history tiles are [tb, th_end)
-  if (tb < th_end) load_hist(tb, cur);  // in flight while the block finishes its setup
-  __syncthreads();
-
-  for (int tile = tb; tile < te; ++tile) {
-    const bool hist = tile < NTh;
-    const int t0 = hist ? tile * kGroup : (tile - NTh) * kGroup;
-    f32x4 accS[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    f32x4 accC = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (hist) {
-      if (tile + 1 < th_end) load_hist(tile + 1, nxt);
-      // ---- key operand A (query x group scale) and split(query x zero-point)
-#pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        const int pi = lane + 64 * u;
-        if (pi < D / 2) {
-          const int s = pi >> 4, q4 = (pi >> 2) & 3, jj = pi & 3;
-          const int c0 = key_channel<BITS, KS>(s, q4, jj, 0), c1 = key_channel<BITS, KS>(s, q4, jj, 1);
-          const float sc0 = f16_bits_to_f32(cur.km[u][0] & 0xFFFFu), sc1 = f16_bits_to_f32(cur.km[u][1] & 0xFFFFu);
-          const float zp0 = f16_bits_to_f32(cur.km[u][0] >> 16), zp1 = f16_bits_to_f32(cur.km[u][1] >> 16);
-          const int ob = s * R2 * 32 + 8 * q4 + 2 * jj;
-#pragma unroll
-          for (int h = 0; h < kHB; ++h) {
-            if (h < Gb) {
-              const Split a0 = split2(qx[h * D + c0] * sc0), a1 = split2(qx[h * D + c1] * sc1);
-              const Split z0 = split2(qf[h * D + c0] * zp0), z1 = split2(qf[h * D + c1] * zp1);
-              const int o_hi = ob + 64 * h, o_lo = o_hi + 32;
-              *reinterpret_cast<uint32_t*>(AK + o_hi) = a0.hi | (a1.hi << 16);
-              *reinterpret_cast<uint32_t*>(AK + o_lo) = a0.lo | (a1.lo << 16);
-              *reinterpret_cast<uint32_t*>(AKz + o_hi) = z0.hi | (z1.hi << 16);
-              *reinterpret_cast<uint32_t*>(AKz + o_lo) = z0.lo | (z1.lo << 16);
-            }
-          }
-        }
-      }
-      wave_sync();
-      // ---- key MFMAs: two 16-token column tiles, then offset/zero corrections
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AK + (s * R2 + ln) * 32 + 8 * lq) : zero4;
-        const u32x4 az = row_on ? *reinterpret_cast<const u32x4*>(AKz + (s * R2 + ln) * 32 + 8 * lq) : zero4;
-        const int half = BITS == 2 ? ((lq * KS + s) & 1) : 0;
-        accS[0] = mfma(af, unpack4<BITS>(cur.kw[0][s], half), accS[0]);
-        accS[1] = mfma(af, unpack4<BITS>(cur.kw[1][s], half), accS[1]);
-        accC = mfma(af, neg4, accC);
-        accC = mfma(az, ones4, accC);
-      }
-    } else {
-      // residual keys: bf16 rows as stored (appended token from the input)
-      const bool has_new = a.r_new >= t0 && a.r_new < t0 + kGroup;
-      u32x4 knew[KS];
-      if (has_new) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int c = 32 * s + 8 * lq;
-          knew[s].x = load_bf16_pair(knp, c);
-          knew[s].y = load_bf16_pair(knp, c + 2);
-          knew[s].z = load_bf16_pair(knp, c + 4);
-          knew[s].w = load_bf16_pair(knp, c + 6);
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int t = t0 + col_token(ct, ln);
-        const int tc = min(t, a.r_total - 1);
-        u32x4 kb[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          kb[s] = *reinterpret_cast<const u32x4*>(kr + static_cast<size_t>(tc) * D + 32 * s + 8 * lq);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          u32x4 bf = (t < a.r_total) ? kb[s] : zero4;
-          if (has_new && t == a.r_new) bf = knew[s];
-          const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(ares + (s * R2 + ln) * 32 + 8 * lq) : zero4;
-          accS[ct] = mfma(af, bf, accS[ct]);
-        }
-      }
-    }
-
-    // ---- scores and the online softmax (lane holds heads 2lq, 2lq+1)
-    float p[2][2];
+  // ---- the online softmax update shared by both tile kinds.  x[hh][ct] are
+  // log2-scaled scores (-inf when masked); returns p in place and rescales the
+  // accumulators when a running max moves (skipped when no lane's moves, which
+  // leaves the result bit-identical).
+  auto softmax_update = [&](float (&x)[2][2]) {
     float alpha[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int head = 2 * lq + hh;
-      float x[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        float v = accS[ct][2 * hh] + accS[ct][2 * hh + 1];
-        if (hist) v += accC[2 * hh] + accC[2 * hh + 1];
-        const bool ok = head < Gb && (hist || t0 + col_token(ct, ln) < a.r_total);
-        x[ct] = ok ? v * a.scale2 : -INFINITY;
-      }
-      const float mt = max16(fmaxf(x[0], x[1]));
+      const float mt = max16(fmaxf(x[hh][0], x[hh][1]));
       const float mnew = fmaxf(m_run[hh], mt);
       if (mnew == -INFINITY) {
         alpha[hh] = 1.0f;
-        p[hh][0] = p[hh][1] = 0.0f;
+        x[hh][0] = x[hh][1] = 0.0f;
       } else {
         alpha[hh] = exp2f(m_run[hh] - mnew);
-        p[hh][0] = exp2f(x[0] - mnew);
-        p[hh][1] = exp2f(x[1] - mnew);
+        x[hh][0] = exp2f(x[hh][0] - mnew);
+        x[hh][1] = exp2f(x[hh][1] - mnew);
       }
       m_run[hh] = mnew;
-      l_part[hh] = l_part[hh] * alpha[hh] + p[hh][0] + p[hh][1];
+      l_part[hh] = l_part[hh] * alpha[hh] + x[hh][0] + x[hh][1];
+      const int head = 2 * lq + hh;
       if (head < Gb) {
-        pbuf[head * 32 + col_token(0, ln)] = p[hh][0];
-        pbuf[head * 32 + col_token(1, ln)] = p[hh][1];
+        pbuf[head * 32 + col_token(0, ln)] = x[hh][0];
+        pbuf[head * 32 + col_token(1, ln)] = x[hh][1];
       }
     }
     if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
@@ -408,88 +342,192 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
       }
     }
     wave_sync();
+  };
 
-    if (hist) {
-      // ---- value operand A (p x token scale per group) and split(p x zero-point)
+  // ---- one packed-history tile from its prefetched registers
+  auto process_hist = [&](const HistRegs& cur, int tile) {
+    // key operand A (query x group scale) and split(query x zero-point)
 #pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        const int vi = lane + 64 * u;
-        if (vi < D / 2) {
-          const int g = vi >> 4, pr = vi & 15, jj = pr & 3;
-          const int t_lo = value_token<BITS>(pr >> 2, jj, 0), t_hi = value_token<BITS>(pr >> 2, jj, 1);
-          const float f = static_cast<float>(1 << (7 - code_pos<BITS>(jj)));
-          const float sc0 = f16_bits_to_f32(cur.vm[u][0] & 0xFFFFu) * f;
-          const float sc1 = f16_bits_to_f32(cur.vm[u][1] & 0xFFFFu) * f;
-          const float zp0 = f16_bits_to_f32(cur.vm[u][0] >> 16), zp1 = f16_bits_to_f32(cur.vm[u][1] >> 16);
-          const int ob = g * R2 * 32 + 2 * pr;
-#pragma unroll
-          for (int h = 0; h < kHB; ++h) {
-            if (h < Gb) {
-              const float p0 = pbuf[h * 32 + t_lo], p1 = pbuf[h * 32 + t_hi];
-              const Split a0 = split2(p0 * sc0), a1 = split2(p1 * sc1);
-              const Split z0 = split2(p0 * zp0), z1 = split2(p1 * zp1);
-              const int o_hi = ob + 64 * h, o_lo = o_hi + 32;
-              *reinterpret_cast<uint32_t*>(AV + o_hi) = a0.hi | (a1.hi << 16);
-              *reinterpret_cast<uint32_t*>(AV + o_lo) = a0.lo | (a1.lo << 16);
-              *reinterpret_cast<uint32_t*>(AVz + o_hi) = z0.hi | (z1.hi << 16);
-              *reinterpret_cast<uint32_t*>(AVz + o_lo) = z0.lo | (z1.lo << 16);
-            }
-          }
+    for (int u = 0; u < NP; ++u) {
+      const int pi = lane + 64 * u;
+      if (pi < D / 2) {
+        const int s = pi >> 4, q4 = (pi >> 2) & 3, jj = pi & 3;
+        const int c0 = key_channel<BITS, KS>(s, q4, jj, 0), c1 = key_channel<BITS, KS>(s, q4, jj, 1);
+        const float sc0 = f16_bits_to_f32(cur.km[u][0] & 0xFFFFu), sc1 = f16_bits_to_f32(cur.km[u][1] & 0xFFFFu);
+        const float zp0 = f16_bits_to_f32(cur.km[u][0] >> 16), zp1 = f16_bits_to_f32(cur.km[u][1] >> 16);
+        const int ob = s * R2 * 32 + 8 * q4 + 2 * jj;
+#pragma unroll 1
+        for (int h = 0; h < Gb; ++h) {
+          const Split a0 = split2(qx[h * D + c0] * sc0), a1 = split2(qx[h * D + c1] * sc1);
+          const Split z0 = split2(qf[h * D + c0] * zp0), z1 = split2(qf[h * D + c1] * zp1);
+          const int o_hi = ob + 64 * h, o_lo = o_hi + 32;
+          *reinterpret_cast<uint32_t*>(AK + o_hi) = a0.hi | (a1.hi << 16);
+          *reinterpret_cast<uint32_t*>(AK + o_lo) = a0.lo | (a1.lo << 16);
+          *reinterpret_cast<uint32_t*>(AKz + o_hi) = z0.hi | (z1.hi << 16);
+          *reinterpret_cast<uint32_t*>(AKz + o_lo) = z0.lo | (z1.lo << 16);
         }
       }
-      wave_sync();
-      const int half = (BITS == 2) ? (lq & 1) : 0;
+    }
+    wave_sync();
+    // key MFMAs: two 16-token column tiles, then the offset/zero corrections
+    f32x4 accS[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 accC = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < NGV; ++g) {
-        const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AV + (g * R2 + ln) * 32 + 8 * lq) : zero4;
-        const u32x4 az = row_on ? *reinterpret_cast<const u32x4*>(AVz + (g * R2 + ln) * 32 + 8 * lq) : zero4;
-        oacc[2 * g] = mfma(af, unpack4<BITS>(cur.vw[g].x, half), oacc[2 * g]);
-        oacc[2 * g + 1] = mfma(af, unpack4<BITS>(cur.vw[g].y, half), oacc[2 * g + 1]);
-        vcorr[g] = mfma(af, neg4, vcorr[g]);
-        vcorr[g] = mfma(az, ones4, vcorr[g]);
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AK + (s * R2 + ln) * 32 + 8 * lq) : zero4;
+      const u32x4 az = row_on ? *reinterpret_cast<const u32x4*>(AKz + (s * R2 + ln) * 32 + 8 * lq) : zero4;
+      uint32_t kw0, kw1;
+      int half = 0;
+      if constexpr (BITS == 2) {
+        const int hw = (lq * KS) & 1;  // parity of the lane's first half-word
+        half = (hw + s) & 1;
+        const int i0 = s >> 1, i1 = (s + 1) >> 1;  // word index for hw == 0 / hw == 1
+        kw0 = hw ? cur.kw[0][i1] : cur.kw[0][i0];
+        kw1 = hw ? cur.kw[1][i1] : cur.kw[1][i0];
+      } else {
+        kw0 = cur.kw[0][s];
+        kw1 = cur.kw[1][s];
       }
-      cur = nxt;
-    } else {
-      // residual values: A = p in natural token order, B = values as stored
-      // (channel-major: 8 consecutive tokens of one channel per load)
-      for (int i = lane; i < Gb * 16; i += 64) {
-        const int h = i % Gb, pr = i / Gb;
-        const Split a0 = split2(pbuf[h * 32 + 2 * pr]);
-        const Split a1 = split2(pbuf[h * 32 + 2 * pr + 1]);
-        const int o_hi = (2 * h) * 32 + 2 * pr, o_lo = o_hi + 32;
-        *reinterpret_cast<uint32_t*>(AV + o_hi) = a0.hi | (a1.hi << 16);
-        *reinterpret_cast<uint32_t*>(AV + o_lo) = a0.lo | (a1.lo << 16);
-      }
-      const int tl = t0 + 8 * lq;                        // first token of this lane's 8 slots
-      const int tlc = min(tl, (a.r_total - 1) & ~7);     // an in-range chunk for loading
-      u32x4 vb[2 * NGV];
+      accS[0] = mfma(af, unpack4<BITS>(kw0, half), accS[0]);
+      accS[1] = mfma(af, unpack4<BITS>(kw1, half), accS[1]);
+      accC = mfma(af, neg4, accC);
+      accC = mfma(az, ones4, accC);
+    }
+    float x[2][2];
 #pragma unroll
-      for (int g = 0; g < NGV; ++g)
+    for (int hh = 0; hh < 2; ++hh) {
+      const bool ok = 2 * lq + hh < Gb;
+      const float corr = accC[2 * hh] + accC[2 * hh + 1];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          vb[2 * g + u] = *reinterpret_cast<const u32x4*>(vr + static_cast<size_t>(32 * g + 2 * ln + u) * a.r_cap + tlc);
-      wave_sync();
-      const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AV + ln * 32 + 8 * lq) : zero4;
-      const bool clean = tl + 8 <= a.r_total && !(a.r_new >= tl && a.r_new < tl + 8);
+      for (int ct = 0; ct < 2; ++ct)
+        x[hh][ct] = ok ? (accS[ct][2 * hh] + accS[ct][2 * hh + 1] + corr) * a.scale2 : -INFINITY;
+    }
+    softmax_update(x);
+    // value operand A (p x token scale per group) and split(p x zero-point)
 #pragma unroll
-      for (int g = 0; g < NGV; ++g) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          u32x4 bf = vb[2 * g + u];
-          if (!clean) {
-            // zero slots past the residual, substitute the appended token
-            const int c = 32 * g + 2 * ln + u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int t = tl + e;
-              uint32_t hv = (bf[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-              if (t == a.r_new) hv = f32_to_bf16(load_f32(vnp, c));
-              else if (t >= a.r_total) hv = 0u;
-              bf[e >> 1] = (bf[e >> 1] & (0xFFFF0000u >> (16 * (e & 1)))) | (hv << (16 * (e & 1)));
-            }
-          }
-          oacc[2 * g + u] = mfma(af, bf, oacc[2 * g + u]);
+    for (int u = 0; u < NP; ++u) {
+      const int vi = lane + 64 * u;
+      if (vi < D / 2) {
+        const int g = vi >> 4, pr = vi & 15, jj = pr & 3;
+        const int t_lo = value_token<BITS>(pr >> 2, jj, 0), t_hi = value_token<BITS>(pr >> 2, jj, 1);
+        const float f = static_cast<float>(1 << (7 - code_pos<BITS>(jj)));
+        const float sc0 = f16_bits_to_f32(cur.vm[u][0] & 0xFFFFu) * f;
+        const float sc1 = f16_bits_to_f32(cur.vm[u][1] & 0xFFFFu) * f;
+        const float zp0 = f16_bits_to_f32(cur.vm[u][0] >> 16), zp1 = f16_bits_to_f32(cur.vm[u][1] >> 16);
+        const int ob = g * R2 * 32 + 2 * pr;
+#pragma unroll 1
+        for (int h = 0; h < Gb; ++h) {
+          const float p0 = pbuf[h * 32 + t_lo], p1 = pbuf[h * 32 + t_hi];
+          const Split a0 = split2(p0 * sc0), a1 = split2(p1 * sc1);
+          const Split z0 = split2(p0 * zp0), z1 = split2(p1 * zp1);
+          const int o_hi = ob + 64 * h, o_lo = o_hi + 32;
+          *reinterpret_cast<uint32_t*>(AV + o_hi) = a0.hi | (a1.hi << 16);
+          *reinterpret_cast<uint32_t*>(AV + o_lo) = a0.lo | (a1.lo << 16);
+          *reinterpret_cast<uint32_t*>(AVz + o_hi) = z0.hi | (z1.hi << 16);
+          *reinterpret_cast<uint32_t*>(AVz + o_lo) = z0.lo | (z1.lo << 16);
         }
+      }
+    }
+    wave_sync();
+    const int half = (BITS == 2) ? (lq & 1) : 0;
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) {
+      const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AV + (g * R2 + ln) * 32 + 8 * lq) : zero4;
+      const u32x4 az = row_on ? *reinterpret_cast<const u32x4*>(AVz + (g * R2 + ln) * 32 + 8 * lq) : zero4;
+      oacc[2 * g] = mfma(af, unpack4<BITS>(cur.vw[g].x, half), oacc[2 * g]);
+      oacc[2 * g + 1] = mfma(af, unpack4<BITS>(cur.vw[g].y, half), oacc[2 * g + 1]);
+      vcorr[g] = mfma(af, neg4, vcorr[g]);
+      vcorr[g] = mfma(az, ones4, vcorr[g]);
+    }
+    wave_sync();
+  };
+
+  // ---- packed history tiles [tb, th_end) with a kPrefetch-deep register ring:
+  // the slot just consumed is refilled with the tile kPrefetch ahead
+  const int th_end = min(te, NTh);
+  HistRegs ring[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u)
+    if (tb + u < th_end) load_hist(tb + u, ring[u]);
+  __syncthreads();  // the block's q setup is complete
+  for (int tile = tb; tile < th_end; tile += kPrefetch) {
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) {
+      const int t = tile + u;
+      if (t < th_end) {
+        process_hist(ring[u], t);
+        if (t + kPrefetch < th_end) load_hist(t + kPrefetch, ring[u]);
+      }
+    }
+  }
+
+  // ---- residual tiles: bf16 keys/values as stored (appended token from the input)
+  for (int tile = max(tb, NTh); tile < te; ++tile) {
+    const int t0 = (tile - NTh) * kGroup;
+    const bool has_new = a.r_new >= t0 && a.r_new < t0 + kGroup;
+    f32x4 accS[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int t = t0 + col_token(ct, ln);
+      const int tc = min(t, a.r_total - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 bf = *reinterpret_cast<const u32x4*>(kr + static_cast<size_t>(tc) * D + 32 * s + 8 * lq);
+        if (t >= a.r_total) bf = zero4;
+        if (has_new && t == a.r_new) {
+          const int c = 32 * s + 8 * lq;
+          bf.x = load_bf16_pair(knp, c);
+          bf.y = load_bf16_pair(knp, c + 2);
+          bf.z = load_bf16_pair(knp, c + 4);
+          bf.w = load_bf16_pair(knp, c + 6);
+        }
+        const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(ares + (s * R2 + ln) * 32 + 8 * lq) : zero4;
+        accS[ct] = mfma(af, bf, accS[ct]);
+      }
+    }
+    float x[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bool okh = 2 * lq + hh < Gb;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const bool ok = okh && t0 + col_token(ct, ln) < a.r_total;
+        x[hh][ct] = ok ? (accS[ct][2 * hh] + accS[ct][2 * hh + 1]) * a.scale2 : -INFINITY;
+      }
+    }
+    softmax_update(x);
+    // values: A = p in natural token order, B = values as stored (channel-major)
+    for (int i = lane; i < Gb * 16; i += 64) {
+      const int h = i % Gb, pr = i / Gb;
+      const Split a0 = split2(pbuf[h * 32 + 2 * pr]);
+      const Split a1 = split2(pbuf[h * 32 + 2 * pr + 1]);
+      const int o_hi = (2 * h) * 32 + 2 * pr, o_lo = o_hi + 32;
+      *reinterpret_cast<uint32_t*>(AV + o_hi) = a0.hi | (a1.hi << 16);
+      *reinterpret_cast<uint32_t*>(AV + o_lo) = a0.lo | (a1.lo << 16);
+    }
+    wave_sync();
+    const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AV + ln * 32 + 8 * lq) : zero4;
+    const int tl = t0 + 8 * lq;                     // first token of this lane's 8 slots
+    const int tlc = min(tl, (a.r_total - 1) & ~7);  // an in-range chunk for loading
+    const bool clean = tl + 8 <= a.r_total && !(a.r_new >= tl && a.r_new < tl + 8);
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = 32 * g + 2 * ln + u;
+        u32x4 bf = *reinterpret_cast<const u32x4*>(vr + static_cast<size_t>(c) * a.r_cap + tlc);
+        if (!clean) {
+          // zero slots past the residual, substitute the appended token
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = tl + e;
+            uint32_t hv = (bf[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            if (t == a.r_new) hv = f32_to_bf16(load_f32(vnp, c));
+            else if (t >= a.r_total) hv = 0u;
+            bf[e >> 1] = (bf[e >> 1] & (0xFFFF0000u >> (16 * (e & 1)))) | (hv << (16 * (e & 1)));
+          }
+        }
+        oacc[2 * g + u] = mfma(af, bf, oacc[2 * g + u]);
       }
     }
     wave_sync();
@@ -601,12 +639,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* part_o, co
 struct Plan {
   int tpw, nb;  // tiles per wave, blocks per (batch, KV head, head block)
 };
-Plan plan(int NT, int units) {
+// One round of resident workgroups: as many blocks per unit as fit the chip at
+// once (two workgroups per CU when the kernel fits two waves per SIMD), then
+// spread the unit's tiles evenly over their waves.
+constexpr int kCUs = 256;
+Plan plan(int NT, int units, int KS) {
+  const int per_cu = (KS == 2 || KS == 4) ? 2 : 1;
   Plan p;
-  p.tpw = std::max(1, static_cast<int>((static_cast<long long>(NT) * units + kTargetWaves - 1) / kTargetWaves));
-  p.tpw = std::max(p.tpw, (NT + kWaves * kMaxNb - 1) / (kWaves * kMaxNb));  // nb <= kMaxNb
-  const int waves = std::max(1, (NT + p.tpw - 1) / p.tpw);
-  p.nb = (waves + kWaves - 1) / kWaves;
+  int nb = std::max(1, kCUs * per_cu / units);
+  nb = std::min(nb, (NT + kWaves - 1) / kWaves);  // no block without a tile
+  nb = std::min(nb, kMaxNb);
+  p.tpw = (NT + kWaves * nb - 1) / (kWaves * nb);
+  p.nb = (NT + kWaves * p.tpw - 1) / (kWaves * p.tpw);
   return p;
 }
 
@@ -619,7 +663,7 @@ WsLayout ws_layout(const kvc_cache* c, int HB) {
   const int NTmax = c->q_cap / kGroup + (c->r_cap + kGroup - 1) / kGroup;
   int nmax = 1;
   // nb is not monotone in NT; take the maximum over every possible length
-  for (int nt = 1; nt <= NTmax; ++nt) nmax = std::max(nmax, plan(nt, units).nb);
+  for (int nt = 1; nt <= NTmax; ++nt) nmax = std::max(nmax, plan(nt, units, c->head_dim / 32).nb);
   WsLayout w;
   w.nb_max = nmax;
   w.part_ml = 0;
@@ -716,7 +760,7 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   a.q_len = cache->q_len;
   const int units = cache->batch * Hkv * HB;
   const int NT = a.q_len / kGroup + (a.r_total + kGroup - 1) / kGroup;
-  const Plan p = plan(NT, units);
+  const Plan p = plan(NT, units, cache->head_dim / 32);
   a.tpw = p.tpw;
   a.nb = p.nb;
   char* w = static_cast<char*>(ws);
