@@ -50,6 +50,24 @@ def decode_call_bytes(B, Hq, Hkv, D, bits, q_len, r_total, in_bytes):
     return B * Hkv * (hist + resid) + io
 
 
+def counted_traffic(workload, bits):
+    """HBM bytes per kvc_decode_attn call from the committed rocprofv3 counter
+    summary of this workload, or None when the decode source has changed since
+    the counters were taken (or no summary exists)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_{bits}bit_hbm_counters.md")
+    src = os.path.join(ROOT, "kv_cache_compression_snapkv_amd", "csrc", "decode.hip")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"traffic: bytes_per_call=(\d+) workload=(\S+) bits=(\d+) decode_src_sha256=([0-9a-f]+)",
+                  open(path).read())
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if not m or m.group(2) != workload or int(m.group(3)) != bits or m.group(4) != sha:
+        return None
+    return int(m.group(1))
+
+
 def cpu_baseline(cfg, bits, layers_budget, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -201,8 +219,10 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None):
         "roofline": {
             "kernel": "decode_kernel (+ merge_kernel; flush_kernel on 1 step in 32), per kvc_decode_attn call",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(cfg.name, bits),
             "avg_call_us": dec_ms * 1e3 / ncalls, "algorithmic_bytes_per_call": sum(call_bytes) / ncalls,
+            "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated), "
+                            "profiles/decode_<workload>_<bits>bit_hbm_counters.md; null if decode.hip changed since",
         },
     }
     del prompts, dec, caches, idxs, sel_ws, dec_ws, g_pre, g_dec
