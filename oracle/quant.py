@@ -41,38 +41,48 @@ def f16_to_f32(bits):
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
 
 
-# ---------------------------------------------------------------- one group
-def quantize_group(x, bits):
-    """Asymmetric min/max quantization of one group of 32 float32 values.
+# ---------------------------------------------------------------- groups
+def quantize_groups(X, bits):
+    """Asymmetric min/max quantization of groups of 32 float32 values.
 
+    X: float32 [..., 32], one group per row of the last axis.
     Blog, "Measured on a real model", ``round_to``: lo/hi per group, step
     (hi-lo)/(2^b-1), codes round((x-lo)/step).  MiniKV Sec. 4.4: zero-point and
     scale are stored as FP16.  Reading fixed for bit-exactness: scale and zero
     are rounded to fp16 first and the codes use the stored values;
     t = (x - zero) * (1/scale) with one fp32 reciprocal per group; codes round
     half to even and clamp to [0, 2^b-1]; a zero (or non-finite) scale gives all
-    codes 0.  Every arithmetic step is one IEEE float32 operation.
+    codes 0.  Every arithmetic step is one IEEE float32 operation per element
+    (numpy float32 array arithmetic), so rows are independent of each other.
 
-    Returns (scale_bits uint16, zero_bits uint16, codes uint32[len(x)]).
+    Returns (scale_bits uint16 [...], zero_bits uint16 [...], codes uint32 [..., 32]).
     """
-    x = np.asarray(x, dtype=np.float32)
+    X = np.asarray(X, dtype=np.float32)
     qmax = np.float32(2 ** bits - 1)
-    lo = x.min()
-    hi = x.max()
-    s_bits = f16_bits(np.float32(np.float32(hi - lo) / qmax))
+    lo = X.min(axis=-1)
+    hi = X.max(axis=-1)
+    s_bits = f16_bits((hi - lo).astype(np.float32) / qmax)
     z_bits = f16_bits(lo)
     s = f16_to_f32(s_bits)
     z = f16_to_f32(z_bits)
-    if s == 0 or not np.isfinite(s):
-        return s_bits, z_bits, np.zeros(x.shape, dtype=np.uint32)
-    inv = np.float32(np.float32(1.0) / s)
-    t = ((x - z).astype(np.float32) * inv).astype(np.float32)
-    codes = np.clip(np.rint(t), 0, qmax).astype(np.uint32)
+    ok = (s != 0) & np.isfinite(s)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        inv = (np.float32(1.0) / np.where(ok, s, np.float32(1.0))).astype(np.float32)
+        t = ((X - z[..., None]).astype(np.float32) * inv[..., None]).astype(np.float32)
+        codes = np.clip(np.rint(t), 0, qmax).astype(np.uint32)
+    codes[~ok] = 0
     return s_bits, z_bits, codes
 
 
+def quantize_group(x, bits):
+    """One group of 32 values (``quantize_groups`` on a single row)."""
+    s_bits, z_bits, codes = quantize_groups(np.asarray(x, dtype=np.float32)[None], bits)
+    return s_bits[0], z_bits[0], codes[0]
+
+
 def meta_word(s_bits, z_bits):
-    return np.uint32(int(s_bits)) | (np.uint32(int(z_bits)) << np.uint32(16))
+    """Metadata word(s): fp16 scale bits | fp16 zero bits << 16."""
+    return np.asarray(s_bits).astype(np.uint32) | (np.asarray(z_bits).astype(np.uint32) << np.uint32(16))
 
 
 def dequant(codes, s_bits, z_bits):
@@ -84,13 +94,22 @@ def dequant(codes, s_bits, z_bits):
 
 # ---------------------------------------------------------------- packing
 def pack_words(codes, bits):
-    """Pack a 1-D run of 32/b codes into one uint32, LSB first."""
+    """Pack runs of 32/b codes into uint32 words, LSB first.
+
+    codes: [..., 32/b] -> uint32 [...]; code i of a run goes to bits b*i.
+    """
+    codes = np.asarray(codes, dtype=np.uint64)
     per = 32 // bits
-    assert len(codes) == per
-    w = 0
-    for i, c in enumerate(codes):
-        w |= int(c) << (bits * i)
-    return np.uint32(w)
+    assert codes.shape[-1] == per
+    shifts = (bits * np.arange(per)).astype(np.uint64)
+    return np.bitwise_or.reduce(codes << shifts, axis=-1).astype(np.uint32)
+
+
+def unpack_words(words, bits):
+    """Inverse of ``pack_words``: uint32 [...] -> codes uint32 [..., 32/b]."""
+    per = 32 // bits
+    shifts = (bits * np.arange(per)).astype(np.uint32)
+    return (np.asarray(words, dtype=np.uint32)[..., None] >> shifts) & np.uint32((1 << bits) - 1)
 
 
 def quantize_tokens(Kt, Vt, bits):
@@ -103,59 +122,34 @@ def quantize_tokens(Kt, Vt, bits):
     Q, D = Kt.shape
     assert Q % GROUP == 0 and D % GROUP == 0
     per = 32 // bits
-    kc = np.zeros((Q, D), dtype=np.uint32)
-    vc = np.zeros((Q, D), dtype=np.uint32)
-    k_meta = np.zeros((Q // GROUP, D), dtype=np.uint32)
-    v_meta = np.zeros((Q, D // GROUP), dtype=np.uint32)
-    for g in range(Q // GROUP):
-        for c in range(D):
-            s, z, codes = quantize_group(Kt[g * GROUP:(g + 1) * GROUP, c], bits)
-            k_meta[g, c] = meta_word(s, z)
-            kc[g * GROUP:(g + 1) * GROUP, c] = codes
-    for t in range(Q):
-        for j in range(D // GROUP):
-            s, z, codes = quantize_group(Vt[t, j * GROUP:(j + 1) * GROUP], bits)
-            v_meta[t, j] = meta_word(s, z)
-            vc[t, j * GROUP:(j + 1) * GROUP] = codes
-    k_codes = np.zeros((Q, D // per), dtype=np.uint32)
-    for t in range(Q):
-        for w in range(D // per):
-            k_codes[t, w] = pack_words(kc[t, w * per:(w + 1) * per], bits)
-    v_codes = np.zeros((Q // per, D), dtype=np.uint32)
-    for w in range(Q // per):
-        for c in range(D):
-            v_codes[w, c] = pack_words(vc[w * per:(w + 1) * per, c], bits)
+    # keys: group (g, c) = Kt[32g:32g+32, c]
+    kg = np.ascontiguousarray(Kt.reshape(Q // GROUP, GROUP, D).transpose(0, 2, 1))  # [Q/32][D][32]
+    ks, kz, kcodes = quantize_groups(kg, bits)
+    k_meta = meta_word(ks, kz)                                        # [Q/32][D]
+    kc = kcodes.transpose(0, 2, 1).reshape(Q, D)                      # code of (token, channel)
+    # values: group (t, j) = Vt[t, 32j:32j+32]
+    vs, vz, vcodes = quantize_groups(Vt.reshape(Q, D // GROUP, GROUP), bits)
+    v_meta = meta_word(vs, vz)                                        # [Q][D/32]
+    vc = vcodes.reshape(Q, D)
+    k_codes = pack_words(kc.reshape(Q, D // per, per), bits)          # channels of a token
+    v_codes = pack_words(vc.reshape(Q // per, per, D).transpose(0, 2, 1), bits)  # tokens of a channel
     return k_codes, k_meta, v_codes, v_meta
 
 
 def unpack_keys(k_codes, k_meta, bits):
     """Dequantized keys float32 [Q][D] from the packed layout."""
     Q, nw = k_codes.shape
-    per = 32 // bits
-    D = nw * per
-    out = np.zeros((Q, D), dtype=np.float32)
-    mask = (1 << bits) - 1
-    for t in range(Q):
-        for c in range(D):
-            code = (int(k_codes[t, c // per]) >> (bits * (c % per))) & mask
-            m = int(k_meta[t // GROUP, c])
-            out[t, c] = dequant(code, m & 0xFFFF, m >> 16)
-    return out
+    codes = unpack_words(k_codes, bits).reshape(Q, nw * (32 // bits))  # [Q][D]
+    m = np.repeat(np.asarray(k_meta, dtype=np.uint32), GROUP, axis=0)  # meta of (t // 32, c)
+    return dequant(codes, (m & 0xFFFF).astype(np.uint16), (m >> 16).astype(np.uint16))
 
 
 def unpack_values(v_codes, v_meta, bits):
     """Dequantized values float32 [Q][D] from the packed layout."""
     nrow, D = v_codes.shape
-    per = 32 // bits
-    Q = nrow * per
-    out = np.zeros((Q, D), dtype=np.float32)
-    mask = (1 << bits) - 1
-    for t in range(Q):
-        for c in range(D):
-            code = (int(v_codes[t // per, c]) >> (bits * (t % per))) & mask
-            m = int(v_meta[t, c // GROUP])
-            out[t, c] = dequant(code, m & 0xFFFF, m >> 16)
-    return out
+    codes = unpack_words(v_codes, bits).transpose(0, 2, 1).reshape(nrow * (32 // bits), D)  # [Q][D]
+    m = np.repeat(np.asarray(v_meta, dtype=np.uint32), GROUP, axis=1)      # meta of (t, c // 32)
+    return dequant(codes, (m & 0xFFFF).astype(np.uint16), (m >> 16).astype(np.uint16))
 
 
 # ---------------------------------------------------------------- cache builder
