@@ -1,0 +1,102 @@
+"""Full-size parity: every workload at its real shape, through the C ABI, in the
+launch configuration the benchmark times (same sizes, capacities and calls).
+
+All heads run on the GPU; the oracle checks what it can afford at this size:
+  * selection: idx equals the oracle's top-k of the GPU's own pooled scores for
+    every (batch, KV head) (bit-exact), and for sampled heads the scores match
+    the oracle's window scores and the kept set matches up to near-ties;
+  * quantization: the whole packed cache of sampled heads is bit-exact against
+    the oracle run on the GPU's indices;
+  * decode: every step of the workload's decode run, on sampled heads, against
+    the oracle stepping its own (bit-identical) cache, including the flushes;
+    after the last step the sampled caches are compared again.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import decode as odecode
+from oracle import quant as oquant
+from oracle import select as oselect
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("llama3_8b", 2, 0),
+    ("mistral_pyramid", 2, 0),
+    ("mistral_pyramid", 2, 31),
+    ("llama2_13b_mha", 4, 0),
+    ("llama2_13b_mha", 2, 0),
+    ("long_context", 2, 0),
+    ("long_context", 2, 31),
+]
+
+
+def _sampled_heads(cfg):
+    return sorted({(0, 0), (cfg.batch - 1, cfg.kv_heads - 1)})
+
+
+@pytest.mark.parametrize("name,bits,layer", CASES)
+def test_fullsize_workload(name, bits, layer):
+    gu.need_gpu()
+    import kv_cache_compression_snapkv_amd as kvc
+
+    cfg = synth.CONFIGS[name]
+    B, Hq, Hkv, D, n, W, R = cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.prompt, cfg.window, cfg.residual
+    G = cfg.group
+    budgets, _ = kvc.kvc_budget(cfg.layers, Hkv, D, n, W, cfg.decode_steps, cfg.budget, cfg.pyramid, cfg.beta,
+                                bits=bits, group=32, meta_bits=16, residual=R)
+    kb = budgets[layer]
+    print(f"[fullsize] {name} layer {layer} bits {bits} budget {kb}", flush=True)
+    p = synth.prompt_layer(cfg, layer, "cuda")
+    heads = _sampled_heads(cfg)
+
+    # ---- selection
+    idx = None
+    if cfg.budget >= 0:
+        idx, scores = kvc.kvc_select(p["q_win"], p["k"], W, cfg.pool, kb, want_scores=True)
+        torch.cuda.synchronize()
+        sc, ix = scores.cpu().numpy(), idx.cpu().numpy()
+        for b in range(B):
+            for j in range(Hkv):
+                np.testing.assert_array_equal(ix[b, j], oselect.top_k(sc[b, j], ix.shape[-1]), f"b{b} j{j}")
+        for b, j in heads:
+            qw = gu.as_f32(p["q_win"][b:b + 1, j * G:(j + 1) * G])
+            kh = gu.as_f32(p["k"][b:b + 1, j:j + 1])
+            pooled = oselect.max_pool(oselect.window_scores(qw, kh, W), cfg.pool)[0, 0]
+            gu.check_selection(ix[b, j], sc[b, j], pooled, kb)
+
+    # ---- quantization, in the benchmark's capacities
+    T = kb + W if cfg.budget >= 0 else n
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=T + cfg.decode_steps + 32, device="cuda")
+    kvc.kvc_quantize(p["k"], p["v"], cache, idx=idx, W=W)
+    torch.cuda.synchronize()
+    ref = {}
+    for b, j in heads:
+        kept = oquant.kept_positions(n, W, idx[b, j].cpu().numpy() if idx is not None else None)
+        ref[(b, j)] = oquant.build_head_cache(gu.as_f32(p["k"][b, j]), gu.as_f32(p["v"][b, j]), kept, R, bits)
+        gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[(b, j)], f"prefill b{b} j{j}")
+    del p
+
+    # ---- decode: the workload's whole decode run on this layer
+    flushes, worst = 0, 0.0
+    for s in range(cfg.decode_steps):
+        d = synth.decode_inputs(cfg, layer, s, "cuda")
+        ql = cache.q_len
+        out = kvc.kvc_decode_attn(cache, d["q"], d["k_new"], d["v_new"]).cpu().numpy()
+        flushes += cache.q_len != ql
+        qf = gu.as_f32(d["q"]).astype(np.float64)
+        knb, vnb = gu.bf16_bits(d["k_new"]), gu.bf16_bits(d["v_new"])
+        for b, j in heads:
+            o_ref, (ref[(b, j)],) = odecode.decode_step([ref[(b, j)]], qf[b, j * G:(j + 1) * G], knb[b, j:j + 1],
+                                                        vnb[b, j:j + 1], R, bits)
+            err = gu.assert_decode_close(out[b, j * G:(j + 1) * G], o_ref, f"step {s} b{b} j{j}")
+            worst = max(worst, err / max(1.0, float(np.abs(o_ref).max())))
+    torch.cuda.synchronize()
+    for b, j in heads:
+        gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[(b, j)], f"after decode b{b} j{j}")
+    print(f"[fullsize] {name} layer {layer}: q_len {cache.q_len} r_len {cache.r_len}, {flushes} flushes, "
+          f"worst normalized decode error {worst:.2e}", flush=True)

@@ -1,0 +1,76 @@
+"""The whole path captured into one HIP graph (as the benchmark runs it) and
+replayed several times, with eager work and synchronizations between replays:
+every replay must reproduce the eager run bit for bit (the kernels are
+deterministic: no floating-point atomics), including a residual flush."""
+
+import pytest
+import torch
+
+import synth
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_equal_eager():
+    gu.need_gpu()
+    import kv_cache_compression_snapkv_amd as kvc
+
+    B, Hkv, G, D, n, W, pool, budget, bits, R, steps = 2, 2, 4, 128, 700, 16, 7, 150, 2, 16, 40
+    Hq = Hkv * G
+    k, v = synth.random_case(21, B, Hkv, Hkv, D, n, "bf16", device="cuda")
+    q_win = synth.random_tensor(22, (B, Hq, W, D), "bf16", tag="qw").cuda()
+    dec = [(synth.random_tensor(30 + s, (B, Hq, D), "bf16", tag="q").cuda(),
+            synth.random_tensor(130 + s, (B, Hkv, D), "bf16", tag="kn").cuda(),
+            synth.random_tensor(230 + s, (B, Hkv, D), "bf16", tag="vn").cuda()) for s in range(steps)]
+    T = budget + W
+
+    def make_cache():
+        return kvc.Cache(B, Hkv, D, bits, R, q_cap=T + steps + 32, device="cuda")
+
+    sel_ws = torch.empty(kvc.select_ws_bytes(1, B, Hq, Hkv, n, D, W, pool, budget), dtype=torch.uint8,
+                         device="cuda")
+
+    def run(cache, idx, dec_ws, outs):
+        cache.reset()
+        kvc.kvc_select(q_win, k, W, pool, budget, ws=sel_ws, idx=idx)
+        kvc.kvc_quantize(k, v, cache, idx=idx, W=W)
+        for s, (q, kn, vn) in enumerate(dec):
+            kvc.kvc_decode_attn(cache, q, kn, vn, out=outs[s], ws=dec_ws)
+
+    # eager reference
+    c0 = make_cache()
+    idx0 = torch.empty(B, Hkv, budget, dtype=torch.int32, device="cuda")
+    ws0 = torch.zeros(kvc.decode_ws_bytes(c0, Hq), dtype=torch.uint8, device="cuda")
+    outs0 = [torch.empty(B, Hq, D, dtype=torch.float32, device="cuda") for _ in range(steps)]
+    run(c0, idx0, ws0, outs0)
+    torch.cuda.synchronize()
+    assert c0.q_len > 32 * ((T - R) // 32), "the run must include a flush"
+    ref = [o.clone() for o in outs0]
+    ref_cache = {key: t.clone() for key, t in c0.views().items()}
+
+    # capture the same run
+    c1 = make_cache()
+    idx1 = torch.empty_like(idx0)
+    ws1 = torch.zeros_like(ws0)
+    outs1 = [torch.empty_like(o) for o in outs0]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(c1, idx1, ws1, outs1)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs1:
+            o.fill_(float("nan"))
+        idx1.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx0), f"replay {rep}: idx"
+        for s in range(steps):
+            assert torch.equal(outs1[s], ref[s]), f"replay {rep}: step {s}"
+        for key, t in c1.views().items():
+            assert torch.equal(t, ref_cache[key]), f"replay {rep}: {key}"
+        # eager work between replays
+        run(c0, idx0, ws0, outs0)
+        torch.cuda.synchronize()
+        for s in range(steps):
+            assert torch.equal(outs0[s], ref[s]), f"eager rerun {rep}: step {s}"
