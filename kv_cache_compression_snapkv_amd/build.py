@@ -29,9 +29,15 @@ FLAGS = [
 ]
 
 
+# Per-source extras.  decode.hip: its values are never NaN (scores, softmax
+# weights, -inf masks), so fmax needs no canonicalization and the 16-lane DPP max
+# folds into v_max_f32_dpp.
+EXTRA = {"decode.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

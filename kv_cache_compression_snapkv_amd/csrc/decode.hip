@@ -4,26 +4,29 @@
 //
 // Work split.  The tokens of one (batch, KV head) are cut into 32-token tiles:
 // Q/32 packed-history tiles (one key group each) followed by the bf16 residual
-// tiles.  Every wavefront owns a contiguous run of tiles for up to 8 query heads
-// of that KV head and keeps its own online-softmax state; the four waves of a
+// tiles.  Every wavefront owns a contiguous run of tiles for up to 4 query heads
+// of that KV head and keeps its own online-softmax state; the waves of a
 // workgroup merge through LDS, M = max m_w, o = sum_w 2^(m_w-M) o_w,
 // l = sum_w 2^(m_w-M) l_w (log2 units), and write the output directly when one
-// workgroup covers the whole (batch, KV head), else a partial that a small
-// merge kernel combines the same way.  (No cross-workgroup atomics: a
-// device-scope release fence costs an L2 write-back per wavefront.)
+// workgroup covers the whole (batch, KV head) -- short histories, 8 waves --
+// else a partial that a small merge kernel combines the same way.  (No
+// cross-workgroup atomics: a device-scope release fence costs an L2 write-back
+// per wavefront.)  Within a wave the history tiles are software-pipelined: the
+// key stage of tile t+1 and the value stage of tile t share each LDS barrier.
 //
-// Contractions on MFMA (v_mfma_f32_16x16x32_bf16).  Rows of the 16-row operand
-// are (head, split) pairs: row 2h holds the bf16 truncation of a float32 value
-// and row 2h+1 the bf16 truncation of its remainder, so hi+lo carries 16
-// significant bits and products accumulate in fp32.
-//   keys:   S[t] = sum_c A[c] B[c][t] with B = 1 + code*2^(pos-7), the code OR-ed
-//           into the mantissa of bf16 1.0 (one bitwise op per two codes), and
-//           A = q*scale*2^(7-pos) per group; the 1.0 offset is removed by the
-//           same A against an all-(-1) operand and the zero-point added by
-//           split(q*zero) against an all-ones operand.
+// Contractions on MFMA (v_mfma_f32_16x16x32_bf16).  A float32 operand value x is
+// carried as two bf16 rows, hi = x truncated to bf16 and lo = (x - hi) truncated,
+// so hi + lo holds 16 significant bits and products accumulate in fp32.
+//   keys:   S[t] = sum_c A[c] B[c][t] with B = 1 + code*2^(pos-7): the code is
+//           OR-ed into the mantissa of bf16 1.0 (one v_and_or_b32 per two codes)
+//           and A = q*scale*2^(7-pos) per (group, channel) in rows 2h, 2h+1.
+//           Rows 8+2h, 9+2h of the same operand hold -split(q*zero); one more
+//           MFMA of that operand against all -1 gives, per head, the exact sum
+//           of the A pieces (the 1.0 offset to remove) and the zero-point term.
 //   values: o[c] = sum_t A[t] B[t][c] with the same code encoding and
-//           A = p*scale*2^(7-pos) per (token, 32-channel group), with the same
-//           two corrections (A x -1, split(p*zero) x 1).
+//           A = p*scale*2^(7-pos) per (token, 32-channel group); each lane adds
+//           p*zero - (hi + lo) for the pieces it wrote into a float32 register,
+//           and the lanes of a group are summed once at the end of the run.
 //   residual: B = bf16 keys/values as stored, A = q or p split in two.
 #include <algorithm>
 
@@ -38,10 +41,7 @@ kvc_status cache_shape_status(const kvc_cache* c);
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kHB = 8;              // query heads per head block (2 MFMA rows each)
-constexpr int kPrefetch = 2;        // history tiles in flight per wave
+constexpr int kHB = 4;  // query heads per workgroup (MFMA rows 2h, 2h+1)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -50,70 +50,110 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kOne2 = 0x3F803F80u;     // two bf16 1.0
 constexpr uint32_t kNegOne2 = 0xBF80BF80u;  // two bf16 -1.0
+constexpr uint32_t kHi = 0xFFFF0000u;
+constexpr uint32_t kHighHalves = 0x07060302u;  // v_perm: high halves of (src1, src0)
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                  c, 0, 0, 0);
 }
 
-// x = hi + lo with hi, lo bf16 (truncations); eff = hi + lo as float.
-struct Split {
-  uint32_t hi, lo;
-  float eff;
+// A value the compiler must keep in a VGPR (VOP3 instructions such as
+// v_and_or_b32 take no literal operand on this target).
+__device__ __forceinline__ uint32_t vreg(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+struct Consts {
+  uint32_t one, m0, m1, m2, m4;
 };
-__device__ __forceinline__ Split split2(float x) {
-  Split s;
-  const uint32_t hb = __float_as_uint(x) & 0xFFFF0000u;
-  const float r = x - __uint_as_float(hb);
-  const uint32_t lb = __float_as_uint(r) & 0xFFFF0000u;
-  s.hi = hb >> 16;
-  s.lo = lb >> 16;
-  s.eff = __uint_as_float(hb) + __uint_as_float(lb);
-  return s;
+
+// bf16 pair {hi(x0), hi(x1)} and {lo(x0), lo(x1)}: truncations of x and of its
+// remainder.  eff0/eff1 = hi + lo as float (exact).
+struct Pair {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Pair split_pair(float x0, float x1) {
+  const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+  const float r0 = x0 - __uint_as_float(u0 & kHi);
+  const float r1 = x1 - __uint_as_float(u1 & kHi);
+  Pair p;
+  p.hi = __builtin_amdgcn_perm(u1, u0, kHighHalves);
+  p.lo = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), kHighHalves);
+  return p;
+}
+__device__ __forceinline__ float piece_sum(float x) {
+  const float h = __uint_as_float(__float_as_uint(x) & kHi);
+  return h + __uint_as_float(__float_as_uint(x - h) & kHi);
 }
 
-// bf16 bit position of the code inside register jj of an unpacked word.
-// 2-bit: jj 0..2 -> 0,2,4 and jj 3 -> 0 (after a 6-bit shift); 4-bit: 0.
-template <int BITS> __device__ __forceinline__ int code_pos(int jj) {
-  return BITS == 2 ? (jj < 3 ? 2 * jj : 0) : 0;
+// Packed-word layout inside MFMA operands.  An operand is 4 registers, i.e. 8
+// bf16 k-slots e = 0..7 (register e/2, half e%2).
+//   2-bit word (16 codes, code i at bits 2i), half hf: k-slot e holds code
+//     e/2 + 4*hf + 8*(e%2).  Two register forms:
+//       wave-uniform hf: registers m = e/2 + 4*hf from w, w>>6, w>>12, the code
+//         at bit position 2*(m%3) of each bf16 half (10 instructions per word);
+//       per-lane hf: the hf = 0 form applied to w >> 8*hf, position
+//         2*((e/2)%3) (6 instructions per half-word).
+//   4-bit word (8 codes, code i at bits 4i): register m = e/2 holds codes
+//     (m, m+4) at position 0 (from w>>4m).
+template <int BITS> __device__ __forceinline__ int slot_code(int e, int hf) {
+  return BITS == 2 ? (e >> 1) + 4 * hf + 8 * (e & 1) : (e >> 1) + 4 * (e & 1);
 }
-
-// Four bf16x2 registers from one packed word: register jj holds codes of the
-// pair (p, p + half-word span) as 1 + code*2^(pos-7).
-// 2-bit (16 codes, i at bits 2i): `half` picks pairs 0..3 or 4..7, pair p =
-//   codes (p, p+8).  4-bit (8 codes, i at bits 4i): pair p = codes (p, p+4).
-template <int BITS> __device__ __forceinline__ u32x4 unpack4(uint32_t w, int half) {
+template <int BITS> __device__ __forceinline__ int slot_pos(int e, int hf, bool uniform) {
+  return BITS == 2 ? 2 * (((e >> 1) + (uniform ? 4 * hf : 0)) % 3) : 0;
+}
+template <int BITS> __device__ __forceinline__ u32x4 unpack(uint32_t w, int hf, const Consts& k) {
   u32x4 r;
   if (BITS == 2) {
-    const uint32_t x = w >> (8 * half);
-    r.x = (x & 0x00030003u) | kOne2;
-    r.y = (x & 0x000C000Cu) | kOne2;
-    r.z = (x & 0x00300030u) | kOne2;
-    r.w = ((x >> 6) & 0x00030003u) | kOne2;
+    const uint32_t w6 = w >> 6, w12 = w >> 12;
+    if (hf == 0) {
+      r.x = (w & k.m0) | k.one;
+      r.y = (w & k.m1) | k.one;
+      r.z = (w & k.m2) | k.one;
+      r.w = (w6 & k.m0) | k.one;
+    } else {
+      r.x = (w6 & k.m1) | k.one;
+      r.y = (w6 & k.m2) | k.one;
+      r.z = (w12 & k.m0) | k.one;
+      r.w = (w12 & k.m1) | k.one;
+    }
   } else {
-    r.x = (w & 0x000F000Fu) | kOne2;
-    r.y = ((w >> 4) & 0x000F000Fu) | kOne2;
-    r.z = ((w >> 8) & 0x000F000Fu) | kOne2;
-    r.w = ((w >> 12) & 0x000F000Fu) | kOne2;
+    r.x = (w & k.m4) | k.one;
+    r.y = ((w >> 4) & k.m4) | k.one;
+    r.z = ((w >> 8) & k.m4) | k.one;
+    r.w = ((w >> 12) & k.m4) | k.one;
   }
   return r;
 }
+// 2-bit half-word chosen per lane: shift amount sh = 8*hf (a per-lane value).
+__device__ __forceinline__ u32x4 unpack_lane(uint32_t w, uint32_t sh, const Consts& k) {
+  return unpack<2>(w >> sh, 0, k);
+}
 
-// Channel held in k-slot (8*lq + 2*jj + e) of k-step s for a packed history key.
-template <int BITS, int KS> __device__ __forceinline__ int key_channel(int s, int lq, int jj, int e) {
+// Keys: lane quarter lq, k-step s reads half-word hw = lq*KS + s of the
+// token's codes (2-bit) or word lq*KS + s (4-bit).
+template <int BITS, int KS> __device__ __forceinline__ int key_channel(int s, int lq, int e) {
   if (BITS == 2) {
-    const int hw = lq * KS + s;  // half-word index within the token's codes
-    return 16 * (hw >> 1) + 4 * (hw & 1) + jj + 8 * e;
+    const int hw = lq * KS + s;
+    return 16 * (hw >> 1) + slot_code<2>(e, hw & 1);
   }
-  return 8 * (lq * KS + s) + jj + 4 * e;
+  return 8 * (lq * KS + s) + slot_code<4>(e, 0);
 }
-// Token (within a 32-token tile) held in value k-slot (8*lq + 2*jj + e).
-template <int BITS> __device__ __forceinline__ int value_token(int lq, int jj, int e) {
-  if (BITS == 2) return 16 * (lq >> 1) + 4 * (lq & 1) + jj + 8 * e;
-  return 8 * lq + jj + 4 * e;
+template <int BITS, int KS> __device__ __forceinline__ int key_pos(int s, int lq, int e) {
+  // the half is wave-uniform when KS is even
+  return BITS == 2 ? slot_pos<2>(e, (lq * KS + s) & 1, (KS & 1) == 0) : 0;
 }
-// Token of column n in key column tile ct: tile 0 holds tokens {0..7,16..23},
-// tile 1 holds {8..15,24..31}, so one lane's two tokens are a value slot pair.
+// Values: lane quarter lq reads word row lq/2, half lq%2 (2-bit) or row lq (4-bit).
+template <int BITS> __device__ __forceinline__ int value_token(int lq, int e) {
+  if (BITS == 2) return 16 * (lq >> 1) + slot_code<2>(e, lq & 1);
+  return 8 * lq + slot_code<4>(e, 0);
+}
+template <int BITS> __device__ __forceinline__ int value_pos(int lq, int e) {
+  return BITS == 2 ? slot_pos<2>(e, lq & 1, false) : 0;
+}
+// Token of column n in key column tile ct.
 __device__ __forceinline__ int col_token(int ct, int n) { return 16 * (n >> 3) + (n & 7) + 8 * ct; }
 
 struct DecArgs {
@@ -122,34 +162,36 @@ struct DecArgs {
   const void* v_new;
   const uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;  // k_res [bj][r_cap][D], v_res [bj][D][r_cap]
-  float* part_o;            // [bjh][nb][8][D] (used when nb > 1)
-  float2* part_ml;          // [bjh][nb][8]
+  float* part_o;            // [bjh][nb][kHB][D] (used when nb > 1)
+  float2* part_ml;          // [bjh][nb][kHB]
   float* out;               // [B][Hq][D]
   int Hq, Hkv, G, HB, q_cap, r_cap;
   int q_len, r_total, r_new;
-  int nb, tpw;
+  int nb;
   float scale2;  // log2(e)/sqrt(D)
 };
 
-// LDS layout (bytes), shared by host sizing and the kernel.
+
+// LDS layout (bytes), shared by host sizing and the kernel.  Operand areas hold
+// 16 MFMA rows of 32 bf16 per k-step (keys) or channel group (values), padded
+// so that both the 16-byte fragment reads (8 lanes, rows ln..ln+7) and the
+// dword writes (lanes of two blocks) fall in distinct banks: rows are kRowW
+// dwords apart and blocks kBlkW dwords (16 mod 32) apart.
+constexpr int kRowW = 20;
+constexpr int kBlkW = 336;
 struct Lds {
-  int qf, qx, ares, wave0, wave_bytes, total;
-  int ak, akz, av, avz, pbuf;  // offsets inside one wave's region
+  int wave0, wave_bytes, total;
+  int ak, av, pbuf, vcorr;  // offsets inside one wave's region
 };
-__host__ __device__ inline Lds lds_layout(int KS, int Gb) {
-  const int D = 32 * KS, R2 = 2 * Gb;
-  Lds L;
-  L.qf = 0;
-  L.qx = Gb * D * 4;
-  L.ares = 2 * Gb * D * 4;
-  L.wave0 = (L.ares + KS * R2 * 64 + 15) / 16 * 16;
+__host__ __device__ constexpr Lds lds_layout(int KS, int nwv) {
+  Lds L{};
+  L.wave0 = 0;
   L.ak = 0;
-  L.akz = KS * R2 * 64;
-  L.av = 2 * KS * R2 * 64;
-  L.avz = 3 * KS * R2 * 64;
-  L.pbuf = 4 * KS * R2 * 64;
-  L.wave_bytes = (L.pbuf + Gb * 32 * 4 + 15) / 16 * 16;
-  L.total = L.wave0 + kWaves * L.wave_bytes;
+  L.av = KS * kBlkW * 4;
+  L.pbuf = 2 * KS * kBlkW * 4;
+  L.vcorr = L.pbuf + kHB * 32 * 4;
+  L.wave_bytes = (L.vcorr + kHB * 8 * 4 + 15) / 16 * 16;
+  L.total = L.wave0 + nwv * L.wave_bytes;
   return L;
 }
 
@@ -162,7 +204,7 @@ __device__ __forceinline__ uint32_t load_bf16_pair(const T* p, int i) {
 // All-reduce over the 16 lanes of a DPP row: swap neighbours, swap pairs,
 // mirror within 8, mirror within 16.
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float max16(float x) {
   x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
@@ -184,11 +226,21 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename T, int BITS, int KS>
-__global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode_kernel(DecArgs a) {
+// Resident workgroups per CU that the register budget allows (the occupancy
+// the planner assumes): 4-wave groups at up to 168 VGPRs fit three per CU.
+template <int KS, int NWV> constexpr int min_blocks() { return NWV == 8 ? 1 : (KS <= 4 ? 3 : KS <= 6 ? 2 : 1); }
+
+template <typename T, int BITS, int KS, int NWV>
+__global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kernel(DecArgs a) {
   constexpr int D = 32 * KS;
-  constexpr int NGV = KS;  // value channel groups
-  constexpr int NW = D * BITS / 32;  // key words per token
+  constexpr int NTHR = 64 * NWV;
+  constexpr int NGV = KS;                   // value channel groups
+  constexpr int NW = D * BITS / 32;         // key words per token
+  constexpr int NP = (D / 2 + 63) / 64;     // operand pairs per lane per tile
+  constexpr int PAIR = BITS == 2 ? 8 : 4;   // code distance of the two halves of a register
+  // history tiles in flight per wave (register ring): deep for the latency-bound
+  // short runs, shallow where three workgroups share a CU
+  constexpr int NR = (NWV == 8 && KS <= 4) ? 4 : 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -199,68 +251,57 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
   const int bjh = bj * a.HB + hb;
   const int h0 = hb * kHB;
   const int Gb = min(kHB, a.G - h0);
-  const int R2 = 2 * Gb;
-  const Lds L = lds_layout(KS, Gb);
-  float* qf = reinterpret_cast<float*>(smem + L.qf);
-  float* qx = reinterpret_cast<float*>(smem + L.qx);
-  uint16_t* ares = reinterpret_cast<uint16_t*>(smem + L.ares);
+  constexpr Lds L = lds_layout(KS, NWV);
   unsigned char* wbase = smem + L.wave0 + wave * L.wave_bytes;
   uint16_t* AK = reinterpret_cast<uint16_t*>(wbase + L.ak);
-  uint16_t* AKz = reinterpret_cast<uint16_t*>(wbase + L.akz);
   uint16_t* AV = reinterpret_cast<uint16_t*>(wbase + L.av);
-  uint16_t* AVz = reinterpret_cast<uint16_t*>(wbase + L.avz);
   float* pbuf = reinterpret_cast<float*>(wbase + L.pbuf);
+  float* vcs = reinterpret_cast<float*>(wbase + L.vcorr);
 
-  // ---------------------------------------------------------------- setup (block)
-  // q (plain and scaled for the key operand) and the residual key operand
-  // split(q) in natural channel order, from one load per element
-  const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.Hq + j * a.G + h0) * D;
-  for (int e = tid; e < Gb * D; e += kThreads) {
-    const float v = load_f32(qp, e);
-    const int h = e / D, c = e % D;
-    qf[e] = v;
-    const int jj = (BITS == 2) ? (c & 3) : 0;  // key register index of channel c
-    qx[e] = v * static_cast<float>(1 << (7 - code_pos<BITS>(jj)));
-    const Split sp = split2(v);
-    ares[((c >> 5) * R2 + 2 * h) * 32 + (c & 31)] = static_cast<uint16_t>(sp.hi);
-    ares[((c >> 5) * R2 + 2 * h + 1) * 32 + (c & 31)] = static_cast<uint16_t>(sp.lo);
-  }
+  Consts K;
+  K.one = vreg(kOne2);
+  K.m0 = vreg(0x00030003u);
+  K.m1 = vreg(0x000C000Cu);
+  K.m2 = vreg(0x00300030u);
+  K.m4 = vreg(0x000F000Fu);
+
   const size_t qc = a.q_cap;
-  const uint32_t* kc = a.k_codes + static_cast<size_t>(bj) * qc * NW;
-  const uint32_t* km = a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D;
-  const uint32_t* vc = a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D;
-  const uint32_t* vm = a.v_meta + static_cast<size_t>(bj) * qc * NGV;
   const uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;
+  // With no packed history the (never used) prefetches read this unit's residual
+  // keys instead: at least 32*D*2 bytes, more than one history tile's 16*D.
+  const bool hist = a.q_len > 0;
+  const uint32_t* kres32 = reinterpret_cast<const uint32_t*>(kr);
+  const uint32_t* kc = hist ? a.k_codes + static_cast<size_t>(bj) * qc * NW : kres32;
+  const uint32_t* km = hist ? a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D : kres32;
+  const uint32_t* vc = hist ? a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D : kres32;
+  const uint32_t* vm = hist ? a.v_meta + static_cast<size_t>(bj) * qc * NGV : kres32;
   const uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;
   const T* knp = static_cast<const T*>(a.k_new) + static_cast<size_t>(bj) * D;
   const T* vnp = static_cast<const T*>(a.v_new) + static_cast<size_t>(bj) * D;
 
-  const int sp = blockIdx.x * kWaves + wave;
+  // Tiles of this wave: an even share of the history tiles (a contiguous run)
+  // and every NWT-th residual tile counted from the last wave, so the costlier
+  // bf16 tiles land on the waves with the fewest history tiles.
+  const int NWT = gridDim.x * NWV;  // waves of this unit
+  const int sp = blockIdx.x * NWV + wave;
   const int NTh = a.q_len / kGroup;
-  const int NT = NTh + (a.r_total + kGroup - 1) / kGroup;
-  const int tb = sp * a.tpw, te = min(NT, tb + a.tpw);
+  const int NTr = (a.r_total + kGroup - 1) / kGroup;
+  const int tb = static_cast<int>((static_cast<long long>(sp) * NTh) / NWT);
+  const int th_end = static_cast<int>((static_cast<long long>(sp + 1) * NTh) / NWT);
+  const int r_first = NWT - 1 - sp;  // residual tiles r_first, r_first + NWT, ...
+  // Every prefetch is issued on every path (clamped to an existing tile) so the
+  // number of loads in flight is the same at each wait and the compiler can wait
+  // for exactly the tile it needs.
+  const int hlast = max(th_end - 1, 0);
 
-  f32x4 oacc[2 * NGV], vcorr[NGV];
-#pragma unroll
-  for (int i = 0; i < 2 * NGV; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < NGV; ++i) vcorr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
-  const bool row_on = ln < R2;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const u32x4 ones4 = {kOne2, kOne2, kOne2, kOne2};
-  const u32x4 neg4 = {kNegOne2, kNegOne2, kNegOne2, kNegOne2};
-
-  // Per tile, D/2 key channel pairs and D/2 value (group, token pair) items;
-  // lane l owns positions l + 64u and loops over the heads, so its meta loads do
-  // not depend on the head and can be issued a tile ahead.
-  constexpr int NP = (D / 2 + 63) / 64;
+  // Per tile, D/2 key operand pairs and D/2 value operand pairs; lane l owns
+  // pairs l + 64u for every head, so its meta loads do not depend on the head.
   constexpr int NKW = (BITS == 2) ? KS / 2 + (KS & 1) : KS;  // key words a lane reads per token
   struct HistRegs {
     uint32_t kw[2][NKW];  // key code words, per column tile
-    uint32_t km[NP][2];  // key meta of the lane's channel pairs
-    uint32_t vm[NP][2];  // value meta of the lane's token pairs
-    u32x2 vw[NGV];       // value code words, per channel group
+    uint32_t km[NP][2];   // key meta of the lane's channel pairs
+    uint32_t vm[NP][2];   // value meta of the lane's token pairs
+    u32x2 vw[NGV];        // value code words, per channel group
   };
   auto load_hist = [&](int tile, HistRegs& r) {
     const int t0 = tile * kGroup;
@@ -268,10 +309,10 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const uint32_t* row = kc + (t0 + col_token(ct, ln)) * NW + w_first;
-      if constexpr (NKW == 4) {
+      if constexpr (NKW == 4 && (BITS == 4 || (KS & 1) == 0)) {
         const u32x4 w4 = *reinterpret_cast<const u32x4*>(row);
         r.kw[ct][0] = w4.x; r.kw[ct][1] = w4.y; r.kw[ct][2] = w4.z; r.kw[ct][3] = w4.w;
-      } else if constexpr (NKW == 2) {
+      } else if constexpr (NKW == 2 && (BITS == 4 || (KS & 1) == 0)) {
         const u32x2 w2 = *reinterpret_cast<const u32x2*>(row);
         r.kw[ct][0] = w2.x; r.kw[ct][1] = w2.y;
       } else {
@@ -285,12 +326,14 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
       const int pi = lane + 64 * u;
       r.km[u][0] = r.km[u][1] = r.vm[u][0] = r.vm[u][1] = 0u;
       if (pi < D / 2) {
-        const int s = pi >> 4, q4 = (pi >> 2) & 3, jj = pi & 3;
-        r.km[u][0] = kmg[key_channel<BITS, KS>(s, q4, jj, 0)];
-        r.km[u][1] = kmg[key_channel<BITS, KS>(s, q4, jj, 1)];
+        const int s = pi >> 4, q4 = (pi >> 2) & 3, m = pi & 3;
+        const int c0 = key_channel<BITS, KS>(s, q4, 2 * m);
+        r.km[u][0] = kmg[c0];
+        r.km[u][1] = kmg[c0 + PAIR];
         const int g = pi >> 4, pr = pi & 15;
-        r.vm[u][0] = vm[(t0 + value_token<BITS>(pr >> 2, pr & 3, 0)) * NGV + g];
-        r.vm[u][1] = vm[(t0 + value_token<BITS>(pr >> 2, pr & 3, 1)) * NGV + g];
+        const int t_lo = value_token<BITS>(pr >> 2, 2 * (pr & 3));
+        r.vm[u][0] = vm[(t0 + t_lo) * NGV + g];
+        r.vm[u][1] = vm[(t0 + t_lo + PAIR) * NGV + g];
       }
     }
     const int wrow = (BITS == 2) ? (t0 / 16 + (lq >> 1)) : (t0 / 8 + lq);
@@ -299,23 +342,66 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
     for (int g = 0; g < NGV; ++g) r.vw[g] = *reinterpret_cast<const u32x2*>(vrow + 32 * g + 2 * ln);
   };
 
+  // ---------------------------------------------------------------- setup
+  // Each wave loads the query values of its lanes' key channel pairs (they never
+  // change) and its first NR history tiles before anything waits; meanwhile its
+  // operand rows that no head writes are zeroed.  No workgroup barrier.
+  const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.Hq + j * a.G + h0) * D;
+  float qa0[NP][kHB], qa1[NP][kHB];
+  int cpair[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int pi = min(lane + 64 * u, D / 2 - 1);
+    const int s = pi >> 4, q4 = (pi >> 2) & 3, m = pi & 3;
+    cpair[u] = key_channel<BITS, KS>(s, q4, 2 * m);
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      const int hc = min(h, Gb - 1);
+      qa0[u][h] = load_f32(qp, hc * D + cpair[u]);
+      qa1[u][h] = load_f32(qp, hc * D + cpair[u] + PAIR);
+    }
+  }
+  HistRegs ring[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) load_hist(min(tb + u, hlast), ring[u]);
+  {
+    uint32_t* zero_area = reinterpret_cast<uint32_t*>(wbase);
+    for (int e = lane; e < (L.pbuf >> 2); e += 64) zero_area[e] = 0u;  // AK and AV of this wave
+  }
+  wave_sync();
+
+  f32x4 oacc[2 * NGV];
+#pragma unroll
+  for (int i = 0; i < 2 * NGV; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float vcorr[NP][kHB];
+#pragma unroll
+  for (int u = 0; u < NP; ++u)
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) vcorr[u][h] = 0.0f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  const u32x4 neg4 = {vreg(kNegOne2), vreg(kNegOne2), vreg(kNegOne2), vreg(kNegOne2)};
+  const uint32_t vsh = 8u * static_cast<uint32_t>(lq & 1);  // value half-word of this lane (2-bit)
+  const int nhh = Gb > 1 ? 2 : 1;                           // head rows per lane quarter in use
+
   // ---- the online softmax update shared by both tile kinds.  x[hh][ct] are
-  // log2-scaled scores (-inf when masked); returns p in place and rescales the
+  // log2-scaled scores (-inf when masked); writes p to pbuf and rescales the
   // accumulators when a running max moves (skipped when no lane's moves, which
   // leaves the result bit-identical).
   auto softmax_update = [&](float (&x)[2][2]) {
-    float alpha[2];
+    float alpha[2] = {1.0f, 1.0f};
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+      if (hh >= nhh) continue;  // no lane holds a second head
       const float mt = max16(fmaxf(x[hh][0], x[hh][1]));
       const float mnew = fmaxf(m_run[hh], mt);
       if (mnew == -INFINITY) {
-        alpha[hh] = 1.0f;
         x[hh][0] = x[hh][1] = 0.0f;
       } else {
-        alpha[hh] = exp2f(m_run[hh] - mnew);
-        x[hh][0] = exp2f(x[hh][0] - mnew);
-        x[hh][1] = exp2f(x[hh][1] - mnew);
+        // arguments are <= 0 (or -inf): the hardware exp2 is exact enough and
+        // needs no range reduction
+        alpha[hh] = __builtin_amdgcn_exp2f(m_run[hh] - mnew);
+        x[hh][0] = __builtin_amdgcn_exp2f(x[hh][0] - mnew);
+        x[hh][1] = __builtin_amdgcn_exp2f(x[hh][1] - mnew);
       }
       m_run[hh] = mnew;
       l_part[hh] = l_part[hh] * alpha[hh] + x[hh][0] + x[hh][1];
@@ -333,138 +419,195 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
         oacc[i][2] *= alpha[1];
         oacc[i][3] *= alpha[1];
       }
+      // per-head factors for the value corrections (lanes of quarter h/2 hold head h)
 #pragma unroll
-      for (int g = 0; g < NGV; ++g) {
-        vcorr[g][0] *= alpha[0];
-        vcorr[g][1] *= alpha[0];
-        vcorr[g][2] *= alpha[1];
-        vcorr[g][3] *= alpha[1];
+      for (int h = 0; h < kHB; ++h) {
+        const float ah = __shfl(alpha[h & 1], 16 * (h >> 1));
+#pragma unroll
+        for (int u = 0; u < NP; ++u) vcorr[u][h] *= ah;
       }
     }
-    wave_sync();
   };
 
-  // ---- one packed-history tile from its prefetched registers
-  auto process_hist = [&](const HistRegs& cur, int tile) {
-    // key operand A (query x group scale) and split(query x zero-point)
+  // ---- key stage of a history tile: rows 2h, 2h+1 = split(q*scale*2^(7-pos)),
+  // rows 8+2h, 9+2h = -split(q*zero)
+  auto k_stage = [&](const HistRegs& cur) {
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int pi = lane + 64 * u;
       if (pi < D / 2) {
-        const int s = pi >> 4, q4 = (pi >> 2) & 3, jj = pi & 3;
-        const int c0 = key_channel<BITS, KS>(s, q4, jj, 0), c1 = key_channel<BITS, KS>(s, q4, jj, 1);
-        const float sc0 = f16_bits_to_f32(cur.km[u][0] & 0xFFFFu), sc1 = f16_bits_to_f32(cur.km[u][1] & 0xFFFFu);
+        const int s = pi >> 4, q4 = (pi >> 2) & 3, m = pi & 3;
+        const float f = static_cast<float>(1 << (7 - key_pos<BITS, KS>(s, q4, 2 * m)));
+        const float sc0 = f16_bits_to_f32(cur.km[u][0] & 0xFFFFu) * f;
+        const float sc1 = f16_bits_to_f32(cur.km[u][1] & 0xFFFFu) * f;
         const float zp0 = f16_bits_to_f32(cur.km[u][0] >> 16), zp1 = f16_bits_to_f32(cur.km[u][1] >> 16);
-        const int ob = s * R2 * 32 + 8 * q4 + 2 * jj;
-#pragma unroll 1
-        for (int h = 0; h < Gb; ++h) {
-          const Split a0 = split2(qx[h * D + c0] * sc0), a1 = split2(qx[h * D + c1] * sc1);
-          const Split z0 = split2(qf[h * D + c0] * zp0), z1 = split2(qf[h * D + c1] * zp1);
-          const int o_hi = ob + 64 * h, o_lo = o_hi + 32;
-          *reinterpret_cast<uint32_t*>(AK + o_hi) = a0.hi | (a1.hi << 16);
-          *reinterpret_cast<uint32_t*>(AK + o_lo) = a0.lo | (a1.lo << 16);
-          *reinterpret_cast<uint32_t*>(AKz + o_hi) = z0.hi | (z1.hi << 16);
-          *reinterpret_cast<uint32_t*>(AKz + o_lo) = z0.lo | (z1.lo << 16);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(AK) + s * kBlkW + 4 * q4 + m;
+#pragma unroll
+        for (int h = 0; h < kHB; ++h) {
+          if (h < Gb) {
+            const Pair pa = split_pair(qa0[u][h] * sc0, qa1[u][h] * sc1);
+            const Pair pz = split_pair(qa0[u][h] * zp0, qa1[u][h] * zp1);
+            dst[(2 * h) * kRowW] = pa.hi;
+            dst[(2 * h + 1) * kRowW] = pa.lo;
+            dst[(8 + 2 * h) * kRowW] = pz.hi ^ 0x80008000u;
+            dst[(9 + 2 * h) * kRowW] = pz.lo ^ 0x80008000u;
+          }
         }
       }
     }
-    wave_sync();
-    // key MFMAs: two 16-token column tiles, then the offset/zero corrections
+  };
+  // ---- key MFMAs of a history tile (operand rows visible): log2-scaled scores
+  auto k_mma = [&](const HistRegs& cur, float (&x)[2][2]) {
     f32x4 accS[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 accC = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AK + (s * R2 + ln) * 32 + 8 * lq) : zero4;
-      const u32x4 az = row_on ? *reinterpret_cast<const u32x4*>(AKz + (s * R2 + ln) * 32 + 8 * lq) : zero4;
-      uint32_t kw0, kw1;
-      int half = 0;
-      if constexpr (BITS == 2) {
-        const int hw = (lq * KS) & 1;  // parity of the lane's first half-word
-        half = (hw + s) & 1;
-        const int i0 = s >> 1, i1 = (s + 1) >> 1;  // word index for hw == 0 / hw == 1
-        kw0 = hw ? cur.kw[0][i1] : cur.kw[0][i0];
-        kw1 = hw ? cur.kw[1][i1] : cur.kw[1][i0];
+      const u32x4 af = *reinterpret_cast<const u32x4*>(AK + 2 * (s * kBlkW + ln * kRowW + 4 * lq));
+      if constexpr (BITS == 2 && (KS & 1) == 0) {
+        accS[0] = mfma(af, unpack<2>(cur.kw[0][s >> 1], s & 1, K), accS[0]);
+        accS[1] = mfma(af, unpack<2>(cur.kw[1][s >> 1], s & 1, K), accS[1]);
+      } else if constexpr (BITS == 2) {
+        const int hw0 = (lq * KS) & 1;  // parity of the lane's first half-word
+        const uint32_t sh = 8 * ((hw0 + s) & 1);
+        const int i0 = s >> 1, i1 = (s + 1) >> 1;  // word index for hw0 == 0 / hw0 == 1
+        const uint32_t kw0 = hw0 ? cur.kw[0][i1] : cur.kw[0][i0];
+        const uint32_t kw1 = hw0 ? cur.kw[1][i1] : cur.kw[1][i0];
+        accS[0] = mfma(af, unpack_lane(kw0, sh, K), accS[0]);
+        accS[1] = mfma(af, unpack_lane(kw1, sh, K), accS[1]);
       } else {
-        kw0 = cur.kw[0][s];
-        kw1 = cur.kw[1][s];
+        accS[0] = mfma(af, unpack<4>(cur.kw[0][s], 0, K), accS[0]);
+        accS[1] = mfma(af, unpack<4>(cur.kw[1][s], 0, K), accS[1]);
       }
-      accS[0] = mfma(af, unpack4<BITS>(kw0, half), accS[0]);
-      accS[1] = mfma(af, unpack4<BITS>(kw1, half), accS[1]);
       accC = mfma(af, neg4, accC);
-      accC = mfma(az, ones4, accC);
     }
-    float x[2][2];
+    // lanes of quarters 0-1 hold rows 0-7 (minus the offset of heads 2lq, 2lq+1),
+    // quarters 2-3 rows 8-15 (their zero-point terms)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+      const float own = accC[2 * hh] + accC[2 * hh + 1];
+      // lanes 0-31 take the zero-point sums of lanes 32-63
+      const float corr = own + __uint_as_float(__builtin_amdgcn_permlane32_swap(
+                                   __float_as_uint(own), __float_as_uint(own), false, false)[1]);
       const bool ok = 2 * lq + hh < Gb;
-      const float corr = accC[2 * hh] + accC[2 * hh + 1];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
         x[hh][ct] = ok ? (accS[ct][2 * hh] + accS[ct][2 * hh + 1] + corr) * a.scale2 : -INFINITY;
     }
-    softmax_update(x);
-    // value operand A (p x token scale per group) and split(p x zero-point)
+  };
+  // ---- value stage of a history tile: rows 2h, 2h+1 = split(p*scale*2^(7-pos));
+  // the lane keeps p*zero - (hi + lo) of its pieces in vcorr
+  auto v_stage = [&](const HistRegs& cur) {
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int vi = lane + 64 * u;
       if (vi < D / 2) {
-        const int g = vi >> 4, pr = vi & 15, jj = pr & 3;
-        const int t_lo = value_token<BITS>(pr >> 2, jj, 0), t_hi = value_token<BITS>(pr >> 2, jj, 1);
-        const float f = static_cast<float>(1 << (7 - code_pos<BITS>(jj)));
+        const int g = vi >> 4, pr = vi & 15, q4 = pr >> 2, m = pr & 3;
+        const int t_lo = value_token<BITS>(q4, 2 * m), t_hi = t_lo + PAIR;
+        const float f = static_cast<float>(1 << (7 - value_pos<BITS>(q4, 2 * m)));
         const float sc0 = f16_bits_to_f32(cur.vm[u][0] & 0xFFFFu) * f;
         const float sc1 = f16_bits_to_f32(cur.vm[u][1] & 0xFFFFu) * f;
         const float zp0 = f16_bits_to_f32(cur.vm[u][0] >> 16), zp1 = f16_bits_to_f32(cur.vm[u][1] >> 16);
-        const int ob = g * R2 * 32 + 2 * pr;
-#pragma unroll 1
-        for (int h = 0; h < Gb; ++h) {
-          const float p0 = pbuf[h * 32 + t_lo], p1 = pbuf[h * 32 + t_hi];
-          const Split a0 = split2(p0 * sc0), a1 = split2(p1 * sc1);
-          const Split z0 = split2(p0 * zp0), z1 = split2(p1 * zp1);
-          const int o_hi = ob + 64 * h, o_lo = o_hi + 32;
-          *reinterpret_cast<uint32_t*>(AV + o_hi) = a0.hi | (a1.hi << 16);
-          *reinterpret_cast<uint32_t*>(AV + o_lo) = a0.lo | (a1.lo << 16);
-          *reinterpret_cast<uint32_t*>(AVz + o_hi) = z0.hi | (z1.hi << 16);
-          *reinterpret_cast<uint32_t*>(AVz + o_lo) = z0.lo | (z1.lo << 16);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(AV) + g * kBlkW + pr;
+#pragma unroll
+        for (int h = 0; h < kHB; ++h) {
+          if (h < Gb) {
+            const float p0 = pbuf[h * 32 + t_lo], p1 = pbuf[h * 32 + t_hi];
+            const float x0 = p0 * sc0, x1 = p1 * sc1;
+            const Pair pa = split_pair(x0, x1);
+            dst[(2 * h) * kRowW] = pa.hi;
+            dst[(2 * h + 1) * kRowW] = pa.lo;
+            vcorr[u][h] += (__builtin_fmaf(p0, zp0, -piece_sum(x0)) + __builtin_fmaf(p1, zp1, -piece_sum(x1)));
+          }
+        }
+      }
+    }
+  };
+  // ---- value MFMAs of a history tile
+  auto v_mma = [&](const HistRegs& cur) {
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) {
+      const u32x4 af = *reinterpret_cast<const u32x4*>(AV + 2 * (g * kBlkW + ln * kRowW + 4 * lq));
+      if constexpr (BITS == 2) {
+        oacc[2 * g] = mfma(af, unpack_lane(cur.vw[g].x, vsh, K), oacc[2 * g]);
+        oacc[2 * g + 1] = mfma(af, unpack_lane(cur.vw[g].y, vsh, K), oacc[2 * g + 1]);
+      } else {
+        oacc[2 * g] = mfma(af, unpack<4>(cur.vw[g].x, 0, K), oacc[2 * g]);
+        oacc[2 * g + 1] = mfma(af, unpack<4>(cur.vw[g].y, 0, K), oacc[2 * g + 1]);
+      }
+    }
+  };
+
+  // ---- packed history tiles [tb, th_end), software-pipelined: the key stage
+  // of tile t+1 and the value stage of tile t share each barrier, and the
+  // register slot of tile t is refilled with tile t+NR once its value MFMAs are
+  // issued.  Tile tb+i lives in ring[i % NR].
+  if (tb < th_end) {
+    k_stage(ring[0]);
+    wave_sync();
+    float x[2][2];
+    k_mma(ring[0], x);
+    softmax_update(x);
+    wave_sync();
+  }
+  for (int t = tb; t < th_end; t += NR) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int tt = t + u;
+      if (tt < th_end) {
+        const bool nxt = tt + 1 < th_end;
+        if (nxt) k_stage(ring[(u + 1) % NR]);
+        v_stage(ring[u]);
+        wave_sync();
+        float x[2][2];
+        if (nxt) k_mma(ring[(u + 1) % NR], x);
+        v_mma(ring[u]);
+        if (nxt) softmax_update(x);
+        wave_sync();
+      }
+      load_hist(min(tt + NR, hlast), ring[u]);
+    }
+  }
+
+  // ---- residual tiles: bf16 keys/values as stored (appended token from the
+  // input).  Their key operand split(q), in natural channel order, goes to this
+  // wave's key area (no longer needed): rows 2h, 2h+1 for h < Gb, zeros elsewhere.
+  if (r_first < NTr) {
+    uint32_t* ak32 = reinterpret_cast<uint32_t*>(AK);
+    for (int e = lane; e < KS * kBlkW; e += 64) ak32[e] = 0u;
+    wave_sync();
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      if (lane + 64 * u < D / 2) {
+#pragma unroll
+        for (int h = 0; h < kHB; ++h) {
+          if (h < Gb) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int c = cpair[u] + i * PAIR;
+              const float v = i ? qa1[u][h] : qa0[u][h];
+              const float r = v - __uint_as_float(__float_as_uint(v) & kHi);
+              uint16_t* row = AK + 2 * ((c >> 5) * kBlkW + 2 * h * kRowW) + (c & 31);
+              row[0] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+              row[2 * kRowW] = static_cast<uint16_t>(__float_as_uint(r) >> 16);
+            }
+          }
         }
       }
     }
     wave_sync();
-    const int half = (BITS == 2) ? (lq & 1) : 0;
-#pragma unroll
-    for (int g = 0; g < NGV; ++g) {
-      const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AV + (g * R2 + ln) * 32 + 8 * lq) : zero4;
-      const u32x4 az = row_on ? *reinterpret_cast<const u32x4*>(AVz + (g * R2 + ln) * 32 + 8 * lq) : zero4;
-      oacc[2 * g] = mfma(af, unpack4<BITS>(cur.vw[g].x, half), oacc[2 * g]);
-      oacc[2 * g + 1] = mfma(af, unpack4<BITS>(cur.vw[g].y, half), oacc[2 * g + 1]);
-      vcorr[g] = mfma(af, neg4, vcorr[g]);
-      vcorr[g] = mfma(az, ones4, vcorr[g]);
-    }
-    wave_sync();
-  };
-
-  // ---- packed history tiles [tb, th_end) with a kPrefetch-deep register ring:
-  // the slot just consumed is refilled with the tile kPrefetch ahead
-  const int th_end = min(te, NTh);
-  HistRegs ring[kPrefetch];
-#pragma unroll
-  for (int u = 0; u < kPrefetch; ++u)
-    if (tb + u < th_end) load_hist(tb + u, ring[u]);
-  __syncthreads();  // the block's q setup is complete
-  for (int tile = tb; tile < th_end; tile += kPrefetch) {
-#pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) {
-      const int t = tile + u;
-      if (t < th_end) {
-        process_hist(ring[u], t);
-        if (t + kPrefetch < th_end) load_hist(t + kPrefetch, ring[u]);
-      }
-    }
   }
-
-  // ---- residual tiles: bf16 keys/values as stored (appended token from the input)
-  for (int tile = max(tb, NTh); tile < te; ++tile) {
-    const int t0 = (tile - NTh) * kGroup;
+  for (int rt = r_first; rt < NTr; rt += NWT) {
+    const int t0 = rt * kGroup;
     const bool has_new = a.r_new >= t0 && a.r_new < t0 + kGroup;
+    // value rows of this lane (8 tokens of 2*NGV channels), requested first
+    const int tl = t0 + 8 * lq;                     // first token of this lane's 8 slots
+    const int tlc = min(tl, (a.r_total - 1) & ~7);  // an in-range chunk for loading
+    u32x4 vraw[NGV][2];
+#pragma unroll
+    for (int g = 0; g < NGV; ++g)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        vraw[g][u] = *reinterpret_cast<const u32x4*>(vr + static_cast<size_t>(32 * g + 2 * ln + u) * a.r_cap + tlc);
     f32x4 accS[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -473,7 +616,7 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 bf = *reinterpret_cast<const u32x4*>(kr + static_cast<size_t>(tc) * D + 32 * s + 8 * lq);
-        if (t >= a.r_total) bf = zero4;
+        if (t >= a.r_total) bf = u32x4{0u, 0u, 0u, 0u};
         if (has_new && t == a.r_new) {
           const int c = 32 * s + 8 * lq;
           bf.x = load_bf16_pair(knp, c);
@@ -481,7 +624,7 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
           bf.z = load_bf16_pair(knp, c + 4);
           bf.w = load_bf16_pair(knp, c + 6);
         }
-        const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(ares + (s * R2 + ln) * 32 + 8 * lq) : zero4;
+        const u32x4 af = *reinterpret_cast<const u32x4*>(AK + 2 * (s * kBlkW + ln * kRowW + 4 * lq));
         accS[ct] = mfma(af, bf, accS[ct]);
       }
     }
@@ -496,26 +639,25 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
       }
     }
     softmax_update(x);
-    // values: A = p in natural token order, B = values as stored (channel-major)
+    wave_sync();
+    // values: A = p in natural token order (rows of group area 0), B = values as
+    // stored (channel-major)
     for (int i = lane; i < Gb * 16; i += 64) {
       const int h = i % Gb, pr = i / Gb;
-      const Split a0 = split2(pbuf[h * 32 + 2 * pr]);
-      const Split a1 = split2(pbuf[h * 32 + 2 * pr + 1]);
-      const int o_hi = (2 * h) * 32 + 2 * pr, o_lo = o_hi + 32;
-      *reinterpret_cast<uint32_t*>(AV + o_hi) = a0.hi | (a1.hi << 16);
-      *reinterpret_cast<uint32_t*>(AV + o_lo) = a0.lo | (a1.lo << 16);
+      const Pair pa = split_pair(pbuf[h * 32 + 2 * pr], pbuf[h * 32 + 2 * pr + 1]);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(AV) + pr;
+      dst[(2 * h) * kRowW] = pa.hi;
+      dst[(2 * h + 1) * kRowW] = pa.lo;
     }
     wave_sync();
-    const u32x4 af = row_on ? *reinterpret_cast<const u32x4*>(AV + ln * 32 + 8 * lq) : zero4;
-    const int tl = t0 + 8 * lq;                     // first token of this lane's 8 slots
-    const int tlc = min(tl, (a.r_total - 1) & ~7);  // an in-range chunk for loading
+    const u32x4 af = *reinterpret_cast<const u32x4*>(AV + 2 * (ln * kRowW + 4 * lq));
     const bool clean = tl + 8 <= a.r_total && !(a.r_new >= tl && a.r_new < tl + 8);
 #pragma unroll
     for (int g = 0; g < NGV; ++g) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = 32 * g + 2 * ln + u;
-        u32x4 bf = *reinterpret_cast<const u32x4*>(vr + static_cast<size_t>(c) * a.r_cap + tlc);
+        u32x4 bf = vraw[g][u];
         if (!clean) {
           // zero slots past the residual, substitute the appended token
 #pragma unroll
@@ -534,7 +676,7 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
   }
 
   // the wave that owns the appended token's tile stores it
-  if (a.r_new >= 0 && hb == 0 && te > tb && tb <= NTh + a.r_new / kGroup && NTh + a.r_new / kGroup < te) {
+  if (a.r_new >= 0 && hb == 0 && r_first <= a.r_new / kGroup && (a.r_new / kGroup - r_first) % NWT == 0) {
     uint16_t* kw = a.k_res + (static_cast<size_t>(bj) * a.r_cap + a.r_new) * D;
     uint16_t* vw = a.v_res + static_cast<size_t>(bj) * D * a.r_cap + a.r_new;
     for (int c = lane; c < D; c += 64) {
@@ -543,9 +685,27 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
     }
   }
 
+  // ---- value corrections: sum the lanes of each channel group (one DPP row)
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int g = (lane + 64 * u) >> 4;
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      const float s = sum16(vcorr[u][h]);
+      if (ln == 0 && g < NGV) vcs[h * 8 + g] = s;
+    }
+  }
+  wave_sync();
+
   // ---------------------------------------------------------------- merge the block's waves
   // Each wave leaves (o[Gb][D], m[Gb], l[Gb]) in its own LDS region (its operand
-  // area is no longer needed); after one barrier the block combines the four.
+  // area is no longer needed); after one barrier the block combines them.
+  float corr_g[2][NGV];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) corr_g[hh][g] = vcs[((2 * lq + hh) & (kHB - 1)) * 8 + g];
+  wave_sync();
   float* wst = reinterpret_cast<float*>(wbase);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
@@ -553,15 +713,14 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
     const float l = sum16(l_part[hh]);
     if (head < Gb) {
       if (ln == 0) {
-        wst[Gb * D + head] = m_run[hh];
-        wst[Gb * D + Gb + head] = l;
+        wst[kHB * D + head] = m_run[hh];
+        wst[kHB * D + kHB + head] = l;
       }
 #pragma unroll
       for (int g = 0; g < NGV; ++g) {
-        const float corr = vcorr[g][2 * hh] + vcorr[g][2 * hh + 1];
         float2 v;
-        v.x = oacc[2 * g][2 * hh] + oacc[2 * g][2 * hh + 1] + corr;
-        v.y = oacc[2 * g + 1][2 * hh] + oacc[2 * g + 1][2 * hh + 1] + corr;
+        v.x = oacc[2 * g][2 * hh] + oacc[2 * g][2 * hh + 1] + corr_g[hh][g];
+        v.y = oacc[2 * g + 1][2 * hh] + oacc[2 * g + 1][2 * hh + 1] + corr_g[hh][g];
         *reinterpret_cast<float2*>(wst + head * D + 32 * g + 2 * ln) = v;
       }
     }
@@ -569,21 +728,21 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
   __syncthreads();
   const bool final_out = gridDim.x == 1;
   const size_t pb = (static_cast<size_t>(bjh) * gridDim.x + blockIdx.x) * kHB;
-  for (int e = tid; e < Gb * D; e += kThreads) {
+  for (int e = tid; e < Gb * D; e += NTHR) {
     const int h = e / D, c = e % D;
-    float mw[kWaves], lw[kWaves], M = -INFINITY;
+    float mw[NWV], lw[NWV], M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       const float* ws_w = reinterpret_cast<const float*>(smem + L.wave0 + w * L.wave_bytes);
-      mw[w] = ws_w[Gb * D + h];
-      lw[w] = ws_w[Gb * D + Gb + h];
+      mw[w] = ws_w[kHB * D + h];
+      lw[w] = ws_w[kHB * D + kHB + h];
       M = fmaxf(M, mw[w]);
     }
     float Lsum = 0.0f, acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       if (lw[w] > 0.0f) {
-        const float f = exp2f(mw[w] - M);
+        const float f = __builtin_amdgcn_exp2f(mw[w] - M);
         Lsum += lw[w] * f;
         acc += f * reinterpret_cast<const float*>(smem + L.wave0 + w * L.wave_bytes)[h * D + c];
       }
@@ -601,8 +760,9 @@ __global__ __launch_bounds__(kThreads, (KS == 2 || KS == 4) ? 2 : 1) void decode
 // split weights 2^(m_s - M)/L per head go to LDS first, then every output is an
 // independent-load weighted sum over the splits.
 constexpr int kMaxNb = 64;
-__global__ __launch_bounds__(kThreads) void merge_kernel(const float* part_o, const float2* part_ml, float* out,
-                                                         int Hq, int Hkv, int G, int HB, int D, int nb) {
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* part_o, const float2* part_ml, float* out,
+                                                              int Hq, int Hkv, int G, int HB, int D, int nb) {
   __shared__ float wgt[kHB][kMaxNb];
   const int jh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int j = jh / HB, hb = jh % HB, h0 = hb * kHB;
@@ -610,19 +770,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* part_o, co
   const size_t base = ((static_cast<size_t>(b) * Hkv + j) * HB + hb) * nb;
   // one 64-lane wave per head: lane s holds split s
   const int wave = tid >> 6, lane = tid & 63;
-  for (int h = wave; h < Gb; h += kThreads / 64) {
+  for (int h = wave; h < Gb; h += kMergeThreads / 64) {
     const float2 ml = lane < nb ? part_ml[(base + lane) * kHB + h] : make_float2(-INFINITY, 0.0f);
     float M = ml.x;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = ml.y > 0.0f ? exp2f(ml.x - M) : 0.0f;
+    const float f = ml.y > 0.0f ? __builtin_amdgcn_exp2f(ml.x - M) : 0.0f;
     float Lsum = f * ml.y;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) Lsum += __shfl_xor(Lsum, o);
     if (lane < nb) wgt[h][lane] = f / Lsum;
   }
   __syncthreads();
-  for (int e = tid; e < Gb * D; e += kThreads) {
+  for (int e = tid; e < Gb * D; e += kMergeThreads) {
     const int h = e / D, c = e % D;
     const float* po = part_o + (base * kHB + h) * D + c;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -636,21 +796,84 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* part_o, co
   }
 }
 
+// ---------------------------------------------------------------- planning
+// Short runs: one workgroup per (batch, KV head, head block) -- eight waves when
+// registers allow -- so no merge pass is needed.  Long runs: one round of the
+// 4-wave workgroups the chip holds at once (the occupancy query below), spread
+// over the units, each unit's tiles evenly over its waves, then merge_kernel.
+constexpr int kShortTilesPerWave = 6;
+
 struct Plan {
-  int tpw, nb;  // tiles per wave, blocks per (batch, KV head, head block)
+  int nb, nwv;  // workgroups per unit, waves per workgroup
 };
-// One round of resident workgroups: as many blocks per unit as fit the chip at
-// once (two workgroups per CU when the kernel fits two waves per SIMD), then
-// spread the unit's tiles evenly over their waves.
-constexpr int kCUs = 256;
-Plan plan(int NT, int units, int KS) {
-  const int per_cu = (KS == 2 || KS == 4) ? 2 : 1;
+
+template <typename T, int BITS, int KS, int NWV> const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&decode_kernel<T, BITS, KS, NWV>);
+}
+const void* kernel_for(int dt, int bits, int KS, int nwv) {
+#define KVC_PTRS(k)                                                                              \
+  case k:                                                                                        \
+    if (dt == KVC_F32) return bits == 2 ? kernel_ptr<float, 2, k, NWV>() : kernel_ptr<float, 4, k, NWV>(); \
+    return bits == 2 ? kernel_ptr<uint16_t, 2, k, NWV>() : kernel_ptr<uint16_t, 4, k, NWV>();
+  if (nwv == 8) {
+    constexpr int NWV = 8;
+    switch (KS) { KVC_PTRS(1) KVC_PTRS(2) KVC_PTRS(3) KVC_PTRS(4) KVC_PTRS(5) KVC_PTRS(6) default: return nullptr; }
+  }
+  constexpr int NWV = 4;
+  switch (KS) {
+    KVC_PTRS(1) KVC_PTRS(2) KVC_PTRS(3) KVC_PTRS(4) KVC_PTRS(5) KVC_PTRS(6) KVC_PTRS(7) KVC_PTRS(8)
+    default: return nullptr;
+  }
+#undef KVC_PTRS
+}
+
+// Workgroups of the 4-wave kernel resident per CU, and the CU count of the
+// current device (queried once per device and instantiation).
+struct Occupancy {
+  int per_cu, cus;
+};
+Occupancy occupancy(int dt, int bits, int KS) {
+  static int cache[8][2][2][9] = {};  // [device][dtype][bits][KS]: per_cu * 4096 + cus
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) dev = 0;
+  int& c = cache[dev][dt == KVC_F32 ? 0 : 1][bits == 2 ? 0 : 1][KS];
+  if (c == 0) {
+    // allow the dynamic LDS of both workgroup shapes, then ask for the occupancy
+    for (int nwv = 4; nwv <= 8; nwv += 4) {
+      const void* k = kernel_for(dt, bits, KS, nwv);
+      const int bytes = lds_layout(KS, nwv).total;
+      if (k && bytes > 65536) {
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) {
+          set_last_hip_error(e);
+          return Occupancy{0, 0};
+        }
+      }
+    }
+    int per_cu = 0, cus = 0;
+    const void* k = kernel_for(dt, bits, KS, 4);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_layout(KS, 4).total) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    c = per_cu * 4096 + cus;
+  }
+  return Occupancy{c / 4096, c % 4096};
+}
+
+Plan plan(int NT, int units, int KS, const Occupancy& oc) {
   Plan p;
-  int nb = std::max(1, kCUs * per_cu / units);
-  nb = std::min(nb, (NT + kWaves - 1) / kWaves);  // no block without a tile
+  const int nwv_short = KS <= 6 ? 8 : 4;
+  if ((NT + nwv_short - 1) / nwv_short <= kShortTilesPerWave) {
+    p.nwv = nwv_short;
+    p.nb = 1;
+    return p;
+  }
+  p.nwv = 4;
+  int nb = std::max(1, oc.cus * oc.per_cu / units);
+  nb = std::min(nb, (NT + 3) / 4);  // no workgroup without a tile
   nb = std::min(nb, kMaxNb);
-  p.tpw = (NT + kWaves * nb - 1) / (kWaves * nb);
-  p.nb = (NT + kWaves * p.tpw - 1) / (kWaves * p.tpw);
+  p.nb = nb;
   return p;
 }
 
@@ -658,12 +881,12 @@ struct WsLayout {
   size_t part_ml, part_o, total;
   int nb_max;
 };
-WsLayout ws_layout(const kvc_cache* c, int HB) {
+WsLayout ws_layout(const kvc_cache* c, int HB, const Occupancy& oc) {
   const int units = c->batch * c->kv_heads * HB;
   const int NTmax = c->q_cap / kGroup + (c->r_cap + kGroup - 1) / kGroup;
   int nmax = 1;
   // nb is not monotone in NT; take the maximum over every possible length
-  for (int nt = 1; nt <= NTmax; ++nt) nmax = std::max(nmax, plan(nt, units, c->head_dim / 32).nb);
+  for (int nt = 1; nt <= NTmax; ++nt) nmax = std::max(nmax, plan(nt, units, c->head_dim / 32, oc).nb);
   WsLayout w;
   w.nb_max = nmax;
   w.part_ml = 0;
@@ -672,31 +895,20 @@ WsLayout ws_layout(const kvc_cache* c, int HB) {
   return w;
 }
 
-template <typename T, int BITS>
-kvc_status launch_decode(const DecArgs& a, int KS, int B, hipStream_t st) {
-  const int Gmax = std::min(kHB, a.G);
-  const Lds L = lds_layout(KS, Gmax);
+kvc_status launch_decode(const DecArgs& a, int dt, int bits, int KS, int nwv, int B, hipStream_t st) {
+  const void* k = kernel_for(dt, bits, KS, nwv);
+  if (!k) return KVC_ERR_SHAPE;
+  const int bytes = lds_layout(KS, nwv).total;
   dim3 grid(a.nb, a.Hkv * a.HB, B);
-  switch (KS) {
-#define KVC_CASE(k)                                                                                      \
-  case k:                                                                                                \
-    if (L.total > 65536) {                                                                               \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, BITS, k>),     \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, L.total);           \
-      if (e != hipSuccess) {                                                                             \
-        set_last_hip_error(e);                                                                           \
-        return KVC_ERR_HIP;                                                                              \
-      }                                                                                                  \
-    }                                                                                                    \
-    hipLaunchKernelGGL((decode_kernel<T, BITS, k>), grid, dim3(kThreads), L.total, st, a);              \
-    break;
-    KVC_CASE(1) KVC_CASE(2) KVC_CASE(3) KVC_CASE(4) KVC_CASE(5) KVC_CASE(6) KVC_CASE(7) KVC_CASE(8)
-#undef KVC_CASE
-    default: return KVC_ERR_SHAPE;
+  void* args[] = {const_cast<DecArgs*>(&a)};
+  hipError_t e = hipLaunchKernel(k, grid, dim3(64 * nwv), args, bytes, st);
+  if (e != hipSuccess) {
+    set_last_hip_error(e);
+    return KVC_ERR_HIP;
   }
   kvc_status st2 = check_launch();
   if (st2 != KVC_OK || a.nb == 1) return st2;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.Hkv * a.HB, B), dim3(kThreads), 0, st, a.part_o, a.part_ml, a.out,
+  hipLaunchKernelGGL(merge_kernel, dim3(a.Hkv * a.HB, B), dim3(kMergeThreads), 0, st, a.part_o, a.part_ml, a.out,
                      a.Hq, a.Hkv, a.G, a.HB, 32 * KS, a.nb);
   return check_launch();
 }
@@ -716,7 +928,10 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   if (Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return KVC_ERR_SHAPE;
   const int G = Hq / Hkv;
   const int HB = (G + kHB - 1) / kHB;
-  const WsLayout W = ws_layout(cache, HB);
+  const int KS = cache->head_dim / 32;
+  const Occupancy oc = occupancy(dtype, cache->bits, KS);
+  if (oc.cus == 0) return KVC_ERR_HIP;
+  const WsLayout W = ws_layout(cache, HB, oc);
   if (!ws) {
     *ws_bytes = W.total;
     return KVC_OK;
@@ -760,18 +975,12 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   a.q_len = cache->q_len;
   const int units = cache->batch * Hkv * HB;
   const int NT = a.q_len / kGroup + (a.r_total + kGroup - 1) / kGroup;
-  const Plan p = plan(NT, units, cache->head_dim / 32);
-  a.tpw = p.tpw;
+  const Plan p = plan(NT, units, KS, oc);
   a.nb = p.nb;
   char* w = static_cast<char*>(ws);
   a.part_ml = reinterpret_cast<float2*>(w + W.part_ml);
   a.part_o = reinterpret_cast<float*>(w + W.part_o);
   a.out = out;
   a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(cache->head_dim));
-  const int KS = cache->head_dim / 32;
-  if (dtype == KVC_F32)
-    return cache->bits == 2 ? launch_decode<float, 2>(a, KS, cache->batch, st)
-                            : launch_decode<float, 4>(a, KS, cache->batch, st);
-  return cache->bits == 2 ? launch_decode<uint16_t, 2>(a, KS, cache->batch, st)
-                          : launch_decode<uint16_t, 4>(a, KS, cache->batch, st);
+  return launch_decode(a, dtype, cache->bits, KS, p.nwv, cache->batch, st);
 }
