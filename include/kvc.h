@@ -45,11 +45,13 @@
  *                                       token (32/bits)*w+i at bits bits*i
  *   v_meta  [B][Hkv][q_cap][D/32]       uint32: token t, channels 32j..32j+31
  *   meta word = fp16 scale bits | (fp16 zero-point bits << 16)
- *   k_res [B][Hkv][r_cap][D]            uint16 bfloat16 keys, token-major,
- *                                       oldest first
+ *   k_res [B][Hkv][r_cap][D]            uint16 bfloat16 keys, token-major
  *   v_res [B][Hkv][D][r_cap]            uint16 bfloat16 values, channel-major
  *                                       (a decode step reads 8 consecutive
  *                                       tokens of one channel per load)
+ *   The residual is a ring: its i-th oldest token (i < r_len) is row
+ *   (r_start + i) % r_cap of every (b, head).  A flush quantizes the 32 oldest
+ *   and advances r_start by 32, so no residual data is ever moved.
  * Codes are LSB-first (MiniKV Sec. 4.4: 16 INT2 values shifted into one INT32).
  * Dequantized value = zero + code * scale.
  */
@@ -86,6 +88,8 @@ typedef struct {
   int32_t q_cap, q_len;              /* packed history, tokens (multiples of 32)*/
   int32_t r_cap, r_len;              /* bf16 residual, tokens; r_cap >= R + 32,
                                         r_cap a multiple of 8                  */
+  int32_t r_start;                   /* ring row of the oldest residual token
+                                        (a multiple of 8, < r_cap)             */
   uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;
 } kvc_cache;
@@ -164,7 +168,8 @@ kvc_status kvc_select(const void *q_win, const void *k, kvc_dtype dtype, int32_t
  * float32 (scale 0 -> codes 0); the last T-Q go to the residual as bf16.
  *   k, v [B][Hkv][n][D] dtype; idx [B][Hkv][k_sel] int32 (ascending, < n-W) or
  *   NULL; cache: batch/kv_heads/head_dim/bits/residual/capacities/pointers set,
- *   q_len == r_len == 0.  On success cache->q_len = Q, cache->r_len = T-Q.
+ *   q_len == r_len == 0.  On success cache->q_len = Q, cache->r_len = T-Q,
+ *   cache->r_start = 0.
  * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_BITS, KVC_ERR_SHAPE,
  *   KVC_ERR_CAPACITY (cache not empty, Q > q_cap, T-Q > r_cap or
  *   r_cap < R+32), KVC_ERR_HIP. */

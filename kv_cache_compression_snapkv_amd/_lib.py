@@ -30,7 +30,7 @@ class CacheStruct(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("q_cap", ctypes.c_int32), ("q_len", ctypes.c_int32),
-                ("r_cap", ctypes.c_int32), ("r_len", ctypes.c_int32),
+                ("r_cap", ctypes.c_int32), ("r_len", ctypes.c_int32), ("r_start", ctypes.c_int32),
                 ("k_codes", ctypes.c_void_p), ("k_meta", ctypes.c_void_p),
                 ("v_codes", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
                 ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p)]
@@ -159,7 +159,7 @@ class Cache:
         self.k_codes, self.k_meta = u32(sizes[0]), u32(sizes[1])
         self.v_codes, self.v_meta = u32(sizes[2]), u32(sizes[3])
         self.k_res, self.v_res = u16(sizes[4]), u16(sizes[5])
-        self.s = CacheStruct(batch, kv_heads, head_dim, bits, residual, q_cap, 0, r_cap, 0,
+        self.s = CacheStruct(batch, kv_heads, head_dim, bits, residual, q_cap, 0, r_cap, 0, 0,
                              self.k_codes.data_ptr(), self.k_meta.data_ptr(), self.v_codes.data_ptr(),
                              self.v_meta.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr())
         self._ws = None
@@ -172,23 +172,30 @@ class Cache:
     def r_len(self):
         return self.s.r_len
 
+    @property
+    def r_start(self):
+        return self.s.r_start
+
     def reset(self):
         """Mark the cache empty (buffers are kept; the next kvc_quantize refills them)."""
         self.s.q_len = 0
         self.s.r_len = 0
+        self.s.r_start = 0
 
     def views(self):
         """Logical views of the stored state (for tests): codes/meta/residual per (b, j)."""
         s = self.s
         B, H, D, b = s.batch, s.kv_heads, s.head_dim, s.bits
         qc, rc = s.q_cap, s.r_cap
+        # residual ring rows, oldest first
+        rows = (s.r_start + torch.arange(s.r_len, device=self.k_res.device)) % max(rc, 1)
         return {
             "k_codes": self.k_codes.view(B, H, qc, D * b // 32)[:, :, : s.q_len],
             "k_meta": self.k_meta.view(B, H, qc // 32, D)[:, :, : s.q_len // 32],
             "v_codes": self.v_codes.view(B, H, qc * b // 32, D)[:, :, : s.q_len * b // 32],
             "v_meta": self.v_meta.view(B, H, qc, D // 32)[:, :, : s.q_len],
-            "k_res": self.k_res.view(B, H, rc, D)[:, :, : s.r_len],
-            "v_res": self.v_res.view(B, H, D, rc)[:, :, :, : s.r_len].transpose(-1, -2),
+            "k_res": self.k_res.view(B, H, rc, D).index_select(2, rows),
+            "v_res": self.v_res.view(B, H, D, rc).index_select(3, rows).transpose(-1, -2),
         }
 
 

@@ -167,6 +167,7 @@ struct DecArgs {
   float* out;               // [B][Hq][D]
   int Hq, Hkv, G, HB, q_cap, r_cap;
   int q_len, r_total, r_new;
+  int r_start;  // ring row of residual token 0 (residual token t is row (r_start + t) % r_cap)
   int nb;
   float scale2;  // log2(e)/sqrt(D)
 };
@@ -278,6 +279,10 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   const uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;
   const T* knp = static_cast<const T*>(a.k_new) + static_cast<size_t>(bj) * D;
   const T* vnp = static_cast<const T*>(a.v_new) + static_cast<size_t>(bj) * D;
+  auto rrow = [&](int t) {  // residual token -> ring row (t < r_cap)
+    const int p = a.r_start + t;
+    return p >= a.r_cap ? p - a.r_cap : p;
+  };
 
   // Tiles of this wave: an even share of the history tiles (a contiguous run)
   // and every NWT-th residual tile counted from the last wave, so the costlier
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
     const bool has_new = a.r_new >= t0 && a.r_new < t0 + kGroup;
     // value rows of this lane (8 tokens of 2*NGV channels), requested first
     const int tl = t0 + 8 * lq;                     // first token of this lane's 8 slots
-    const int tlc = min(tl, (a.r_total - 1) & ~7);  // an in-range chunk for loading
+    const int tlc = rrow(min(tl, (a.r_total - 1) & ~7));  // an in-range chunk for loading (ring row)
     u32x4 vraw[NGV][2];
 #pragma unroll
     for (int g = 0; g < NGV; ++g)
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int t = t0 + col_token(ct, ln);
-      const int tc = min(t, a.r_total - 1);
+      const int tc = rrow(min(t, a.r_total - 1));
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 bf = *reinterpret_cast<const u32x4*>(kr + static_cast<size_t>(tc) * D + 32 * s + 8 * lq);
@@ -677,8 +682,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
 
   // the wave that owns the appended token's tile stores it
   if (a.r_new >= 0 && hb == 0 && r_first <= a.r_new / kGroup && (a.r_new / kGroup - r_first) % NWT == 0) {
-    uint16_t* kw = a.k_res + (static_cast<size_t>(bj) * a.r_cap + a.r_new) * D;
-    uint16_t* vw = a.v_res + static_cast<size_t>(bj) * D * a.r_cap + a.r_new;
+    uint16_t* kw = a.k_res + (static_cast<size_t>(bj) * a.r_cap + rrow(a.r_new)) * D;
+    uint16_t* vw = a.v_res + static_cast<size_t>(bj) * D * a.r_cap + rrow(a.r_new);
     for (int c = lane; c < D; c += 64) {
       kw[c] = f32_to_bf16(load_f32(knp, c));
       vw[static_cast<size_t>(c) * a.r_cap] = f32_to_bf16(load_f32(vnp, c));
@@ -953,6 +958,7 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
     if (s != KVC_OK) return s;
     cache->q_len += kGroup;
     cache->r_len = R;
+    cache->r_start = (cache->r_start + kGroup) % cache->r_cap;
     a.r_total = R;
     a.r_new = -1;
   } else {
@@ -972,6 +978,7 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   a.HB = HB;
   a.q_cap = cache->q_cap;
   a.r_cap = cache->r_cap;
+  a.r_start = cache->r_start;
   a.q_len = cache->q_len;
   const int units = cache->batch * Hkv * HB;
   const int NT = a.q_len / kGroup + (a.r_total + kGroup - 1) / kGroup;

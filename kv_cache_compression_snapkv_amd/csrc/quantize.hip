@@ -159,15 +159,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 struct FlushArgs {
   const void* k_new;
   const void* v_new;
-  int D, Hkv, R, r_old, q_len, q_cap, r_cap;
+  int D, Hkv, R, r_old, r_start, q_len, q_cap, r_cap;
   uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;
 };
 
-// Decode-step flush: the residual held r_old = R+31 tokens; the new token makes
-// it R+32.  Quantize the oldest 32 (the new token is among them only when R==0),
-// append them at q_len, and shift the remaining R tokens (ending with the new
-// one) to the front of the residual.
+// Decode-step flush: the residual ring held r_old = R+31 tokens; the new token
+// makes it R+32.  Quantize the oldest 32 (the new token is among them only when
+// R == 0) and append them to the packed history at q_len; the new token takes
+// ring row r_start + r_old.  The host then advances r_start by 32.  Keys are
+// staged with 16-byte row loads, values with 16-byte loads of 8 consecutive
+// ring rows of one channel (r_start and r_cap are multiples of 8, so such a
+// chunk never wraps).
 template <typename T, int BITS>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   __shared__ QuantLds L;
@@ -179,13 +182,43 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   const T* vn = static_cast<const T*>(a.v_new) + static_cast<size_t>(bj) * D;
   uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
   uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
-  for (int e = tid; e < kGroup * D; e += kThreads) {
-    const int t = e / D, c = e % D;  // keys: token-major
-    const uint16_t kb = t < a.r_old ? kr[static_cast<size_t>(t) * D + c] : f32_to_bf16(load_f32(kn, c));
-    L.k[t][c] = bf16_to_f32(kb);
-    const int cv = e / kGroup, tv = e % kGroup;  // values: channel-major
-    const uint16_t vb = tv < a.r_old ? vr[static_cast<size_t>(cv) * a.r_cap + tv] : f32_to_bf16(load_f32(vn, cv));
-    L.v[tv][cv] = bf16_to_f32(vb);
+  auto ring = [&](int t) {
+    const int p = a.r_start + t;
+    return p >= a.r_cap ? p - a.r_cap : p;
+  };
+  const int cpr = D / 8;  // 16-byte chunks per key row
+  for (int e = tid; e < kGroup * cpr; e += kThreads) {
+    const int t = e / cpr, c8 = (e % cpr) * 8;
+    const uint4 w = *reinterpret_cast<const uint4*>(kr + static_cast<size_t>(ring(t)) * D + c8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      L.k[t][c8 + 2 * i] = bf16_to_f32(static_cast<uint16_t>(ws[i] & 0xFFFFu));
+      L.k[t][c8 + 2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(ws[i] >> 16));
+    }
+  }
+  for (int e = tid; e < D * (kGroup / 8); e += kThreads) {
+    const int c = e / (kGroup / 8), t8 = (e % (kGroup / 8)) * 8;
+    const uint4 w = *reinterpret_cast<const uint4*>(vr + static_cast<size_t>(c) * a.r_cap + ring(t8));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      L.v[t8 + 2 * i][c] = bf16_to_f32(static_cast<uint16_t>(ws[i] & 0xFFFFu));
+      L.v[t8 + 2 * i + 1][c] = bf16_to_f32(static_cast<uint16_t>(ws[i] >> 16));
+    }
+  }
+  __syncthreads();
+  // the new token: quantized with the group when R == 0, else kept in the ring
+  for (int c = tid; c < D; c += kThreads) {
+    const uint16_t kb = f32_to_bf16(load_f32(kn, c)), vb = f32_to_bf16(load_f32(vn, c));
+    if (a.r_old < kGroup) {
+      L.k[a.r_old][c] = bf16_to_f32(kb);
+      L.v[a.r_old][c] = bf16_to_f32(vb);
+    } else {
+      const int p = ring(a.r_old);
+      kr[static_cast<size_t>(p) * D + c] = kb;
+      vr[static_cast<size_t>(c) * a.r_cap + p] = vb;
+    }
   }
   __syncthreads();
   const size_t qc = a.q_cap;
@@ -193,34 +226,6 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
                        a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D,
                        a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
                        a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
-  // shift tokens [32, R+32) -> [0, R) in chunks of 32 tokens: each chunk is read
-  // in full before it is written, and it overwrites only the previous chunk's
-  // (already read) source tokens.  Token r_old is the appended one.
-  constexpr int kPer = kGroup * kMaxD / kThreads;
-  for (int r0 = 0; r0 < a.R; r0 += kGroup) {
-    const int nr = min(kGroup, a.R - r0);
-    uint16_t kb[kPer], vb[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < nr * D) {
-        const int t = r0 + e / D + kGroup, c = e % D;  // keys: token-major
-        kb[u] = t < a.r_old ? kr[static_cast<size_t>(t) * D + c] : f32_to_bf16(load_f32(kn, c));
-        const int cv = e / nr, tv = r0 + e % nr + kGroup;  // values: channel-major
-        vb[u] = tv < a.r_old ? vr[static_cast<size_t>(cv) * a.r_cap + tv] : f32_to_bf16(load_f32(vn, cv));
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < nr * D) {
-        kr[static_cast<size_t>(r0 + e / D) * D + e % D] = kb[u];
-        vr[static_cast<size_t>(e / nr) * a.r_cap + r0 + e % nr] = vb[u];
-      }
-    }
-    __syncthreads();
-  }
 }
 
 template <typename T>
@@ -246,6 +251,7 @@ kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new
   a.Hkv = c->kv_heads;
   a.R = c->residual;
   a.r_old = c->r_len;
+  a.r_start = c->r_start;
   a.q_len = c->q_len;
   a.q_cap = c->q_cap;
   a.r_cap = c->r_cap;
@@ -280,6 +286,7 @@ kvc_status cache_shape_status(const kvc_cache* c) {
       c->q_cap < 0 || c->q_cap % kGroup != 0 || c->r_cap < 0 || c->r_cap % 8 != 0 || c->q_len < 0 || c->r_len < 0 ||
       c->q_len % kGroup != 0)
     return KVC_ERR_SHAPE;
+  if (c->r_start < 0 || c->r_start % 8 != 0 || (c->r_cap > 0 && c->r_start >= c->r_cap)) return KVC_ERR_SHAPE;
   if (c->q_len > c->q_cap || c->r_len > c->r_cap || c->r_cap < c->residual + kGroup)
     return KVC_ERR_CAPACITY;
   return KVC_OK;
@@ -332,5 +339,6 @@ extern "C" kvc_status kvc_quantize(const void* k, const void* v, kvc_dtype dtype
   if (s != KVC_OK) return s;
   cache->q_len = Q;
   cache->r_len = T - Q;
+  cache->r_start = 0;
   return KVC_OK;
 }

@@ -100,7 +100,7 @@ def test_select_validation_and_ws_query():
 
 def _cache(**kw):
     L = _lib()
-    c = L.CacheStruct(1, 4, 64, 2, 16, 64, 0, 48, 0, 16, 16, 16, 16, 16, 16)
+    c = L.CacheStruct(1, 4, 64, 2, 16, 64, 0, 48, 0, 0, 16, 16, 16, 16, 16, 16)
     for k, v in kw.items():
         setattr(c, k, v)
     return c
@@ -119,6 +119,8 @@ def test_quantize_and_decode_validation():
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_cap=24)), None) == 5    # r_cap < R+32
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(q_cap=40)), None) == 2    # q_cap % 32
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_cap=52)), None) == 2    # r_cap % 8
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_start=4)), None) == 2   # ring start % 8
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_start=48)), None) == 2  # ring start >= r_cap
     d = L.lib.kvc_decode_attn
     need = ctypes.c_size_t(0)
     assert d(ctypes.byref(_cache()), None, None, None, 1, 4, None, None, ctypes.byref(need), None) == 0
