@@ -19,9 +19,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxD = 256;
 
+constexpr int kLdsRow = kMaxD + 4;  // float row stride: 16-byte aligned rows, column reads conflict-free
 struct QuantLds {
-  float k[kGroup][kMaxD + 1];
-  float v[kGroup][kMaxD + 1];
+  float k[kGroup][kLdsRow];
+  float v[kGroup][kLdsRow];
   float kz[kMaxD], kinv[kMaxD];
   float vz[kGroup][kMaxD / kGroup], vinv[kGroup][kMaxD / kGroup];
   uint8_t kok[kMaxD];
@@ -112,24 +113,64 @@ __device__ __forceinline__ int kept_pos(const QuantArgs& a, int bj, int t) {
   return min(max(p, 0), a.n - 1);
 }
 
+// Stage `count` kept tokens starting at kept index t_first (rows beyond count
+// are zero) as float32 rows of L.k / L.v.  Every 16-byte load of the 32 rows is
+// issued before the first LDS store: one memory round trip for the positions,
+// one for the data.
+template <typename T>
+__device__ void stage_rows(QuantLds& L, const QuantArgs& a, int bj, int t_first, int count) {
+  constexpr int VEC = 16 / sizeof(T);                      // elements per 16 bytes
+  constexpr int MAXV = kGroup * kMaxD / VEC / kThreads;    // pieces per thread at D = kMaxD
+  const int D = a.D, ppr = D / VEC, total = kGroup * ppr;  // pieces per row, per tensor
+  const T* k = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
+  const T* v = static_cast<const T*>(a.v) + static_cast<size_t>(bj) * a.n * D;
+  const int tid = threadIdx.x;
+  int pos[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = tid + i * kThreads, t = e / ppr;
+    pos[i] = (e < total && t < count) ? kept_pos(a, bj, t_first + t) : 0;
+  }
+  uint4 kv[MAXV], vv[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = tid + i * kThreads;
+    const size_t src = static_cast<size_t>(pos[i]) * D + (e % ppr) * VEC;
+    kv[i] = vv[i] = make_uint4(0, 0, 0, 0);
+    if (e < total && e / ppr < count) {
+      kv[i] = *reinterpret_cast<const uint4*>(k + src);
+      vv[i] = *reinterpret_cast<const uint4*>(v + src);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = tid + i * kThreads;
+    if (e < total) {
+      const int t = e / ppr, c = (e % ppr) * VEC;
+      const T* kx = reinterpret_cast<const T*>(&kv[i]);
+      const T* vx = reinterpret_cast<const T*>(&vv[i]);
+#pragma unroll
+      for (int u = 0; u < VEC; u += 4) {
+        *reinterpret_cast<float4*>(&L.k[t][c + u]) =
+            make_float4(load_f32(kx, u), load_f32(kx, u + 1), load_f32(kx, u + 2), load_f32(kx, u + 3));
+        *reinterpret_cast<float4*>(&L.v[t][c + u]) =
+            make_float4(load_f32(vx, u), load_f32(vx, u + 1), load_f32(vx, u + 2), load_f32(vx, u + 3));
+      }
+    }
+  }
+}
+
 template <typename T, int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ QuantLds L;
+  __shared__ __attribute__((aligned(16))) QuantLds L;
   const int blk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int bj = b * a.Hkv + j;
   const int D = a.D;
   const int tid = threadIdx.x;
-  const T* k = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
-  const T* v = static_cast<const T*>(a.v) + static_cast<size_t>(bj) * a.n * D;
   const int nqb = a.Q / kGroup;
   if (blk < nqb) {
     const int t0 = blk * kGroup;
-    for (int e = tid; e < kGroup * D; e += kThreads) {
-      const int t = e / D, c = e % D;
-      const size_t src = static_cast<size_t>(kept_pos(a, bj, t0 + t)) * D + c;
-      L.k[t][c] = load_f32(k, src);
-      L.v[t][c] = load_f32(v, src);
-    }
+    stage_rows<T>(L, a, bj, t0, kGroup);
     __syncthreads();
     const size_t qc = a.q_cap;
     quantize_block<BITS>(L, D, t0, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
@@ -137,21 +178,40 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
                          a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
                          a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
   } else {
-    // residual: kept tokens [Q, T) -> bf16 rows 0..T-Q-1
+    // residual: kept tokens [Q, T) -> bf16 ring rows 0..T-Q-1
     const int r0 = (blk - nqb) * kGroup;
     const int nr = min(kGroup, a.T - a.Q - r0);
+    stage_rows<T>(L, a, bj, a.Q + r0, nr);
+    __syncthreads();
     uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
     uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
-    for (int e = tid; e < nr * D; e += kThreads) {
-      const int t = e / D, c = e % D;
-      const size_t src = static_cast<size_t>(kept_pos(a, bj, a.Q + r0 + t)) * D + c;
-      kr[static_cast<size_t>(r0 + t) * D + c] = f32_to_bf16(load_f32(k, src));
+    // keys token-major, values channel-major; 8 bf16 (16 bytes) per store
+    for (int e = tid; e < nr * (D / 8); e += kThreads) {
+      const int t = e / (D / 8), c = (e % (D / 8)) * 8;
+      uint4 w;
+      w.x = f32_to_bf16(L.k[t][c]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 1])) << 16);
+      w.y = f32_to_bf16(L.k[t][c + 2]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 3])) << 16);
+      w.z = f32_to_bf16(L.k[t][c + 4]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 5])) << 16);
+      w.w = f32_to_bf16(L.k[t][c + 6]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 7])) << 16);
+      *reinterpret_cast<uint4*>(kr + static_cast<size_t>(r0 + t) * D + c) = w;
     }
-    // values are channel-major: consecutive threads take consecutive tokens
-    for (int e = tid; e < nr * D; e += kThreads) {
-      const int c = e / nr, t = e % nr;
-      const size_t src = static_cast<size_t>(kept_pos(a, bj, a.Q + r0 + t)) * D + c;
-      vr[static_cast<size_t>(c) * a.r_cap + r0 + t] = f32_to_bf16(load_f32(v, src));
+    const int nc8 = (nr + 7) / 8;  // 8-token chunks (r0 and r_cap are multiples of 8)
+    for (int e = tid; e < D * nc8; e += kThreads) {
+      const int c = e / nc8, t8 = (e % nc8) * 8;
+      uint16_t h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = f32_to_bf16(L.v[t8 + u][c]);
+      uint16_t* dst = vr + static_cast<size_t>(c) * a.r_cap + r0 + t8;
+      if (t8 + 8 <= nr) {
+        uint4 w;
+        w.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+        w.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+        w.z = h[4] | (static_cast<uint32_t>(h[5]) << 16);
+        w.w = h[6] | (static_cast<uint32_t>(h[7]) << 16);
+        *reinterpret_cast<uint4*>(dst) = w;
+      } else {
+        for (int u = 0; t8 + u < nr; ++u) dst[u] = h[u];
+      }
     }
   }
 }

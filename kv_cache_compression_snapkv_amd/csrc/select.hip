@@ -73,6 +73,9 @@ __device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b,
 template <typename T> struct ChunkCols { static constexpr int value = 128; };
 template <> struct ChunkCols<float> { static constexpr int value = 64; };
 
+// 2^x for x <= 0 (or -inf): the hardware exp2 needs no range reduction here.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Reduce (max, sum) pairs across the 16 lanes that share a row group.
 __device__ __forceinline__ void merge16(float& m, float& l) {
 #pragma unroll
@@ -83,7 +86,7 @@ __device__ __forceinline__ void merge16(float& m, float& l) {
     if (M == -INFINITY) {
       l = 0.0f;
     } else {
-      l = l * exp2f(m - M) + l2 * exp2f(m2 - M);
+      l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
     }
     m = M;
   }
@@ -106,14 +109,26 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   const int c0 = chunk * CH;
   const int ncol_valid = (PASS == 1) ? a.n : a.N;
 
-  // stage the key chunk (zero-filled beyond the valid columns)
+  // stage the key chunk (zero-filled beyond the valid columns): every 16-byte
+  // load is issued before the first LDS store, so the chunk costs one memory
+  // round trip rather than one per loop iteration
   const T* kp = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
   constexpr int VEC = 16 / sizeof(T);
-  for (int e = tid; e < CH * D / VEC; e += kThreads) {
+  constexpr int NV = CH * D / VEC / kThreads;  // 16-byte pieces per thread
+  static_assert(CH * D / VEC % kThreads == 0, "chunk must split evenly");
+  uint4 kv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = tid + i * kThreads;
     const int c = e / (D / VEC), d = (e % (D / VEC)) * VEC;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (c0 + c < ncol_valid) val = *reinterpret_cast<const uint4*>(kp + static_cast<size_t>(c0 + c) * D + d);
-    *reinterpret_cast<uint4*>(&ks[c * LD + d]) = val;
+    const int cc = min(c0 + c, a.n - 1);  // always in bounds; zeroed below if invalid
+    kv[i] = *reinterpret_cast<const uint4*>(kp + static_cast<size_t>(cc) * D + d);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = tid + i * kThreads;
+    const int c = e / (D / VEC), d = (e % (D / VEC)) * VEC;
+    *reinterpret_cast<uint4*>(&ks[c * LD + d]) = (c0 + c < ncol_valid) ? kv[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
@@ -173,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
             for (int ct = 0; ct < CT; ++ct) {
               const int c = c0 + ct * 16 + ln;
               const float x = acc[u][ct][i] * a.scale2;
-              if (c <= lim && c < a.n) l += exp2f(x - m);
+              if (c <= lim && c < a.n) l += fast_exp2(x - m);
             }
           }
           merge16(m, l);
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = row0[u] + 4 * lq + i;
-            if (r < a.R) v += exp2f(acc[u][ct][i] * a.scale2 - st[u][i].x) * st[u][i].y;
+            if (r < a.R) v += fast_exp2(acc[u][ct][i] * a.scale2 - st[u][i].x) * st[u][i].y;
           }
         }
         v += __shfl_xor(v, 16);
@@ -283,6 +298,46 @@ __device__ int block_exclusive_scan(int x, int* sh, int* total) {
   return res;
 }
 
+// Add one vote per active lane to hist[bin] with one atomic per distinct bin in
+// the wave (scores share their leading key bytes, so plain per-lane atomics on
+// one address would serialize).
+__device__ __forceinline__ void wave_hist_add(int* hist, bool valid, uint32_t bin) {
+  uint64_t active = __ballot(valid);
+  while (active) {
+    const int leader = __builtin_ctzll(active);
+    const uint32_t b0 = __builtin_amdgcn_readlane(bin, leader);
+    const uint64_t same = __ballot(valid && bin == b0) & active;
+    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[b0], __popcll(same));
+    active &= ~same;
+  }
+}
+
+// Digit selection of one radix pass: the largest d with sum_{d' >= d} cnt[d'] >=
+// krem, by an inclusive scan over the 256 bins taken from the top (threads
+// 0..255, cnt of bin 255 - t); the owning thread writes (d, krem - above).
+__device__ __forceinline__ void select_digit(const int* cnt, int krem, int* wsum, uint32_t* sel) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int c = t < 256 ? cnt[255 - t] : 0;
+  int inc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (t < 256 && lane == 63) wsum[w] = inc;
+  __syncthreads();
+  if (t < 256) {
+    int off = 0;
+    for (int i = 0; i < w; ++i) off += wsum[i];
+    inc += off;
+    const int above = inc - c;
+    if (inc >= krem && above < krem) {
+      sel[0] = static_cast<uint32_t>(255 - t);
+      sel[1] = static_cast<uint32_t>(krem - above);
+    }
+  }
+}
+
 struct TopArgs {
   const float* raw;  // [B][Hkv][N]
   uint32_t* keys;    // [B][Hkv][N]
@@ -321,9 +376,10 @@ __global__ __launch_bounds__(kTopThreads) void pool_topk_kernel(TopArgs a) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int c = tid; c < N; c += kTopThreads) {
-      const uint32_t key = keys[c];
-      if ((key & pmask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1);
+    for (int base = 0; base < N; base += kTopThreads) {  // uniform trip count (ballots inside)
+      const int c = base + tid;
+      const uint32_t key = c < N ? keys[c] : 0u;
+      wave_hist_add(hist[w], c < N && (key & pmask) == prefix, (key >> shift) & 255u);
     }
     __syncthreads();
     if (tid < 256) {
@@ -332,16 +388,7 @@ __global__ __launch_bounds__(kTopThreads) void pool_topk_kernel(TopArgs a) {
       hist[0][tid] = s;
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (acc + hist[0][d] >= krem) break;
-        acc += hist[0][d];
-      }
-      sel_sh[0] = static_cast<uint32_t>(d);
-      sel_sh[1] = static_cast<uint32_t>(krem - acc);
-    }
+    select_digit(hist[0], krem, scan_sh, sel_sh);
     __syncthreads();
     prefix |= sel_sh[0] << shift;
     pmask |= 255u << shift;
@@ -362,6 +409,103 @@ __global__ __launch_bounds__(kTopThreads) void pool_topk_kernel(TopArgs a) {
     if (take && pos < a.kk) idx[pos] = c;
     eq_seen += eq_total;
     out_pos += take_total;
+  }
+}
+
+// Short score rows (N <= KPT * 1024): the raw scores are staged in LDS once,
+// thread t owns the KPT consecutive candidates [t*KPT, t*KPT + KPT) and keeps
+// their pooled keys in registers for the four radix passes, and the index-order
+// emission needs two block scans in total.
+template <int KPT>
+__global__ __launch_bounds__(kTopThreads) void pool_topk_lds_kernel(TopArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float rs[];  // [N] raw scores
+  __shared__ int hist[kTopThreads / 64][256];
+  __shared__ int scan_sh[kTopThreads / 64 + 1];
+  __shared__ uint32_t sel_sh[2];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int N = a.N, h = a.pool / 2;
+  const float* raw = a.raw + bj * N;
+  int32_t* idx = a.idx + bj * a.kk;
+  {
+    float v[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * kTopThreads;
+      v[i] = c < N ? raw[c] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * kTopThreads;
+      if (c < N) rs[c] = v[i];
+    }
+  }
+  __syncthreads();
+  const int cb = tid * KPT;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = cb + i;
+    key[i] = 0u;
+    if (c < N) {
+      float m = rs[c];
+      const int lo = max(0, c - h), hi = min(N - 1, c + h);
+      for (int d = lo; d <= hi; ++d) m = fmaxf(m, rs[d]);
+      key[i] = order_key(m);
+      if (a.scores) a.scores[bj * N + c] = m;
+    }
+  }
+  if (a.kk == 0) return;
+  if (a.kk == N) {
+    for (int c = tid; c < N; c += kTopThreads) idx[c] = c;
+    return;
+  }
+  uint32_t prefix = 0, pmask = 0;
+  int krem = a.kk;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      wave_hist_add(hist[w], cb + i < N && (key[i] & pmask) == prefix, (key[i] >> shift) & 255u);
+    __syncthreads();
+    if (tid < 256) {
+      int s2 = 0;
+      for (int i = 0; i < kTopThreads / 64; ++i) s2 += hist[i][tid];
+      hist[0][tid] = s2;
+    }
+    __syncthreads();
+    select_digit(hist[0], krem, scan_sh, sel_sh);
+    __syncthreads();
+    prefix |= sel_sh[0] << shift;
+    pmask |= 255u << shift;
+    krem = static_cast<int>(sel_sh[1]);
+    __syncthreads();
+  }
+  // prefix is the k'-th largest key: take every larger key and the krem
+  // lowest-index keys equal to it, in index order
+  int n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) n_eq += (cb + i < N && key[i] == prefix) ? 1 : 0;
+  int tot;
+  int eq_rank = block_exclusive_scan(n_eq, scan_sh, &tot);
+  int n_take = 0;
+  bool take[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const bool ok = cb + i < N;
+    const bool eq = ok && key[i] == prefix;
+    take[i] = ok && (key[i] > prefix || (eq && eq_rank < krem));
+    eq_rank += eq ? 1 : 0;
+    n_take += take[i] ? 1 : 0;
+  }
+  int pos = block_exclusive_scan(n_take, scan_sh, &tot);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (take[i] && pos < a.kk) idx[pos] = cb + i;
+    pos += take[i] ? 1 : 0;
   }
 }
 
@@ -388,7 +532,26 @@ kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t
   if ((s = check_launch()) != KVC_OK) return s;
   s = launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
   if (s != KVC_OK) return s;
-  hipLaunchKernelGGL(pool_topk_kernel, dim3(a.Hkv, B), dim3(kTopThreads), 0, st, t);
+  // short rows: raw scores in LDS, keys in registers
+  const int kpt = (t.N + kTopThreads - 1) / kTopThreads;
+  const size_t lds = static_cast<size_t>(t.N) * sizeof(float);
+  if (kpt <= 8) {
+    hipLaunchKernelGGL(pool_topk_lds_kernel<8>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
+  } else if (kpt <= 16) {
+    hipLaunchKernelGGL(pool_topk_lds_kernel<16>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
+  } else if (kpt <= 32) {
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_topk_lds_kernel<32>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) {
+        set_last_hip_error(e);
+        return KVC_ERR_HIP;
+      }
+    }
+    hipLaunchKernelGGL(pool_topk_lds_kernel<32>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
+  } else {
+    hipLaunchKernelGGL(pool_topk_kernel, dim3(a.Hkv, B), dim3(kTopThreads), 0, st, t);
+  }
   return check_launch();
 }
 
