@@ -59,6 +59,19 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                  c, 0, 0, 0);
 }
 
+// Global load, optionally with the non-temporal hint (streamed data read once:
+// measured 12-15% more HBM bandwidth on this access pattern).
+template <bool NT, typename V> __device__ __forceinline__ V ldg(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// Load at a wave-uniform base plus a per-lane byte offset (the scalar-base
+// addressing form: no per-lane 64-bit address arithmetic per tile).
+template <bool NT, typename V> __device__ __forceinline__ V ldo(const uint32_t* base, uint32_t byte_off) {
+  return ldg<NT>(reinterpret_cast<const V*>(reinterpret_cast<const unsigned char*>(base) + byte_off));
+}
+
 // A value the compiler must keep in a VGPR (VOP3 instructions such as
 // v_and_or_b32 take no literal operand on this target).
 __device__ __forceinline__ uint32_t vreg(uint32_t x) {
@@ -175,24 +188,37 @@ struct DecArgs {
 
 
 // LDS layout (bytes), shared by host sizing and the kernel.  Operand areas hold
-// 16 MFMA rows of 32 bf16 per k-step (keys) or channel group (values), padded
+// the MFMA rows of 32 bf16 per k-step (keys) or channel group (values), padded
 // so that both the 16-byte fragment reads (8 lanes, rows ln..ln+7) and the
 // dword writes (lanes of two blocks) fall in distinct banks: rows are kRowW
-// dwords apart and blocks kBlkW dwords (16 mod 32) apart.
+// dwords apart and blocks blk_w(HBS) dwords (16 mod 32) apart.
+//
+// With HBS heads per workgroup only rows 2h, 2h+1, 8+2h, 9+2h (h < HBS) can be
+// non-zero; for HBS < kHB those rows are stored compactly followed by one zero
+// row that every other row maps to (the fragment reads of those lanes become
+// broadcasts of the zero row).
 constexpr int kRowW = 20;
-constexpr int kBlkW = 336;
+__host__ __device__ constexpr int phys_rows(int hbs) { return hbs == kHB ? 16 : 4 * hbs + 1; }
+__host__ __device__ constexpr int blk_w(int hbs) { return (phys_rows(hbs) * kRowW + 15) / 32 * 32 + 16; }
+template <int HBS> __device__ __forceinline__ int arow(int r) {
+  if (HBS == kHB) return r;
+  const int h = (r & 7) >> 1;
+  return h < HBS ? (r >> 3) * 2 * HBS + (r & 7) : 4 * HBS;
+}
 struct Lds {
   int wave0, wave_bytes, total;
   int ak, av, pbuf, vcorr;  // offsets inside one wave's region
 };
-__host__ __device__ constexpr Lds lds_layout(int KS, int nwv) {
+__host__ __device__ constexpr Lds lds_layout(int KS, int nwv, int hbs) {
   Lds L{};
   L.wave0 = 0;
   L.ak = 0;
-  L.av = KS * kBlkW * 4;
-  L.pbuf = 2 * KS * kBlkW * 4;
-  L.vcorr = L.pbuf + kHB * 32 * 4;
-  L.wave_bytes = (L.vcorr + kHB * 8 * 4 + 15) / 16 * 16;
+  L.av = KS * blk_w(hbs) * 4;
+  L.pbuf = 2 * KS * blk_w(hbs) * 4;
+  L.vcorr = L.pbuf + hbs * 32 * 4;
+  L.wave_bytes = (L.vcorr + hbs * 8 * 4 + 15) / 16 * 16;
+  // the final merge reuses the region for (o[hbs][D], m[hbs], l[hbs])
+  L.wave_bytes = (L.wave_bytes > (hbs * 32 * KS + 2 * hbs) * 4) ? L.wave_bytes : ((hbs * 32 * KS + 2 * hbs) * 4 + 15) / 16 * 16;
   L.total = L.wave0 + nwv * L.wave_bytes;
   return L;
 }
@@ -230,22 +256,35 @@ __device__ __forceinline__ void wave_sync() {
 
 // Resident workgroups per CU that the register budget allows (the occupancy
 // the planner assumes): 4-wave groups at up to 168 VGPRs fit three per CU.
-template <int KS, int NWV> constexpr int min_blocks() { return NWV == 8 ? 1 : (KS <= 4 ? 3 : KS <= 6 ? 2 : 1); }
+template <int KS, int NWV, int HBS> constexpr int min_blocks() {
+  return NWV == 8 ? 1 : (KS <= 4 ? (HBS == 1 ? 4 : 3) : KS <= 6 ? 2 : 1);
+}
 
-template <typename T, int BITS, int KS, int NWV>
-__global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kernel(DecArgs a) {
+// HBS: query heads per workgroup, kHB (up to four heads of a KV head) or 1
+// (one head: multi-head attention, and the short runs).
+template <typename T, int BITS, int KS, int NWV, int HBS>
+__global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode_kernel(DecArgs a) {
   constexpr int D = 32 * KS;
   constexpr int NTHR = 64 * NWV;
   constexpr int NGV = KS;                   // value channel groups
   constexpr int NW = D * BITS / 32;         // key words per token
   constexpr int NP = (D / 2 + 63) / 64;     // operand pairs per lane per tile
   constexpr int PAIR = BITS == 2 ? 8 : 4;   // code distance of the two halves of a register
-  // history tiles in flight per wave (register ring): deep for the latency-bound
-  // short runs, shallow where three workgroups share a CU
-  constexpr int NR = (NWV == 8 && KS <= 4) ? 4 : 2;
+  // History tiles in flight per wave, in two register rings: the key part of
+  // tile t (codes, meta) is consumed one iteration before its value part, so
+  // its slot frees earlier.  A slot is refilled as soon as it frees, so key
+  // loads lead their use by NK-1 whole iterations and value loads by NV-1.
+  constexpr int NK = (NWV == 8 && KS <= 4) ? 4 : 2;
+  constexpr int NV = (NWV == 8 && KS <= 4) ? 4 : 2;
+  constexpr int NPER = NK == NV ? NK : NK * NV;  // loop period (ring slots are compile-time)
+  // Long runs stream each packed tile once; short runs share tiles between the
+  // head workgroups of a unit through L2, so they keep the default policy.
+  constexpr bool NTL = NWV == 4;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is wave-uniform: say so, so that tile indices, loop control
+  // and tile base addresses live in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ln = lane & 15, lq = lane >> 4;
   // Workgroup -> (unit bj, head block hb).  With one workgroup per unit and
   // several head blocks, the head blocks of a unit get linear ids 8 apart:
@@ -269,7 +308,9 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   const int bjh = bj * a.HB + hb;
   const int h0 = hb * a.hbs;
   const int Gb = min(a.hbs, a.G - h0);
-  constexpr Lds L = lds_layout(KS, NWV);
+  constexpr Lds L = lds_layout(KS, NWV, HBS);
+  constexpr int BLK = blk_w(HBS);
+  const int rk = arow<HBS>(ln);  // operand row this lane reads
   unsigned char* wbase = smem + L.wave0 + wave * L.wave_bytes;
   uint16_t* AK = reinterpret_cast<uint16_t*>(wbase + L.ak);
   uint16_t* AV = reinterpret_cast<uint16_t*>(wbase + L.av);
@@ -319,57 +360,74 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   // Per tile, D/2 key operand pairs and D/2 value operand pairs; lane l owns
   // pairs l + 64u for every head, so its meta loads do not depend on the head.
   constexpr int NKW = (BITS == 2) ? KS / 2 + (KS & 1) : KS;  // key words a lane reads per token
-  struct HistRegs {
+  struct KRegs {
     uint32_t kw[2][NKW];  // key code words, per column tile
     uint32_t km[NP][2];   // key meta of the lane's channel pairs
+  };
+  struct VRegs {
     uint32_t vm[NP][2];   // value meta of the lane's token pairs
     u32x2 vw[NGV];        // value code words, per channel group
   };
-  auto load_hist = [&](int tile, HistRegs& r) {
-    const int t0 = tile * kGroup;
-    const int w_first = (BITS == 2) ? ((lq * KS) >> 1) : lq * KS;
+  // Per-lane byte offsets inside a tile (the tile bases are wave-uniform).
+  const int w_first = (BITS == 2) ? ((lq * KS) >> 1) : lq * KS;
+  const uint32_t off_k = static_cast<uint32_t>(col_token(0, ln) * NW + w_first) * 4u;  // + ct * 8 rows
+  uint32_t off_km[NP], off_vm[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int pi = min(lane + 64 * u, D / 2 - 1);
+    const int s = pi >> 4, q4 = (pi >> 2) & 3, m = pi & 3;
+    off_km[u] = static_cast<uint32_t>(key_channel<BITS, KS>(s, q4, 2 * m)) * 4u;  // + PAIR channels
+    const int g = pi >> 4, pr = pi & 15;
+    off_vm[u] = static_cast<uint32_t>(value_token<BITS>(pr >> 2, 2 * (pr & 3)) * NGV + g) * 4u;  // + PAIR tokens
+  }
+  const uint32_t off_vw = static_cast<uint32_t>(((BITS == 2) ? (lq >> 1) : lq) * D + 2 * ln) * 4u;  // + 32 g words
+  auto load_k = [&](int tile, KRegs& r) {
+    const uint32_t* kt = kc + static_cast<size_t>(tile) * kGroup * NW;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const uint32_t* row = kc + (t0 + col_token(ct, ln)) * NW + w_first;
+      const uint32_t o = off_k + ct * 8 * NW * 4;
       if constexpr (NKW == 4 && (BITS == 4 || (KS & 1) == 0)) {
-        const u32x4 w4 = *reinterpret_cast<const u32x4*>(row);
+        const u32x4 w4 = ldo<NTL, u32x4>(kt, o);
         r.kw[ct][0] = w4.x; r.kw[ct][1] = w4.y; r.kw[ct][2] = w4.z; r.kw[ct][3] = w4.w;
       } else if constexpr (NKW == 2 && (BITS == 4 || (KS & 1) == 0)) {
-        const u32x2 w2 = *reinterpret_cast<const u32x2*>(row);
+        const u32x2 w2 = ldo<NTL, u32x2>(kt, o);
         r.kw[ct][0] = w2.x; r.kw[ct][1] = w2.y;
       } else {
 #pragma unroll
-        for (int i = 0; i < NKW; ++i) r.kw[ct][i] = (w_first + i < NW) ? row[i] : 0u;
+        for (int i = 0; i < NKW; ++i) r.kw[ct][i] = (w_first + i < NW) ? ldo<NTL, uint32_t>(kt, o + 4 * i) : 0u;
       }
     }
-    const uint32_t* kmg = km + tile * D;
+    const uint32_t* kmg = km + static_cast<size_t>(tile) * D;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-      const int pi = lane + 64 * u;
-      r.km[u][0] = r.km[u][1] = r.vm[u][0] = r.vm[u][1] = 0u;
-      if (pi < D / 2) {
-        const int s = pi >> 4, q4 = (pi >> 2) & 3, m = pi & 3;
-        const int c0 = key_channel<BITS, KS>(s, q4, 2 * m);
-        r.km[u][0] = kmg[c0];
-        r.km[u][1] = kmg[c0 + PAIR];
-        const int g = pi >> 4, pr = pi & 15;
-        const int t_lo = value_token<BITS>(pr >> 2, 2 * (pr & 3));
-        r.vm[u][0] = vm[(t0 + t_lo) * NGV + g];
-        r.vm[u][1] = vm[(t0 + t_lo + PAIR) * NGV + g];
+      r.km[u][0] = r.km[u][1] = 0u;
+      if (lane + 64 * u < D / 2) {
+        r.km[u][0] = ldo<NTL, uint32_t>(kmg, off_km[u]);
+        r.km[u][1] = ldo<NTL, uint32_t>(kmg, off_km[u] + PAIR * 4);
       }
     }
-    const int wrow = (BITS == 2) ? (t0 / 16 + (lq >> 1)) : (t0 / 8 + lq);
-    const uint32_t* vrow = vc + wrow * D;
+  };
+  auto load_v = [&](int tile, VRegs& r) {
+    const uint32_t* vmt = vm + static_cast<size_t>(tile) * kGroup * NGV;
 #pragma unroll
-    for (int g = 0; g < NGV; ++g) r.vw[g] = *reinterpret_cast<const u32x2*>(vrow + 32 * g + 2 * ln);
+    for (int u = 0; u < NP; ++u) {
+      r.vm[u][0] = r.vm[u][1] = 0u;
+      if (lane + 64 * u < D / 2) {
+        r.vm[u][0] = ldo<NTL, uint32_t>(vmt, off_vm[u]);
+        r.vm[u][1] = ldo<NTL, uint32_t>(vmt, off_vm[u] + PAIR * NGV * 4);
+      }
+    }
+    const uint32_t* vct = vc + static_cast<size_t>(tile) * (kGroup * BITS / 32) * D;
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) r.vw[g] = ldo<NTL, u32x2>(vct, off_vw + 128 * g);
   };
 
   // ---------------------------------------------------------------- setup
   // Each wave loads the query values of its lanes' key channel pairs (they never
-  // change) and its first NR history tiles before anything waits; meanwhile its
+  // change) and its first history tiles before anything waits; meanwhile its
   // operand rows that no head writes are zeroed.  No workgroup barrier.
   const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.Hq + j * a.G + h0) * D;
-  float qa0[NP][kHB], qa1[NP][kHB];
+  float qa0[NP][HBS], qa1[NP][HBS];
   int cpair[NP];
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
@@ -377,15 +435,18 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
     const int s = pi >> 4, q4 = (pi >> 2) & 3, m = pi & 3;
     cpair[u] = key_channel<BITS, KS>(s, q4, 2 * m);
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) {
+    for (int h = 0; h < HBS; ++h) {
       const int hc = min(h, Gb - 1);
       qa0[u][h] = load_f32(qp, hc * D + cpair[u]);
       qa1[u][h] = load_f32(qp, hc * D + cpair[u] + PAIR);
     }
   }
-  HistRegs ring[NR];
+  KRegs kring[NK];
+  VRegs vring[NV];
 #pragma unroll
-  for (int u = 0; u < NR; ++u) load_hist(min(tb + u, hlast), ring[u]);
+  for (int u = 0; u < NK; ++u) load_k(min(tb + u, hlast), kring[u]);
+#pragma unroll
+  for (int u = 0; u < NV; ++u) load_v(min(tb + u, hlast), vring[u]);
   {
     uint32_t* zero_area = reinterpret_cast<uint32_t*>(wbase);
     for (int e = lane; e < (L.pbuf >> 2); e += 64) zero_area[e] = 0u;  // AK and AV of this wave
@@ -395,15 +456,15 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   f32x4 oacc[2 * NGV];
 #pragma unroll
   for (int i = 0; i < 2 * NGV; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float vcorr[NP][kHB];
+  float vcorr[NP][HBS];
 #pragma unroll
   for (int u = 0; u < NP; ++u)
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) vcorr[u][h] = 0.0f;
+    for (int h = 0; h < HBS; ++h) vcorr[u][h] = 0.0f;
   float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
   const u32x4 neg4 = {vreg(kNegOne2), vreg(kNegOne2), vreg(kNegOne2), vreg(kNegOne2)};
   const uint32_t vsh = 8u * static_cast<uint32_t>(lq & 1);  // value half-word of this lane (2-bit)
-  const int nhh = Gb > 1 ? 2 : 1;                           // head rows per lane quarter in use
+  const int nhh = (HBS > 1 && Gb > 1) ? 2 : 1;              // head rows per lane quarter in use
 
   // ---- the online softmax update shared by both tile kinds.  x[hh][ct] are
   // log2-scaled scores (-inf when masked); writes p to pbuf and rescales the
@@ -443,8 +504,9 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
       }
       // per-head factors for the value corrections (lanes of quarter h/2 hold head h)
 #pragma unroll
-      for (int h = 0; h < kHB; ++h) {
-        const float ah = __shfl(alpha[h & 1], 16 * (h >> 1));
+      for (int h = 0; h < HBS; ++h) {
+        const float ah = HBS == 1 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[0]), 0))
+                                  : __shfl(alpha[h & 1], 16 * (h >> 1));
 #pragma unroll
         for (int u = 0; u < NP; ++u) vcorr[u][h] *= ah;
       }
@@ -453,7 +515,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
 
   // ---- key stage of a history tile: rows 2h, 2h+1 = split(q*scale*2^(7-pos)),
   // rows 8+2h, 9+2h = -split(q*zero)
-  auto k_stage = [&](const HistRegs& cur) {
+  auto k_stage = [&](const KRegs& cur) {
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int pi = lane + 64 * u;
@@ -463,28 +525,28 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
         const float sc0 = f16_bits_to_f32(cur.km[u][0] & 0xFFFFu) * f;
         const float sc1 = f16_bits_to_f32(cur.km[u][1] & 0xFFFFu) * f;
         const float zp0 = f16_bits_to_f32(cur.km[u][0] >> 16), zp1 = f16_bits_to_f32(cur.km[u][1] >> 16);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(AK) + s * kBlkW + 4 * q4 + m;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(AK) + s * BLK + 4 * q4 + m;
 #pragma unroll
-        for (int h = 0; h < kHB; ++h) {
+        for (int h = 0; h < HBS; ++h) {
           if (h < Gb) {
             const Pair pa = split_pair(qa0[u][h] * sc0, qa1[u][h] * sc1);
             const Pair pz = split_pair(qa0[u][h] * zp0, qa1[u][h] * zp1);
-            dst[(2 * h) * kRowW] = pa.hi;
-            dst[(2 * h + 1) * kRowW] = pa.lo;
-            dst[(8 + 2 * h) * kRowW] = pz.hi ^ 0x80008000u;
-            dst[(9 + 2 * h) * kRowW] = pz.lo ^ 0x80008000u;
+            dst[arow<HBS>(2 * h) * kRowW] = pa.hi;
+            dst[arow<HBS>(2 * h + 1) * kRowW] = pa.lo;
+            dst[arow<HBS>(8 + 2 * h) * kRowW] = pz.hi ^ 0x80008000u;
+            dst[arow<HBS>(9 + 2 * h) * kRowW] = pz.lo ^ 0x80008000u;
           }
         }
       }
     }
   };
   // ---- key MFMAs of a history tile (operand rows visible): log2-scaled scores
-  auto k_mma = [&](const HistRegs& cur, float (&x)[2][2]) {
+  auto k_mma = [&](const KRegs& cur, float (&x)[2][2]) {
     f32x4 accS[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 accC = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(AK + 2 * (s * kBlkW + ln * kRowW + 4 * lq));
+      const u32x4 af = *reinterpret_cast<const u32x4*>(AK + 2 * (s * BLK + rk * kRowW + 4 * lq));
       if constexpr (BITS == 2 && (KS & 1) == 0) {
         accS[0] = mfma(af, unpack<2>(cur.kw[0][s >> 1], s & 1, K), accS[0]);
         accS[1] = mfma(af, unpack<2>(cur.kw[1][s >> 1], s & 1, K), accS[1]);
@@ -518,7 +580,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   };
   // ---- value stage of a history tile: rows 2h, 2h+1 = split(p*scale*2^(7-pos));
   // the lane keeps p*zero - (hi + lo) of its pieces in vcorr
-  auto v_stage = [&](const HistRegs& cur) {
+  auto v_stage = [&](const VRegs& cur) {
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int vi = lane + 64 * u;
@@ -529,15 +591,15 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
         const float sc0 = f16_bits_to_f32(cur.vm[u][0] & 0xFFFFu) * f;
         const float sc1 = f16_bits_to_f32(cur.vm[u][1] & 0xFFFFu) * f;
         const float zp0 = f16_bits_to_f32(cur.vm[u][0] >> 16), zp1 = f16_bits_to_f32(cur.vm[u][1] >> 16);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(AV) + g * kBlkW + pr;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(AV) + g * BLK + pr;
 #pragma unroll
-        for (int h = 0; h < kHB; ++h) {
+        for (int h = 0; h < HBS; ++h) {
           if (h < Gb) {
             const float p0 = pbuf[h * 32 + t_lo], p1 = pbuf[h * 32 + t_hi];
             const float x0 = p0 * sc0, x1 = p1 * sc1;
             const Pair pa = split_pair(x0, x1);
-            dst[(2 * h) * kRowW] = pa.hi;
-            dst[(2 * h + 1) * kRowW] = pa.lo;
+            dst[arow<HBS>(2 * h) * kRowW] = pa.hi;
+            dst[arow<HBS>(2 * h + 1) * kRowW] = pa.lo;
             vcorr[u][h] += (__builtin_fmaf(p0, zp0, -piece_sum(x0)) + __builtin_fmaf(p1, zp1, -piece_sum(x1)));
           }
         }
@@ -545,10 +607,10 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
     }
   };
   // ---- value MFMAs of a history tile
-  auto v_mma = [&](const HistRegs& cur) {
+  auto v_mma = [&](const VRegs& cur) {
 #pragma unroll
     for (int g = 0; g < NGV; ++g) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(AV + 2 * (g * kBlkW + ln * kRowW + 4 * lq));
+      const u32x4 af = *reinterpret_cast<const u32x4*>(AV + 2 * (g * BLK + rk * kRowW + 4 * lq));
       if constexpr (BITS == 2) {
         oacc[2 * g] = mfma(af, unpack_lane(cur.vw[g].x, vsh, K), oacc[2 * g]);
         oacc[2 * g + 1] = mfma(af, unpack_lane(cur.vw[g].y, vsh, K), oacc[2 * g + 1]);
@@ -560,33 +622,38 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   };
 
   // ---- packed history tiles [tb, th_end), software-pipelined: the key stage
-  // of tile t+1 and the value stage of tile t share each barrier, and the
-  // register slot of tile t is refilled with tile t+NR once its value MFMAs are
-  // issued.  Tile tb+i lives in ring[i % NR].
+  // of tile t+1 and the value stage of tile t share each barrier.  Tile tb+i
+  // lives in kring[i % NK] and vring[i % NV]; the key slot of tile t+1 is
+  // refilled with tile t+1+NK once its key MFMAs are issued, the value slot of
+  // tile t with tile t+NV once its value MFMAs are.
   if (tb < th_end) {
-    k_stage(ring[0]);
+    k_stage(kring[0]);
     wave_sync();
     float x[2][2];
-    k_mma(ring[0], x);
+    k_mma(kring[0], x);
     softmax_update(x);
     wave_sync();
   }
-  for (int t = tb; t < th_end; t += NR) {
+  load_k(min(tb + NK, hlast), kring[0]);
+  for (int t = tb; t < th_end; t += NPER) {
 #pragma unroll
-    for (int u = 0; u < NR; ++u) {
+    for (int u = 0; u < NPER; ++u) {
       const int tt = t + u;
+      KRegs& kn = kring[(u + 1) % NK];
+      VRegs& vcur = vring[u % NV];
       if (tt < th_end) {
         const bool nxt = tt + 1 < th_end;
-        if (nxt) k_stage(ring[(u + 1) % NR]);
-        v_stage(ring[u]);
+        if (nxt) k_stage(kn);
+        v_stage(vcur);
         wave_sync();
         float x[2][2];
-        if (nxt) k_mma(ring[(u + 1) % NR], x);
-        v_mma(ring[u]);
+        if (nxt) k_mma(kn, x);
+        v_mma(vcur);
         if (nxt) softmax_update(x);
         wave_sync();
       }
-      load_hist(min(tt + NR, hlast), ring[u]);
+      load_k(min(tt + 1 + NK, hlast), kn);
+      load_v(min(tt + NV, hlast), vcur);
     }
   }
 
@@ -595,22 +662,22 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   // wave's key area (no longer needed): rows 2h, 2h+1 for h < Gb, zeros elsewhere.
   if (r_first < NTr) {
     uint32_t* ak32 = reinterpret_cast<uint32_t*>(AK);
-    for (int e = lane; e < KS * kBlkW; e += 64) ak32[e] = 0u;
+    for (int e = lane; e < KS * BLK; e += 64) ak32[e] = 0u;
     wave_sync();
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       if (lane + 64 * u < D / 2) {
 #pragma unroll
-        for (int h = 0; h < kHB; ++h) {
+        for (int h = 0; h < HBS; ++h) {
           if (h < Gb) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
               const int c = cpair[u] + i * PAIR;
               const float v = i ? qa1[u][h] : qa0[u][h];
               const float r = v - __uint_as_float(__float_as_uint(v) & kHi);
-              uint16_t* row = AK + 2 * ((c >> 5) * kBlkW + 2 * h * kRowW) + (c & 31);
-              row[0] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
-              row[2 * kRowW] = static_cast<uint16_t>(__float_as_uint(r) >> 16);
+              uint16_t* blk = AK + 2 * ((c >> 5) * BLK) + (c & 31);
+              blk[2 * arow<HBS>(2 * h) * kRowW] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+              blk[2 * arow<HBS>(2 * h + 1) * kRowW] = static_cast<uint16_t>(__float_as_uint(r) >> 16);
             }
           }
         }
@@ -646,7 +713,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
           bf.z = load_bf16_pair(knp, c + 4);
           bf.w = load_bf16_pair(knp, c + 6);
         }
-        const u32x4 af = *reinterpret_cast<const u32x4*>(AK + 2 * (s * kBlkW + ln * kRowW + 4 * lq));
+        const u32x4 af = *reinterpret_cast<const u32x4*>(AK + 2 * (s * BLK + rk * kRowW + 4 * lq));
         accS[ct] = mfma(af, bf, accS[ct]);
       }
     }
@@ -668,11 +735,11 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
       const int h = i % Gb, pr = i / Gb;
       const Pair pa = split_pair(pbuf[h * 32 + 2 * pr], pbuf[h * 32 + 2 * pr + 1]);
       uint32_t* dst = reinterpret_cast<uint32_t*>(AV) + pr;
-      dst[(2 * h) * kRowW] = pa.hi;
-      dst[(2 * h + 1) * kRowW] = pa.lo;
+      dst[arow<HBS>(2 * h) * kRowW] = pa.hi;
+      dst[arow<HBS>(2 * h + 1) * kRowW] = pa.lo;
     }
     wave_sync();
-    const u32x4 af = *reinterpret_cast<const u32x4*>(AV + 2 * (ln * kRowW + 4 * lq));
+    const u32x4 af = *reinterpret_cast<const u32x4*>(AV + 2 * (rk * kRowW + 4 * lq));
     const bool clean = tl + 8 <= a.r_total && !(a.r_new >= tl && a.r_new < tl + 8);
 #pragma unroll
     for (int g = 0; g < NGV; ++g) {
@@ -712,7 +779,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
   for (int u = 0; u < NP; ++u) {
     const int g = (lane + 64 * u) >> 4;
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) {
+    for (int h = 0; h < HBS; ++h) {
       const float s = sum16(vcorr[u][h]);
       if (ln == 0 && g < NGV) vcs[h * 8 + g] = s;
     }
@@ -726,7 +793,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int g = 0; g < NGV; ++g) corr_g[hh][g] = vcs[((2 * lq + hh) & (kHB - 1)) * 8 + g];
+    for (int g = 0; g < NGV; ++g) corr_g[hh][g] = vcs[min(2 * lq + hh, HBS - 1) * 8 + g];
   wave_sync();
   float* wst = reinterpret_cast<float*>(wbase);
 #pragma unroll
@@ -735,8 +802,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
     const float l = sum16(l_part[hh]);
     if (head < Gb) {
       if (ln == 0) {
-        wst[kHB * D + head] = m_run[hh];
-        wst[kHB * D + kHB + head] = l;
+        wst[HBS * D + head] = m_run[hh];
+        wst[HBS * D + HBS + head] = l;
       }
 #pragma unroll
       for (int g = 0; g < NGV; ++g) {
@@ -756,8 +823,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV>())) void decode_kern
 #pragma unroll
     for (int w = 0; w < NWV; ++w) {
       const float* ws_w = reinterpret_cast<const float*>(smem + L.wave0 + w * L.wave_bytes);
-      mw[w] = ws_w[kHB * D + h];
-      lw[w] = ws_w[kHB * D + kHB + h];
+      mw[w] = ws_w[HBS * D + h];
+      lw[w] = ws_w[HBS * D + HBS + h];
       M = fmaxf(M, mw[w]);
     }
     float Lsum = 0.0f, acc = 0.0f;
@@ -829,41 +896,56 @@ struct Plan {
   int nb, nwv, hbs;  // workgroups per unit, waves per workgroup, query heads per workgroup
 };
 
-template <typename T, int BITS, int KS, int NWV> const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&decode_kernel<T, BITS, KS, NWV>);
+template <typename T, int BITS, int KS, int NWV, int HBS> const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&decode_kernel<T, BITS, KS, NWV, HBS>);
 }
-const void* kernel_for(int dt, int bits, int KS, int nwv) {
-#define KVC_PTRS(k)                                                                              \
-  case k:                                                                                        \
-    if (dt == KVC_F32) return bits == 2 ? kernel_ptr<float, 2, k, NWV>() : kernel_ptr<float, 4, k, NWV>(); \
-    return bits == 2 ? kernel_ptr<uint16_t, 2, k, NWV>() : kernel_ptr<uint16_t, 4, k, NWV>();
+// Instantiations: 8-wave workgroups (short runs) with one head; 4-wave
+// workgroups with one head or kHB heads.
+const void* kernel_for(int dt, int bits, int KS, int nwv, int hbs) {
+#define KVC_PTRS(k)                                                                                      \
+  case k:                                                                                                \
+    if (dt == KVC_F32) return bits == 2 ? kernel_ptr<float, 2, k, NWV, HBS>() : kernel_ptr<float, 4, k, NWV, HBS>(); \
+    return bits == 2 ? kernel_ptr<uint16_t, 2, k, NWV, HBS>() : kernel_ptr<uint16_t, 4, k, NWV, HBS>();
   if (nwv == 8) {
-    constexpr int NWV = 8;
+    if (hbs != 1) return nullptr;
+    constexpr int NWV = 8, HBS = 1;
     switch (KS) { KVC_PTRS(1) KVC_PTRS(2) KVC_PTRS(3) KVC_PTRS(4) KVC_PTRS(5) KVC_PTRS(6) default: return nullptr; }
   }
-  constexpr int NWV = 4;
+  if (hbs == 1) {
+    constexpr int NWV = 4, HBS = 1;
+    switch (KS) {
+      KVC_PTRS(1) KVC_PTRS(2) KVC_PTRS(3) KVC_PTRS(4) KVC_PTRS(5) KVC_PTRS(6) KVC_PTRS(7) KVC_PTRS(8)
+      default: return nullptr;
+    }
+  }
+  constexpr int NWV = 4, HBS = kHB;
   switch (KS) {
     KVC_PTRS(1) KVC_PTRS(2) KVC_PTRS(3) KVC_PTRS(4) KVC_PTRS(5) KVC_PTRS(6) KVC_PTRS(7) KVC_PTRS(8)
     default: return nullptr;
   }
 #undef KVC_PTRS
 }
+// Compile-time head count of the kernel that runs hbs heads per workgroup.
+int hbs_kernel(int hbs) { return hbs == 1 ? 1 : kHB; }
 
-// Workgroups of the 4-wave kernel resident per CU, and the CU count of the
-// current device (queried once per device and instantiation).
+// Workgroups of the 4-wave long-run kernel resident per CU, and the CU count of
+// the current device (queried once per device and instantiation).  Long runs
+// put min(kHB, G) heads in a workgroup.
 struct Occupancy {
   int per_cu, cus;
 };
-Occupancy occupancy(int dt, int bits, int KS) {
-  static int cache[8][2][2][9] = {};  // [device][dtype][bits][KS]: per_cu * 4096 + cus
+Occupancy occupancy(int dt, int bits, int KS, int G) {
+  static int cache[8][2][2][9][2] = {};  // [device][dtype][bits][KS][one head]: per_cu * 4096 + cus
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) dev = 0;
-  int& c = cache[dev][dt == KVC_F32 ? 0 : 1][bits == 2 ? 0 : 1][KS];
+  const int hk = hbs_kernel(std::min(kHB, G));
+  int& c = cache[dev][dt == KVC_F32 ? 0 : 1][bits == 2 ? 0 : 1][KS][hk == 1 ? 1 : 0];
   if (c == 0) {
-    // allow the dynamic LDS of both workgroup shapes, then ask for the occupancy
-    for (int nwv = 4; nwv <= 8; nwv += 4) {
-      const void* k = kernel_for(dt, bits, KS, nwv);
-      const int bytes = lds_layout(KS, nwv).total;
+    // allow the dynamic LDS of every workgroup shape, then ask for the occupancy
+    const int shapes[3][2] = {{8, 1}, {4, 1}, {4, kHB}};
+    for (const auto& sh : shapes) {
+      const void* k = kernel_for(dt, bits, KS, sh[0], sh[1]);
+      const int bytes = lds_layout(KS, sh[0], sh[1]).total;
       if (k && bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (e != hipSuccess) {
@@ -873,8 +955,8 @@ Occupancy occupancy(int dt, int bits, int KS) {
       }
     }
     int per_cu = 0, cus = 0;
-    const void* k = kernel_for(dt, bits, KS, 4);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_layout(KS, 4).total) != hipSuccess ||
+    const void* k = kernel_for(dt, bits, KS, 4, hk);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_layout(KS, 4, hk).total) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
@@ -934,9 +1016,10 @@ WsLayout ws_layout(const kvc_cache* c, int G, const Occupancy& oc) {
 }
 
 kvc_status launch_decode(const DecArgs& a, int dt, int bits, int KS, int nwv, int B, hipStream_t st) {
-  const void* k = kernel_for(dt, bits, KS, nwv);
+  const int hk = hbs_kernel(a.hbs);
+  const void* k = kernel_for(dt, bits, KS, nwv, hk);
   if (!k) return KVC_ERR_SHAPE;
-  const int bytes = lds_layout(KS, nwv).total;
+  const int bytes = lds_layout(KS, nwv, hk).total;
   dim3 grid(a.nb, a.Hkv * a.HB, B);
   void* args[] = {const_cast<DecArgs*>(&a)};
   hipError_t e = hipLaunchKernel(k, grid, dim3(64 * nwv), args, bytes, st);
@@ -966,7 +1049,7 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   if (Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return KVC_ERR_SHAPE;
   const int G = Hq / Hkv;
   const int KS = cache->head_dim / 32;
-  const Occupancy oc = occupancy(dtype, cache->bits, KS);
+  const Occupancy oc = occupancy(dtype, cache->bits, KS, G);
   if (oc.cus == 0) return KVC_ERR_HIP;
   const WsLayout W = ws_layout(cache, G, oc);
   if (!ws) {
