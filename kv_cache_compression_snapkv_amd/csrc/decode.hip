@@ -254,6 +254,20 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// First history tile of wave w of a unit (w = NWT gives NTh): the prefix sums of
+// a per-wave share that is non-increasing in w, rounded, so the runs partition
+// [0, NTh).  Waves w >= NWT - NTr also hold a residual tile and get kResW fewer
+// history tiles than the others (none if the even share is below kResW).
+constexpr float kResW = 5.0f;
+__device__ __forceinline__ int hist_split(int w, int NWT, int NTh, int NTr) {
+  if (NTr <= 0 || NTr >= NWT) return static_cast<int>((static_cast<long long>(w) * NTh) / NWT);
+  const int nA = NWT - NTr;
+  const float hB = fmaxf(0.0f, (static_cast<float>(NTh) + kResW * NTr) / NWT - kResW);
+  const float hA = (static_cast<float>(NTh) - hB * NTr) / nA;
+  const float c = static_cast<float>(min(w, nA)) * hA + static_cast<float>(max(w - nA, 0)) * hB;
+  return min(NTh, static_cast<int>(c + 0.5f));
+}
+
 // Resident workgroups per CU that the register budget allows (the occupancy
 // the planner assumes): 4-wave groups at up to 168 VGPRs fit three per CU.
 template <int KS, int NWV, int HBS> constexpr int min_blocks() {
@@ -342,15 +356,17 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode
     return p >= a.r_cap ? p - a.r_cap : p;
   };
 
-  // Tiles of this wave: an even share of the history tiles (a contiguous run)
-  // and every NWT-th residual tile counted from the last wave, so the costlier
-  // bf16 tiles land on the waves with the fewest history tiles.
+  // Tiles of this wave: every NWT-th residual tile counted from the last wave,
+  // and a contiguous run of history tiles.  When there are fewer residual tiles
+  // than waves, the last NTr waves hold one each and take correspondingly fewer
+  // history tiles (a residual tile costs about kResW history tiles: eight times
+  // the bytes, loaded without prefetch), so the waves of a unit finish together.
   const int NWT = gridDim.x * NWV;  // waves of this unit
   const int sp = blockIdx.x * NWV + wave;
   const int NTh = a.q_len / kGroup;
   const int NTr = (a.r_total + kGroup - 1) / kGroup;
-  const int tb = static_cast<int>((static_cast<long long>(sp) * NTh) / NWT);
-  const int th_end = static_cast<int>((static_cast<long long>(sp + 1) * NTh) / NWT);
+  const int tb = hist_split(sp, NWT, NTh, NTr);
+  const int th_end = hist_split(sp + 1, NWT, NTh, NTr);
   const int r_first = NWT - 1 - sp;  // residual tiles r_first, r_first + NWT, ...
   // Every prefetch is issued on every path (clamped to an existing tile) so the
   // number of loads in flight is the same at each wait and the compiler can wait
