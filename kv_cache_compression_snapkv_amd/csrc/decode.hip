@@ -207,20 +207,48 @@ template <int HBS> __device__ __forceinline__ int arow(int r) {
 }
 struct Lds {
   int wave0, wave_bytes, total;
-  int ak, av, pbuf, vcorr;  // offsets inside one wave's region
+  int ak, av, pbuf, vcorr, ring;  // offsets inside one wave's region
 };
-__host__ __device__ constexpr Lds lds_layout(int KS, int nwv, int hbs) {
+__host__ __device__ constexpr Lds lds_layout(int KS, int nwv, int hbs, int ring_bytes) {
   Lds L{};
   L.wave0 = 0;
   L.ak = 0;
   L.av = KS * blk_w(hbs) * 4;
   L.pbuf = 2 * KS * blk_w(hbs) * 4;
   L.vcorr = L.pbuf + hbs * 32 * 4;
-  L.wave_bytes = (L.vcorr + hbs * 8 * 4 + 15) / 16 * 16;
+  L.ring = (L.vcorr + hbs * 8 * 4 + 15) / 16 * 16;
   // the final merge reuses the region for (o[hbs][D], m[hbs], l[hbs])
-  L.wave_bytes = (L.wave_bytes > (hbs * 32 * KS + 2 * hbs) * 4) ? L.wave_bytes : ((hbs * 32 * KS + 2 * hbs) * 4 + 15) / 16 * 16;
+  L.ring = (L.ring > (hbs * 32 * KS + 2 * hbs) * 4) ? L.ring : ((hbs * 32 * KS + 2 * hbs) * 4 + 15) / 16 * 16;
+  L.wave_bytes = L.ring + ring_bytes;
   L.total = L.wave0 + nwv * L.wave_bytes;
   return L;
+}
+
+// Staging of packed history tiles in LDS.  A tile image holds the tile's key
+// codes, key meta, value meta and value codes back to back, copied from memory
+// by direct-to-LDS loads of 16 bytes per lane (1 KB per instruction, whatever
+// the pattern in which the lanes later read them: narrow or scattered loads
+// straight into registers reach measurably less of the memory bandwidth).
+// Used where kRingSlots images per wave still let four 4-wave workgroups share
+// a CU; elsewhere tiles go through registers.
+constexpr int kRingSlots = 2;
+constexpr int kLdsBytesPerCu = 160 * 1024;
+__host__ __device__ constexpr int img_bytes(int KS, int bits) { return 4 * 32 * KS * (2 * bits + 2); }
+__host__ __device__ constexpr bool use_dma(int bits, int KS, int nwv, int hbs) {
+  return nwv == 4 && hbs == 1 &&
+         16 * (lds_layout(KS, nwv, hbs, 0).wave_bytes + kRingSlots * img_bytes(KS, bits)) <= kLdsBytesPerCu;
+}
+__host__ __device__ constexpr Lds kernel_lds(int bits, int KS, int nwv, int hbs) {
+  return lds_layout(KS, nwv, hbs, use_dma(bits, KS, nwv, hbs) ? kRingSlots * img_bytes(KS, bits) : 0);
+}
+template <bool B> struct Tag {
+  static constexpr bool value = B;
+};
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (the direct-to-LDS loads are not tracked by the compiler's own waits).
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <typename T>
@@ -322,7 +350,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode
   const int bjh = bj * a.HB + hb;
   const int h0 = hb * a.hbs;
   const int Gb = min(a.hbs, a.G - h0);
-  constexpr Lds L = lds_layout(KS, NWV, HBS);
+  constexpr Lds L = kernel_lds(BITS, KS, NWV, HBS);
+  constexpr bool DMA = use_dma(BITS, KS, NWV, HBS);
   constexpr int BLK = blk_w(HBS);
   const int rk = arow<HBS>(ln);  // operand row this lane reads
   unsigned char* wbase = smem + L.wave0 + wave * L.wave_bytes;
@@ -397,45 +426,87 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode
     off_vm[u] = static_cast<uint32_t>(value_token<BITS>(pr >> 2, 2 * (pr & 3)) * NGV + g) * 4u;  // + PAIR tokens
   }
   const uint32_t off_vw = static_cast<uint32_t>(((BITS == 2) ? (lq >> 1) : lq) * D + 2 * ln) * 4u;  // + 32 g words
-  auto load_k = [&](int tile, KRegs& r) {
-    const uint32_t* kt = kc + static_cast<size_t>(tile) * kGroup * NW;
+  // A tile's key part (codes at kt, meta at kmg) and value part (meta at vmt,
+  // codes at vct) into registers, from memory or from a staged LDS image.
+  auto read_k = [&](const uint32_t* kt, const uint32_t* kmg, KRegs& r, auto tag) {
+    constexpr bool nt = decltype(tag)::value;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const uint32_t o = off_k + ct * 8 * NW * 4;
       if constexpr (NKW == 4 && (BITS == 4 || (KS & 1) == 0)) {
-        const u32x4 w4 = ldo<NTL, u32x4>(kt, o);
+        const u32x4 w4 = ldo<nt, u32x4>(kt, o);
         r.kw[ct][0] = w4.x; r.kw[ct][1] = w4.y; r.kw[ct][2] = w4.z; r.kw[ct][3] = w4.w;
       } else if constexpr (NKW == 2 && (BITS == 4 || (KS & 1) == 0)) {
-        const u32x2 w2 = ldo<NTL, u32x2>(kt, o);
+        const u32x2 w2 = ldo<nt, u32x2>(kt, o);
         r.kw[ct][0] = w2.x; r.kw[ct][1] = w2.y;
       } else {
 #pragma unroll
-        for (int i = 0; i < NKW; ++i) r.kw[ct][i] = (w_first + i < NW) ? ldo<NTL, uint32_t>(kt, o + 4 * i) : 0u;
+        for (int i = 0; i < NKW; ++i) r.kw[ct][i] = (w_first + i < NW) ? ldo<nt, uint32_t>(kt, o + 4 * i) : 0u;
       }
     }
-    const uint32_t* kmg = km + static_cast<size_t>(tile) * D;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       r.km[u][0] = r.km[u][1] = 0u;
       if (lane + 64 * u < D / 2) {
-        r.km[u][0] = ldo<NTL, uint32_t>(kmg, off_km[u]);
-        r.km[u][1] = ldo<NTL, uint32_t>(kmg, off_km[u] + PAIR * 4);
+        r.km[u][0] = ldo<nt, uint32_t>(kmg, off_km[u]);
+        r.km[u][1] = ldo<nt, uint32_t>(kmg, off_km[u] + PAIR * 4);
       }
     }
   };
-  auto load_v = [&](int tile, VRegs& r) {
-    const uint32_t* vmt = vm + static_cast<size_t>(tile) * kGroup * NGV;
+  auto read_v = [&](const uint32_t* vmt, const uint32_t* vct, VRegs& r, auto tag) {
+    constexpr bool nt = decltype(tag)::value;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       r.vm[u][0] = r.vm[u][1] = 0u;
       if (lane + 64 * u < D / 2) {
-        r.vm[u][0] = ldo<NTL, uint32_t>(vmt, off_vm[u]);
-        r.vm[u][1] = ldo<NTL, uint32_t>(vmt, off_vm[u] + PAIR * NGV * 4);
+        r.vm[u][0] = ldo<nt, uint32_t>(vmt, off_vm[u]);
+        r.vm[u][1] = ldo<nt, uint32_t>(vmt, off_vm[u] + PAIR * NGV * 4);
       }
     }
-    const uint32_t* vct = vc + static_cast<size_t>(tile) * (kGroup * BITS / 32) * D;
 #pragma unroll
-    for (int g = 0; g < NGV; ++g) r.vw[g] = ldo<NTL, u32x2>(vct, off_vw + 128 * g);
+    for (int g = 0; g < NGV; ++g) r.vw[g] = ldo<nt, u32x2>(vct, off_vw + 128 * g);
+  };
+  auto k_tile = [&](int tile) { return kc + static_cast<size_t>(tile) * kGroup * NW; };
+  auto km_tile = [&](int tile) { return km + static_cast<size_t>(tile) * D; };
+  auto vm_tile = [&](int tile) { return vm + static_cast<size_t>(tile) * kGroup * NGV; };
+  auto vc_tile = [&](int tile) { return vc + static_cast<size_t>(tile) * (kGroup * BITS / 32) * D; };
+  auto load_k = [&](int tile, KRegs& r) { read_k(k_tile(tile), km_tile(tile), r, Tag<NTL>{}); };
+  auto load_v = [&](int tile, VRegs& r) { read_v(vm_tile(tile), vc_tile(tile), r, Tag<NTL>{}); };
+
+  // LDS staging (DMA kernels): ring slot i holds the key part of tile ka and the
+  // value part of tile vb, i.e. what one pipelined iteration consumes.
+  constexpr int IMG = img_bytes(KS, BITS);
+  constexpr int IMG_KM = 4 * D * BITS, IMG_VM = IMG_KM + 4 * D, IMG_VC = IMG_VM + 4 * D;
+  constexpr int NDMA = (IMG + 1023) / 1024;  // direct-to-LDS loads per slot fill
+  unsigned char* ring = wbase + L.ring;
+  auto dma_fill = [&](int ka, int vb, int slot) {
+    if constexpr (DMA) {
+      unsigned char* dst = ring + slot * IMG;
+      const unsigned char* kcb = reinterpret_cast<const unsigned char*>(k_tile(ka));
+      const unsigned char* kmb = reinterpret_cast<const unsigned char*>(km_tile(ka));
+      const unsigned char* vmb = reinterpret_cast<const unsigned char*>(vm_tile(vb));
+      const unsigned char* vcb = reinterpret_cast<const unsigned char*>(vc_tile(vb));
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int e = 1024 * i + 16 * lane;  // image byte this lane copies
+        if (e < IMG) {
+          const unsigned char* src = e < IMG_KM   ? kcb + e
+                                     : e < IMG_VM ? kmb + (e - IMG_KM)
+                                     : e < IMG_VC ? vmb + (e - IMG_VM)
+                                                  : vcb + (e - IMG_VC);
+          __builtin_amdgcn_global_load_lds(src, dst + 1024 * i, 16, 0, 2 /* non-temporal */);
+        }
+      }
+    }
+  };
+  auto slot_k = [&](int slot, KRegs& r) {
+    const unsigned char* img = ring + slot * IMG;
+    read_k(reinterpret_cast<const uint32_t*>(img), reinterpret_cast<const uint32_t*>(img + IMG_KM), r, Tag<false>{});
+  };
+  auto slot_v = [&](int slot, VRegs& r) {
+    const unsigned char* img = ring + slot * IMG;
+    read_v(reinterpret_cast<const uint32_t*>(img + IMG_VM), reinterpret_cast<const uint32_t*>(img + IMG_VC), r,
+           Tag<false>{});
   };
 
   // ---------------------------------------------------------------- setup
@@ -457,12 +528,19 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode
       qa1[u][h] = load_f32(qp, hc * D + cpair[u] + PAIR);
     }
   }
-  KRegs kring[NK];
-  VRegs vring[NV];
+  // register rings (no staging) or ring slots: fill f holds the key part of
+  // tile tb+f and the value part of tile tb+f-1
+  KRegs kring[DMA ? 1 : NK];
+  VRegs vring[DMA ? 1 : NV];
+  if constexpr (DMA) {
 #pragma unroll
-  for (int u = 0; u < NK; ++u) load_k(min(tb + u, hlast), kring[u]);
+    for (int f = 0; f < kRingSlots; ++f) dma_fill(min(tb + f, hlast), min(max(tb + f - 1, 0), hlast), f);
+  } else {
 #pragma unroll
-  for (int u = 0; u < NV; ++u) load_v(min(tb + u, hlast), vring[u]);
+    for (int u = 0; u < NK; ++u) load_k(min(tb + u, hlast), kring[u]);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) load_v(min(tb + u, hlast), vring[u]);
+  }
   {
     uint32_t* zero_area = reinterpret_cast<uint32_t*>(wbase);
     for (int e = lane; e < (L.pbuf >> 2); e += 64) zero_area[e] = 0u;  // AK and AV of this wave
@@ -642,6 +720,49 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode
   // lives in kring[i % NK] and vring[i % NV]; the key slot of tile t+1 is
   // refilled with tile t+1+NK once its key MFMAs are issued, the value slot of
   // tile t with tile t+NV once its value MFMAs are.
+  if constexpr (DMA) {
+    // Iteration tt consumes fill tt-tb+1 (slot (tt-tb+1) % kRingSlots) and then
+    // refills that slot kRingSlots fills ahead; before a slot is read, only the
+    // younger fills may still be in flight.
+    constexpr int kWait = (kRingSlots - 1) * NDMA;
+    wait_vmem<kWait>();
+    if (tb < th_end) {
+      KRegs k0;
+      slot_k(0, k0);
+      k_stage(k0);
+      wave_sync();
+      float x[2][2];
+      k_mma(k0, x);
+      softmax_update(x);
+      wave_sync();
+    }
+    dma_fill(min(tb + kRingSlots, hlast), min(tb + kRingSlots - 1, hlast), 0);
+    for (int t = tb; t < th_end; t += kRingSlots) {
+#pragma unroll
+      for (int u = 0; u < kRingSlots; ++u) {
+        const int tt = t + u;
+        const int slot = (u + 1) % kRingSlots;
+        if (tt < th_end) {
+          const bool nxt = tt + 1 < th_end;
+          wait_vmem<kWait>();
+          KRegs kn;
+          VRegs vcur;
+          slot_k(slot, kn);
+          slot_v(slot, vcur);
+          if (nxt) k_stage(kn);
+          v_stage(vcur);
+          wave_sync();
+          float x[2][2];
+          if (nxt) k_mma(kn, x);
+          v_mma(vcur);
+          if (nxt) softmax_update(x);
+          wave_sync();
+        }
+        dma_fill(min(tt + 1 + kRingSlots, hlast), min(tt + kRingSlots, hlast), slot);
+      }
+    }
+    wait_vmem<0>();  // no copy may land in this wave's LDS after it moves on
+  } else {
   if (tb < th_end) {
     k_stage(kring[0]);
     wave_sync();
@@ -671,6 +792,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode
       load_k(min(tt + 1 + NK, hlast), kn);
       load_v(min(tt + NV, hlast), vcur);
     }
+  }
   }
 
   // ---- residual tiles: bf16 keys/values as stored (appended token from the
@@ -961,7 +1083,7 @@ Occupancy occupancy(int dt, int bits, int KS, int G) {
     const int shapes[3][2] = {{8, 1}, {4, 1}, {4, kHB}};
     for (const auto& sh : shapes) {
       const void* k = kernel_for(dt, bits, KS, sh[0], sh[1]);
-      const int bytes = lds_layout(KS, sh[0], sh[1]).total;
+      const int bytes = kernel_lds(bits, KS, sh[0], sh[1]).total;
       if (k && bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (e != hipSuccess) {
@@ -972,7 +1094,7 @@ Occupancy occupancy(int dt, int bits, int KS, int G) {
     }
     int per_cu = 0, cus = 0;
     const void* k = kernel_for(dt, bits, KS, 4, hk);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_layout(KS, 4, hk).total) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, kernel_lds(bits, KS, 4, hk).total) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
@@ -1035,7 +1157,7 @@ kvc_status launch_decode(const DecArgs& a, int dt, int bits, int KS, int nwv, in
   const int hk = hbs_kernel(a.hbs);
   const void* k = kernel_for(dt, bits, KS, nwv, hk);
   if (!k) return KVC_ERR_SHAPE;
-  const int bytes = lds_layout(KS, nwv, hk).total;
+  const int bytes = kernel_lds(bits, KS, nwv, hk).total;
   dim3 grid(a.nb, a.Hkv * a.HB, B);
   void* args[] = {const_cast<DecArgs*>(&a)};
   hipError_t e = hipLaunchKernel(k, grid, dim3(64 * nwv), args, bytes, st);
