@@ -229,14 +229,19 @@ __host__ __device__ constexpr Lds lds_layout(int KS, int nwv, int hbs, int ring_
 // by direct-to-LDS loads of 16 bytes per lane (1 KB per instruction, whatever
 // the pattern in which the lanes later read them: narrow or scattered loads
 // straight into registers reach measurably less of the memory bandwidth).
-// Used where kRingSlots images per wave still let four 4-wave workgroups share
-// a CU; elsewhere tiles go through registers.
+// Used where kRingSlots images per wave still let kMinDmaBlocks 4-wave
+// workgroups share a CU; elsewhere tiles go through registers.
 constexpr int kRingSlots = 2;
+constexpr int kMinDmaBlocks = 2;
 constexpr int kLdsBytesPerCu = 160 * 1024;
 __host__ __device__ constexpr int img_bytes(int KS, int bits) { return 4 * 32 * KS * (2 * bits + 2); }
+__host__ __device__ constexpr int dma_blocks(int bits, int KS, int nwv, int hbs) {
+  return nwv == 4 && hbs == 1
+             ? kLdsBytesPerCu / (4 * (lds_layout(KS, nwv, hbs, 0).wave_bytes + kRingSlots * img_bytes(KS, bits)))
+             : 0;
+}
 __host__ __device__ constexpr bool use_dma(int bits, int KS, int nwv, int hbs) {
-  return nwv == 4 && hbs == 1 &&
-         16 * (lds_layout(KS, nwv, hbs, 0).wave_bytes + kRingSlots * img_bytes(KS, bits)) <= kLdsBytesPerCu;
+  return dma_blocks(bits, KS, nwv, hbs) >= kMinDmaBlocks;
 }
 __host__ __device__ constexpr Lds kernel_lds(int bits, int KS, int nwv, int hbs) {
   return lds_layout(KS, nwv, hbs, use_dma(bits, KS, nwv, hbs) ? kRingSlots * img_bytes(KS, bits) : 0);
@@ -298,14 +303,15 @@ __device__ __forceinline__ int hist_split(int w, int NWT, int NTh, int NTr) {
 
 // Resident workgroups per CU that the register budget allows (the occupancy
 // the planner assumes): 4-wave groups at up to 168 VGPRs fit three per CU.
-template <int KS, int NWV, int HBS> constexpr int min_blocks() {
+template <int BITS, int KS, int NWV, int HBS> constexpr int min_blocks() {
+  if (use_dma(BITS, KS, NWV, HBS)) return dma_blocks(BITS, KS, NWV, HBS) < 4 ? dma_blocks(BITS, KS, NWV, HBS) : 4;
   return NWV == 8 ? 1 : (KS <= 4 ? (HBS == 1 ? 4 : 3) : KS <= 6 ? 2 : 1);
 }
 
 // HBS: query heads per workgroup, kHB (up to four heads of a KV head) or 1
 // (one head: multi-head attention, and the short runs).
 template <typename T, int BITS, int KS, int NWV, int HBS>
-__global__ __launch_bounds__(64 * NWV, (min_blocks<KS, NWV, HBS>())) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void decode_kernel(DecArgs a) {
   constexpr int D = 32 * KS;
   constexpr int NTHR = 64 * NWV;
   constexpr int NGV = KS;                   // value channel groups
