@@ -256,10 +256,24 @@ template <int N> __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename T>
-__device__ __forceinline__ uint32_t load_bf16_pair(const T* p, int i) {
-  return static_cast<uint32_t>(f32_to_bf16(load_f32(p, i))) |
-         (static_cast<uint32_t>(f32_to_bf16(load_f32(p, i + 1))) << 16);
+// Elements i, i+1 (i even) and i..i+7 (i % 8 == 0) of an input row as bf16
+// pairs (low half = lower index), with one or two vector loads.
+__device__ __forceinline__ uint32_t bf16_pair(float x0, float x1) {
+  return static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
+}
+__device__ __forceinline__ uint32_t load_bf16x2(const uint16_t* p, int i) {
+  return *reinterpret_cast<const uint32_t*>(p + i);
+}
+__device__ __forceinline__ uint32_t load_bf16x2(const float* p, int i) {
+  const float2 v = *reinterpret_cast<const float2*>(p + i);
+  return bf16_pair(v.x, v.y);
+}
+__device__ __forceinline__ u32x4 load_bf16x8(const uint16_t* p, int i) {
+  return *reinterpret_cast<const u32x4*>(p + i);
+}
+__device__ __forceinline__ u32x4 load_bf16x8(const float* p, int i) {
+  const float4 a = *reinterpret_cast<const float4*>(p + i), b = *reinterpret_cast<const float4*>(p + i + 4);
+  return u32x4{bf16_pair(a.x, a.y), bf16_pair(a.z, a.w), bf16_pair(b.x, b.y), bf16_pair(b.z, b.w)};
 }
 
 // All-reduce over the 16 lanes of a DPP row: swap neighbours, swap pairs,
@@ -534,6 +548,61 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
       qa1[u][h] = load_f32(qp, hc * D + cpair[u] + PAIR);
     }
   }
+  // ---- residual tiles are bf16 as stored.  A lane holds, per tile, the 8
+  // tokens from 8*lq of its 2*NGV value channels and the 8-channel slices of its
+  // two key columns; the appended token (not yet in the ring) comes from the
+  // inputs: its key channels 32s+8lq.. and value channels 32g+2ln, +1 for
+  // substitution, and channels lane+64i for storing it into the ring.
+  struct ResRegs {
+    u32x4 v[NGV][2];
+    u32x4 k[2][KS];
+  };
+  constexpr int NST = (D + 63) / 64;
+  struct NewRegs {
+    u32x4 kn[KS];
+    uint32_t vn[NGV];
+    uint16_t st_k[NST], st_v[NST];
+  };
+  auto res_load = [&](int rt, ResRegs& r) {
+    const int t0 = rt * kGroup;
+    const int tlc = rrow(min(t0 + 8 * lq, (a.r_total - 1) & ~7));  // an in-range 8-token chunk (ring row)
+#pragma unroll
+    for (int g = 0; g < NGV; ++g)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        r.v[g][u] = *reinterpret_cast<const u32x4*>(vr + static_cast<size_t>(32 * g + 2 * ln + u) * a.r_cap + tlc);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int tc = rrow(min(t0 + col_token(ct, ln), a.r_total - 1));
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        r.k[ct][s] = *reinterpret_cast<const u32x4*>(kr + static_cast<size_t>(tc) * D + 32 * s + 8 * lq);
+    }
+  };
+  auto res_new = [&](NewRegs& n) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) n.kn[s] = load_bf16x8(knp, 32 * s + 8 * lq);
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) n.vn[g] = load_bf16x2(vnp, 32 * g + 2 * ln);
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int c = min(lane + 64 * i, D - 1);
+      n.st_k[i] = f32_to_bf16(load_f32(knp, c));
+      n.st_v[i] = f32_to_bf16(load_f32(vnp, c));
+    }
+  };
+  // This wave processes the tile holding the appended token (if any).
+  const int r_new_tile = a.r_new >= 0 ? a.r_new / kGroup : -1;
+  const bool new_here = r_new_tile >= r_first && (r_new_tile - r_first) % NWT == 0;
+  // Short runs: a wave with no history tiles issues its first residual tile's
+  // loads and the appended token's at once, with the query loads (one memory
+  // round trip before its first result instead of three).  Elsewhere the tile
+  // loads are issued when the tile starts (fewer registers held).
+  constexpr bool kEarly = NWV == 8 && KS <= 4;
+  const bool early = kEarly && tb >= th_end && r_first < NTr;
+  ResRegs rres;
+  NewRegs rnew;
+
   // register rings (no staging) or ring slots: fill f holds the key part of
   // tile tb+f and the value part of tile tb+f-1
   KRegs kring[DMA ? 1 : NK];
@@ -541,12 +610,15 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   if constexpr (DMA) {
 #pragma unroll
     for (int f = 0; f < kRingSlots; ++f) dma_fill(min(tb + f, hlast), min(max(tb + f - 1, 0), hlast), f);
+  } else if (early) {
+    res_load(r_first, rres);
   } else {
 #pragma unroll
     for (int u = 0; u < NK; ++u) load_k(min(tb + u, hlast), kring[u]);
 #pragma unroll
     for (int u = 0; u < NV; ++u) load_v(min(tb + u, hlast), vring[u]);
   }
+  if (early && new_here) res_new(rnew);
   {
     uint32_t* zero_area = reinterpret_cast<uint32_t*>(wbase);
     for (int e = lane; e < (L.pbuf >> 2); e += 64) zero_area[e] = 0u;  // AK and AV of this wave
@@ -831,16 +903,24 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   }
   for (int rt = r_first; rt < NTr; rt += NWT) {
     const int t0 = rt * kGroup;
-    const bool has_new = a.r_new >= t0 && a.r_new < t0 + kGroup;
+    const bool has_new = rt == r_new_tile;
+    const bool pre = early && rt == r_first;  // loaded at setup
+    const int tl = t0 + 8 * lq;               // first token of this lane's 8 value slots
     // value rows of this lane (8 tokens of 2*NGV channels), requested first
-    const int tl = t0 + 8 * lq;                     // first token of this lane's 8 slots
-    const int tlc = rrow(min(tl, (a.r_total - 1) & ~7));  // an in-range chunk for loading (ring row)
     u32x4 vraw[NGV][2];
+    if (pre) {
 #pragma unroll
-    for (int g = 0; g < NGV; ++g)
+      for (int g = 0; g < NGV; ++g)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        vraw[g][u] = *reinterpret_cast<const u32x4*>(vr + static_cast<size_t>(32 * g + 2 * ln + u) * a.r_cap + tlc);
+        for (int u = 0; u < 2; ++u) vraw[g][u] = rres.v[g][u];
+    } else {
+      const int tlc = rrow(min(tl, (a.r_total - 1) & ~7));  // an in-range chunk for loading (ring row)
+#pragma unroll
+      for (int g = 0; g < NGV; ++g)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          vraw[g][u] = *reinterpret_cast<const u32x4*>(vr + static_cast<size_t>(32 * g + 2 * ln + u) * a.r_cap + tlc);
+    }
     f32x4 accS[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -848,15 +928,9 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
       const int tc = rrow(min(t, a.r_total - 1));
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        u32x4 bf = *reinterpret_cast<const u32x4*>(kr + static_cast<size_t>(tc) * D + 32 * s + 8 * lq);
+        u32x4 bf = pre ? rres.k[ct][s] : *reinterpret_cast<const u32x4*>(kr + static_cast<size_t>(tc) * D + 32 * s + 8 * lq);
         if (t >= a.r_total) bf = u32x4{0u, 0u, 0u, 0u};
-        if (has_new && t == a.r_new) {
-          const int c = 32 * s + 8 * lq;
-          bf.x = load_bf16_pair(knp, c);
-          bf.y = load_bf16_pair(knp, c + 2);
-          bf.z = load_bf16_pair(knp, c + 4);
-          bf.w = load_bf16_pair(knp, c + 6);
-        }
+        if (has_new && t == a.r_new) bf = pre ? rnew.kn[s] : load_bf16x8(knp, 32 * s + 8 * lq);
         const u32x4 af = *reinterpret_cast<const u32x4*>(AK + 2 * (s * BLK + rk * kRowW + 4 * lq));
         accS[ct] = mfma(af, bf, accS[ct]);
       }
@@ -889,7 +963,6 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
     for (int g = 0; g < NGV; ++g) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int c = 32 * g + 2 * ln + u;
         u32x4 bf = vraw[g][u];
         if (!clean) {
           // zero slots past the residual, substitute the appended token
@@ -897,7 +970,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
           for (int e = 0; e < 8; ++e) {
             const int t = tl + e;
             uint32_t hv = (bf[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            if (t == a.r_new) hv = f32_to_bf16(load_f32(vnp, c));
+            if (t == a.r_new)
+              hv = pre ? (rnew.vn[g] >> (16 * u)) & 0xFFFFu : f32_to_bf16(load_f32(vnp, 32 * g + 2 * ln + u));
             else if (t >= a.r_total) hv = 0u;
             bf[e >> 1] = (bf[e >> 1] & (0xFFFF0000u >> (16 * (e & 1)))) | (hv << (16 * (e & 1)));
           }
@@ -908,13 +982,17 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
     wave_sync();
   }
 
-  // the wave that owns the appended token's tile stores it
-  if (a.r_new >= 0 && hb == 0 && r_first <= a.r_new / kGroup && (a.r_new / kGroup - r_first) % NWT == 0) {
+  // the wave that owns the appended token's tile stores it (the first head block's)
+  if (new_here && hb == 0) {
     uint16_t* kw = a.k_res + (static_cast<size_t>(bj) * a.r_cap + rrow(a.r_new)) * D;
     uint16_t* vw = a.v_res + static_cast<size_t>(bj) * D * a.r_cap + rrow(a.r_new);
-    for (int c = lane; c < D; c += 64) {
-      kw[c] = f32_to_bf16(load_f32(knp, c));
-      vw[static_cast<size_t>(c) * a.r_cap] = f32_to_bf16(load_f32(vnp, c));
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int c = lane + 64 * i;
+      if (c < D) {
+        kw[c] = early ? rnew.st_k[i] : f32_to_bf16(load_f32(knp, c));
+        vw[static_cast<size_t>(c) * a.r_cap] = early ? rnew.st_v[i] : f32_to_bf16(load_f32(vnp, c));
+      }
     }
   }
 
