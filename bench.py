@@ -12,8 +12,9 @@ Prints one JSON line.  value = decode-attention tokens/s (batch * decode steps /
 time of the decode part); the selection+quantization time per prompt is
 reported beside it.  Inputs are generated on the GPU before timing (seeded).
 By default the line also carries `hbm_stress`: the decode-only, no-eviction
-Llama-2-13B-shaped case (40 layers x 0.5 GB of packed cache per step), the one
-large enough to be bound by HBM rather than by launch latency.
+Llama-2-13B-shaped case (40 layers x 0.5 GB (2-bit) or 0.85 GB (4-bit) of packed
+cache per step), the one large enough to be bound by HBM rather than by launch
+latency, at 2 and at 4 bits.
 """
 
 import argparse
@@ -264,12 +265,15 @@ def main():
         "footprint_bytes_per_prompt_token": r["footprint"]["bytes_per_prompt_token"],
     }
     if not args.no_hbm_stress and args.workload != "llama2_13b_mha":
-        # the HBM-bound decode case: no eviction, full 32k cache of 40 layers
+        # the HBM-bound decode case: no eviction, full 32k cache of 40 layers,
+        # at each of its quantization widths
         hc = synth.CONFIGS["llama2_13b_mha"]
-        h = run(hc, 2, 2, 1)
-        res["hbm_stress"] = {"workload": h["desc"], "decode_tokens_per_s": h["tokens_per_s"],
-                             "quantize_ms_per_prompt": h["pre_ms"] / hc.batch, "steps": 2, "warmup": 1,
-                             "roofline": h["roofline"]}
+        res["hbm_stress"] = []
+        for hb in sorted(hc.bits):
+            h = run(hc, hb, 2, 1)
+            res["hbm_stress"].append({"workload": h["desc"], "bits": hb, "decode_tokens_per_s": h["tokens_per_s"],
+                                      "quantize_ms_per_prompt": h["pre_ms"] / hc.batch, "steps": 2, "warmup": 1,
+                                      "roofline": h["roofline"]})
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"])
     print(json.dumps(res))
