@@ -508,8 +508,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
       const unsigned char* vcb = reinterpret_cast<const unsigned char*>(vc_tile(vb));
 #pragma unroll
       for (int i = 0; i < NDMA; ++i) {
-        const int e = 1024 * i + 16 * lane;  // image byte this lane copies
-        if (e < IMG) {
+        const uint32_t e = 1024u * i + 16u * static_cast<uint32_t>(lane);  // image byte this lane copies
+        if (e < static_cast<uint32_t>(IMG)) {
           const unsigned char* src = e < IMG_KM   ? kcb + e
                                      : e < IMG_VM ? kmb + (e - IMG_KM)
                                      : e < IMG_VC ? vmb + (e - IMG_VM)
@@ -544,8 +544,9 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
 #pragma unroll
     for (int h = 0; h < HBS; ++h) {
       const int hc = min(h, Gb - 1);
-      qa0[u][h] = load_f32(qp, hc * D + cpair[u]);
-      qa1[u][h] = load_f32(qp, hc * D + cpair[u] + PAIR);
+      // scores come out of the MFMAs already in log2 units: q is scaled once
+      qa0[u][h] = load_f32(qp, hc * D + cpair[u]) * a.scale2;
+      qa1[u][h] = load_f32(qp, hc * D + cpair[u] + PAIR) * a.scale2;
     }
   }
   // ---- residual tiles are bf16 as stored.  A lane holds, per tile, the 8
@@ -747,7 +748,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
       const bool ok = 2 * lq + hh < Gb;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        x[hh][ct] = ok ? (accS[ct][2 * hh] + accS[ct][2 * hh + 1] + corr) * a.scale2 : -INFINITY;
+        x[hh][ct] = ok ? accS[ct][2 * hh] + accS[ct][2 * hh + 1] + corr : -INFINITY;
     }
   };
   // ---- value stage of a history tile: rows 2h, 2h+1 = split(p*scale*2^(7-pos));
@@ -942,7 +943,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const bool ok = okh && t0 + col_token(ct, ln) < a.r_total;
-        x[hh][ct] = ok ? (accS[ct][2 * hh] + accS[ct][2 * hh + 1]) * a.scale2 : -INFINITY;
+        x[hh][ct] = ok ? accS[ct][2 * hh] + accS[ct][2 * hh + 1] : -INFINITY;
       }
     }
     softmax_update(x);
