@@ -76,24 +76,37 @@ template <> struct ChunkCols<float> { static constexpr int value = 64; };
 // 2^x for x <= 0 (or -inf): the hardware exp2 needs no range reduction here.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Reduce (max, sum) pairs across the 16 lanes that share a row group.
-__device__ __forceinline__ void merge16(float& m, float& l) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const float m2 = __shfl_xor(m, o);
-    const float l2 = __shfl_xor(l, o);
-    const float M = fmaxf(m, m2);
-    if (M == -INFINITY) {
-      l = 0.0f;
-    } else {
-      l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
-    }
-    m = M;
-  }
+// All-reduce over the 16 lanes of a DPP row (the lanes that share an MFMA
+// output row): swap neighbours, swap pairs, mirror within 8, mirror within 16.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float max16(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  return x;
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+// Sum over the four lanes l, l^16, l^32, l^48 (the lane quarters of one column).
+__device__ __forceinline__ float sum_quarters(float x) {
+  const int lane = threadIdx.x & 63;
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x += __uint_as_float(lane < 32 ? s32[1] : s32[0]);  // + value of lane ^ 32
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x += __uint_as_float((lane & 16) ? s16[0] : s16[1]);  // + value of lane ^ 16
+  return x;
 }
 
 template <typename T, int KS, int PASS>
-__global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
   constexpr int CH = ChunkCols<T>::value;
   constexpr int D = KS * 32;
   constexpr int PAD = 16 / sizeof(T);
@@ -113,6 +126,25 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   // load is issued before the first LDS store, so the chunk costs one memory
   // round trip rather than one per loop iteration
   const T* kp = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
+  const T* qbase = static_cast<const T*>(a.q_win) + static_cast<size_t>(b * a.Hq + j * a.G) * a.W * D;
+  // query fragments of a row block: lane (ln, lq) holds row ln of each of its
+  // two tiles, channels 32s+8lq..+7; the first block's are requested together
+  // with the key chunk
+  Frag<T> qf[2][KS];
+  int row0[2];
+  auto load_q = [&](int rb) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      row0[u] = rb + (wave + 4 * u) * 16;  // first row of this wave's tile u
+      const int r = row0[u] + ln;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (r < a.R) qf[u][s].load(qbase + static_cast<size_t>(r) * D + 32 * s + 8 * lq);
+        else qf[u][s].zero();
+      }
+    }
+  };
+  load_q(0);
   constexpr int VEC = 16 / sizeof(T);
   constexpr int NV = CH * D / VEC / kThreads;  // 16-byte pieces per thread
   static_assert(CH * D / VEC % kThreads == 0, "chunk must split evenly");
@@ -124,32 +156,25 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     const int cc = min(c0 + c, a.n - 1);  // always in bounds; zeroed below if invalid
     kv[i] = *reinterpret_cast<const uint4*>(kp + static_cast<size_t>(cc) * D + d);
   }
+  const bool chunk_valid = c0 + CH <= ncol_valid;  // no zero fill needed
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = tid + i * kThreads;
     const int c = e / (D / VEC), d = (e % (D / VEC)) * VEC;
-    *reinterpret_cast<uint4*>(&ks[c * LD + d]) = (c0 + c < ncol_valid) ? kv[i] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&ks[c * LD + d]) =
+        (chunk_valid || c0 + c < ncol_valid) ? kv[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
-  const T* qbase = static_cast<const T*>(a.q_win) + static_cast<size_t>(b * a.Hq + j * a.G) * a.W * D;
+  // Chunks clear of the causal window (pass 1) or of the candidate bound (pass
+  // 2) need no per-element masks.
+  const bool full = c0 + CH <= ((PASS == 1) ? a.n - a.W + 1 : a.N);
   float colacc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) colacc[ct] = 0.0f;
 
   for (int rb = 0; rb < a.R; rb += kRowBlock) {
-    Frag<T> qf[2][KS];
-    int row0[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      row0[u] = rb + (wave + 4 * u) * 16;  // first row of this wave's tile u
-      const int r = row0[u] + ln;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (r < a.R) qf[u][s].load(qbase + static_cast<size_t>(r) * D + 32 * s + 8 * lq);
-        else qf[u][s].zero();
-      }
-    }
+    if (rb > 0) load_q(rb);
     const bool active0 = row0[0] < a.R, active1 = row0[1] < a.R;
     if (!active0) continue;  // wave-uniform
 
@@ -168,6 +193,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     }
 
     if (PASS == 1) {
+      // per row: max over the row's 16 lanes x CT columns, then the sum of
+      // 2^(x - M) with x = logit * scale2 (scale2 > 0, so max(x) = scale2 * max)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (u == 1 && !active1) break;
@@ -175,23 +202,22 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int r = row0[u] + 4 * lq + i;
           const int lim = a.n - a.W + (r % a.W);  // last key this row may see
-          float m = -INFINITY;
+          float v[CT];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             const int c = c0 + ct * 16 + ln;
-            const float x = acc[u][ct][i] * a.scale2;
-            if (c <= lim && c < a.n) m = fmaxf(m, x);
+            v[ct] = (full || (c <= lim && c < a.n)) ? acc[u][ct][i] : -INFINITY;
           }
+          float mx = v[0];
+#pragma unroll
+          for (int ct = 1; ct < CT; ++ct) mx = fmaxf(mx, v[ct]);
+          const float m = max16(mx) * a.scale2;
           float l = 0.0f;
           if (m != -INFINITY) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-              const int c = c0 + ct * 16 + ln;
-              const float x = acc[u][ct][i] * a.scale2;
-              if (c <= lim && c < a.n) l += fast_exp2(x - m);
-            }
+            for (int ct = 0; ct < CT; ++ct) l += fast_exp2(__builtin_fmaf(v[ct], a.scale2, -m));
           }
-          merge16(m, l);
+          l = sum16(l);
           if (ln == 0 && r < a.R)
             a.stats[(static_cast<size_t>(bj) * a.nc1 + chunk) * a.R + r] = make_float2(m, l);
         }
@@ -213,12 +239,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = row0[u] + 4 * lq + i;
-            if (r < a.R) v += fast_exp2(acc[u][ct][i] * a.scale2 - st[u][i].x) * st[u][i].y;
+            if (r < a.R) v = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[u][ct][i], a.scale2, -st[u][i].x)),
+                                            st[u][i].y, v);
           }
         }
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        colacc[ct] += v;
+        colacc[ct] += sum_quarters(v);
       }
     }
   }
