@@ -323,18 +323,21 @@ __device__ int block_exclusive_scan(int x, int* sh, int* total) {
   return res;
 }
 
-// Add one vote per active lane to hist[bin] with one atomic per distinct bin in
-// the wave (scores share their leading key bytes, so plain per-lane atomics on
-// one address would serialize).
+// Add one vote per active lane to hist[bin] (bin < 256) with one atomic per
+// distinct bin in the wave (scores share their leading key bytes, so plain
+// per-lane atomics on one address would serialize).  The lanes with this lane's
+// bin are found with one ballot per bin bit, at a cost that does not depend on
+// how many distinct bins the wave holds.
 __device__ __forceinline__ void wave_hist_add(int* hist, bool valid, uint32_t bin) {
-  uint64_t active = __ballot(valid);
-  while (active) {
-    const int leader = __builtin_ctzll(active);
-    const uint32_t b0 = __builtin_amdgcn_readlane(bin, leader);
-    const uint64_t same = __ballot(valid && bin == b0) & active;
-    if ((threadIdx.x & 63) == leader) atomicAdd(&hist[b0], __popcll(same));
-    active &= ~same;
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool set = (bin >> bit) & 1u;
+    const uint64_t ones = __ballot(set);
+    peers &= set ? ones : ~ones;
   }
+  const int lane = threadIdx.x & 63;
+  if (valid && __builtin_ctzll(peers) == lane) atomicAdd(&hist[bin], __popcll(peers));
 }
 
 // Digit selection of one radix pass: the largest d with sum_{d' >= d} cnt[d'] >=
@@ -362,6 +365,8 @@ __device__ __forceinline__ void select_digit(const int* cnt, int krem, int* wsum
     }
   }
 }
+
+constexpr int kMaxPoolHalf = 4;  // pooling kernels up to 9 use the register window
 
 struct TopArgs {
   const float* raw;  // [B][Hkv][N]
@@ -469,16 +474,37 @@ __global__ __launch_bounds__(kTopThreads) void pool_topk_lds_kernel(TopArgs a) {
   __syncthreads();
   const int cb = tid * KPT;
   uint32_t key[KPT];
+  if (h <= kMaxPoolHalf) {
+    // the thread's pooling window [cb - h, cb + KPT + h) in registers, clamped
+    // at the row ends (the same maximum as a window clipped to the row)
+    float win[KPT + 2 * kMaxPoolHalf];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int c = cb + i;
-    key[i] = 0u;
-    if (c < N) {
-      float m = rs[c];
-      const int lo = max(0, c - h), hi = min(N - 1, c + h);
-      for (int d = lo; d <= hi; ++d) m = fmaxf(m, rs[d]);
-      key[i] = order_key(m);
-      if (a.scores) a.scores[bj * N + c] = m;
+    for (int i = 0; i < KPT + 2 * kMaxPoolHalf; ++i) {
+      const int c = min(max(cb - h + i, 0), N - 1);
+      win[i] = (i < KPT + 2 * h) ? rs[c] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      float m = win[i];
+#pragma unroll
+      for (int d = 1; d <= 2 * kMaxPoolHalf; ++d)
+        if (d <= 2 * h) m = fmaxf(m, win[i + d]);
+      const int c = cb + i;
+      key[i] = c < N ? order_key(m) : 0u;
+      if (a.scores && c < N) a.scores[bj * N + c] = m;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = cb + i;
+      key[i] = 0u;
+      if (c < N) {
+        float m = rs[c];
+        const int lo = max(0, c - h), hi = min(N - 1, c + h);
+        for (int d = lo; d <= hi; ++d) m = fmaxf(m, rs[d]);
+        key[i] = order_key(m);
+        if (a.scores) a.scores[bj * N + c] = m;
+      }
     }
   }
   if (a.kk == 0) return;
