@@ -261,31 +261,36 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
   }
 }
 
-// Per row: M = max over chunks, 1/L with L = sum l_k 2^(m_k - M).
+// Per row: M = max over chunks, 1/L with L = sum l_k 2^(m_k - M).  One wave
+// per row; lane i takes chunks i, i+64, ... (one round of loads for up to 64
+// chunks, i.e. rows of 8k keys), then the wave reduces max and sum.
+constexpr int kRowsPerBlock = kThreads / 64;
+__device__ __forceinline__ float wave_max(float x) {
+  x = max16(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum(float x) { return sum_quarters(sum16(x)); }
 __global__ __launch_bounds__(kThreads) void rowstat_kernel(ScoreArgs a) {
-  const int r = blockIdx.x * kThreads + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   const int j = blockIdx.y, b = blockIdx.z;
-  if (r >= a.R) return;
+  if (r >= a.R) return;  // wave-uniform
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
   const float2* st = a.stats + bj * a.nc1 * a.R + r;
-  // online (max, sum) merge; blocks of 8 independent loads keep them in flight
-  float M = -INFINITY, L = 0.0f;
-  for (int c0 = 0; c0 < a.nc1; c0 += 8) {
-    float2 ml[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      ml[u] = (c0 + u < a.nc1) ? st[static_cast<size_t>(c0 + u) * a.R] : make_float2(-INFINITY, 0.0f);
-    float m8 = M;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m8 = fmaxf(m8, ml[u].x);
-    if (m8 == -INFINITY) continue;
-    L = (M == -INFINITY) ? 0.0f : L * exp2f(M - m8);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (ml[u].x != -INFINITY) L += ml[u].y * exp2f(ml[u].x - m8);
-    M = m8;
+  float m = -INFINITY, l = 0.0f;  // this lane's chunks, merged
+  for (int c0 = 0; c0 < a.nc1; c0 += 64) {
+    const int c = c0 + lane;
+    const float2 ml = c < a.nc1 ? st[static_cast<size_t>(c) * a.R] : make_float2(-INFINITY, 0.0f);
+    const float M = fmaxf(m, ml.x);
+    if (M != -INFINITY) {
+      l = (m == -INFINITY ? 0.0f : l * exp2f(m - M)) + (ml.x == -INFINITY ? 0.0f : ml.y * exp2f(ml.x - M));
+      m = M;
+    }
   }
-  a.rowstat[bj * a.R + r] = make_float2(M, 1.0f / L);
+  const float M = wave_max(m);
+  const float L = wave_sum(m == -INFINITY ? 0.0f : l * exp2f(m - M));
+  if (lane == 0) a.rowstat[bj * a.R + r] = make_float2(M, 1.0f / L);
 }
 
 constexpr int kTopThreads = 1024;
@@ -579,7 +584,7 @@ kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t
   constexpr int CH = ChunkCols<T>::value;
   kvc_status s = launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
   if (s != KVC_OK) return s;
-  hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kThreads - 1) / kThreads, a.Hkv, B), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.Hkv, B), dim3(kThreads), 0, st, a);
   if ((s = check_launch()) != KVC_OK) return s;
   s = launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
   if (s != KVC_OK) return s;
