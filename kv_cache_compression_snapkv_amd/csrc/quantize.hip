@@ -7,7 +7,9 @@
 // "Quantization" (KIVI grouping; recent tokens kept exact until a group fills).
 //
 // One workgroup owns one 32-token block of one (batch, KV head): the block's
-// gathered keys and values are staged in LDS as float32, the per-channel key
+// gathered keys and values are staged in LDS (bfloat16 inputs as they are,
+// float32 inputs as float32; the layout is sized by a bound DM >= D so that
+// small heads take little LDS), the per-channel key
 // groups and per-token value groups get their fp16 scale/zero, and the codes
 // are packed: keys along channels (a word holds 32/b channels of one token),
 // values along tokens (a word holds 32/b tokens of one channel).
@@ -17,32 +19,37 @@ namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxD = 256;
 
-constexpr int kLdsRow = kMaxD + 4;  // float row stride: 16-byte aligned rows, column reads conflict-free
-struct QuantLds {
-  float k[kGroup][kLdsRow];
-  float v[kGroup][kLdsRow];
-  float kz[kMaxD], kinv[kMaxD];
-  float vz[kGroup][kMaxD / kGroup], vinv[kGroup][kMaxD / kGroup];
-  uint8_t kok[kMaxD];
-  uint8_t vok[kGroup][kMaxD / kGroup];
+// Staged element as float32 (bf16 -> float32 is exact).
+__device__ __forceinline__ float as_f32(float x) { return x; }
+__device__ __forceinline__ float as_f32(uint16_t x) { return bf16_to_f32(x); }
+
+// S: staged element type, DM: head-dim bound.  Rows are 16 bytes longer than
+// DM elements (16-byte aligned rows; a column walk changes bank every row).
+template <typename S, int DM> struct QuantLds {
+  static constexpr int LD = DM + 16 / sizeof(S);
+  S k[kGroup][LD];
+  S v[kGroup][LD];
+  float kz[DM], kinv[DM];
+  float vz[kGroup][DM / kGroup], vinv[kGroup][DM / kGroup];
+  uint8_t kok[DM];
+  uint8_t vok[kGroup][DM / kGroup];
 };
 
 // Quantize the 32 tokens staged in L and write them at token offset q0 of the
 // (batch, KV head) slice whose base pointers are given.
-template <int BITS>
-__device__ void quantize_block(QuantLds& L, int D, int q0, uint32_t* k_codes, uint32_t* k_meta,
+template <int BITS, typename S, int DM>
+__device__ void quantize_block(QuantLds<S, DM>& L, int D, int q0, uint32_t* k_codes, uint32_t* k_meta,
                                uint32_t* v_codes, uint32_t* v_meta) {
   const int tid = threadIdx.x;
   const float qmax = static_cast<float>((1 << BITS) - 1);
   const int ngv = D / kGroup;
   // key groups: one channel over the 32 tokens
   for (int c = tid; c < D; c += kThreads) {
-    float lo = L.k[0][c], hi = lo;
+    float lo = as_f32(L.k[0][c]), hi = lo;
     for (int t = 1; t < kGroup; ++t) {
-      lo = fminf(lo, L.k[t][c]);
-      hi = fmaxf(hi, L.k[t][c]);
+      lo = fminf(lo, as_f32(L.k[t][c]));
+      hi = fmaxf(hi, as_f32(L.k[t][c]));
     }
     const GroupQ g = make_group(lo, hi, qmax);
     L.kz[c] = g.z;
@@ -53,10 +60,10 @@ __device__ void quantize_block(QuantLds& L, int D, int q0, uint32_t* k_codes, ui
   // value groups: one token over 32 channels
   for (int e = tid; e < kGroup * ngv; e += kThreads) {
     const int t = e / ngv, j = e % ngv;
-    float lo = L.v[t][j * kGroup], hi = lo;
+    float lo = as_f32(L.v[t][j * kGroup]), hi = lo;
     for (int i = 1; i < kGroup; ++i) {
-      lo = fminf(lo, L.v[t][j * kGroup + i]);
-      hi = fmaxf(hi, L.v[t][j * kGroup + i]);
+      lo = fminf(lo, as_f32(L.v[t][j * kGroup + i]));
+      hi = fmaxf(hi, as_f32(L.v[t][j * kGroup + i]));
     }
     const GroupQ g = make_group(lo, hi, qmax);
     L.vz[t][j] = g.z;
@@ -73,7 +80,7 @@ __device__ void quantize_block(QuantLds& L, int D, int q0, uint32_t* k_codes, ui
 #pragma unroll
     for (int i = 0; i < per; ++i) {
       const int c = w * per + i;
-      word |= code_of(L.k[t][c], L.kz[c], L.kinv[c], L.kok[c], qmax) << (BITS * i);
+      word |= code_of(as_f32(L.k[t][c]), L.kz[c], L.kinv[c], L.kok[c], qmax) << (BITS * i);
     }
     k_codes[static_cast<size_t>(q0 + t) * nw + w] = word;
   }
@@ -84,7 +91,7 @@ __device__ void quantize_block(QuantLds& L, int D, int q0, uint32_t* k_codes, ui
 #pragma unroll
     for (int i = 0; i < per; ++i) {
       const int t = r * per + i;
-      word |= code_of(L.v[t][c], L.vz[t][j], L.vinv[t][j], L.vok[t][j], qmax) << (BITS * i);
+      word |= code_of(as_f32(L.v[t][c]), L.vz[t][j], L.vinv[t][j], L.vok[t][j], qmax) << (BITS * i);
     }
     v_codes[(static_cast<size_t>(q0) / per + r) * D + c] = word;
   }
@@ -117,10 +124,10 @@ __device__ __forceinline__ int kept_pos(const QuantArgs& a, int bj, int t) {
 // are zero) as float32 rows of L.k / L.v.  Every 16-byte load of the 32 rows is
 // issued before the first LDS store: one memory round trip for the positions,
 // one for the data.
-template <typename T>
-__device__ void stage_rows(QuantLds& L, const QuantArgs& a, int bj, int t_first, int count) {
+template <typename T, int DM>
+__device__ void stage_rows(QuantLds<T, DM>& L, const QuantArgs& a, int bj, int t_first, int count) {
   constexpr int VEC = 16 / sizeof(T);                      // elements per 16 bytes
-  constexpr int MAXV = kGroup * kMaxD / VEC / kThreads;    // pieces per thread at D = kMaxD
+  constexpr int MAXV = (kGroup * DM / VEC + kThreads - 1) / kThreads;  // pieces per thread at D = DM
   const int D = a.D, ppr = D / VEC, total = kGroup * ppr;  // pieces per row, per tensor
   const T* k = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
   const T* v = static_cast<const T*>(a.v) + static_cast<size_t>(bj) * a.n * D;
@@ -147,22 +154,15 @@ __device__ void stage_rows(QuantLds& L, const QuantArgs& a, int bj, int t_first,
     const int e = tid + i * kThreads;
     if (e < total) {
       const int t = e / ppr, c = (e % ppr) * VEC;
-      const T* kx = reinterpret_cast<const T*>(&kv[i]);
-      const T* vx = reinterpret_cast<const T*>(&vv[i]);
-#pragma unroll
-      for (int u = 0; u < VEC; u += 4) {
-        *reinterpret_cast<float4*>(&L.k[t][c + u]) =
-            make_float4(load_f32(kx, u), load_f32(kx, u + 1), load_f32(kx, u + 2), load_f32(kx, u + 3));
-        *reinterpret_cast<float4*>(&L.v[t][c + u]) =
-            make_float4(load_f32(vx, u), load_f32(vx, u + 1), load_f32(vx, u + 2), load_f32(vx, u + 3));
-      }
+      *reinterpret_cast<uint4*>(&L.k[t][c]) = kv[i];
+      *reinterpret_cast<uint4*>(&L.v[t][c]) = vv[i];
     }
   }
 }
 
-template <typename T, int BITS>
+template <typename T, int BITS, int DM>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ __attribute__((aligned(16))) QuantLds L;
+  __shared__ __attribute__((aligned(16))) QuantLds<T, DM> L;
   const int blk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int bj = b * a.Hkv + j;
   const int D = a.D;
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   const int nqb = a.Q / kGroup;
   if (blk < nqb) {
     const int t0 = blk * kGroup;
-    stage_rows<T>(L, a, bj, t0, kGroup);
+    stage_rows<T, DM>(L, a, bj, t0, kGroup);
     __syncthreads();
     const size_t qc = a.q_cap;
     quantize_block<BITS>(L, D, t0, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     // residual: kept tokens [Q, T) -> bf16 ring rows 0..T-Q-1
     const int r0 = (blk - nqb) * kGroup;
     const int nr = min(kGroup, a.T - a.Q - r0);
-    stage_rows<T>(L, a, bj, a.Q + r0, nr);
+    stage_rows<T, DM>(L, a, bj, a.Q + r0, nr);
     __syncthreads();
     uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
     uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
@@ -189,10 +189,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     for (int e = tid; e < nr * (D / 8); e += kThreads) {
       const int t = e / (D / 8), c = (e % (D / 8)) * 8;
       uint4 w;
-      w.x = f32_to_bf16(L.k[t][c]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 1])) << 16);
-      w.y = f32_to_bf16(L.k[t][c + 2]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 3])) << 16);
-      w.z = f32_to_bf16(L.k[t][c + 4]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 5])) << 16);
-      w.w = f32_to_bf16(L.k[t][c + 6]) | (static_cast<uint32_t>(f32_to_bf16(L.k[t][c + 7])) << 16);
+      auto bf = [&](int cc) { return static_cast<uint32_t>(f32_to_bf16(as_f32(L.k[t][cc]))); };
+      w.x = bf(c) | (bf(c + 1) << 16);
+      w.y = bf(c + 2) | (bf(c + 3) << 16);
+      w.z = bf(c + 4) | (bf(c + 5) << 16);
+      w.w = bf(c + 6) | (bf(c + 7) << 16);
       *reinterpret_cast<uint4*>(kr + static_cast<size_t>(r0 + t) * D + c) = w;
     }
     const int nc8 = (nr + 7) / 8;  // 8-token chunks (r0 and r_cap are multiples of 8)
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
       const int c = e / nc8, t8 = (e % nc8) * 8;
       uint16_t h[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) h[u] = f32_to_bf16(L.v[t8 + u][c]);
+      for (int u = 0; u < 8; ++u) h[u] = f32_to_bf16(as_f32(L.v[t8 + u][c]));
       uint16_t* dst = vr + static_cast<size_t>(c) * a.r_cap + r0 + t8;
       if (t8 + 8 <= nr) {
         uint4 w;
@@ -231,9 +232,9 @@ struct FlushArgs {
 // staged with 16-byte row loads, values with 16-byte loads of 8 consecutive
 // ring rows of one channel (r_start and r_cap are multiples of 8, so such a
 // chunk never wraps).
-template <typename T, int BITS>
+template <typename T, int BITS, int DM>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
-  __shared__ QuantLds L;
+  __shared__ __attribute__((aligned(16))) QuantLds<uint16_t, DM> L;  // the ring holds bf16
   const int j = blockIdx.x, b = blockIdx.y;
   const int bj = b * a.Hkv + j;
   const int D = a.D;
@@ -249,13 +250,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   const int cpr = D / 8;  // 16-byte chunks per key row
   for (int e = tid; e < kGroup * cpr; e += kThreads) {
     const int t = e / cpr, c8 = (e % cpr) * 8;
-    const uint4 w = *reinterpret_cast<const uint4*>(kr + static_cast<size_t>(ring(t)) * D + c8);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      L.k[t][c8 + 2 * i] = bf16_to_f32(static_cast<uint16_t>(ws[i] & 0xFFFFu));
-      L.k[t][c8 + 2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(ws[i] >> 16));
-    }
+    *reinterpret_cast<uint4*>(&L.k[t][c8]) = *reinterpret_cast<const uint4*>(kr + static_cast<size_t>(ring(t)) * D + c8);
   }
   for (int e = tid; e < D * (kGroup / 8); e += kThreads) {
     const int c = e / (kGroup / 8), t8 = (e % (kGroup / 8)) * 8;
@@ -263,8 +258,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      L.v[t8 + 2 * i][c] = bf16_to_f32(static_cast<uint16_t>(ws[i] & 0xFFFFu));
-      L.v[t8 + 2 * i + 1][c] = bf16_to_f32(static_cast<uint16_t>(ws[i] >> 16));
+      L.v[t8 + 2 * i][c] = static_cast<uint16_t>(ws[i] & 0xFFFFu);
+      L.v[t8 + 2 * i + 1][c] = static_cast<uint16_t>(ws[i] >> 16);
     }
   }
   __syncthreads();
@@ -272,8 +267,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   for (int c = tid; c < D; c += kThreads) {
     const uint16_t kb = f32_to_bf16(load_f32(kn, c)), vb = f32_to_bf16(load_f32(vn, c));
     if (a.r_old < kGroup) {
-      L.k[a.r_old][c] = bf16_to_f32(kb);
-      L.v[a.r_old][c] = bf16_to_f32(vb);
+      L.k[a.r_old][c] = kb;
+      L.v[a.r_old][c] = vb;
     } else {
       const int p = ring(a.r_old);
       kr[static_cast<size_t>(p) * D + c] = kb;
@@ -288,15 +283,22 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
                        a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
 }
 
+// Head-dim bound of the LDS layout.
+int dm_for(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : 256; }
+
 template <typename T>
 kvc_status launch_quantize(const QuantArgs& a, int bits, int B, hipStream_t st) {
   const int nblk = a.Q / kGroup + (a.T - a.Q + kGroup - 1) / kGroup;
   if (nblk == 0) return KVC_OK;
   dim3 grid(nblk, a.Hkv, B);
-  if (bits == 2)
-    hipLaunchKernelGGL((quantize_kernel<T, 2>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((quantize_kernel<T, 4>), grid, dim3(kThreads), 0, st, a);
+  const int dm = dm_for(a.D);
+#define KVC_Q(B_, DM_) hipLaunchKernelGGL((quantize_kernel<T, B_, DM_>), grid, dim3(kThreads), 0, st, a)
+  if (bits == 2) {
+    if (dm == 64) KVC_Q(2, 64); else if (dm == 128) KVC_Q(2, 128); else KVC_Q(2, 256);
+  } else {
+    if (dm == 64) KVC_Q(4, 64); else if (dm == 128) KVC_Q(4, 128); else KVC_Q(4, 256);
+  }
+#undef KVC_Q
   return check_launch();
 }
 
@@ -322,17 +324,19 @@ kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new
   a.k_res = c->k_res;
   a.v_res = c->v_res;
   dim3 grid(c->kv_heads, c->batch);
+  const int dm = dm_for(a.D);
+#define KVC_F(T_, B_)                                                                                        \
+  do {                                                                                                       \
+    if (dm == 64) hipLaunchKernelGGL((flush_kernel<T_, B_, 64>), grid, dim3(kThreads), 0, st, a);          \
+    else if (dm == 128) hipLaunchKernelGGL((flush_kernel<T_, B_, 128>), grid, dim3(kThreads), 0, st, a);   \
+    else hipLaunchKernelGGL((flush_kernel<T_, B_, 256>), grid, dim3(kThreads), 0, st, a);                  \
+  } while (0)
   if (dt == KVC_F32) {
-    if (c->bits == 2)
-      hipLaunchKernelGGL((flush_kernel<float, 2>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((flush_kernel<float, 4>), grid, dim3(kThreads), 0, st, a);
+    if (c->bits == 2) KVC_F(float, 2); else KVC_F(float, 4);
   } else {
-    if (c->bits == 2)
-      hipLaunchKernelGGL((flush_kernel<uint16_t, 2>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((flush_kernel<uint16_t, 4>), grid, dim3(kThreads), 0, st, a);
+    if (c->bits == 2) KVC_F(uint16_t, 2); else KVC_F(uint16_t, 4);
   }
+#undef KVC_F
   return check_launch();
 }
 
