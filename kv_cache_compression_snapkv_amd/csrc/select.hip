@@ -31,7 +31,7 @@ struct ScoreArgs {
   const void* q_win;  // [B][Hq][W][D]
   const void* k;      // [B][Hkv][n][D]
   float2* stats;      // pass 1: [B][Hkv][nc1][R] (max, sum) in log2 units
-  float2* rowstat;    // [B][Hkv][R] (M, 1/L)
+  float* rowstat;     // [B][Hkv][R] M + log2(L): 2^(x - it) is x's softmax weight
   float* raw;         // [B][Hkv][N] column sums
   int Hq, Hkv, G, n, W, R, N, nc1;
   float scale2;
@@ -223,13 +223,13 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
         }
       }
     } else {
-      float2 st[2][4];
+      float st[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = row0[u] + 4 * lq + i;
-          st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : make_float2(0.f, 0.f);
+          st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : 0.0f;
         }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -239,8 +239,7 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = row0[u] + 4 * lq + i;
-            if (r < a.R) v = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[u][ct][i], a.scale2, -st[u][i].x)),
-                                            st[u][i].y, v);
+            if (r < a.R) v += fast_exp2(__builtin_fmaf(acc[u][ct][i], a.scale2, -st[u][i]));
           }
         }
         colacc[ct] += sum_quarters(v);
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
   }
 }
 
-// Per row: M = max over chunks, 1/L with L = sum l_k 2^(m_k - M).  One wave
+// Per row: M = max over chunks, L = sum l_k 2^(m_k - M); stored as M + log2(L).  One wave
 // per row; lane i takes chunks i, i+64, ... (one round of loads for up to 64
 // chunks, i.e. rows of 8k keys), then the wave reduces max and sum.
 constexpr int kRowsPerBlock = kThreads / 64;
@@ -290,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void rowstat_kernel(ScoreArgs a) {
   }
   const float M = wave_max(m);
   const float L = wave_sum(m == -INFINITY ? 0.0f : l * exp2f(m - M));
-  if (lane == 0) a.rowstat[bj * a.R + r] = make_float2(M, 1.0f / L);
+  if (lane == 0) a.rowstat[bj * a.R + r] = M + log2f(L);
 }
 
 constexpr int kTopThreads = 1024;
@@ -647,7 +646,7 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   a.q_win = q_win;
   a.k = k;
   a.stats = reinterpret_cast<float2*>(w);
-  a.rowstat = reinterpret_cast<float2*>(w + sz_stats);
+  a.rowstat = reinterpret_cast<float*>(w + sz_stats);
   a.raw = reinterpret_cast<float*>(w + sz_stats + sz_row);
   a.Hq = Hq;
   a.Hkv = Hkv;
