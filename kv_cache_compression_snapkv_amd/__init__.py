@@ -4,7 +4,7 @@ SnapKV/PyramidKV window selection -> KIVI/MiniKV 2/4-bit group quantization ->
 single-query decode attention over the packed cache plus a bf16 residual, all in
 hand-written HIP kernels behind the C ABI of ``include/kvc.h``.  This package is
 the thin Python binding (same entry-point names); it needs ``libkvc.so``, built
-by ``python -m kv_cache_compression_snapkv_amd.build``.
+by ``python kv_cache_compression_snapkv_amd/build.py`` (or ``__graft_entry__.build()``).
 """
 
 from ._lib import (Cache, KvcError, LIB_PATH, decode_ws_bytes, kvc_budget, kvc_decode_attn,  # noqa: F401

@@ -51,7 +51,7 @@ class Footprint(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_compression_snapkv_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python kv_cache_compression_snapkv_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)
     lib.kvc_budget.argtypes = [ctypes.POINTER(BudgetArgs), ctypes.POINTER(I32), ctypes.POINTER(Footprint)]

@@ -1,6 +1,6 @@
 """Build libkvc.so (all HIP kernels + the C ABI) in-tree for gfx950.
 
-    python -m kv_cache_compression_snapkv_amd.build   (or __graft_entry__.build())
+    python kv_cache_compression_snapkv_amd/build.py   (or __graft_entry__.build())
 
 Each source is compiled to an object in parallel, then linked.  Flags:
   --offload-arch=gfx950                      MI355X only

@@ -22,7 +22,8 @@ namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowBlock = 128;  // rows per pass over the staged chunk (8 tiles, 2 per wave)
+constexpr int kRowBlock = 128;  // rows per pass over the staged chunk (8 tiles of 16)
+constexpr int kScoreWaves = 4;  // waves per scorer workgroup (two row tiles each; 8 waves x one tile measured slower)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -105,15 +106,103 @@ __device__ __forceinline__ float sum_quarters(float x) {
   return x;
 }
 
-template <typename T, int KS, int PASS>
-__global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
+// Window rows row0[u]..row0[u]+15 (u = 0, 1) of one wave against the CH = 16*CT
+// columns of chunk `chunk` (first column c0): MFMA products with the key
+// fragments that kload(ct, s, frag) supplies, then pass 1 writes each row's
+// (max, sum) for the chunk and pass 2 adds the rows' softmax weights to the
+// lane's column partials.  st: pass 2's per-row M + log2(L).
+template <typename T, int KS, int PASS, int TPW, int CT, typename KLoad>
+__device__ __forceinline__ void score_rows(const ScoreArgs& a, int bj, int chunk, int c0, bool full,
+                                           const Frag<T> (&qf)[TPW][KS], const int (&row0)[TPW],
+                                           const float (&st)[TPW][4], float (&colacc)[CT], KLoad kload) {
+  const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
+  const bool active0 = row0[0] < a.R, active1 = TPW > 1 && row0[TPW - 1] < a.R;
+  if (!active0) return;  // wave-uniform
+  f32x4 acc[TPW][CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) acc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      Frag<T> kf;
+      kload(ct, s, kf);
+      acc[0][ct] = mma(qf[0][s], kf, acc[0][ct]);
+      if (TPW > 1 && active1) acc[TPW - 1][ct] = mma(qf[TPW - 1][s], kf, acc[TPW - 1][ct]);
+    }
+  }
+  if (PASS == 1) {
+    // per row: max over the row's 16 lanes x CT columns, then the sum of
+    // 2^(x - M) with x = logit * scale2 (scale2 > 0, so max(x) = scale2 * max)
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (u == 1 && !active1) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0[u] + 4 * lq + i;
+        const int lim = a.n - a.W + (r % a.W);  // last key this row may see
+        float v[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int c = c0 + ct * 16 + ln;
+          v[ct] = (full || (c <= lim && c < a.n)) ? acc[u][ct][i] : -INFINITY;
+        }
+        float mx = v[0];
+#pragma unroll
+        for (int ct = 1; ct < CT; ++ct) mx = fmaxf(mx, v[ct]);
+        const float m = max16(mx) * a.scale2;
+        float l = 0.0f;
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) l += fast_exp2(__builtin_fmaf(v[ct], a.scale2, -m));
+        }
+        l = sum16(l);
+        if (ln == 0 && r < a.R)
+          a.stats[(static_cast<size_t>(bj) * a.nc1 + chunk) * a.R + r] = make_float2(m, l);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float v = 0.0f;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0[u] + 4 * lq + i;
+          if (r < a.R) v += fast_exp2(__builtin_fmaf(acc[u][ct][i], a.scale2, -st[u][i]));
+        }
+      }
+      colacc[ct] += sum_quarters(v);
+    }
+  }
+}
+
+// Pass 2's row statistics for the lane's eight rows.
+template <int TPW>
+__device__ __forceinline__ void load_rowstat(const ScoreArgs& a, int bj, const int (&row0)[TPW], float (&st)[TPW][4]) {
+  const int lq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0[u] + 4 * lq + i;
+      st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : 0.0f;
+    }
+}
+
+// NWAVE waves per workgroup (4: two 16-row tiles per wave, 8: one), 128 rows
+// per pass over the staged chunk.
+template <typename T, int KS, int PASS, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE, (NWAVE == 8 ? 2 : 4)) void score_kernel(ScoreArgs a) {
+  constexpr int NTHR = 64 * NWAVE, TPW = 8 / NWAVE;
   constexpr int CH = ChunkCols<T>::value;
   constexpr int D = KS * 32;
   constexpr int PAD = 16 / sizeof(T);
   constexpr int LD = D + PAD;  // padded LDS row (elements)
   constexpr int CT = CH / 16;  // column tiles per chunk
   __shared__ __attribute__((aligned(16))) T ks[CH * LD];
-  __shared__ float colred[4][CH];
+  __shared__ float colred[NWAVE][CH];
 
   const int chunk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int bj = b * a.Hkv + j;
@@ -130,12 +219,12 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
   // query fragments of a row block: lane (ln, lq) holds row ln of each of its
   // two tiles, channels 32s+8lq..+7; the first block's are requested together
   // with the key chunk
-  Frag<T> qf[2][KS];
-  int row0[2];
+  Frag<T> qf[TPW][KS];
+  int row0[TPW];
   auto load_q = [&](int rb) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      row0[u] = rb + (wave + 4 * u) * 16;  // first row of this wave's tile u
+    for (int u = 0; u < TPW; ++u) {
+      row0[u] = rb + (wave + NWAVE * u) * 16;  // first row of this wave's tile u
       const int r = row0[u] + ln;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -146,12 +235,12 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
   };
   load_q(0);
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int NV = CH * D / VEC / kThreads;  // 16-byte pieces per thread
-  static_assert(CH * D / VEC % kThreads == 0, "chunk must split evenly");
+  constexpr int NV = CH * D / VEC / NTHR;  // 16-byte pieces per thread
+  static_assert(CH * D / VEC % NTHR == 0, "chunk must split evenly");
   uint4 kv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = tid + i * kThreads;
+    const int e = tid + i * NTHR;
     const int c = e / (D / VEC), d = (e % (D / VEC)) * VEC;
     const int cc = min(c0 + c, a.n - 1);  // always in bounds; zeroed below if invalid
     kv[i] = *reinterpret_cast<const uint4*>(kp + static_cast<size_t>(cc) * D + d);
@@ -159,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
   const bool chunk_valid = c0 + CH <= ncol_valid;  // no zero fill needed
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = tid + i * kThreads;
+    const int e = tid + i * NTHR;
     const int c = e / (D / VEC), d = (e % (D / VEC)) * VEC;
     *reinterpret_cast<uint4*>(&ks[c * LD + d]) =
         (chunk_valid || c0 + c < ncol_valid) ? kv[i] : make_uint4(0, 0, 0, 0);
@@ -175,76 +264,11 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
 
   for (int rb = 0; rb < a.R; rb += kRowBlock) {
     if (rb > 0) load_q(rb);
-    const bool active0 = row0[0] < a.R, active1 = row0[1] < a.R;
-    if (!active0) continue;  // wave-uniform
-
-    f32x4 acc[2][CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      acc[0][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        Frag<T> kf;
-        kf.load(&ks[(ct * 16 + ln) * LD + 32 * s + 8 * lq]);
-        acc[0][ct] = mma(qf[0][s], kf, acc[0][ct]);
-        if (active1) acc[1][ct] = mma(qf[1][s], kf, acc[1][ct]);
-      }
-    }
-
-    if (PASS == 1) {
-      // per row: max over the row's 16 lanes x CT columns, then the sum of
-      // 2^(x - M) with x = logit * scale2 (scale2 > 0, so max(x) = scale2 * max)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (u == 1 && !active1) break;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = row0[u] + 4 * lq + i;
-          const int lim = a.n - a.W + (r % a.W);  // last key this row may see
-          float v[CT];
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const int c = c0 + ct * 16 + ln;
-            v[ct] = (full || (c <= lim && c < a.n)) ? acc[u][ct][i] : -INFINITY;
-          }
-          float mx = v[0];
-#pragma unroll
-          for (int ct = 1; ct < CT; ++ct) mx = fmaxf(mx, v[ct]);
-          const float m = max16(mx) * a.scale2;
-          float l = 0.0f;
-          if (m != -INFINITY) {
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) l += fast_exp2(__builtin_fmaf(v[ct], a.scale2, -m));
-          }
-          l = sum16(l);
-          if (ln == 0 && r < a.R)
-            a.stats[(static_cast<size_t>(bj) * a.nc1 + chunk) * a.R + r] = make_float2(m, l);
-        }
-      }
-    } else {
-      float st[2][4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = row0[u] + 4 * lq + i;
-          st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : 0.0f;
-        }
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        float v = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = row0[u] + 4 * lq + i;
-            if (r < a.R) v += fast_exp2(__builtin_fmaf(acc[u][ct][i], a.scale2, -st[u][i]));
-          }
-        }
-        colacc[ct] += sum_quarters(v);
-      }
-    }
+    float st[TPW][4];
+    if (PASS == 2) load_rowstat<TPW>(a, bj, row0, st);
+    score_rows<T, KS, PASS, TPW>(a, bj, chunk, c0, full, qf, row0, st, colacc, [&](int ct, int s, Frag<T>& kf) {
+      kf.load(&ks[(ct * 16 + ln) * LD + 32 * s + 8 * lq]);
+    });
   }
 
   if (PASS == 2) {
@@ -253,8 +277,10 @@ __global__ __launch_bounds__(kThreads, 4) void score_kernel(ScoreArgs a) {
       for (int ct = 0; ct < CT; ++ct) colred[wave][ct * 16 + ln] = colacc[ct];
     }
     __syncthreads();
-    for (int c = tid; c < CH; c += kThreads) {
-      const float v = ((colred[0][c] + colred[1][c]) + colred[2][c]) + colred[3][c];
+    for (int c = tid; c < CH; c += NTHR) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) v += colred[w][c];
       if (c0 + c < a.N) a.raw[static_cast<size_t>(bj) * a.N + c0 + c] = v;
     }
   }
@@ -569,7 +595,7 @@ kvc_status launch_score(const ScoreArgs& a, int KS, dim3 grid, hipStream_t st) {
   switch (KS) {
 #define KVC_CASE(k)                                                                     \
   case k:                                                                               \
-    hipLaunchKernelGGL((score_kernel<T, k, PASS>), grid, dim3(kThreads), 0, st, a); \
+    hipLaunchKernelGGL((score_kernel<T, k, PASS, kScoreWaves>), grid, dim3(64 * kScoreWaves), 0, st, a); \
     break;
     KVC_CASE(1) KVC_CASE(2) KVC_CASE(3) KVC_CASE(4) KVC_CASE(5) KVC_CASE(6) KVC_CASE(7) KVC_CASE(8)
 #undef KVC_CASE
