@@ -10,10 +10,12 @@
 //           small kernel into (M_r, 1/L_r);
 //   pass 2: column sums of 2^(x - M_r)/L_r over the rows for candidates
 //           c < n-W, written in fixed order (deterministic).
-// Then one workgroup per (b, j) max-pools the scores, maps them to
-// order-preserving uint32 keys and finds the k'-th largest by a 4x8-bit radix
-// select; an index-order scan emits every key above the threshold plus the
-// lowest-index ties, so idx comes out ascending with ties to the lower index.
+// Then the scores are max-pooled and mapped to order-preserving uint32 keys and
+// the k'-th largest is found by a radix select (rows up to 32k candidates: one
+// workgroup per (b, j), keys in registers, 4x8-bit digits; longer rows: 4096-
+// candidate chunks over many workgroups, 8+12+12-bit digits); an index-order
+// scan emits every key above the threshold plus the lowest-index ties, so idx
+// comes out ascending with ties to the lower index.
 #include <algorithm>
 
 #include "kvc_internal.h"
@@ -353,15 +355,16 @@ __device__ int block_exclusive_scan(int x, int* sh, int* total) {
   return res;
 }
 
-// Add one vote per active lane to hist[bin] (bin < 256) with one atomic per
+// Add one vote per active lane to hist[bin] (bin < 2^NBITS) with one atomic per
 // distinct bin in the wave (scores share their leading key bytes, so plain
 // per-lane atomics on one address would serialize).  The lanes with this lane's
 // bin are found with one ballot per bin bit, at a cost that does not depend on
 // how many distinct bins the wave holds.
+template <int NBITS = 8>
 __device__ __forceinline__ void wave_hist_add(int* hist, bool valid, uint32_t bin) {
   uint64_t peers = __ballot(valid);
 #pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
+  for (int bit = 0; bit < NBITS; ++bit) {
     const bool set = (bin >> bit) & 1u;
     const uint64_t ones = __ballot(set);
     peers &= set ? ones : ~ones;
@@ -397,78 +400,269 @@ __device__ __forceinline__ void select_digit(const int* cnt, int krem, int* wsum
 }
 
 constexpr int kMaxPoolHalf = 4;  // pooling kernels up to 9 use the register window
+constexpr int kChunkKpt = 4;                          // candidates per thread in the chunked path
+constexpr int kChunk = kTopThreads * kChunkKpt;       // candidates per workgroup in the chunked path
+constexpr int kWideBins = 4096;                       // 12-bit digits of radix passes 2 and 3
+constexpr int kSelSlots = 8;
+
+// Digit selection over NB >= kTopThreads bins: thread t takes the NB/kTopThreads
+// bins below the top's t-th group, a block scan gives the count above its first
+// bin, and the thread whose bin first reaches krem writes (digit, krem - above).
+template <int NB>
+__device__ __forceinline__ void select_digit_wide(const int* cnt, int krem, int* scan_sh, uint32_t* sel) {
+  constexpr int BPT = NB / kTopThreads;
+  const int t = threadIdx.x;
+  int c[BPT], tot = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    c[i] = cnt[NB - 1 - (t * BPT + i)];
+    tot += c[i];
+  }
+  int all;
+  int above = block_exclusive_scan(tot, scan_sh, &all);
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    if (above < krem && above + c[i] >= krem) {
+      sel[0] = static_cast<uint32_t>(NB - 1 - (t * BPT + i));
+      sel[1] = static_cast<uint32_t>(krem - above);
+    }
+    above += c[i];
+  }
+}
 
 struct TopArgs {
   const float* raw;  // [B][Hkv][N]
-  uint32_t* keys;    // [B][Hkv][N]
+  uint32_t* keys;    // [B][Hkv][NP] (chunked path)
   float* scores;     // pooled scores out, or null
   int32_t* idx;      // [B][Hkv][kk]
-  int Hkv, N, kk, pool;
+  int* hist1;        // [B][Hkv][nch][256] per-chunk counts of the top key byte (chunked path)
+  int* ghist;        // [B][Hkv][2][kWideBins] counts of the 12-bit digits of passes 2 and 3
+  uint32_t* sel;     // [B][Hkv][kSelSlots]: (prefix, remaining k) after passes 1, 2 and 3
+  int2* cnt;         // [B][Hkv][nch] (keys above the threshold, keys equal to it) per chunk
+  int Hkv, N, kk, pool, NP, nch;
 };
 
-__global__ __launch_bounds__(kTopThreads) void pool_topk_kernel(TopArgs a) {
+// Long score rows: the candidates are split into chunks of kChunk, one
+// workgroup each (thread t owns kChunkKpt consecutive candidates), and the
+// radix select runs as a chain of launches over all chunks of all heads:
+//   chunk_pool_kernel    pooled keys, per-chunk counts of the top key byte;
+//   chunk_hist_kernel    (x2) merge the previous digit's counts, pick the digit,
+//                        count the next 12 bits of the keys still in play;
+//   chunk_count_kernel   pick the last digit (the threshold key), count each
+//                        chunk's keys above and equal to it;
+//   chunk_emit_kernel    emit in index order from the chunk counts before it.
+// Each launch picks the previous digit redundantly in every workgroup; the
+// first chunk's workgroup stores it for the next launch.
+__device__ __forceinline__ uint4 load_chunk_keys(const TopArgs& a, size_t bj, int cb) {
+  return *reinterpret_cast<const uint4*>(a.keys + bj * a.NP + cb);
+}
+__device__ __forceinline__ uint32_t key_at(const uint4& k, int i) { return i == 0 ? k.x : i == 1 ? k.y : i == 2 ? k.z : k.w; }
+
+__global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
+  __shared__ float rs[kChunk + 2 * kMaxPoolHalf];  // raw[c0 - kMaxPoolHalf + i]
   __shared__ int hist[kTopThreads / 64][256];
-  __shared__ int scan_sh[kTopThreads / 64 + 1];
-  __shared__ uint32_t sel_sh[2];
-  const int j = blockIdx.x, b = blockIdx.y;
+  const int ch = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
   const int tid = threadIdx.x, w = tid >> 6;
-  const int N = a.N, h = a.pool / 2;
+  const int N = a.N, h = a.pool / 2, c0 = ch * kChunk;
   const float* raw = a.raw + bj * N;
-  uint32_t* keys = a.keys + bj * N;
-  int32_t* idx = a.idx + bj * a.kk;
-  for (int c = tid; c < N; c += kTopThreads) {
-    float m = raw[c];
-    const int lo = max(0, c - h), hi = min(N - 1, c + h);
-    for (int d = lo; d <= hi; ++d) m = fmaxf(m, raw[d]);
-    keys[c] = order_key(m);
-    if (a.scores) a.scores[bj * N + c] = m;
-  }
-  if (a.kk == 0) return;
-  if (a.kk == N) {
-    for (int c = tid; c < N; c += kTopThreads) idx[c] = c;
-    return;
+  for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
+  if (ch == 0)  // the counts of passes 2 and 3 are accumulated by later launches
+    for (int i = tid; i < 2 * kWideBins; i += kTopThreads) a.ghist[bj * 2 * kWideBins + i] = 0;
+  for (int i = tid; i < kChunk + 2 * kMaxPoolHalf; i += kTopThreads) {
+    const int c = c0 - kMaxPoolHalf + i;
+    if (c >= 0 && c < N) rs[i] = raw[c];
   }
   __syncthreads();
-  uint32_t prefix = 0, pmask = 0;
-  int krem = a.kk;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    for (int base = 0; base < N; base += kTopThreads) {  // uniform trip count (ballots inside)
-      const int c = base + tid;
-      const uint32_t key = c < N ? keys[c] : 0u;
-      wave_hist_add(hist[w], c < N && (key & pmask) == prefix, (key >> shift) & 255u);
+  const int cb = c0 + tid * kChunkKpt;
+  uint32_t key[kChunkKpt];
+  if (h <= kMaxPoolHalf) {
+    // window [cb - h, cb + kChunkKpt + h) clamped to the row: every clamped
+    // position lies in the staged range
+    float win[kChunkKpt + 2 * kMaxPoolHalf];
+#pragma unroll
+    for (int i = 0; i < kChunkKpt + 2 * kMaxPoolHalf; ++i) {
+      const int c = min(max(cb - h + i, 0), N - 1);
+      win[i] = (i < kChunkKpt + 2 * h) ? rs[c - (c0 - kMaxPoolHalf)] : 0.0f;
     }
-    __syncthreads();
-    if (tid < 256) {
-      int s = 0;
-      for (int i = 0; i < kTopThreads / 64; ++i) s += hist[i][tid];
-      hist[0][tid] = s;
+#pragma unroll
+    for (int i = 0; i < kChunkKpt; ++i) {
+      float m = win[i];
+#pragma unroll
+      for (int d = 1; d <= 2 * kMaxPoolHalf; ++d)
+        if (d <= 2 * h) m = fmaxf(m, win[i + d]);
+      const int c = cb + i;
+      key[i] = c < N ? order_key(m) : 0u;
+      if (a.scores && c < N) a.scores[bj * N + c] = m;
     }
-    __syncthreads();
-    select_digit(hist[0], krem, scan_sh, sel_sh);
-    __syncthreads();
-    prefix |= sel_sh[0] << shift;
-    pmask |= 255u << shift;
-    krem = static_cast<int>(sel_sh[1]);
-    __syncthreads();
+  } else {
+#pragma unroll
+    for (int i = 0; i < kChunkKpt; ++i) {
+      const int c = cb + i;
+      key[i] = 0u;
+      if (c < N) {
+        float m = raw[c];
+        const int lo = max(0, c - h), hi = min(N - 1, c + h);
+        for (int d = lo; d <= hi; ++d) m = fmaxf(m, raw[d]);
+        key[i] = order_key(m);
+        if (a.scores) a.scores[bj * N + c] = m;
+      }
+    }
   }
-  // prefix is the k'-th largest key; krem ties at that key are taken, lowest index first
-  int out_pos = 0, eq_seen = 0;
-  for (int base = 0; base < N; base += kTopThreads) {
-    const int c = base + tid;
-    const uint32_t key = c < N ? keys[c] : 0u;
-    const int is_eq = (c < N && key == prefix) ? 1 : 0;
-    int eq_total;
-    const int eq_rank = block_exclusive_scan(is_eq, scan_sh, &eq_total) + eq_seen;
-    const int take = (c < N && (key > prefix || (is_eq && eq_rank < krem))) ? 1 : 0;
-    int take_total;
-    const int pos = block_exclusive_scan(take, scan_sh, &take_total) + out_pos;
-    if (take && pos < a.kk) idx[pos] = c;
-    eq_seen += eq_total;
-    out_pos += take_total;
+  *reinterpret_cast<uint4*>(a.keys + bj * a.NP + cb) = make_uint4(key[0], key[1], key[2], key[3]);
+  if (a.kk == 0) return;
+#pragma unroll
+  for (int i = 0; i < kChunkKpt; ++i) wave_hist_add(hist[w], cb + i < N, key[i] >> 24);
+  __syncthreads();
+  if (tid < 256) {
+    int s = 0;
+    for (int i = 0; i < kTopThreads / 64; ++i) s += hist[i][tid];
+    a.hist1[(bj * a.nch + ch) * 256 + tid] = s;
+  }
+}
+
+// PASS 2: digit 1 from the per-chunk byte counts, then counts of key bits
+// 12..23 among keys with that top byte.  PASS 3: digit 2 from pass 2's counts,
+// then counts of bits 0..11 among keys with that 20-bit prefix.
+template <int PASS>
+__global__ __launch_bounds__(kTopThreads) void chunk_hist_kernel(TopArgs a) {
+  __shared__ int hist[kWideBins];
+  __shared__ int scan_sh[kTopThreads / 64 + 1];
+  __shared__ uint32_t sel_sh[2];
+  const int ch = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
+  const int tid = threadIdx.x;
+  uint32_t prefix, pmask;
+  int krem;
+  if (PASS == 2) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    {
+      const int bin = tid & 255;
+      int s = 0;
+      for (int c = tid >> 8; c < a.nch; c += kTopThreads / 256) s += a.hist1[(bj * a.nch + c) * 256 + bin];
+      atomicAdd(&hist[bin], s);
+    }
+    __syncthreads();
+    select_digit(hist, a.kk, scan_sh, sel_sh);
+    __syncthreads();
+    prefix = sel_sh[0] << 24;
+    pmask = 0xFF000000u;
+  } else {
+    for (int i = tid; i < kWideBins; i += kTopThreads) hist[i] = a.ghist[bj * 2 * kWideBins + i];
+    __syncthreads();
+    select_digit_wide<kWideBins>(hist, static_cast<int>(a.sel[bj * kSelSlots + 1]), scan_sh, sel_sh);
+    __syncthreads();
+    prefix = a.sel[bj * kSelSlots] | (sel_sh[0] << 12);
+    pmask = 0xFFFFF000u;
+  }
+  krem = static_cast<int>(sel_sh[1]);
+  if (ch == 0 && tid == 0) {
+    a.sel[bj * kSelSlots + 2 * (PASS - 2)] = prefix;
+    a.sel[bj * kSelSlots + 2 * (PASS - 2) + 1] = static_cast<uint32_t>(krem);
+  }
+  __syncthreads();
+  for (int i = tid; i < kWideBins; i += kTopThreads) hist[i] = 0;
+  __syncthreads();
+  constexpr int shift = PASS == 2 ? 12 : 0;
+  const int cb = ch * kChunk + tid * kChunkKpt;
+  const uint4 k4 = load_chunk_keys(a, bj, cb);
+#pragma unroll
+  for (int i = 0; i < kChunkKpt; ++i) {
+    const uint32_t key = key_at(k4, i);
+    wave_hist_add<12>(hist, cb + i < a.N && (key & pmask) == prefix, (key >> shift) & (kWideBins - 1));
+  }
+  __syncthreads();
+  int* g = a.ghist + (bj * 2 + (PASS - 2)) * kWideBins;
+  for (int i = tid; i < kWideBins; i += kTopThreads)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+__global__ __launch_bounds__(kTopThreads) void chunk_count_kernel(TopArgs a) {
+  __shared__ int hist[kWideBins];
+  __shared__ int scan_sh[kTopThreads / 64 + 1];
+  __shared__ uint32_t sel_sh[2];
+  const int ch = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kWideBins; i += kTopThreads) hist[i] = a.ghist[(bj * 2 + 1) * kWideBins + i];
+  __syncthreads();
+  select_digit_wide<kWideBins>(hist, static_cast<int>(a.sel[bj * kSelSlots + 3]), scan_sh, sel_sh);
+  __syncthreads();
+  const uint32_t tau = a.sel[bj * kSelSlots + 2] | sel_sh[0];
+  if (ch == 0 && tid == 0) {
+    a.sel[bj * kSelSlots + 4] = tau;
+    a.sel[bj * kSelSlots + 5] = sel_sh[1];
+  }
+  const int cb = ch * kChunk + tid * kChunkKpt;
+  const uint4 k4 = load_chunk_keys(a, bj, cb);
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkKpt; ++i) {
+    const uint32_t key = key_at(k4, i);
+    const bool ok = cb + i < a.N;
+    gt += (ok && key > tau) ? 1 : 0;
+    eq += (ok && key == tau) ? 1 : 0;
+  }
+  int tg, te;
+  block_exclusive_scan(gt, scan_sh, &tg);
+  block_exclusive_scan(eq, scan_sh, &te);
+  if (tid == 0) a.cnt[bj * a.nch + ch] = make_int2(tg, te);
+}
+
+// Chunk ch's keys above the threshold go after those of chunks 0..ch-1; of the
+// keys equal to it the first krem in index order are taken.
+__global__ __launch_bounds__(kTopThreads) void chunk_emit_kernel(TopArgs a) {
+  __shared__ int scan_sh[kTopThreads / 64 + 1];
+  __shared__ int before[2];
+  const int ch = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
+  const int tid = threadIdx.x;
+  const uint32_t tau = a.sel[bj * kSelSlots + 4];
+  const int krem = static_cast<int>(a.sel[bj * kSelSlots + 5]);
+  if (tid < 64) {
+    int g = 0, e = 0;
+    for (int c = tid; c < ch; c += 64) {
+      const int2 v = a.cnt[bj * a.nch + c];
+      g += v.x;
+      e += v.y;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      g += __shfl_xor(g, o);
+      e += __shfl_xor(e, o);
+    }
+    if (tid == 0) {
+      before[0] = g;
+      before[1] = e;
+    }
+  }
+  __syncthreads();
+  const int g_before = before[0], e_before = before[1];
+  const int cb = ch * kChunk + tid * kChunkKpt;
+  const uint4 k4 = load_chunk_keys(a, bj, cb);
+  int n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkKpt; ++i) n_eq += (cb + i < a.N && key_at(k4, i) == tau) ? 1 : 0;
+  int tot;
+  int eq_rank = block_exclusive_scan(n_eq, scan_sh, &tot) + e_before;
+  bool take[kChunkKpt];
+  int n_take = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkKpt; ++i) {
+    const uint32_t key = key_at(k4, i);
+    const bool ok = cb + i < a.N;
+    const bool eq = ok && key == tau;
+    take[i] = ok && (key > tau || (eq && eq_rank < krem));
+    eq_rank += eq ? 1 : 0;
+    n_take += take[i] ? 1 : 0;
+  }
+  int pos = block_exclusive_scan(n_take, scan_sh, &tot) + g_before + min(krem, e_before);
+  int32_t* idx = a.idx + bj * a.kk;
+#pragma unroll
+  for (int i = 0; i < kChunkKpt; ++i) {
+    if (take[i] && pos < a.kk) idx[pos] = cb + i;
+    pos += take[i] ? 1 : 0;
   }
 }
 
@@ -604,6 +798,26 @@ kvc_status launch_score(const ScoreArgs& a, int KS, dim3 grid, hipStream_t st) {
   return check_launch();
 }
 
+// Rows longer than one workgroup's LDS take the chunked top-k, and so do rows
+// whose heads are too few to spread one workgroup per head over the chip.
+constexpr int kChunkedMinN = 32 * kTopThreads;
+bool chunked_topk(int N) { return N > kChunkedMinN; }
+
+kvc_status run_chunked_topk(const TopArgs& t, int B, hipStream_t st) {
+  const dim3 grid(t.nch, t.Hkv, B);
+  hipLaunchKernelGGL(chunk_pool_kernel, grid, dim3(kTopThreads), 0, st, t);
+  kvc_status s = check_launch();
+  if (s != KVC_OK || t.kk == 0) return s;
+  hipLaunchKernelGGL(chunk_hist_kernel<2>, grid, dim3(kTopThreads), 0, st, t);
+  if ((s = check_launch()) != KVC_OK) return s;
+  hipLaunchKernelGGL(chunk_hist_kernel<3>, grid, dim3(kTopThreads), 0, st, t);
+  if ((s = check_launch()) != KVC_OK) return s;
+  hipLaunchKernelGGL(chunk_count_kernel, grid, dim3(kTopThreads), 0, st, t);
+  if ((s = check_launch()) != KVC_OK) return s;
+  hipLaunchKernelGGL(chunk_emit_kernel, grid, dim3(kTopThreads), 0, st, t);
+  return check_launch();
+}
+
 template <typename T>
 kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t st) {
   constexpr int CH = ChunkCols<T>::value;
@@ -613,6 +827,7 @@ kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t
   if ((s = check_launch()) != KVC_OK) return s;
   s = launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
   if (s != KVC_OK) return s;
+  if (chunked_topk(t.N)) return run_chunked_topk(t, B, st);
   // short rows: raw scores in LDS, keys in registers
   const int kpt = (t.N + kTopThreads - 1) / kTopThreads;
   const size_t lds = static_cast<size_t>(t.N) * sizeof(float);
@@ -620,7 +835,7 @@ kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t
     hipLaunchKernelGGL(pool_topk_lds_kernel<8>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
   } else if (kpt <= 16) {
     hipLaunchKernelGGL(pool_topk_lds_kernel<16>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
-  } else if (kpt <= 32) {
+  } else {
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_topk_lds_kernel<32>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -630,8 +845,6 @@ kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t
       }
     }
     hipLaunchKernelGGL(pool_topk_lds_kernel<32>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
-  } else {
-    hipLaunchKernelGGL(pool_topk_kernel, dim3(a.Hkv, B), dim3(kTopThreads), 0, st, t);
   }
   return check_launch();
 }
@@ -657,7 +870,13 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   const size_t sz_stats = align_up(units * nc1 * R * sizeof(float2), 256);
   const size_t sz_row = align_up(units * R * sizeof(float2), 256);
   const size_t sz_raw = align_up(units * N * sizeof(float), 256);
-  const size_t need = sz_stats + sz_row + 2 * sz_raw;
+  const int nch = (N + kChunk - 1) / kChunk;  // chunked top-k
+  const size_t sz_keys = align_up(units * nch * kChunk * sizeof(uint32_t), 256);
+  const size_t sz_hist1 = align_up(units * nch * 256 * sizeof(int), 256);
+  const size_t sz_ghist = align_up(units * 2 * kWideBins * sizeof(int), 256);
+  const size_t sz_sel = align_up(units * kSelSlots * sizeof(uint32_t), 256);
+  const size_t sz_cnt = align_up(units * nch * sizeof(int2), 256);
+  const size_t need = sz_stats + sz_row + sz_raw + sz_keys + sz_hist1 + sz_ghist + sz_sel + sz_cnt;
   if (!ws) {
     *ws_bytes = need;
     return KVC_OK;
@@ -684,14 +903,21 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   a.nc1 = nc1;
   a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   TopArgs t;
+  char* tw = w + sz_stats + sz_row + sz_raw;
   t.raw = a.raw;
-  t.keys = reinterpret_cast<uint32_t*>(w + sz_stats + sz_row + sz_raw);
+  t.keys = reinterpret_cast<uint32_t*>(tw);
+  t.hist1 = reinterpret_cast<int*>(tw + sz_keys);
+  t.ghist = reinterpret_cast<int*>(tw + sz_keys + sz_hist1);
+  t.sel = reinterpret_cast<uint32_t*>(tw + sz_keys + sz_hist1 + sz_ghist);
+  t.cnt = reinterpret_cast<int2*>(tw + sz_keys + sz_hist1 + sz_ghist + sz_sel);
   t.scores = scores;
   t.idx = idx;
   t.Hkv = Hkv;
   t.N = N;
   t.kk = kk;
   t.pool = pool;
+  t.nch = nch;
+  t.NP = nch * kChunk;
   return dtype == KVC_F32 ? run_select<float>(a, D / 32, B, t, st)
                           : run_select<uint16_t>(a, D / 32, B, t, st);
 }

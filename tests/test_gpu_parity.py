@@ -99,7 +99,12 @@ def test_decode_parity_multi_step(dtype, bits, G, D, R, n):
     ("bf16", 1, 2, 3, 333, 64, 5, 3, 40), ("bf16", 1, 8, 1, 1000, 256, 32, 7, 200),
     ("f32", 2, 3, 1, 257, 32, 13, 1, 30), ("bf16", 1, 4, 2, 300, 128, 300, 7, 10),
     ("bf16", 1, 4, 2, 300, 128, 20, 7, 0), ("bf16", 1, 4, 2, 300, 128, 20, 7, 5000),
-    ("bf16", 1, 4, 2, 300, 128, 20, 7, -1), ("bf16", 1, 1, 1, 2000, 128, 150, 9, 333)])
+    ("bf16", 1, 4, 2, 300, 128, 20, 7, -1), ("bf16", 1, 1, 1, 2000, 128, 150, 9, 333),
+    # rows of 9k-32k candidates (keys in registers, raw scores in LDS)
+    ("bf16", 1, 2, 1, 12000, 64, 16, 7, 900), ("bf16", 1, 1, 1, 30000, 64, 8, 7, 2000),
+    # rows above 32k candidates: 4096-candidate chunks over many workgroups
+    ("bf16", 1, 2, 2, 40000, 64, 16, 7, 1500), ("f32", 1, 1, 1, 36000, 32, 8, 13, 700),
+    ("bf16", 1, 1, 2, 34000, 64, 8, 3, -1), ("bf16", 1, 1, 1, 34000, 64, 8, 5, 0)])
 def test_select_parity(dtype, B, G, Hkv, n, D, W, pool, budget):
     kvc = _kvc()
     Hq = G * Hkv
@@ -117,6 +122,23 @@ def test_select_parity(dtype, B, G, Hkv, n, D, W, pool, budget):
     for b in range(B):
         for j in range(Hkv):
             gu.check_selection(ix[b, j], sc[b, j], pooled[b, j], budget)
+
+
+@pytest.mark.parametrize("n", [3000, 40000])
+def test_select_all_scores_tied(n):
+    """Zero keys make every logit 0, so every candidate gets the same score (the
+    same terms summed in the same order) and the top-k is the k lowest
+    positions; with 40000 the tie spans every chunk of the long-row path."""
+    kvc = _kvc()
+    B, Hkv, G, D, W, pool, budget = 1, 2, 2, 64, 16, 7, 1234
+    k = torch.zeros(B, Hkv, n, D, dtype=torch.bfloat16, device="cuda")
+    q_win = synth.random_tensor(7, (B, Hkv * G, W, D), "bf16", tag="qw").cuda()
+    idx, scores = kvc.kvc_select(q_win, k, W, pool, budget, want_scores=True)
+    torch.cuda.synchronize()
+    sc = scores.cpu()
+    assert torch.equal(sc, sc[:, :, :1].expand_as(sc)), "scores not all equal"
+    want = torch.arange(budget, dtype=torch.int32).expand(B, Hkv, budget)
+    assert torch.equal(idx.cpu(), want)
 
 
 def test_select_planted_and_dense_special_case():
