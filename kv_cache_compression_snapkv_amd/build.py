@@ -29,10 +29,10 @@ FLAGS = [
 ]
 
 
-# Per-source extras.  decode.hip: its values are never NaN (scores, softmax
-# weights, -inf masks), so fmax needs no canonicalization and the 16-lane DPP max
-# folds into v_max_f32_dpp.
-EXTRA = {"decode.hip": ["-fno-honor-nans"]}
+# Per-source extras.  decode.hip and select.hip: their values are never NaN for
+# finite inputs (logits, softmax weights, -inf masks), so fmax needs no
+# canonicalization and the 16-lane DPP max folds into v_max_f32_dpp.
+EXTRA = {"decode.hip": ["-fno-honor-nans"], "select.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src):

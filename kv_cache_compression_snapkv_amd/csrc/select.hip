@@ -108,75 +108,108 @@ __device__ __forceinline__ float sum_quarters(float x) {
   return x;
 }
 
-// Window rows row0[u]..row0[u]+15 (u = 0, 1) of one wave against the CH = 16*CT
+// Window rows row0[u]..row0[u]+15 (u < NT) of one wave against the CH = 16*CT
 // columns of chunk `chunk` (first column c0): MFMA products with the key
 // fragments that kload(ct, s, frag) supplies, then pass 1 writes each row's
 // (max, sum) for the chunk and pass 2 adds the rows' softmax weights to the
-// lane's column partials.  st: pass 2's per-row M + log2(L).
-template <typename T, int KS, int PASS, int TPW, int CT, typename KLoad>
+// lane's column partials (reduced over lanes and waves once, at the end).
+// FULL: every column of the chunk is visible to every row (no causal mask).
+// st: pass 2's per-row M + log2(L), +inf for rows beyond R (weight 2^-inf = 0).
+template <typename T, int KS, int PASS, int NT, bool FULL, int TPW, int CT, typename KLoad>
+__device__ __forceinline__ void score_tiles(const ScoreArgs& a, int bj, int chunk, int c0,
+                                            const Frag<T> (&qf)[TPW][KS], const int (&row0)[TPW],
+                                            const float (&st)[TPW][4], float (&colacc)[CT], KLoad kload) {
+  const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
+  // pass 1 keeps at most two tiles of products live (registers); pass 2 takes
+  // all NT at once, so each key fragment feeds NT products
+  constexpr int TG = (PASS == 1 && NT > 2) ? 2 : NT;
+  static_assert(NT % TG == 0, "whole tile groups");
+#pragma unroll
+  for (int gi = 0; gi < NT / TG; ++gi) {
+    const int ug = gi * TG;
+    f32x4 acc[TG][CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int u = 0; u < TG; ++u) acc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Frag<T> kf;
+        kload(ct, s, kf);
+#pragma unroll
+        for (int u = 0; u < TG; ++u) acc[u][ct] = mma(qf[ug + u][s], kf, acc[u][ct]);
+      }
+    }
+    if (PASS == 1) {
+      // per row: max over the row's 16 lanes x CT columns, then the sum of
+      // 2^(x - M) with x = logit * scale2 (scale2 > 0, so max(x) = scale2 * max)
+#pragma unroll
+      for (int u = 0; u < TG; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0[ug + u] + 4 * lq + i;
+          float v[CT];
+          if (FULL) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) v[ct] = acc[u][ct][i];
+          } else {
+            const int lim = a.n - a.W + (r % a.W);  // last key this row may see
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              const int c = c0 + ct * 16 + ln;
+              v[ct] = (c <= lim && c < a.n) ? acc[u][ct][i] : -INFINITY;
+            }
+          }
+          float mx = v[0];
+#pragma unroll
+          for (int ct = 1; ct < CT; ++ct) mx = fmaxf(mx, v[ct]);
+          const float m = max16(mx) * a.scale2;
+          float l = 0.0f;
+          if (FULL || m != -INFINITY) {
+            l = fast_exp2(__builtin_fmaf(v[0], a.scale2, -m));
+#pragma unroll
+            for (int ct = 1; ct < CT; ++ct) l += fast_exp2(__builtin_fmaf(v[ct], a.scale2, -m));
+          }
+          l = sum16(l);
+          if (ln == 0 && r < a.R)
+            a.stats[(static_cast<size_t>(bj) * a.nc1 + chunk) * a.R + r] = make_float2(m, l);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float v = fast_exp2(__builtin_fmaf(acc[0][ct][0], a.scale2, -st[ug][0]));
+#pragma unroll
+        for (int u = 0; u < TG; ++u) {
+#pragma unroll
+          for (int i = (u == 0 ? 1 : 0); i < 4; ++i)
+            v += fast_exp2(__builtin_fmaf(acc[u][ct][i], a.scale2, -st[ug + u][i]));
+        }
+        colacc[ct] += v;
+      }
+    }
+    if (NT / TG > 1) __builtin_amdgcn_sched_barrier(0);  // one tile group's products live at a time
+  }
+}
+
+// A wave with any window row computes its tiles (rows beyond R have zero
+// queries; pass 1 does not store them and pass 2 weights them 0): all TPW of
+// them (ALL), or, when its last tile is idle, only the first (the two-tile
+// scorer); in pass 1 whether the chunk needs causal masks selects the
+// instantiation.
+template <bool ALL, typename T, int KS, int PASS, int TPW, int CT, typename KLoad>
 __device__ __forceinline__ void score_rows(const ScoreArgs& a, int bj, int chunk, int c0, bool full,
                                            const Frag<T> (&qf)[TPW][KS], const int (&row0)[TPW],
                                            const float (&st)[TPW][4], float (&colacc)[CT], KLoad kload) {
-  const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
-  const bool active0 = row0[0] < a.R, active1 = TPW > 1 && row0[TPW - 1] < a.R;
-  if (!active0) return;  // wave-uniform
-  f32x4 acc[TPW][CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) acc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      Frag<T> kf;
-      kload(ct, s, kf);
-      acc[0][ct] = mma(qf[0][s], kf, acc[0][ct]);
-      if (TPW > 1 && active1) acc[TPW - 1][ct] = mma(qf[TPW - 1][s], kf, acc[TPW - 1][ct]);
-    }
-  }
-  if (PASS == 1) {
-    // per row: max over the row's 16 lanes x CT columns, then the sum of
-    // 2^(x - M) with x = logit * scale2 (scale2 > 0, so max(x) = scale2 * max)
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      if (u == 1 && !active1) break;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = row0[u] + 4 * lq + i;
-        const int lim = a.n - a.W + (r % a.W);  // last key this row may see
-        float v[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const int c = c0 + ct * 16 + ln;
-          v[ct] = (full || (c <= lim && c < a.n)) ? acc[u][ct][i] : -INFINITY;
-        }
-        float mx = v[0];
-#pragma unroll
-        for (int ct = 1; ct < CT; ++ct) mx = fmaxf(mx, v[ct]);
-        const float m = max16(mx) * a.scale2;
-        float l = 0.0f;
-        if (m != -INFINITY) {
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) l += fast_exp2(__builtin_fmaf(v[ct], a.scale2, -m));
-        }
-        l = sum16(l);
-        if (ln == 0 && r < a.R)
-          a.stats[(static_cast<size_t>(bj) * a.nc1 + chunk) * a.R + r] = make_float2(m, l);
-      }
-    }
+  if (row0[0] >= a.R) return;  // wave-uniform
+  constexpr int NT1 = ALL ? TPW : 1;
+  const bool all = ALL || row0[TPW - 1] < a.R;
+  if (PASS == 2 || full) {
+    if (all) score_tiles<T, KS, PASS, TPW, true>(a, bj, chunk, c0, qf, row0, st, colacc, kload);
+    else score_tiles<T, KS, PASS, NT1, true>(a, bj, chunk, c0, qf, row0, st, colacc, kload);
   } else {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      float v = 0.0f;
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = row0[u] + 4 * lq + i;
-          if (r < a.R) v += fast_exp2(__builtin_fmaf(acc[u][ct][i], a.scale2, -st[u][i]));
-        }
-      }
-      colacc[ct] += sum_quarters(v);
-    }
+    if (all) score_tiles<T, KS, PASS, TPW, false>(a, bj, chunk, c0, qf, row0, st, colacc, kload);
+    else score_tiles<T, KS, PASS, NT1, false>(a, bj, chunk, c0, qf, row0, st, colacc, kload);
   }
 }
 
@@ -189,7 +222,7 @@ __device__ __forceinline__ void load_rowstat(const ScoreArgs& a, int bj, const i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = row0[u] + 4 * lq + i;
-      st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : 0.0f;
+      st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : INFINITY;
     }
 }
 
@@ -204,7 +237,7 @@ __global__ __launch_bounds__(64 * NWAVE, (NWAVE == 8 ? 2 : 4)) void score_kernel
   constexpr int LD = D + PAD;  // padded LDS row (elements)
   constexpr int CT = CH / 16;  // column tiles per chunk
   __shared__ __attribute__((aligned(16))) T ks[CH * LD];
-  __shared__ float colred[NWAVE][CH];
+  static_assert(NWAVE * 4 * CH * sizeof(float) <= CH * LD * sizeof(T), "partials fit in the key chunk");
 
   const int chunk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int bj = b * a.Hkv + j;
@@ -268,22 +301,198 @@ __global__ __launch_bounds__(64 * NWAVE, (NWAVE == 8 ? 2 : 4)) void score_kernel
     if (rb > 0) load_q(rb);
     float st[TPW][4];
     if (PASS == 2) load_rowstat<TPW>(a, bj, row0, st);
-    score_rows<T, KS, PASS, TPW>(a, bj, chunk, c0, full, qf, row0, st, colacc, [&](int ct, int s, Frag<T>& kf) {
+    score_rows<false, T, KS, PASS, TPW>(a, bj, chunk, c0, full, qf, row0, st, colacc, [&](int ct, int s, Frag<T>& kf) {
       kf.load(&ks[(ct * 16 + ln) * LD + 32 * s + 8 * lq]);
     });
   }
 
   if (PASS == 2) {
-    if (lq == 0) {
+    // column partials of every lane quarter of every wave, summed in a fixed order
+    __syncthreads();  // the key chunk is dead: its LDS takes the partials
+    float* colred = reinterpret_cast<float*>(ks);  // [NWAVE * 4][CH]
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) colred[wave][ct * 16 + ln] = colacc[ct];
-    }
+    for (int ct = 0; ct < CT; ++ct) colred[(wave * 4 + lq) * CH + ct * 16 + ln] = colacc[ct];
     __syncthreads();
     for (int c = tid; c < CH; c += NTHR) {
-      float v = 0.0f;
+      float v = colred[c];
 #pragma unroll
-      for (int w = 0; w < NWAVE; ++w) v += colred[w][c];
+      for (int w = 1; w < NWAVE * 4; ++w) v += colred[w * CH + c];
       if (c0 + c < a.N) a.raw[static_cast<size_t>(bj) * a.N + c0 + c] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pipelined scorer
+// bf16 keys, D in {32, 64, 128}, R <= 64*TPW (4 waves, TPW row tiles of 16
+// each; tile u of wave w holds rows (w + 4u)*16..+15): each workgroup walks chunks
+// ch = blockIdx.x, + gridDim.x, ... of its (b, j); while it computes chunk k the
+// direct-to-LDS loads of chunk k+1 are in flight (two LDS buffers), so the
+// memory latency hides behind the MFMA and softmax work and no VGPRs hold
+// staged data.  Staged layout: 16-byte piece p of chunk row r sits in slot
+// r*P + (p ^ sw(r)) (P pieces per row).  One 1 KB load covers whole rows (one
+// contiguous kilobyte of K), and the 16 rows of an MFMA fragment read 16
+// distinct bank groups for any fixed piece.
+constexpr int kPipeCH = 128;  // columns per chunk (also the pass-1 statistics granularity)
+constexpr int kPipeBuf = 2;   // chunk buffers per workgroup: kPipeBuf - 1 chunks in flight
+constexpr int kPipeWaves = 4;
+constexpr int kLdsPerCU = 160 * 1024;
+
+template <int KS> struct PipeGeom {
+  static constexpr int D = 32 * KS;
+  static constexpr int P = D / 8;                 // 16-byte pieces per key row
+  static constexpr int CH = kPipeCH;
+  static constexpr int BYTES = CH * D * 2;        // one staged chunk
+  static constexpr int NI = BYTES / 1024;         // 1 KB direct-to-LDS loads per chunk
+  static constexpr int NIW = NI / kPipeWaves;     // per wave
+  static constexpr int SWDIV = P >= 16 ? 1 : 16 / P;
+  static constexpr int SWMOD = P >= 16 ? 16 : P;
+  static constexpr int LDS = kPipeBuf * BYTES + kPipeWaves * CH * 4;
+  // resident workgroups per CU: what LDS allows, at most 2 (registers: up to
+  // 256 per lane for the four row tiles of R > 128)
+  static constexpr int WGS = kLdsPerCU / LDS < 2 ? kLdsPerCU / LDS : 2;
+  static_assert(NI % kPipeWaves == 0 && NIW * (kPipeBuf - 1) < 64, "loads split evenly; vmcnt range");
+  // depends on r mod 16 only
+  __device__ static int sw(int r) { return (r / SWDIV) % SWMOD; }
+};
+
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `later` chunk fills of NIW loads each (the ones issued
+// after the chunk about to be used) are outstanding.
+template <int NIW, int L = kPipeBuf - 1>
+__device__ __forceinline__ void wait_chunks(int later) {
+  if constexpr (L == 0) {
+    wait_vmem<0>();
+  } else {
+    if (later >= L) wait_vmem<L * NIW>();
+    else wait_chunks<NIW, L - 1>(later);
+  }
+}
+
+// One 16-byte direct-to-LDS load per lane: lane l's bytes land at dst + 16*l.
+__device__ __forceinline__ void lds_load16(const void* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// The lane's source offsets (elements) within a chunk for this wave's loads:
+// load ii fills slot j = (wave*NIW + ii)*64 + lane, i.e. row j/P, piece (j%P)^sw.
+// (The row of a load is off / D.)
+template <int KS> struct PipeOffsets {
+  int off[PipeGeom<KS>::NIW];
+  __device__ __forceinline__ PipeOffsets(int wave, int lane) {
+    using G = PipeGeom<KS>;
+#pragma unroll
+    for (int ii = 0; ii < G::NIW; ++ii) {
+      const int j = (wave * G::NIW + ii) * 64 + lane;
+      const int r = j / G::P;
+      off[ii] = r * G::D + ((j % G::P) ^ G::sw(r)) * 8;
+    }
+  }
+};
+
+// This wave's share of the direct-to-LDS loads of the chunk whose first column
+// is c0 (in the last chunk, rows past the key count read the last key: they are
+// masked or unused).
+template <int KS>
+__device__ __forceinline__ void pipe_fill(const uint16_t* kp, const PipeOffsets<KS>& po, int c0, int n,
+                                          unsigned char* dst, int wave) {
+  using G = PipeGeom<KS>;
+  const uint16_t* base = kp + static_cast<size_t>(c0) * G::D;
+  if (c0 + G::CH <= n) {
+#pragma unroll
+    for (int ii = 0; ii < G::NIW; ++ii) lds_load16(base + po.off[ii], dst + (wave * G::NIW + ii) * 1024);
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < G::NIW; ++ii) {
+      const int excess = max(0, c0 + po.off[ii] / G::D - (n - 1));  // rows to step back
+      lds_load16(base + po.off[ii] - excess * G::D, dst + (wave * G::NIW + ii) * 1024);
+    }
+  }
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only: the
+// direct-to-LDS loads of later chunks stay in flight across it (a
+// __syncthreads() would wait for every outstanding memory operation).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int KS, int PASS, int TPW>
+__global__ __launch_bounds__(64 * kPipeWaves, PipeGeom<KS>::WGS) void score_pipe_kernel(ScoreArgs a) {
+  using G = PipeGeom<KS>;
+  constexpr int NWAVE = kPipeWaves, CH = G::CH, CT = CH / 16, D = G::D, NB = kPipeBuf;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  unsigned char* ring = smem;                                      // [NB][BYTES]
+  float* colred = reinterpret_cast<float*>(smem + NB * G::BYTES);  // [NWAVE][CH]
+  const int j = blockIdx.y, b = blockIdx.z;
+  const int bj = b * a.Hkv + j;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int ln = lane & 15, lq = lane >> 4;
+  const int nchunk = ((PASS == 1 ? a.n : a.N) + CH - 1) / CH;
+  const int g = gridDim.x;
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bj) * a.n * D;
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q_win) + static_cast<size_t>(b * a.Hq + j * a.G) * a.W * D;
+
+  int ch = blockIdx.x;  // < nchunk
+  const PipeOffsets<KS> po(wave, lane);
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i)
+    if (ch + i * g < nchunk) pipe_fill<KS>(kp, po, (ch + i * g) * CH, a.n, ring + i * G::BYTES, wave);
+  // the wave's window rows (all R rows fit one block) and, in pass 2, their statistics
+  Frag<uint16_t> qf[TPW][KS];
+  int row0[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    row0[u] = (wave + NWAVE * u) * 16;
+    const int r = row0[u] + ln;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      if (r < a.R) qf[u][s2].load(qbase + static_cast<size_t>(r) * D + 32 * s2 + 8 * lq);
+      else qf[u][s2].zero();
+    }
+  }
+  float st[TPW][4];
+  if (PASS == 2) load_rowstat<TPW>(a, bj, row0, st);
+  // fragment (ct, s) of lane (ln, lq): row ct*16 + ln, piece 4s + lq
+  int foff[KS];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) foff[s2] = (ln * G::P + ((4 * s2 + lq) ^ G::sw(ln))) * 16;
+
+  for (int k = 0; ch < nchunk; ++k, ch += g) {
+    const int ahead = ch + (NB - 1) * g;
+    if (ahead < nchunk) pipe_fill<KS>(kp, po, ahead * CH, a.n, ring + ((k + NB - 1) % NB) * G::BYTES, wave);
+    wait_chunks<G::NIW>(min(NB - 1, (nchunk - 1 - ch) / g));  // this chunk's loads (and all older accesses) are done
+    lds_barrier();  // every wave's share of this chunk has landed
+    const unsigned char* cur = ring + (k % NB) * G::BYTES;
+    const int c0 = ch * CH;
+    const bool full = c0 + CH <= ((PASS == 1) ? a.n - a.W + 1 : a.N);
+    float colacc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) colacc[ct] = 0.0f;
+    score_rows<true, uint16_t, KS, PASS, TPW>(a, bj, ch, c0, full, qf, row0, st, colacc, [&](int ct, int s2, Frag<uint16_t>& kf) {
+      kf.load(reinterpret_cast<const uint16_t*>(cur + ct * 16 * G::P * 16 + foff[s2]));
+    });
+    if (PASS == 2) {
+      if (row0[0] < a.R) {  // wave-uniform; idle waves leave zeros
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float v = sum_quarters(colacc[ct]);
+          if (lq == 0) colred[wave * CH + ct * 16 + ln] = v;
+        }
+      } else if (lq == 0) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) colred[wave * CH + ct * 16 + ln] = 0.0f;
+      }
+      lds_barrier();  // also: every wave is done with this buffer before it is refilled
+      if (tid < CH) {
+        float v = colred[tid];
+#pragma unroll
+        for (int w = 1; w < NWAVE; ++w) v += colred[w * CH + tid];
+        if (c0 + tid < a.N) a.raw[static_cast<size_t>(bj) * a.N + c0 + tid] = v;
+      }
+    } else {
+      lds_barrier();  // every wave is done with this buffer before it is refilled
     }
   }
 }
@@ -818,14 +1027,54 @@ kvc_status run_chunked_topk(const TopArgs& t, int B, hipStream_t st) {
   return check_launch();
 }
 
+// Pipelined scorer launch: one round of the workgroups the CUs hold at once,
+// each walking an equal share of its head's chunks.
+template <int KS, int PASS, int TPW>
+kvc_status launch_pipe(const ScoreArgs& a, int B, hipStream_t st) {
+  const void* k = reinterpret_cast<const void*>(&score_pipe_kernel<KS, PASS, TPW>);
+  constexpr int bytes = PipeGeom<KS>::LDS;
+  static bool lds_set = false;  // one attribute call per instantiation (idempotent)
+  if (bytes > 65536 && !lds_set) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) {
+      set_last_hip_error(e);
+      return KVC_ERR_HIP;
+    }
+    lds_set = true;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const int nchunk = ((PASS == 1 ? a.n : a.N) + PipeGeom<KS>::CH - 1) / PipeGeom<KS>::CH;
+  const int heads = a.Hkv * B;
+  const int per_head = std::max(1, std::min(nchunk, (PipeGeom<KS>::WGS * cus + heads - 1) / heads));
+  hipLaunchKernelGGL((score_pipe_kernel<KS, PASS, TPW>), dim3(per_head, a.Hkv, B), dim3(64 * kPipeWaves), bytes, st, a);
+  return check_launch();
+}
+
+template <int PASS>
+kvc_status launch_pipe_any(const ScoreArgs& a, int KS, int B, hipStream_t st) {
+  const bool t4 = a.R > 128;
+#define KVC_PIPE(k) \
+  case k: return t4 ? launch_pipe<k, PASS, 4>(a, B, st) : launch_pipe<k, PASS, 2>(a, B, st);
+  switch (KS) {
+    KVC_PIPE(1) KVC_PIPE(2) KVC_PIPE(4)
+    default: return KVC_ERR_SHAPE;
+  }
+#undef KVC_PIPE
+}
+bool pipe_ok(int KS, int R) { return (KS == 1 || KS == 2 || KS == 4) && R <= 256; }
+
 template <typename T>
 kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t st) {
   constexpr int CH = ChunkCols<T>::value;
-  kvc_status s = launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
+  const bool pipe = sizeof(T) == 2 && pipe_ok(KS, a.R);
+  kvc_status s = pipe ? launch_pipe_any<1>(a, KS, B, st) : launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
   if (s != KVC_OK) return s;
   hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.Hkv, B), dim3(kThreads), 0, st, a);
   if ((s = check_launch()) != KVC_OK) return s;
-  s = launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
+  s = pipe ? launch_pipe_any<2>(a, KS, B, st) : launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
   if (s != KVC_OK) return s;
   if (chunked_topk(t.N)) return run_chunked_topk(t, B, st);
   // short rows: raw scores in LDS, keys in registers
@@ -864,7 +1113,8 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   const int G = Hq / Hkv;
   const int N = n - W;
   const int R = G * W;
-  const int CH = dtype == KVC_F32 ? ChunkCols<float>::value : ChunkCols<uint16_t>::value;
+  const bool pipe = dtype != KVC_F32 && head_dim_ok(D) && pipe_ok(D / 32, G * W);
+  const int CH = pipe ? kPipeCH : dtype == KVC_F32 ? ChunkCols<float>::value : ChunkCols<uint16_t>::value;
   const int nc1 = (n + CH - 1) / CH;
   const size_t units = static_cast<size_t>(B) * Hkv;
   const size_t sz_stats = align_up(units * nc1 * R * sizeof(float2), 256);

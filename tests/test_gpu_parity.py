@@ -100,6 +100,7 @@ def test_decode_parity_multi_step(dtype, bits, G, D, R, n):
     ("f32", 2, 3, 1, 257, 32, 13, 1, 30), ("bf16", 1, 4, 2, 300, 128, 300, 7, 10),
     ("bf16", 1, 4, 2, 300, 128, 20, 7, 0), ("bf16", 1, 4, 2, 300, 128, 20, 7, 5000),
     ("bf16", 1, 4, 2, 300, 128, 20, 7, -1), ("bf16", 1, 1, 1, 2000, 128, 150, 9, 333),
+    ("bf16", 2, 2, 2, 600, 32, 24, 5, 80), ("bf16", 1, 16, 1, 900, 64, 16, 7, 100),
     # rows of 9k-32k candidates (keys in registers, raw scores in LDS)
     ("bf16", 1, 2, 1, 12000, 64, 16, 7, 900), ("bf16", 1, 1, 1, 30000, 64, 8, 7, 2000),
     # rows above 32k candidates: 4096-candidate chunks over many workgroups
