@@ -184,6 +184,11 @@ struct DecArgs {
   int r_start;  // ring row of residual token 0 (residual token t is row (r_start + t) % r_cap)
   int nb;
   float scale2;  // log2(e)/sqrt(D)
+  // Host-side index arithmetic (no integer division in the kernel's setup):
+  float rcp_hkv, rcp_hb, rcp_xhb;      // 1/Hkv, 1/HB, 1/(kXcds*HB) for small_divmod
+  int split_nA;                         // history split (see hist_split)
+  float split_hA, split_hB;
+  int sp_new;                           // wave of the unit holding the appended token's tile, or -1
 };
 
 
@@ -304,15 +309,49 @@ __device__ __forceinline__ void wave_sync() {
 // First history tile of wave w of a unit (w = NWT gives NTh): the prefix sums of
 // a per-wave share that is non-increasing in w, rounded, so the runs partition
 // [0, NTh).  Waves w >= NWT - NTr also hold a residual tile and get kResW fewer
-// history tiles than the others (none if the even share is below kResW).
+// history tiles than the others (none if the even share is below kResW).  The
+// shares (nA waves of hA tiles, then waves of hB tiles) come from the host.
 constexpr float kResW = 5.0f;
-__device__ __forceinline__ int hist_split(int w, int NWT, int NTh, int NTr) {
-  if (NTr <= 0 || NTr >= NWT) return static_cast<int>((static_cast<long long>(w) * NTh) / NWT);
-  const int nA = NWT - NTr;
-  const float hB = fmaxf(0.0f, (static_cast<float>(NTh) + kResW * NTr) / NWT - kResW);
-  const float hA = (static_cast<float>(NTh) - hB * NTr) / nA;
+struct SplitParams {
+  int nA;
+  float hA, hB;
+};
+inline SplitParams split_params(int NWT, int NTh, int NTr) {
+  SplitParams p;
+  if (NTr <= 0 || NTr >= NWT) {
+    p.nA = NWT;
+    p.hA = static_cast<float>(NTh) / static_cast<float>(NWT);
+    p.hB = 0.0f;
+  } else {
+    p.nA = NWT - NTr;
+    p.hB = std::max(0.0f, (static_cast<float>(NTh) + kResW * NTr) / NWT - kResW);
+    p.hA = (static_cast<float>(NTh) - p.hB * NTr) / p.nA;
+  }
+  return p;
+}
+__device__ __forceinline__ int hist_split(int w, int NWT, int NTh, int nA, float hA, float hB) {
+  if (w >= NWT) return NTh;
   const float c = static_cast<float>(min(w, nA)) * hA + static_cast<float>(max(w - nA, 0)) * hB;
   return min(NTh, static_cast<int>(c + 0.5f));
+}
+
+// n / d and n % d for 0 <= n < 2^22, d >= 1, from rcp within a few ulps of 1/d:
+// the truncated float quotient is off by at most one, which the remainder test
+// corrects.
+struct QR {
+  int q, r;
+};
+__device__ __forceinline__ QR small_divmod(int n, int d, float rcp) {
+  int q = static_cast<int>(static_cast<float>(n) * rcp);
+  int r = n - q * d;
+  if (r < 0) {
+    --q;
+    r += d;
+  } else if (r >= d) {
+    ++q;
+    r -= d;
+  }
+  return QR{q, r};
 }
 
 // Resident workgroups per CU that the register budget allows (the occupancy
@@ -357,16 +396,24 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
     const int U = a.B * a.Hkv;
     const int L = blockIdx.y + gridDim.y * blockIdx.z;  // gridDim.x == 1 here when HB > 1
     if (gridDim.x == 1 && a.HB > 1) {
-      const int g = L / (kXcds * a.HB), r = L % (kXcds * a.HB);
-      const int ug = min(kXcds, U - g * kXcds);  // units in this group
-      bj = g * kXcds + r % ug;
-      hb = r / ug;
+      const QR gr = small_divmod(L, kXcds * a.HB, a.rcp_xhb);
+      const int ug = min(kXcds, U - gr.q * kXcds);  // units in this group
+      if (ug == kXcds) {
+        bj = gr.q * kXcds + gr.r % kXcds;
+        hb = gr.r / kXcds;
+      } else {
+        const QR u = small_divmod(gr.r, ug, __builtin_amdgcn_rcpf(static_cast<float>(ug)));
+        bj = gr.q * kXcds + u.r;
+        hb = u.q;
+      }
     } else {
-      bj = blockIdx.z * a.Hkv + blockIdx.y / a.HB;
-      hb = blockIdx.y % a.HB;
+      const QR yb = small_divmod(blockIdx.y, a.HB, a.rcp_hb);
+      bj = blockIdx.z * a.Hkv + yb.q;
+      hb = yb.r;
     }
   }
-  const int b = bj / a.Hkv, j = bj % a.Hkv;
+  const QR bq = small_divmod(bj, a.Hkv, a.rcp_hkv);
+  const int b = bq.q, j = bq.r;
   const int bjh = bj * a.HB + hb;
   const int h0 = hb * a.hbs;
   const int Gb = min(a.hbs, a.G - h0);
@@ -414,8 +461,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   const int sp = blockIdx.x * NWV + wave;
   const int NTh = a.q_len / kGroup;
   const int NTr = (a.r_total + kGroup - 1) / kGroup;
-  const int tb = hist_split(sp, NWT, NTh, NTr);
-  const int th_end = hist_split(sp + 1, NWT, NTh, NTr);
+  const int tb = hist_split(sp, NWT, NTh, a.split_nA, a.split_hA, a.split_hB);
+  const int th_end = hist_split(sp + 1, NWT, NTh, a.split_nA, a.split_hA, a.split_hB);
   const int r_first = NWT - 1 - sp;  // residual tiles r_first, r_first + NWT, ...
   // Every prefetch is issued on every path (clamped to an existing tile) so the
   // number of loads in flight is the same at each wait and the compiler can wait
@@ -594,7 +641,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   };
   // This wave processes the tile holding the appended token (if any).
   const int r_new_tile = a.r_new >= 0 ? a.r_new / kGroup : -1;
-  const bool new_here = r_new_tile >= r_first && (r_new_tile - r_first) % NWT == 0;
+  const bool new_here = sp == a.sp_new;  // r_new_tile is r_first + a multiple of NWT
   // Short runs: a wave with no history tiles issues its first residual tile's
   // loads and the appended token's at once, with the query loads (one memory
   // round trip before its first result instead of three).  Elsewhere the tile
@@ -1329,5 +1376,14 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   a.part_o = reinterpret_cast<float*>(w + W.part_o);
   a.out = out;
   a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(cache->head_dim));
+  a.rcp_hkv = 1.0f / static_cast<float>(Hkv);
+  a.rcp_hb = 1.0f / static_cast<float>(a.HB);
+  a.rcp_xhb = 1.0f / static_cast<float>(kXcds * a.HB);
+  const int NWT = p.nb * p.nwv;
+  const SplitParams sp = split_params(NWT, a.q_len / kGroup, (a.r_total + kGroup - 1) / kGroup);
+  a.split_nA = sp.nA;
+  a.split_hA = sp.hA;
+  a.split_hB = sp.hB;
+  a.sp_new = a.r_new >= 0 ? NWT - 1 - (a.r_new / kGroup) % NWT : -1;
   return launch_decode(a, dtype, cache->bits, KS, p.nwv, cache->batch, st);
 }
