@@ -30,17 +30,46 @@ template <typename S, int DM> struct QuantLds {
   static constexpr int LD = DM + 16 / sizeof(S);
   S k[kGroup][LD];
   S v[kGroup][LD];
-  float kz[DM], kinv[DM];
-  float vz[kGroup][DM / kGroup], vinv[kGroup][DM / kGroup];
-  uint8_t kok[DM];
-  uint8_t vok[kGroup][DM / kGroup];
+  float2 kq[DM];                  // per key channel: (zero, 1/scale), 1/scale = 0 for a zero scale
+  float2 vq[kGroup][DM / kGroup];  // per value token group
 };
 
+// The 16 / sizeof(S) elements of a 16-byte LDS piece as float32.
+__device__ __forceinline__ void unpack16(const uint4& w, float (&f)[8]) {  // bf16
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const uint4& w, float (&f)[4]) {  // float32
+  f[0] = __uint_as_float(w.x);
+  f[1] = __uint_as_float(w.y);
+  f[2] = __uint_as_float(w.z);
+  f[3] = __uint_as_float(w.w);
+}
+// Elements c, c+1 (c even) of a staged row as float32.
+__device__ __forceinline__ float2 pair_f32(const uint16_t* p) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+  return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u));
+}
+__device__ __forceinline__ float2 pair_f32(const float* p) { return *reinterpret_cast<const float2*>(p); }
+
+// Code of x in a group (z, inv): a zero scale has inv = 0, so the product is 0
+// (or NaN for a non-finite operand, which the max below turns into 0): code 0.
+__device__ __forceinline__ uint32_t code_q(float x, float2 q, float qmax) {
+  const float t = __fmul_rn(__fsub_rn(x, q.x), q.y);
+  return static_cast<uint32_t>(fminf(fmaxf(__builtin_rintf(t), 0.0f), qmax));
+}
+
 // Quantize the 32 tokens staged in L and write them at token offset q0 of the
-// (batch, KV head) slice whose base pointers are given.
+// (batch, KV head) slice whose base pointers are given.  Row segments and the
+// group parameters are read as 16-byte LDS vectors.
 template <int BITS, typename S, int DM>
-__device__ void quantize_block(QuantLds<S, DM>& L, int D, int q0, uint32_t* k_codes, uint32_t* k_meta,
+__device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0, uint32_t* k_codes, uint32_t* k_meta,
                                uint32_t* v_codes, uint32_t* v_meta) {
+  constexpr int VEC = 16 / sizeof(S);
   const int tid = threadIdx.x;
   const float qmax = static_cast<float>((1 << BITS) - 1);
   const int ngv = D / kGroup;
@@ -52,48 +81,67 @@ __device__ void quantize_block(QuantLds<S, DM>& L, int D, int q0, uint32_t* k_co
       hi = fmaxf(hi, as_f32(L.k[t][c]));
     }
     const GroupQ g = make_group(lo, hi, qmax);
-    L.kz[c] = g.z;
-    L.kinv[c] = g.inv;
-    L.kok[c] = g.ok;
+    L.kq[c] = make_float2(g.z, g.inv);
     k_meta[static_cast<size_t>(q0 / kGroup) * D + c] = g.meta;
   }
-  // value groups: one token over 32 channels
+  // value groups: one token over 32 channels (a row segment)
   for (int e = tid; e < kGroup * ngv; e += kThreads) {
     const int t = e / ngv, j = e % ngv;
-    float lo = as_f32(L.v[t][j * kGroup]), hi = lo;
-    for (int i = 1; i < kGroup; ++i) {
-      lo = fminf(lo, as_f32(L.v[t][j * kGroup + i]));
-      hi = fmaxf(hi, as_f32(L.v[t][j * kGroup + i]));
+    const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][j * kGroup]);
+    float lo = as_f32(L.v[t][j * kGroup]), hi = lo;  // the same fold as a walk from element 0
+#pragma unroll
+    for (int p = 0; p < kGroup / VEC; ++p) {
+      float f[VEC];
+      unpack16(seg[p], f);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        lo = fminf(lo, f[i]);
+        hi = fmaxf(hi, f[i]);
+      }
     }
     const GroupQ g = make_group(lo, hi, qmax);
-    L.vz[t][j] = g.z;
-    L.vinv[t][j] = g.inv;
-    L.vok[t][j] = g.ok;
+    L.vq[t][j] = make_float2(g.z, g.inv);
     v_meta[static_cast<size_t>(q0 + t) * ngv + j] = g.meta;
   }
   __syncthreads();
   constexpr int per = 32 / BITS;
   const int nw = D / per;  // key words per token
+  // key words: word w of token t holds channels w*per.. of t; the lanes of a
+  // wave share w (their parameter reads are broadcasts)
   for (int e = tid; e < kGroup * nw; e += kThreads) {
-    const int t = e / nw, w = e % nw;
+    const int w = e / kGroup, t = e % kGroup;
+    const uint4* xs = reinterpret_cast<const uint4*>(&L.k[t][w * per]);
+    const uint4* qs = reinterpret_cast<const uint4*>(&L.kq[w * per]);
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int c = w * per + i;
-      word |= code_of(as_f32(L.k[t][c]), L.kz[c], L.kinv[c], L.kok[c], qmax) << (BITS * i);
+    for (int p = 0; p < per / VEC; ++p) {
+      float f[VEC];
+      unpack16(xs[p], f);
+#pragma unroll
+      for (int i = 0; i < VEC; i += 2) {
+        const uint4 qq = qs[(p * VEC + i) / 2];  // parameters of channels i, i+1 of this piece
+        const int c = p * VEC + i;
+        word |= code_q(f[i], make_float2(__uint_as_float(qq.x), __uint_as_float(qq.y)), qmax) << (BITS * c);
+        word |= code_q(f[i + 1], make_float2(__uint_as_float(qq.z), __uint_as_float(qq.w)), qmax) << (BITS * (c + 1));
+      }
     }
     k_codes[static_cast<size_t>(q0 + t) * nw + w] = word;
   }
+  // value words: word row r of channel c holds tokens r*per..; a thread takes
+  // the channel pair c, c+1 (same group, same parameters)
   constexpr int rows = kGroup / per;  // value word rows per block
-  for (int e = tid; e < rows * D; e += kThreads) {
-    const int r = e / D, c = e % D, j = c / kGroup;
-    uint32_t word = 0;
+  for (int e = tid; e < rows * (D / 2); e += kThreads) {
+    const int r = e / (D / 2), c = (e % (D / 2)) * 2, j = c / kGroup;
+    uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) {
       const int t = r * per + i;
-      word |= code_of(as_f32(L.v[t][c]), L.vz[t][j], L.vinv[t][j], L.vok[t][j], qmax) << (BITS * i);
+      const float2 q = L.vq[t][j];
+      const float2 x = pair_f32(&L.v[t][c]);
+      w0 |= code_q(x.x, q, qmax) << (BITS * i);
+      w1 |= code_q(x.y, q, qmax) << (BITS * i);
     }
-    v_codes[(static_cast<size_t>(q0) / per + r) * D + c] = word;
+    *reinterpret_cast<uint2*>(&v_codes[(static_cast<size_t>(q0) / per + r) * D + c]) = make_uint2(w0, w1);
   }
 }
 
