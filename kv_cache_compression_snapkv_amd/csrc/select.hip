@@ -572,6 +572,7 @@ __device__ int block_exclusive_scan(int x, int* sh, int* total) {
 template <int NBITS = 8>
 __device__ __forceinline__ void wave_hist_add(int* hist, bool valid, uint32_t bin) {
   uint64_t peers = __ballot(valid);
+  if (peers == 0) return;  // wave-uniform: no lane votes (later radix passes, most waves)
 #pragma unroll
   for (int bit = 0; bit < NBITS; ++bit) {
     const bool set = (bin >> bit) & 1u;
