@@ -25,8 +25,9 @@ even); bfloat16 by round-to-nearest-even bit arithmetic.
 
 Parity status of each function (pins live in ``tests/test_oracle_*.py``):
   budget.*            pinned (blog table, MiniKV example, CSKV/PyramidKV claims,
-                      pyramid invariants)
-  select.*            pinned (torch softmax/max_pool1d, brute force, invariants)
+                      pyramid invariants, weighted-budget closed forms)
+  select.*            pinned (torch softmax/max_pool1d, brute force, invariants,
+                      variance closed forms)
   quant.*             pinned (error bound, exact-nearest brute force, integer
                       groups, blog round_to, pack round trip)
   decode.*            pinned (torch SDPA, dense special case, convex hull, blog

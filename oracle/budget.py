@@ -57,6 +57,42 @@ def layer_budgets(layers, avg, pyramid, beta, prompt_len, window):
     return [min(k, cand) for k in ks]
 
 
+def weighted_budgets(weights, avg):
+    """Budgets proportional to positive per-layer weights, mean ``avg``.
+
+    MiniKV, Sec. 4.2, the variance policies: Var-prop gives a layer a share of
+    the cache proportional to the variance of its cumulated attention, Var-inv
+    a share inversely proportional to it (so the weight is the variance or its
+    reciprocal).  Readings: the shares are x_l = L*avg*w_l / sum(w), so that the
+    mean is avg; integerization as for the pyramid (floor, then +1 to the layers
+    with the largest fractional parts, ties to the lower layer), with the
+    shares computed in IEEE double in this order: S = w_0 + w_1 + ... (left to
+    right), x_l = (L*avg * w_l) / S.  The +1s go to at most L layers and at
+    least none, so the sum is L*avg whenever the rounding of S leaves the
+    floors' deficit in [0, L].
+    """
+    w = [float(x) for x in weights]
+    L = len(w)
+    S = 0.0
+    for x in w:
+        S = S + x
+    tot = float(L * int(avg))
+    xs = [(tot * x) / S for x in w]
+    fl = [math.floor(x) for x in xs]
+    fr = [x - f for x, f in zip(xs, fl)]
+    extra = min(max(L * int(avg) - sum(fl), 0), L)
+    order = sorted(range(L), key=lambda l: (-fr[l], l))
+    for l in order[:extra]:
+        fl[l] += 1
+    return fl
+
+
+def weighted_layer_budgets(weights, avg, prompt_len, window):
+    """Weighted budgets capped at the n - W candidates (as layer_budgets)."""
+    cand = prompt_len - window
+    return [min(k, cand) for k in weighted_budgets(weights, avg)]
+
+
 def bits_per_element(bits, group, meta_bits):
     """Storage bits per cached number.
 

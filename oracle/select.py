@@ -72,6 +72,21 @@ def top_k(scores, k):
     return np.array(sorted(order[:kk]), dtype=np.int32)
 
 
+def score_variance(scores):
+    """Variance of the cumulated attention of each (b, KV head).
+
+    MiniKV, Sec. 4.2 and the caption of Fig. 7: the variance score of a layer is
+    Var(A_cumul), the variance of the cumulated attention map.  Readings: A_cumul
+    of a KV head is its window column sums over the n - W candidates (the scores
+    before pooling), and Var is the population variance over those positions;
+    a layer's score is the mean of these over batch rows and KV heads (done by
+    the caller).  scores: [..., N]; returns float64 [...].
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    mu = s.mean(axis=-1, keepdims=True)
+    return ((s - mu) ** 2).mean(axis=-1)
+
+
 def select(q_win, k, W, pool, budget):
     """Full selection: window scores -> max pool -> per-(b, KV head) top-k.
 

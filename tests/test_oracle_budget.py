@@ -5,6 +5,7 @@ import json
 import math
 import os
 
+import numpy as np
 import pytest
 
 from oracle import budget
@@ -137,3 +138,45 @@ def test_layout_bytes_equal_blog_formula_without_eviction():
                               gen_len=0, avg=-1, pyramid=False, beta=1.0, bits=bits, group=32,
                               meta_bits=16, residual=0)
         assert fp["bytes_layout"] == fp["bytes_per_prompt_token"] * 4096
+
+
+# ---- weighted budgets (MiniKV Sec. 4.2, Var-prop / Var-inv)
+
+@pytest.mark.parametrize("L,avg", [(1, 7), (5, 128), (32, 512), (40, 3)])
+def test_weighted_equal_weights_is_uniform(L, avg):
+    assert budget.weighted_budgets([2.5] * L, avg) == [avg] * L
+
+
+def test_weighted_closed_forms_by_hand():
+    # shares 5 and 15 exactly
+    assert budget.weighted_budgets([1.0, 3.0], 10) == [5, 15]
+    # shares 2/3 and 4/3: floors 0, 1; one +1 to the larger fraction (layer 0)
+    assert budget.weighted_budgets([1.0, 2.0], 1) == [1, 1]
+    # shares 0.625 x4 and 2.5: floors 0,0,0,0,2; three +1s among four tied
+    # fractions go to the lowest layers
+    assert budget.weighted_budgets([1.0, 1.0, 1.0, 1.0, 4.0], 1) == [1, 1, 1, 0, 2]
+    # Var-inv of variances 1, 2, 4: weights 1, 1/2, 1/4 -> shares 3*7*(4/7, 2/7, 1/7) = 12, 6, 3
+    assert budget.weighted_budgets([1.0, 0.5, 0.25], 7) == [12, 6, 3]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_weighted_invariants(seed):
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(2, 48))
+    avg = int(rng.integers(1, 4000))
+    w = list(rng.lognormal(0.0, 1.0, L))
+    ks = budget.weighted_budgets(w, avg)
+    assert sum(ks) == L * avg
+    # within one of the real-valued share, and ordered like the weights
+    for wl, kl in zip(w, ks):
+        assert abs(kl - L * avg * wl / sum(w)) < 1.0 + 1e-9
+    for a in range(L):
+        for b in range(L):
+            if w[a] > w[b]:
+                assert ks[a] >= ks[b]
+    # a power-of-two scale of every weight changes nothing (exact in binary)
+    assert budget.weighted_budgets([x * 8.0 for x in w], avg) == ks
+
+
+def test_weighted_layer_budgets_cap():
+    assert budget.weighted_layer_budgets([1.0, 9.0], 100, prompt_len=150, window=20) == [20, 130]

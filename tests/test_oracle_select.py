@@ -119,3 +119,27 @@ def test_planted_heavy_tokens_are_found():
     k[0, 0, heavy] += 6 * math.sqrt(D) * mu
     idx, _ = select.select(q, k, W, 1, 10)
     assert set(idx[0, 0].tolist()) == set(heavy.tolist())
+
+
+# ---- variance of the cumulated attention (MiniKV Sec. 4.2, Fig. 7)
+
+def test_score_variance_closed_forms():
+    assert select.score_variance(np.full(17, 3.25)) == 0.0
+    assert select.score_variance(np.array([1.0, 2.0, 3.0, 4.0])) == 1.25
+    # 0..N-1: (N^2 - 1) / 12
+    for N in (1, 2, 7, 100):
+        assert math.isclose(select.score_variance(np.arange(N, dtype=np.float64)), (N * N - 1) / 12.0,
+                            rel_tol=1e-12, abs_tol=1e-15)
+
+
+def test_score_variance_batched_and_shift_invariant():
+    rng = np.random.default_rng(3)
+    s = rng.random((2, 3, 50))
+    v = select.score_variance(s)
+    assert v.shape == (2, 3)
+    np.testing.assert_allclose(select.score_variance(s + 7.0), v, rtol=1e-9)
+    np.testing.assert_allclose(select.score_variance(4.0 * s), 16.0 * v, rtol=1e-12)
+    # a single outlier of height h on N zeros: h^2 (N-1) / N^2
+    z = np.zeros(40)
+    z[5] = 3.0
+    assert math.isclose(select.score_variance(z), 9.0 * 39 / 1600, rel_tol=1e-12)
