@@ -14,7 +14,11 @@
  *                   attention over packed history (dequantized on the fly) and
  *                   residual under one softmax.
  *   kvc_budget      host-only per-layer budgets (uniform or pyramid) and the
- *                   cache footprint.
+ *                   cache footprint; kvc_budget_weighted: budgets proportional
+ *                   to per-layer weights (the variance policies).
+ *   kvc_window_scores, kvc_topk
+ *                   the two halves of kvc_select (scores and their variance;
+ *                   pool + top-k of given scores).
  *
  * Conventions shared by every call
  *   Memory:   every device buffer is allocated and owned by the caller; the
@@ -136,6 +140,21 @@ typedef struct {
 
 kvc_status kvc_budget(const kvc_budget_args *args, int32_t *layer_budget, kvc_footprint *fp);
 
+/* Budgets proportional to per-layer weights (MiniKV Sec. 4.2, the variance
+ * policies: Var-prop weights a layer by the variance of its cumulated attention,
+ * Var-inv by the reciprocal; see kvc_window_scores for the variance).  With
+ * S = w_0 + w_1 + ... (in that order) and x_l = (L*avg * w_l) / S in IEEE
+ * double, layer l gets floor(x_l), plus one for the layers with the largest
+ * fractional parts (ties to the lower layer) until the sum is L*avg; then each
+ * is capped at prompt_len - window.  args->pyramid and args->beta are ignored;
+ * the footprint is as for kvc_budget.
+ *   weights [layers] float64, every one finite and > 0.
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE (as kvc_budget, avg_budget < 0, layers *
+ *   avg_budget > INT32_MAX, a weight not finite or <= 0, an infinite sum),
+ *   KVC_ERR_BITS. */
+kvc_status kvc_budget_weighted(const kvc_budget_args *args, const double *weights, int32_t *layer_budget,
+                               kvc_footprint *fp);
+
 /* ------------------------------------------------------------------ select
  * Observation-window token selection for one layer (blog "Eviction": SnapKV;
  * PyramidKV "KV Cache Selection").  For KV head j and each of its G query
@@ -155,6 +174,33 @@ kvc_status kvc_budget(const kvc_budget_args *args, int32_t *layer_budget, kvc_fo
 kvc_status kvc_select(const void *q_win, const void *k, kvc_dtype dtype, int32_t B, int32_t Hq,
                       int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool, int32_t budget,
                       int32_t *idx, float *scores, void *ws, size_t *ws_bytes, void *stream);
+
+/* The two halves of kvc_select, for callers that look at the scores before
+ * choosing budgets (the variance policies of kvc_budget_weighted):
+ *
+ * kvc_window_scores: the window scorer alone (blog "Eviction": SnapKV; PyramidKV
+ * "KV Cache Selection"): raw [B][Hkv][n-W] float32 gets the column sums of the
+ * window rows' causal softmax over the candidates, before pooling (kvc_select's
+ * scores before its max-pool).  var [B][Hkv] float32 (may be NULL) gets the
+ * population variance of each row of raw, accumulated in float64 (MiniKV Sec.
+ * 4.2 and Fig. 7: the variance score Var(A_cumul); a layer's score is the
+ * mean over b and KV heads, left to the caller).  Shapes and dtypes as
+ * kvc_select; with n == W nothing is written.
+ * Errors: KVC_ERR_NULL (raw NULL with n > W), KVC_ERR_DTYPE, KVC_ERR_SHAPE,
+ *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
+kvc_status kvc_window_scores(const void *q_win, const void *k, kvc_dtype dtype, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t n, int32_t D, int32_t W, float *raw, float *var, void *ws,
+                             size_t *ws_bytes, void *stream);
+
+/* kvc_topk: kvc_select's second half on given scores: max-pool raw
+ * [B][Hkv][N] float32 with the odd kernel `pool` (edges clipped), take the
+ * k' = min(budget, N) largest per (b, KV head) (ties to the lower position),
+ * ascending, into idx [B][Hkv][k'] int32; scores [B][Hkv][N] float32 (or NULL)
+ * gets the pooled scores.  budget < 0 keeps all N.  idx may be NULL if k' == 0.
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE (B, Hkv < 1, N < 0, pool even or < 1),
+ *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
+kvc_status kvc_topk(const float *raw, int32_t B, int32_t Hkv, int32_t N, int32_t pool, int32_t budget,
+                    int32_t *idx, float *scores, void *ws, size_t *ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ quantize
  * Prompt compression into an empty cache (MiniKV Alg. 1 prefill: heavy

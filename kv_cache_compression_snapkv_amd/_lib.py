@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 KVC_F32, KVC_BF16 = 0, 1
 STATUS = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_BITS",
           5: "KVC_ERR_CAPACITY", 6: "KVC_ERR_WORKSPACE", 7: "KVC_ERR_HIP"}
-EXPORTS = ("kvc_budget", "kvc_select", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
-           "kvc_last_hip_error", "kvc_status_string")
+EXPORTS = ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_quantize",
+           "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error", "kvc_status_string")
 
 
 class KvcError(RuntimeError):
@@ -55,14 +55,18 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)
     lib.kvc_budget.argtypes = [ctypes.POINTER(BudgetArgs), ctypes.POINTER(I32), ctypes.POINTER(Footprint)]
+    lib.kvc_budget_weighted.argtypes = [ctypes.POINTER(BudgetArgs), ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(I32), ctypes.POINTER(Footprint)]
     lib.kvc_select.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    lib.kvc_window_scores.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    lib.kvc_topk.argtypes = [P, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_quantize.argtypes = [P, P, I32, I32, P, I32, I32, ctypes.POINTER(CacheStruct), P]
     lib.kvc_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P, SZ, P]
     lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_status_string.argtypes = [I32]
     lib.kvc_status_string.restype = ctypes.c_char_p
-    for f in ("kvc_budget", "kvc_select", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
-              "kvc_last_hip_error"):
+    for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_quantize",
+              "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -111,7 +115,79 @@ def kvc_budget(layers, kv_heads, head_dim, prompt_len, window, gen_len, avg_budg
                        "bytes_total": fp.bytes_total, "bytes_layout": fp.bytes_layout}
 
 
+def kvc_budget_weighted(layers, kv_heads, head_dim, prompt_len, window, gen_len, avg_budget, weights, bits=2,
+                        group=32, meta_bits=16, residual=0):
+    """Budgets proportional to ``weights`` (one positive float per layer)."""
+    if len(weights) != layers:
+        raise ValueError("one weight per layer")
+    a = BudgetArgs(layers, kv_heads, head_dim, prompt_len, window, gen_len, avg_budget, 0, 1.0, bits, group,
+                   meta_bits, residual)
+    w = (ctypes.c_double * layers)(*[float(x) for x in weights])
+    out = (ctypes.c_int32 * layers)()
+    fp = Footprint()
+    _check("kvc_budget_weighted", lib.kvc_budget_weighted(ctypes.byref(a), w, out, ctypes.byref(fp)))
+    return list(out), {"bits_per_element": fp.bits_per_element,
+                       "bytes_per_prompt_token": fp.bytes_per_prompt_token,
+                       "bytes_total": fp.bytes_total, "bytes_layout": fp.bytes_layout}
+
+
 # ---------------------------------------------------------------- select
+def window_scores_ws_bytes(dtype, B, Hq, Hkv, n, D, W):
+    need = ctypes.c_size_t(0)
+    _check("kvc_window_scores", lib.kvc_window_scores(None, None, dtype, B, Hq, Hkv, n, D, W, None, None, None,
+                                                      ctypes.byref(need), None))
+    return need.value
+
+
+def kvc_window_scores(q_win, k, W, want_var=True, ws=None, raw=None, var=None, stream=None):
+    """Returns raw window scores [B][Hkv][n-W] float32 (and their variance per (b, KV head))."""
+    _contig(q_win, k)
+    B, Hq, Wq, D = q_win.shape
+    _, Hkv, n, _ = k.shape
+    if Wq != W or k.dtype != q_win.dtype:
+        raise ValueError("q_win must be [B][Hq][W][D] with the dtype of k")
+    dt = _dtype(k)
+    need = window_scores_ws_bytes(dt, B, Hq, Hkv, n, D, W)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    if raw is None:
+        raw = torch.empty(B, Hkv, n - W, dtype=torch.float32, device=k.device)
+    if want_var and var is None:
+        var = torch.empty(B, Hkv, dtype=torch.float32, device=k.device)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("kvc_window_scores", lib.kvc_window_scores(_ptr(q_win), _ptr(k), dt, B, Hq, Hkv, n, D, W, _ptr(raw),
+                                                      _ptr(var) if want_var else None, _ptr(ws), ctypes.byref(wsb),
+                                                      _stream(stream)))
+    return (raw, var) if want_var else raw
+
+
+def topk_ws_bytes(B, Hkv, N, pool, budget):
+    need = ctypes.c_size_t(0)
+    _check("kvc_topk", lib.kvc_topk(None, B, Hkv, N, pool, budget, None, None, None, ctypes.byref(need), None))
+    return need.value
+
+
+def kvc_topk(raw, pool, budget, want_scores=False, ws=None, idx=None, scores=None, stream=None):
+    """Pool + top-k of raw scores [B][Hkv][N] float32: idx [B][Hkv][k'] (and the pooled scores)."""
+    _contig(raw)
+    if raw.dtype != torch.float32:
+        raise TypeError("raw scores are float32")
+    B, Hkv, N = raw.shape
+    kk = N if budget < 0 else min(budget, N)
+    need = topk_ws_bytes(B, Hkv, N, pool, budget)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=raw.device)
+    if idx is None:
+        idx = torch.empty(B, Hkv, kk, dtype=torch.int32, device=raw.device)
+    if want_scores and scores is None:
+        scores = torch.empty(B, Hkv, N, dtype=torch.float32, device=raw.device)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("kvc_topk", lib.kvc_topk(_ptr(raw), B, Hkv, N, pool, budget, _ptr(idx),
+                                    _ptr(scores) if want_scores else None, _ptr(ws), ctypes.byref(wsb),
+                                    _stream(stream)))
+    return (idx, scores) if want_scores else idx
+
+
 def select_ws_bytes(dtype, B, Hq, Hkv, n, D, W, pool, budget):
     need = ctypes.c_size_t(0)
     _check("kvc_select", lib.kvc_select(None, None, dtype, B, Hq, Hkv, n, D, W, pool, budget, None, None,

@@ -107,20 +107,80 @@ void pyramid(int L, int64_t avg, double beta, int32_t* out) {
   for (int i = 0; i < extra && i < L; ++i) out[order[i]] += 1;
 }
 
-}  // namespace
 
-extern "C" kvc_status kvc_budget(const kvc_budget_args* a, int32_t* layer_budget, kvc_footprint* fp) {
-  if (!a || !layer_budget) return KVC_ERR_NULL;
+// Weighted: x_l = (L*avg * w_l) / S with S = w_0 + w_1 + ... in order, in IEEE
+// double; floor, then +1 to the largest fractional parts (ties: lower layer).
+void weighted(int L, int64_t avg, const double* w, int32_t* out) {
+  double S = 0.0;
+  for (int l = 0; l < L; ++l) S = S + w[l];
+  const double tot = static_cast<double>(static_cast<int64_t>(L) * avg);
+  std::vector<double> rem(L);
+  int64_t sum = 0;
+  for (int l = 0; l < L; ++l) {
+    const double t = tot * w[l];
+    const double x = t / S;
+    const double fl = floor(x);
+    rem[l] = x - fl;
+    out[l] = static_cast<int32_t>(fl);
+    sum += static_cast<int64_t>(fl);
+  }
+  int64_t extra = static_cast<int64_t>(L) * avg - sum;
+  extra = std::min<int64_t>(std::max<int64_t>(extra, 0), L);
+  std::vector<int> order(L);
+  for (int l = 0; l < L; ++l) order[l] = l;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return rem[a] > rem[b]; });
+  for (int i = 0; i < extra; ++i) out[order[i]] += 1;
+}
+
+kvc_status check_args(const kvc_budget_args* a) {
   const int L = a->layers;
   if (L < 1 || L > 65536 || a->kv_heads < 1 || a->head_dim < 1 || a->prompt_len < 1 ||
       a->window < 0 || a->window > a->prompt_len || a->gen_len < 0 || a->residual < 0)
     return KVC_ERR_SHAPE;
-  if (a->pyramid && a->avg_budget >= 0 && (!(a->beta >= 1.0) || !isfinite(a->beta) || a->beta > 1048576.0))
-    return KVC_ERR_SHAPE;
   if (a->bits != 2 && a->bits != 4 && a->bits != 8 && a->bits != 16) return KVC_ERR_BITS;
   if (a->group != 16 && a->group != 32) return KVC_ERR_BITS;
   if (a->meta_bits != 8 && a->meta_bits != 16 && a->meta_bits != 32) return KVC_ERR_BITS;
+  return KVC_OK;
+}
 
+// Footprint of the applied budgets (see kvc_budget in kvc.h).
+void footprint(const kvc_budget_args* a, const int32_t* layer_budget, kvc_footprint* fp) {
+  const int L = a->layers;
+  const double bpe = a->bits == 16 ? 16.0 : a->bits + 2.0 * a->meta_bits / a->group;
+  int64_t kept_sum = 0;
+  double total_tokens = 0.0;
+  int64_t layout = 0;
+  const int64_t D = a->head_dim;
+  for (int l = 0; l < L; ++l) {
+    const int64_t T = a->avg_budget < 0 ? a->prompt_len : layer_budget[l] + a->window;
+    kept_sum += T;
+    total_tokens += static_cast<double>(T + a->gen_len);
+    if (a->bits == 16) {
+      layout += 2 * T * D * 2;
+    } else {
+      const int64_t g = a->group;
+      const int64_t q = g * (std::max<int64_t>(T - a->residual, 0) / g);
+      const int64_t pair = 2 * a->meta_bits / 8;
+      layout += 2 * q * D * a->bits / 8 + (q / g) * D * pair + q * (D / g) * pair + 2 * (T - q) * D * 2;
+    }
+  }
+  const double frac = static_cast<double>(kept_sum) / (static_cast<double>(L) * a->prompt_len);
+  const double per_tok = 2.0 * L * a->kv_heads * a->head_dim * bpe / 8.0;
+  fp->bits_per_element = bpe;
+  fp->bytes_per_prompt_token = per_tok * frac;
+  fp->bytes_total = 2.0 * a->kv_heads * a->head_dim * bpe / 8.0 * total_tokens;
+  fp->bytes_layout = static_cast<double>(layout * a->kv_heads);
+}
+
+}  // namespace
+
+extern "C" kvc_status kvc_budget(const kvc_budget_args* a, int32_t* layer_budget, kvc_footprint* fp) {
+  if (!a || !layer_budget) return KVC_ERR_NULL;
+  const kvc_status s = check_args(a);
+  if (s != KVC_OK) return s;
+  const int L = a->layers;
+  if (a->pyramid && a->avg_budget >= 0 && (!(a->beta >= 1.0) || !isfinite(a->beta) || a->beta > 1048576.0))
+    return KVC_ERR_SHAPE;
   const int64_t cand = static_cast<int64_t>(a->prompt_len) - a->window;
   if (a->avg_budget < 0) {
     for (int l = 0; l < L; ++l) layer_budget[l] = static_cast<int32_t>(cand);
@@ -131,32 +191,27 @@ extern "C" kvc_status kvc_budget(const kvc_budget_args* a, int32_t* layer_budget
   }
   for (int l = 0; l < L; ++l)
     if (layer_budget[l] > cand) layer_budget[l] = static_cast<int32_t>(cand);
+  if (fp) footprint(a, layer_budget, fp);
+  return KVC_OK;
+}
 
-  if (fp) {
-    const double bpe = a->bits == 16 ? 16.0 : a->bits + 2.0 * a->meta_bits / a->group;
-    int64_t kept_sum = 0;
-    double total_tokens = 0.0;
-    int64_t layout = 0;
-    const int64_t D = a->head_dim;
-    for (int l = 0; l < L; ++l) {
-      const int64_t T = a->avg_budget < 0 ? a->prompt_len : layer_budget[l] + a->window;
-      kept_sum += T;
-      total_tokens += static_cast<double>(T + a->gen_len);
-      if (a->bits == 16) {
-        layout += 2 * T * D * 2;
-      } else {
-        const int64_t g = a->group;
-        const int64_t q = g * (std::max<int64_t>(T - a->residual, 0) / g);
-        const int64_t pair = 2 * a->meta_bits / 8;
-        layout += 2 * q * D * a->bits / 8 + (q / g) * D * pair + q * (D / g) * pair + 2 * (T - q) * D * 2;
-      }
-    }
-    const double frac = static_cast<double>(kept_sum) / (static_cast<double>(L) * a->prompt_len);
-    const double per_tok = 2.0 * L * a->kv_heads * a->head_dim * bpe / 8.0;
-    fp->bits_per_element = bpe;
-    fp->bytes_per_prompt_token = per_tok * frac;
-    fp->bytes_total = 2.0 * a->kv_heads * a->head_dim * bpe / 8.0 * total_tokens;
-    fp->bytes_layout = static_cast<double>(layout * a->kv_heads);
+extern "C" kvc_status kvc_budget_weighted(const kvc_budget_args* a, const double* weights, int32_t* layer_budget,
+                                          kvc_footprint* fp) {
+  if (!a || !weights || !layer_budget) return KVC_ERR_NULL;
+  const kvc_status s = check_args(a);
+  if (s != KVC_OK) return s;
+  const int L = a->layers;
+  if (a->avg_budget < 0 || static_cast<int64_t>(L) * a->avg_budget > 2147483647LL) return KVC_ERR_SHAPE;
+  double S = 0.0;
+  for (int l = 0; l < L; ++l) {
+    if (!(weights[l] > 0.0) || !isfinite(weights[l])) return KVC_ERR_SHAPE;
+    S = S + weights[l];
   }
+  if (!isfinite(S)) return KVC_ERR_SHAPE;
+  weighted(L, a->avg_budget, weights, layer_budget);
+  const int64_t cand = static_cast<int64_t>(a->prompt_len) - a->window;
+  for (int l = 0; l < L; ++l)
+    if (layer_budget[l] > cand) layer_budget[l] = static_cast<int32_t>(cand);
+  if (fp) footprint(a, layer_budget, fp);
   return KVC_OK;
 }

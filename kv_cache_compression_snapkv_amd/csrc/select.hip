@@ -1068,23 +1068,25 @@ kvc_status launch_pipe_any(const ScoreArgs& a, int KS, int B, hipStream_t st) {
 bool pipe_ok(int KS, int R) { return (KS == 1 || KS == 2 || KS == 4) && R <= 256; }
 
 template <typename T>
-kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t st) {
+kvc_status run_scores(const ScoreArgs& a, int KS, int B, hipStream_t st) {
   constexpr int CH = ChunkCols<T>::value;
   const bool pipe = sizeof(T) == 2 && pipe_ok(KS, a.R);
   kvc_status s = pipe ? launch_pipe_any<1>(a, KS, B, st) : launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
   if (s != KVC_OK) return s;
   hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.Hkv, B), dim3(kThreads), 0, st, a);
   if ((s = check_launch()) != KVC_OK) return s;
-  s = pipe ? launch_pipe_any<2>(a, KS, B, st) : launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
-  if (s != KVC_OK) return s;
+  return pipe ? launch_pipe_any<2>(a, KS, B, st) : launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
+}
+
+kvc_status run_topk(const TopArgs& t, int B, hipStream_t st) {
   if (chunked_topk(t.N)) return run_chunked_topk(t, B, st);
   // short rows: raw scores in LDS, keys in registers
   const int kpt = (t.N + kTopThreads - 1) / kTopThreads;
   const size_t lds = static_cast<size_t>(t.N) * sizeof(float);
   if (kpt <= 8) {
-    hipLaunchKernelGGL(pool_topk_lds_kernel<8>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
+    hipLaunchKernelGGL(pool_topk_lds_kernel<8>, dim3(t.Hkv, B), dim3(kTopThreads), lds, st, t);
   } else if (kpt <= 16) {
-    hipLaunchKernelGGL(pool_topk_lds_kernel<16>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
+    hipLaunchKernelGGL(pool_topk_lds_kernel<16>, dim3(t.Hkv, B), dim3(kTopThreads), lds, st, t);
   } else {
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_topk_lds_kernel<32>),
@@ -1094,9 +1096,114 @@ kvc_status run_select(const ScoreArgs& a, int KS, int B, TopArgs& t, hipStream_t
         return KVC_ERR_HIP;
       }
     }
-    hipLaunchKernelGGL(pool_topk_lds_kernel<32>, dim3(a.Hkv, B), dim3(kTopThreads), lds, st, t);
+    hipLaunchKernelGGL(pool_topk_lds_kernel<32>, dim3(t.Hkv, B), dim3(kTopThreads), lds, st, t);
   }
   return check_launch();
+}
+
+// Population variance over the N scores of each (b, KV head), accumulated in
+// float64 in a fixed order (deterministic): mean first, then the squared
+// deviations.  One workgroup per (b, j).
+__device__ double block_sum_f64(double x, double* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  if (lane == 0) sh[w] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kThreads / 64; ++i) t += sh[i];
+  __syncthreads();
+  return t;
+}
+__global__ __launch_bounds__(kThreads) void variance_kernel(const float* raw, int N, float* var) {
+  __shared__ double sh[kThreads / 64];
+  const size_t bj = blockIdx.x;
+  const float* s = raw + bj * N;
+  double acc = 0.0;
+  for (int c = threadIdx.x; c < N; c += kThreads) acc += s[c];
+  const double mean = block_sum_f64(acc, sh) / N;
+  acc = 0.0;
+  for (int c = threadIdx.x; c < N; c += kThreads) {
+    const double d = s[c] - mean;
+    acc += d * d;
+  }
+  const double v = block_sum_f64(acc, sh) / N;
+  if (threadIdx.x == 0) var[bj] = static_cast<float>(v);
+}
+
+// Workspace of the scorer (per-chunk and per-row statistics) and of the top-k.
+struct ScoreWs {
+  int nc1;
+  size_t stats, row, total;
+};
+ScoreWs score_ws(kvc_dtype dtype, int B, int Hkv, int G, int n, int D, int W) {
+  const bool pipe = dtype != KVC_F32 && pipe_ok(D / 32, G * W);
+  const int CH = pipe ? kPipeCH : dtype == KVC_F32 ? ChunkCols<float>::value : ChunkCols<uint16_t>::value;
+  const size_t units = static_cast<size_t>(B) * Hkv;
+  ScoreWs w;
+  w.nc1 = (n + CH - 1) / CH;
+  w.stats = align_up(units * w.nc1 * (G * W) * sizeof(float2), 256);
+  w.row = align_up(units * (G * W) * sizeof(float2), 256);
+  w.total = w.stats + w.row;
+  return w;
+}
+struct TopWs {
+  int nch;
+  size_t keys, hist1, ghist, sel, cnt, total;
+};
+TopWs top_ws(int B, int Hkv, int N) {
+  const size_t units = static_cast<size_t>(B) * Hkv;
+  TopWs w;
+  w.nch = (N + kChunk - 1) / kChunk;  // chunked top-k
+  w.keys = align_up(units * w.nch * kChunk * sizeof(uint32_t), 256);
+  w.hist1 = align_up(units * w.nch * 256 * sizeof(int), 256);
+  w.ghist = align_up(units * 2 * kWideBins * sizeof(int), 256);
+  w.sel = align_up(units * kSelSlots * sizeof(uint32_t), 256);
+  w.cnt = align_up(units * w.nch * sizeof(int2), 256);
+  w.total = w.keys + w.hist1 + w.ghist + w.sel + w.cnt;
+  return w;
+}
+
+ScoreArgs score_args(const void* q_win, const void* k, int Hq, int Hkv, int n, int D, int W, const ScoreWs& sw,
+                     char* w, float* raw) {
+  ScoreArgs a;
+  a.q_win = q_win;
+  a.k = k;
+  a.stats = reinterpret_cast<float2*>(w);
+  a.rowstat = reinterpret_cast<float*>(w + sw.stats);
+  a.raw = raw;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.n = n;
+  a.W = W;
+  a.R = a.G * W;
+  a.N = n - W;
+  a.nc1 = sw.nc1;
+  a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  return a;
+}
+TopArgs top_args(const float* raw, int Hkv, int N, int kk, int pool, const TopWs& tw, char* w, int32_t* idx,
+                 float* scores) {
+  TopArgs t;
+  t.raw = raw;
+  t.keys = reinterpret_cast<uint32_t*>(w);
+  t.hist1 = reinterpret_cast<int*>(w + tw.keys);
+  t.ghist = reinterpret_cast<int*>(w + tw.keys + tw.hist1);
+  t.sel = reinterpret_cast<uint32_t*>(w + tw.keys + tw.hist1 + tw.ghist);
+  t.cnt = reinterpret_cast<int2*>(w + tw.keys + tw.hist1 + tw.ghist + tw.sel);
+  t.scores = scores;
+  t.idx = idx;
+  t.Hkv = Hkv;
+  t.N = N;
+  t.kk = kk;
+  t.pool = pool;
+  t.nch = tw.nch;
+  t.NP = tw.nch * kChunk;
+  return t;
+}
+bool score_shape_ok(int B, int Hq, int Hkv, int n, int D, int W) {
+  return B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0 && head_dim_ok(D) && n >= 1 && W >= 1 && W <= n;
 }
 
 }  // namespace
@@ -1108,26 +1215,12 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   using namespace kvc;
   if (!ws_bytes) return KVC_ERR_NULL;
   if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
-  if (B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || n < 1 || W < 1 || W > n ||
-      pool < 1 || pool % 2 == 0)
-    return KVC_ERR_SHAPE;
-  const int G = Hq / Hkv;
+  if (!score_shape_ok(B, Hq, Hkv, n, D, W) || pool < 1 || pool % 2 == 0) return KVC_ERR_SHAPE;
   const int N = n - W;
-  const int R = G * W;
-  const bool pipe = dtype != KVC_F32 && head_dim_ok(D) && pipe_ok(D / 32, G * W);
-  const int CH = pipe ? kPipeCH : dtype == KVC_F32 ? ChunkCols<float>::value : ChunkCols<uint16_t>::value;
-  const int nc1 = (n + CH - 1) / CH;
-  const size_t units = static_cast<size_t>(B) * Hkv;
-  const size_t sz_stats = align_up(units * nc1 * R * sizeof(float2), 256);
-  const size_t sz_row = align_up(units * R * sizeof(float2), 256);
-  const size_t sz_raw = align_up(units * N * sizeof(float), 256);
-  const int nch = (N + kChunk - 1) / kChunk;  // chunked top-k
-  const size_t sz_keys = align_up(units * nch * kChunk * sizeof(uint32_t), 256);
-  const size_t sz_hist1 = align_up(units * nch * 256 * sizeof(int), 256);
-  const size_t sz_ghist = align_up(units * 2 * kWideBins * sizeof(int), 256);
-  const size_t sz_sel = align_up(units * kSelSlots * sizeof(uint32_t), 256);
-  const size_t sz_cnt = align_up(units * nch * sizeof(int2), 256);
-  const size_t need = sz_stats + sz_row + sz_raw + sz_keys + sz_hist1 + sz_ghist + sz_sel + sz_cnt;
+  const ScoreWs sw = score_ws(dtype, B, Hkv, Hq / Hkv, n, D, W);
+  const TopWs tw = top_ws(B, Hkv, N);
+  const size_t sz_raw = align_up(static_cast<size_t>(B) * Hkv * N * sizeof(float), 256);
+  const size_t need = sw.total + sz_raw + tw.total;
   if (!ws) {
     *ws_bytes = need;
     return KVC_OK;
@@ -1138,37 +1231,52 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   if (N == 0) return KVC_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  ScoreArgs a;
-  a.q_win = q_win;
-  a.k = k;
-  a.stats = reinterpret_cast<float2*>(w);
-  a.rowstat = reinterpret_cast<float*>(w + sz_stats);
-  a.raw = reinterpret_cast<float*>(w + sz_stats + sz_row);
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.G = G;
-  a.n = n;
-  a.W = W;
-  a.R = R;
-  a.N = N;
-  a.nc1 = nc1;
-  a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
-  TopArgs t;
-  char* tw = w + sz_stats + sz_row + sz_raw;
-  t.raw = a.raw;
-  t.keys = reinterpret_cast<uint32_t*>(tw);
-  t.hist1 = reinterpret_cast<int*>(tw + sz_keys);
-  t.ghist = reinterpret_cast<int*>(tw + sz_keys + sz_hist1);
-  t.sel = reinterpret_cast<uint32_t*>(tw + sz_keys + sz_hist1 + sz_ghist);
-  t.cnt = reinterpret_cast<int2*>(tw + sz_keys + sz_hist1 + sz_ghist + sz_sel);
-  t.scores = scores;
-  t.idx = idx;
-  t.Hkv = Hkv;
-  t.N = N;
-  t.kk = kk;
-  t.pool = pool;
-  t.nch = nch;
-  t.NP = nch * kChunk;
-  return dtype == KVC_F32 ? run_select<float>(a, D / 32, B, t, st)
-                          : run_select<uint16_t>(a, D / 32, B, t, st);
+  float* raw = reinterpret_cast<float*>(w + sw.total);
+  const ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, w, raw);
+  const TopArgs t = top_args(raw, Hkv, N, kk, pool, tw, w + sw.total + sz_raw, idx, scores);
+  kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st) : run_scores<uint16_t>(a, D / 32, B, st);
+  if (s != KVC_OK) return s;
+  return run_topk(t, B, st);
+}
+
+extern "C" kvc_status kvc_window_scores(const void* q_win, const void* k, kvc_dtype dtype, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t n, int32_t D, int32_t W, float* raw, float* var,
+                                        void* ws, size_t* ws_bytes, void* stream) {
+  using namespace kvc;
+  if (!ws_bytes) return KVC_ERR_NULL;
+  if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
+  if (!score_shape_ok(B, Hq, Hkv, n, D, W)) return KVC_ERR_SHAPE;
+  const int N = n - W;
+  const ScoreWs sw = score_ws(dtype, B, Hkv, Hq / Hkv, n, D, W);
+  if (!ws) {
+    *ws_bytes = sw.total;
+    return KVC_OK;
+  }
+  if (!q_win || !k || (N > 0 && !raw)) return KVC_ERR_NULL;
+  if (*ws_bytes < sw.total) return KVC_ERR_WORKSPACE;
+  if (N == 0) return KVC_OK;  // no candidates: nothing written (var included)
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, static_cast<char*>(ws), raw);
+  kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st) : run_scores<uint16_t>(a, D / 32, B, st);
+  if (s != KVC_OK || !var) return s;
+  hipLaunchKernelGGL(variance_kernel, dim3(B * Hkv), dim3(kThreads), 0, st, raw, N, var);
+  return check_launch();
+}
+
+extern "C" kvc_status kvc_topk(const float* raw, int32_t B, int32_t Hkv, int32_t N, int32_t pool, int32_t budget,
+                               int32_t* idx, float* scores, void* ws, size_t* ws_bytes, void* stream) {
+  using namespace kvc;
+  if (!ws_bytes) return KVC_ERR_NULL;
+  if (B < 1 || Hkv < 1 || N < 0 || pool < 1 || pool % 2 == 0) return KVC_ERR_SHAPE;
+  const TopWs tw = top_ws(B, Hkv, N);
+  if (!ws) {
+    *ws_bytes = tw.total;
+    return KVC_OK;
+  }
+  const int kk = budget < 0 ? N : std::min(budget, N);
+  if ((N > 0 && !raw) || (kk > 0 && !idx)) return KVC_ERR_NULL;
+  if (*ws_bytes < tw.total) return KVC_ERR_WORKSPACE;
+  if (N == 0) return KVC_OK;
+  const TopArgs t = top_args(raw, Hkv, N, kk, pool, tw, static_cast<char*>(ws), idx, scores);
+  return run_topk(t, B, static_cast<hipStream_t>(stream));
 }

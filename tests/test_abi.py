@@ -7,6 +7,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 from oracle import budget as obudget
@@ -68,6 +69,67 @@ def test_budget_validation():
         L.kvc_budget(4, 8, 128, 100, 8, 0, 10, bits=3)
     with pytest.raises(L.KvcError, match="BITS"):
         L.kvc_budget(4, 8, 128, 100, 8, 0, 10, group=64)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_budget_weighted_matches_oracle_exactly(seed):
+    rng = np.random.default_rng(100 + seed)
+    L = int(rng.integers(1, 64))
+    avg = int(rng.integers(0, 5000))
+    n = int(rng.integers(64, 200000))
+    W = int(rng.integers(1, 64))
+    w = list(rng.lognormal(0.0, 1.5, L)) if seed % 2 else list(1.0 / rng.lognormal(0.0, 1.5, L))
+    ks, fp = _lib().kvc_budget_weighted(L, 8, 128, n, W, 32, avg, w, bits=2, group=32, meta_bits=16, residual=128)
+    assert ks == obudget.weighted_layer_budgets(w, avg, n, W)
+    if all(k < n - W for k in ks):  # nothing capped
+        assert sum(ks) == L * avg
+
+
+def test_budget_weighted_equal_weights_is_uniform_with_same_footprint():
+    L = _lib()
+    ku, fu = L.kvc_budget(32, 8, 128, 8192, 32, 32, 512, bits=2, residual=128)
+    kw, fw = L.kvc_budget_weighted(32, 8, 128, 8192, 32, 32, 512, [0.37] * 32, bits=2, residual=128)
+    assert ku == kw and fu == fw
+
+
+def test_budget_weighted_validation():
+    L = _lib()
+    for bad in ([1.0, 0.0], [1.0, -2.0], [1.0, float("nan")], [1.0, float("inf")]):
+        with pytest.raises(L.KvcError, match="SHAPE"):
+            L.kvc_budget_weighted(2, 8, 128, 100, 8, 0, 10, bad)
+    with pytest.raises(L.KvcError, match="SHAPE"):
+        L.kvc_budget_weighted(2, 8, 128, 100, 8, 0, -1, [1.0, 1.0])
+    with pytest.raises(L.KvcError, match="SHAPE"):
+        L.kvc_budget_weighted(2, 8, 128, 100, 8, 0, 10, [1e308, 1e308])  # infinite sum
+    with pytest.raises(L.KvcError, match="BITS"):
+        L.kvc_budget_weighted(2, 8, 128, 100, 8, 0, 10, [1.0, 1.0], bits=3)
+    a = L.BudgetArgs(2, 8, 128, 100, 8, 0, 10, 0, 1.0, 2, 32, 16, 0)
+    out = (ctypes.c_int32 * 2)()
+    assert L.lib.kvc_budget_weighted(ctypes.byref(a), None, out, None) == 1
+
+
+def test_window_scores_and_topk_validation_and_ws_query():
+    L = _lib()
+    need = ctypes.c_size_t(0)
+    ws = L.lib.kvc_window_scores
+    assert ws(None, None, 1, 2, 8, 2, 300, 128, 16, None, None, None, ctypes.byref(need), None) == 0 and need.value > 0
+    assert ws(None, None, 5, 2, 8, 2, 300, 128, 16, None, None, None, ctypes.byref(need), None) == 3
+    assert ws(None, None, 1, 2, 6, 4, 300, 128, 16, None, None, None, ctypes.byref(need), None) == 2
+    assert ws(None, None, 1, 2, 8, 2, 300, 128, 301, None, None, None, ctypes.byref(need), None) == 2
+    big = ctypes.c_size_t(1 << 24)
+    P = ctypes.c_void_p(16)
+    assert ws(P, P, 1, 2, 8, 2, 300, 128, 16, None, None, P, ctypes.byref(big), None) == 1  # raw NULL
+    small = ctypes.c_size_t(1)
+    assert ws(P, P, 1, 2, 8, 2, 300, 128, 16, P, None, P, ctypes.byref(small), None) == 6
+    tk = L.lib.kvc_topk
+    assert tk(None, 2, 3, 40000, 7, 100, None, None, None, ctypes.byref(need), None) == 0 and need.value > 0
+    assert tk(None, 2, 3, 400, 4, 100, None, None, None, ctypes.byref(need), None) == 2   # even pool
+    assert tk(None, 0, 3, 400, 5, 100, None, None, None, ctypes.byref(need), None) == 2
+    assert tk(None, 2, 3, 400, 5, 100, None, None, P, ctypes.byref(big), None) == 1        # raw NULL
+    assert tk(P, 2, 3, 400, 5, 100, None, None, P, ctypes.byref(big), None) == 1           # idx NULL
+    assert tk(P, 2, 3, 400, 5, 0, None, None, P, ctypes.byref(small), None) == 6
+    # the fused call's workspace covers both halves plus the raw scores
+    assert L.select_ws_bytes(1, 2, 8, 2, 300, 128, 16, 7, 100) >= L.window_scores_ws_bytes(1, 2, 8, 2, 300, 128, 16)
 
 
 def _call_select(**kw):

@@ -125,6 +125,51 @@ def test_select_parity(dtype, B, G, Hkv, n, D, W, pool, budget):
             gu.check_selection(ix[b, j], sc[b, j], pooled[b, j], budget)
 
 
+@pytest.mark.parametrize("dtype,B,G,Hkv,n,D,W", [
+    ("bf16", 2, 4, 2, 700, 128, 16), ("f32", 1, 1, 3, 300, 64, 8), ("bf16", 1, 8, 1, 1000, 256, 32),
+    ("bf16", 1, 4, 1, 2000, 128, 64), ("bf16", 1, 2, 2, 37000, 64, 16)])
+def test_window_scores_and_variance(dtype, B, G, Hkv, n, D, W):
+    """kvc_window_scores: raw column sums against the oracle's window scores, and
+    their variance (MiniKV's variance score) against the oracle's, on the GPU's
+    own scores (float64 accumulation: tight) and on the oracle's scores."""
+    kvc = _kvc()
+    k, _ = _case(15, B, Hkv, n, D, dtype)
+    q_win = synth.random_tensor(16, (B, Hkv * G, W, D), dtype, tag="qw").cuda()
+    raw, var = kvc.kvc_window_scores(q_win, k, W)
+    torch.cuda.synchronize()
+    ref = oselect.window_scores(gu.as_f32(q_win), gu.as_f32(k), W)
+    r = raw.cpu().numpy()
+    np.testing.assert_array_less(np.abs(r - ref), gu.SCORE_TOL * (np.abs(ref) + ref.max()) + 1e-30)
+    v = var.cpu().numpy()
+    np.testing.assert_allclose(v, oselect.score_variance(r), rtol=1e-5)
+    np.testing.assert_allclose(v, oselect.score_variance(ref), rtol=1e-3)
+    # the fused call selects the same positions as the two halves
+    idx = kvc.kvc_select(q_win, k, W, 7, 100)
+    idx2 = kvc.kvc_topk(raw, 7, 100)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+
+
+@pytest.mark.parametrize("B,Hkv,N,pool,budget", [
+    (2, 3, 500, 7, 100), (1, 2, 40000, 7, 1500), (1, 1, 33000, 13, 700), (2, 2, 1000, 1, -1),
+    (1, 2, 300, 5, 0), (1, 1, 8160, 9, 512), (3, 1, 4096 * 9, 3, 1)])
+def test_topk_on_given_scores(B, Hkv, N, pool, budget):
+    """kvc_topk on seeded scores on a coarse grid (many ties): the pooled scores
+    are maxima of the inputs (exact) and idx is the oracle's top-k of them."""
+    kvc = _kvc()
+    raw = (torch.round(synth.random_tensor(17, (B, Hkv, N), "f32", tag="raw") * 8) / 8).cuda()
+    idx, sc = kvc.kvc_topk(raw, pool, budget, want_scores=True)
+    torch.cuda.synchronize()
+    pooled = oselect.max_pool(raw.cpu().numpy().astype(np.float64), pool)
+    np.testing.assert_array_equal(sc.cpu().numpy(), pooled.astype(np.float32))
+    kk = N if budget < 0 else min(budget, N)
+    ix = idx.cpu().numpy()
+    assert ix.shape == (B, Hkv, kk)
+    for b in range(B):
+        for j in range(Hkv):
+            np.testing.assert_array_equal(ix[b, j], oselect.top_k(pooled[b, j], kk), f"b{b} j{j}")
+
+
 @pytest.mark.parametrize("n", [3000, 40000])
 def test_select_all_scores_tied(n):
     """Zero keys make every logit 0, so every candidate gets the same score (the
