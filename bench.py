@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-hbm-stress", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="eager launches (for counter collection)")
     ap.add_argument("--layers", type=int, default=None, help="run only the first N layers")
+    ap.add_argument("--budget-policy", default="workload", choices=("workload", "var-prop", "var-inv"),
+                    help="per-layer budgets: the workload's (uniform or pyramid), or proportional to the variance "
+                         "of each layer's window scores or to its reciprocal (scores, budgets, then top-k)")
     return ap.parse_args()
 
 
@@ -123,8 +126,14 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=20.0):
     }
 
 
-def run(cfg, bits, steps, warmup, graph=True, layers=None):
-    """Time `steps` graph-replayed steps of the whole path on one workload."""
+def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload"):
+    """Time `steps` graph-replayed steps of the whole path on one workload.
+
+    policy var-prop / var-inv: prompt compression runs kvc_window_scores for
+    every layer (scores and their variance), the per-layer budgets come from
+    kvc_budget_weighted on the layers' mean variances (decided once, on the host,
+    from an untimed pass over the same prompts), then kvc_topk and kvc_quantize
+    run per layer."""
     import torch
 
     import kv_cache_compression_snapkv_amd as kvc
@@ -137,9 +146,24 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None):
     in_bytes = 4 if cfg.dtype == "f32" else 2
     if layers is not None:
         L = min(L, layers)
+    varp = policy != "workload" and cfg.budget >= 0
 
     # inputs resident in HBM before timing
     prompts = [synth.prompt_layer(cfg, l, dev) for l in range(L)]
+    if varp:
+        N = n - W
+        raws = [torch.empty(B, Hkv, N, dtype=torch.float32, device=dev) for _ in range(L)]
+        lvars = [torch.empty(B, Hkv, dtype=torch.float32, device=dev) for _ in range(L)]
+        sc_ws = torch.empty(max(kvc.window_scores_ws_bytes(1 if in_bytes == 2 else 0, B, Hq, Hkv, n, D, W), 1),
+                            dtype=torch.uint8, device=dev)
+        for l in range(L):
+            kvc.kvc_window_scores(prompts[l]["q_win"], prompts[l]["k"], W, ws=sc_ws, raw=raws[l], var=lvars[l])
+        score = [max(float(v.double().mean()), 1e-300) for v in lvars]
+        weights = score if policy == "var-prop" else [1.0 / x for x in score]
+        budgets, fp = kvc.kvc_budget_weighted(L, Hkv, D, n, W, cfg.decode_steps, cfg.budget, weights, bits=bits,
+                                              group=32, meta_bits=16, residual=cfg.residual)
+        tk_ws = torch.empty(max(kvc.topk_ws_bytes(B, Hkv, N, cfg.pool, b) for b in budgets), dtype=torch.uint8,
+                            device=dev)
     dec = [[synth.decode_inputs(cfg, l, s, dev) for l in range(L)] for s in range(cfg.decode_steps)]
     caches, idxs = [], []
     for l in range(L):
@@ -155,6 +179,13 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None):
     def prefill():
         for c in caches:
             c.reset()
+        if varp:
+            for l in range(L):
+                kvc.kvc_window_scores(prompts[l]["q_win"], prompts[l]["k"], W, ws=sc_ws, raw=raws[l], var=lvars[l])
+            for l in range(L):
+                kvc.kvc_topk(raws[l], cfg.pool, budgets[l], ws=tk_ws, idx=idxs[l])
+                kvc.kvc_quantize(prompts[l]["k"], prompts[l]["v"], caches[l], idx=idxs[l], W=W)
+            return
         for l in range(L):
             p = prompts[l]
             if cfg.budget >= 0:
@@ -211,7 +242,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None):
     achieved = sum(call_bytes) / (dec_ms * 1e-3) / 1e9
     desc = (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
             f"prompt {n}, {cfg.dtype} inputs, W={W}, pool {cfg.pool}, budget "
-            f"{'all' if cfg.budget < 0 else ('pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
+            f"{'all' if cfg.budget < 0 else (policy + ' avg ' if varp else 'pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
             f"{bits}-bit g32 fp16 scale/zero, residual {cfg.residual}, {cfg.decode_steps} decode steps")
     res = {
         "desc": desc, "budgets": budgets, "footprint": fp,
@@ -227,6 +258,8 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None):
         },
     }
     del prompts, dec, caches, idxs, sel_ws, dec_ws, g_pre, g_dec
+    if varp:
+        del raws, lvars, sc_ws, tk_ws
     torch.cuda.empty_cache()
     return res
 
@@ -241,7 +274,8 @@ def main():
 
     cfg = synth.CONFIGS[args.workload]
     bits = args.bits or cfg.bits[0]
-    r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers)
+    r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers,
+            policy=args.budget_policy)
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s (% peak); select+quantize ms/prompt",
         "value": r["tokens_per_s"],
@@ -256,7 +290,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": r["desc"], "batch": cfg.batch, "prompt": cfg.prompt, "layers": cfg.layers,
-                   "bits": bits, "decode_steps": cfg.decode_steps},
+                   "bits": bits, "decode_steps": cfg.decode_steps, "budget_policy": args.budget_policy},
         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
         "decode_ms_per_token_all_layers": r["dec_ms"] / cfg.decode_steps,
         "decode_hbm_GBs": r["roofline"]["achieved"],

@@ -184,7 +184,8 @@ kvc_status kvc_select(const void *q_win, const void *k, kvc_dtype dtype, int32_t
  * scores before its max-pool).  var [B][Hkv] float32 (may be NULL) gets the
  * population variance of each row of raw, accumulated in float64 (MiniKV Sec.
  * 4.2 and Fig. 7: the variance score Var(A_cumul); a layer's score is the
- * mean over b and KV heads, left to the caller).  Shapes and dtypes as
+ * mean over b and KV heads, left to the caller; computed as
+ * (sum x^2 - (sum x)^2 / N) / N with float64 sums).  Shapes and dtypes as
  * kvc_select; with n == W nothing is written.
  * Errors: KVC_ERR_NULL (raw NULL with n > W), KVC_ERR_DTYPE, KVC_ERR_SHAPE,
  *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */

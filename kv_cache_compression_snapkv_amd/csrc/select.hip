@@ -1101,34 +1101,39 @@ kvc_status run_topk(const TopArgs& t, int B, hipStream_t st) {
   return check_launch();
 }
 
-// Population variance over the N scores of each (b, KV head), accumulated in
-// float64 in a fixed order (deterministic): mean first, then the squared
-// deviations.  One workgroup per (b, j).
-__device__ double block_sum_f64(double x, double* sh) {
+// Population variance over the N scores of each (b, KV head): one pass of
+// float64 sums of x and x^2 (var = (sum x^2 - (sum x)^2 / N) / N), reduced in
+// a fixed order (deterministic).  One 1024-thread workgroup per (b, j).
+constexpr int kVarThreads = 1024;
+__global__ __launch_bounds__(kVarThreads) void variance_kernel(const float* raw, int N, float* var) {
+  __shared__ double sh[2][kVarThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  if (lane == 0) sh[w] = x;
-  __syncthreads();
-  double t = 0.0;
-  for (int i = 0; i < kThreads / 64; ++i) t += sh[i];
-  __syncthreads();
-  return t;
-}
-__global__ __launch_bounds__(kThreads) void variance_kernel(const float* raw, int N, float* var) {
-  __shared__ double sh[kThreads / 64];
-  const size_t bj = blockIdx.x;
-  const float* s = raw + bj * N;
-  double acc = 0.0;
-  for (int c = threadIdx.x; c < N; c += kThreads) acc += s[c];
-  const double mean = block_sum_f64(acc, sh) / N;
-  acc = 0.0;
-  for (int c = threadIdx.x; c < N; c += kThreads) {
-    const double d = s[c] - mean;
-    acc += d * d;
+  const float* s = raw + static_cast<size_t>(blockIdx.x) * N;
+  double a = 0.0, q = 0.0;
+#pragma unroll 8
+  for (int c = tid; c < N; c += kVarThreads) {
+    const double x = s[c];
+    a += x;
+    q += x * x;
   }
-  const double v = block_sum_f64(acc, sh) / N;
-  if (threadIdx.x == 0) var[bj] = static_cast<float>(v);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o);
+    q += __shfl_xor(q, o);
+  }
+  if (lane == 0) {
+    sh[0][w] = a;
+    sh[1][w] = q;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double sa = 0.0, sq = 0.0;
+    for (int i = 0; i < kVarThreads / 64; ++i) {
+      sa += sh[0][i];
+      sq += sh[1][i];
+    }
+    var[blockIdx.x] = static_cast<float>(fmax(sq - sa * sa / N, 0.0) / N);
+  }
 }
 
 // Workspace of the scorer (per-chunk and per-row statistics) and of the top-k.
@@ -1259,7 +1264,7 @@ extern "C" kvc_status kvc_window_scores(const void* q_win, const void* k, kvc_dt
   const ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, static_cast<char*>(ws), raw);
   kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st) : run_scores<uint16_t>(a, D / 32, B, st);
   if (s != KVC_OK || !var) return s;
-  hipLaunchKernelGGL(variance_kernel, dim3(B * Hkv), dim3(kThreads), 0, st, raw, N, var);
+  hipLaunchKernelGGL(variance_kernel, dim3(B * Hkv), dim3(kVarThreads), 0, st, raw, N, var);
   return check_launch();
 }
 
