@@ -1161,6 +1161,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* part_
 // 4-wave workgroups the chip holds at once (the occupancy query below), spread
 // over the units, each unit's tiles evenly over its waves, then merge_kernel.
 constexpr int kShortTilesPerWave = 6;
+constexpr int kMinTilesPerWave = 3;  // split runs
 
 struct Plan {
   int nb, nwv, hbs;  // workgroups per unit, waves per workgroup, query heads per workgroup
@@ -1256,7 +1257,9 @@ Plan plan(int NT, int BH, int G, int KS, const Occupancy& oc) {
   }
   p.nwv = 4;
   int nb = std::max(1, oc.cus * oc.per_cu / units);
-  nb = std::min(nb, (NT + 3) / 4);  // no workgroup without a tile
+  // at least kMinTilesPerWave tiles per wave: fewer, fuller splits cost less to
+  // merge (measured 5% faster per call at the 128k shape than one tile per wave)
+  nb = std::min(nb, (NT + 4 * kMinTilesPerWave - 1) / (4 * kMinTilesPerWave));
   nb = std::min(nb, kMaxNb);
   p.nb = nb;
   return p;
