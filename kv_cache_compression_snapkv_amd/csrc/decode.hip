@@ -1007,22 +1007,31 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
     wave_sync();
     const u32x4 af = *reinterpret_cast<const u32x4*>(AV + 2 * (rk * kRowW + 4 * lq));
     const bool clean = tl + 8 <= a.r_total && !(a.r_new >= tl && a.r_new < tl + 8);
+    // for the lane's 8 value slots (2 per 32-bit word): keep[w] selects the ring
+    // values kept, put[w] the appended token's slot; slots past the residual are 0
+    uint32_t keep[4], put[4];
+    const int enew = (a.r_new >= tl && a.r_new < tl + 8) ? a.r_new - tl : -1;  // slot of the appended token
+    {
+      const int nvld = min(max(a.r_total - tl, 0), 8);  // slots inside the residual
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        keep[w] = ((2 * w < nvld && 2 * w != enew) ? 0x0000FFFFu : 0u) |
+                  ((2 * w + 1 < nvld && 2 * w + 1 != enew) ? 0xFFFF0000u : 0u);
+        put[w] = (2 * w == enew ? 0x0000FFFFu : 0u) | (2 * w + 1 == enew ? 0xFFFF0000u : 0u);
+      }
+    }
 #pragma unroll
     for (int g = 0; g < NGV; ++g) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         u32x4 bf = vraw[g][u];
         if (!clean) {
-          // zero slots past the residual, substitute the appended token
+          uint32_t hv = 0u;  // the appended token's value of channel 32g + 2ln + u
+          if (enew >= 0)
+            hv = pre ? (rnew.vn[g] >> (16 * u)) & 0xFFFFu : f32_to_bf16(load_f32(vnp, 32 * g + 2 * ln + u));
+          const uint32_t h2 = hv | (hv << 16);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int t = tl + e;
-            uint32_t hv = (bf[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            if (t == a.r_new)
-              hv = pre ? (rnew.vn[g] >> (16 * u)) & 0xFFFFu : f32_to_bf16(load_f32(vnp, 32 * g + 2 * ln + u));
-            else if (t >= a.r_total) hv = 0u;
-            bf[e >> 1] = (bf[e >> 1] & (0xFFFF0000u >> (16 * (e & 1)))) | (hv << (16 * (e & 1)));
-          }
+          for (int w = 0; w < 4; ++w) bf[w] = (bf[w] & keep[w]) | (h2 & put[w]);
         }
         oacc[2 * g + u] = mfma(af, bf, oacc[2 * g + u]);
       }
