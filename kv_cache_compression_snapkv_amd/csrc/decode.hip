@@ -266,6 +266,8 @@ template <int N> __device__ __forceinline__ void wait_vmem() {
 __device__ __forceinline__ uint32_t bf16_pair(float x0, float x1) {
   return static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
 }
+__device__ __forceinline__ float as_f32(float x) { return x; }
+__device__ __forceinline__ float as_f32(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ uint32_t load_bf16x2(const uint16_t* p, int i) {
   return *reinterpret_cast<const uint32_t*>(p + i);
 }
@@ -581,7 +583,9 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   // change) and its first history tiles before anything waits; meanwhile its
   // operand rows that no head writes are zeroed.  No workgroup barrier.
   const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.Hq + j * a.G + h0) * D;
-  float qa0[NP][HBS], qa1[NP][HBS];
+  // loaded as stored and converted after every setup load is issued, so that no
+  // load waits for the query's
+  T qr0[NP][HBS], qr1[NP][HBS];
   int cpair[NP];
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
@@ -591,9 +595,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
 #pragma unroll
     for (int h = 0; h < HBS; ++h) {
       const int hc = min(h, Gb - 1);
-      // scores come out of the MFMAs already in log2 units: q is scaled once
-      qa0[u][h] = load_f32(qp, hc * D + cpair[u]) * a.scale2;
-      qa1[u][h] = load_f32(qp, hc * D + cpair[u] + PAIR) * a.scale2;
+      qr0[u][h] = qp[hc * D + cpair[u]];
+      qr1[u][h] = qp[hc * D + cpair[u] + PAIR];
     }
   }
   // ---- residual tiles are bf16 as stored.  A lane holds, per tile, the 8
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   struct NewRegs {
     u32x4 kn[KS];
     uint32_t vn[NGV];
-    uint16_t st_k[NST], st_v[NST];
+    T st_k[NST], st_v[NST];  // as stored in the inputs
   };
   auto res_load = [&](int rt, ResRegs& r) {
     const int t0 = rt * kGroup;
@@ -635,8 +638,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const int c = min(lane + 64 * i, D - 1);
-      n.st_k[i] = f32_to_bf16(load_f32(knp, c));
-      n.st_v[i] = f32_to_bf16(load_f32(vnp, c));
+      n.st_k[i] = knp[c];
+      n.st_v[i] = vnp[c];
     }
   };
   // This wave processes the tile holding the appended token (if any).
@@ -672,6 +675,15 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
     for (int e = lane; e < (L.pbuf >> 2); e += 64) zero_area[e] = 0u;  // AK and AV of this wave
   }
   wave_sync();
+  // scores come out of the MFMAs already in log2 units: q is scaled once
+  float qa0[NP][HBS], qa1[NP][HBS];
+#pragma unroll
+  for (int u = 0; u < NP; ++u)
+#pragma unroll
+    for (int h = 0; h < HBS; ++h) {
+      qa0[u][h] = as_f32(qr0[u][h]) * a.scale2;
+      qa1[u][h] = as_f32(qr1[u][h]) * a.scale2;
+    }
 
   f32x4 oacc[2 * NGV];
 #pragma unroll
@@ -1047,8 +1059,8 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
     for (int i = 0; i < NST; ++i) {
       const int c = lane + 64 * i;
       if (c < D) {
-        kw[c] = early ? rnew.st_k[i] : f32_to_bf16(load_f32(knp, c));
-        vw[static_cast<size_t>(c) * a.r_cap] = early ? rnew.st_v[i] : f32_to_bf16(load_f32(vnp, c));
+        kw[c] = f32_to_bf16(early ? as_f32(rnew.st_k[i]) : load_f32(knp, c));
+        vw[static_cast<size_t>(c) * a.r_cap] = f32_to_bf16(early ? as_f32(rnew.st_v[i]) : load_f32(vnp, c));
       }
     }
   }
