@@ -87,6 +87,27 @@ def score_variance(scores):
     return ((s - mu) ** 2).mean(axis=-1)
 
 
+def recent_select(n, W, budget, sinks):
+    """Position-only selection: a few leading "sink" tokens plus the most recent.
+
+    Blog, "Eviction: keep fewer tokens": a sliding window keeps only the last
+    tokens; StreamingLLM keeps the first four tokens (attention sinks) as well.
+    PyramidKV Sec. "Baselines": StreamingLLM keeps the first k - alpha and the
+    last alpha tokens of the budget k.  Reading: as for the score-based
+    selection, the observation window [n-W, n) is always kept and the budget
+    k' = min(budget, n-W) (budget < 0: every candidate) counts the other prompt
+    positions; the first s = min(sinks, k') positions are sinks and the last
+    k' - s candidates are the recent part.  sinks = 0 is the sliding window of
+    k' + W tokens.  Returns int32 [k'], ascending.
+    """
+    N = n - W
+    kk = N if budget < 0 else min(budget, N)
+    s = min(sinks, kk)
+    first = list(range(s))
+    recent = list(range(N - (kk - s), N))
+    return np.array(first + recent, dtype=np.int32)
+
+
 def select(q_win, k, W, pool, budget):
     """Full selection: window scores -> max pool -> per-(b, KV head) top-k.
 

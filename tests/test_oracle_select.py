@@ -143,3 +143,53 @@ def test_score_variance_batched_and_shift_invariant():
     z = np.zeros(40)
     z[5] = 3.0
     assert math.isclose(select.score_variance(z), 9.0 * 39 / 1600, rel_tol=1e-12)
+
+
+# ---------------------------------------------------------------- sinks + window
+@pytest.mark.parametrize("sinks,cache", [(4, 512), (0, 256), (4, 256), (0, 128), (4, 128)])
+def test_recent_select_blog_table_configurations(sinks, cache):
+    """Blog, "Eviction" measurements: caches of "4 sink tokens + the last 508",
+    "the last 256 tokens", "4 sink tokens + the last 252", ...  With the window
+    kept as always, the whole cache is the first `sinks` prompt tokens plus the
+    last cache - sinks."""
+    from oracle import quant
+    n = 4096
+    for W in (1, 8, 32):
+        idx = select.recent_select(n, W, cache - W, sinks)
+        kept = quant.kept_positions(n, W, idx)
+        assert len(kept) == cache
+        assert list(kept) == list(range(sinks)) + list(range(n - (cache - sinks), n))
+
+
+def test_recent_select_pyramidkv_baseline_split():
+    """PyramidKV "Baselines": StreamingLLM keeps the first k - alpha and the last
+    alpha tokens of a budget k."""
+    n, W = 1000, 10
+    for k, alpha in ((100, 60), (64, 64), (64, 0), (7, 3)):
+        idx = select.recent_select(n, W, k, k - alpha)
+        assert list(idx[: k - alpha]) == list(range(k - alpha))
+        assert list(idx[k - alpha:]) == list(range(n - W - alpha, n - W))
+
+
+def test_recent_select_is_top_k_of_a_position_priority():
+    """Every tiny case: the selection equals the top-k' candidates when sinks
+    rank first and the others rank by position (a different route through the
+    same definition)."""
+    for n in range(1, 12):
+        for W in range(1, n + 1):
+            N = n - W
+            for budget in range(-1, N + 2):
+                for sinks in range(0, N + 2):
+                    kk = N if budget < 0 else min(budget, N)
+                    pri = np.array([np.inf if c < sinks else float(c) for c in range(N)])
+                    want = select.top_k(pri, kk) if N else np.zeros(0, np.int32)
+                    got = select.recent_select(n, W, budget, sinks)
+                    assert got.dtype == np.int32 and list(got) == list(want), (n, W, budget, sinks)
+
+
+def test_recent_select_degenerate():
+    assert list(select.recent_select(50, 10, 0, 4)) == []
+    assert list(select.recent_select(50, 50, 5, 4)) == []
+    assert list(select.recent_select(50, 10, 100, 4)) == list(range(40))
+    assert list(select.recent_select(50, 10, -1, 0)) == list(range(40))
+    assert list(select.recent_select(50, 10, 3, 9)) == [0, 1, 2]
