@@ -43,7 +43,14 @@ def parse():
     ap.add_argument("--budget-policy", default="workload", choices=("workload", "var-prop", "var-inv"),
                     help="per-layer budgets: the workload's (uniform or pyramid), or proportional to the variance "
                          "of each layer's window scores or to its reciprocal (scores, budgets, then top-k)")
-    return ap.parse_args()
+    ap.add_argument("--selector", default="snapkv", choices=("snapkv", "sinks", "window"),
+                    help="prompt selection: observation-window scores (kvc_select), or position-only with "
+                         "kvc_select_recent: --sinks leading tokens plus the recent window, or the sliding window")
+    ap.add_argument("--sinks", type=int, default=4)
+    a = ap.parse_args()
+    if a.selector != "snapkv" and a.budget_policy != "workload":
+        ap.error("--budget-policy var-prop/var-inv needs the window scores of --selector snapkv")
+    return a
 
 
 def decode_call_bytes(B, Hq, Hkv, D, bits, q_len, r_total, in_bytes):
@@ -126,14 +133,16 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=20.0):
     }
 
 
-def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload"):
+def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", selector="snapkv", sinks=4):
     """Time `steps` graph-replayed steps of the whole path on one workload.
 
     policy var-prop / var-inv: prompt compression runs kvc_window_scores for
     every layer (scores and their variance), the per-layer budgets come from
     kvc_budget_weighted on the layers' mean variances (decided once, on the host,
     from an untimed pass over the same prompts), then kvc_topk and kvc_quantize
-    run per layer."""
+    run per layer.  selector sinks / window: kvc_select_recent replaces
+    kvc_select (first `sinks` prompt tokens plus the most recent; none for the
+    sliding window)."""
     import torch
 
     import kv_cache_compression_snapkv_amd as kvc
@@ -188,7 +197,10 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload"):
             return
         for l in range(L):
             p = prompts[l]
-            if cfg.budget >= 0:
+            if cfg.budget >= 0 and selector != "snapkv":
+                kvc.kvc_select_recent(B, Hkv, n, W, budgets[l], sinks if selector == "sinks" else 0, idx=idxs[l])
+                kvc.kvc_quantize(p["k"], p["v"], caches[l], idx=idxs[l], W=W)
+            elif cfg.budget >= 0:
                 kvc.kvc_select(p["q_win"], p["k"], W, cfg.pool, budgets[l], ws=sel_ws, idx=idxs[l])
                 kvc.kvc_quantize(p["k"], p["v"], caches[l], idx=idxs[l], W=W)
             else:
@@ -240,8 +252,9 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload"):
     step_ms = sum(e0.elapsed_time(e2) for e0, _, e2 in recs) / steps
     ncalls = len(call_bytes)
     achieved = sum(call_bytes) / (dec_ms * 1e-3) / 1e9
+    sel = {"snapkv": "", "sinks": f"{sinks} sinks + recent window, ", "window": "sliding window, "}[selector]
     desc = (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
-            f"prompt {n}, {cfg.dtype} inputs, W={W}, pool {cfg.pool}, budget "
+            f"prompt {n}, {cfg.dtype} inputs, W={W}, {sel}pool {cfg.pool}, budget "
             f"{'all' if cfg.budget < 0 else (policy + ' avg ' if varp else 'pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
             f"{bits}-bit g32 fp16 scale/zero, residual {cfg.residual}, {cfg.decode_steps} decode steps")
     res = {
@@ -275,7 +288,7 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     bits = args.bits or cfg.bits[0]
     r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers,
-            policy=args.budget_policy)
+            policy=args.budget_policy, selector=args.selector, sinks=args.sinks)
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s (% peak); select+quantize ms/prompt",
         "value": r["tokens_per_s"],
@@ -290,7 +303,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": r["desc"], "batch": cfg.batch, "prompt": cfg.prompt, "layers": cfg.layers,
-                   "bits": bits, "decode_steps": cfg.decode_steps, "budget_policy": args.budget_policy},
+                   "bits": bits, "decode_steps": cfg.decode_steps, "budget_policy": args.budget_policy,
+                   "selector": args.selector},
         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
         "decode_ms_per_token_all_layers": r["dec_ms"] / cfg.decode_steps,
         "decode_hbm_GBs": r["roofline"]["achieved"],

@@ -19,6 +19,9 @@
  *   kvc_window_scores, kvc_topk
  *                   the two halves of kvc_select (scores and their variance;
  *                   pool + top-k of given scores).
+ *   kvc_select_recent
+ *                   position-only selection: attention sinks plus the recent
+ *                   window, or the sliding window alone.
  *
  * Conventions shared by every call
  *   Memory:   every device buffer is allocated and owned by the caller; the
@@ -202,6 +205,20 @@ kvc_status kvc_window_scores(const void *q_win, const void *k, kvc_dtype dtype, 
  *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
 kvc_status kvc_topk(const float *raw, int32_t B, int32_t Hkv, int32_t N, int32_t pool, int32_t budget,
                     int32_t *idx, float *scores, void *ws, size_t *ws_bytes, void *stream);
+
+/* kvc_select_recent: position-only selection, no scores (blog "Eviction":
+ * a sliding window keeps the last tokens, StreamingLLM also keeps the first
+ * four "attention sink" tokens; PyramidKV "Baselines": StreamingLLM keeps the
+ * first k - alpha and the last alpha tokens).  With the window [n-W, n) kept as
+ * by kvc_select and k' = min(budget, n-W) (budget < 0: n-W), every (b, KV
+ * head) row of idx [B][Hkv][k'] int32 gets the s = min(sinks, k') positions
+ * 0..s-1 followed by the last k' - s candidates n-W-(k'-s) .. n-W-1, ascending:
+ * the cache then holds the first s prompt tokens and the last k' - s + W.
+ * sinks = 0 is the sliding window.  idx may be NULL if k' == 0.
+ * Errors: KVC_ERR_SHAPE (B, Hkv < 1, W < 1, W > n, sinks < 0), KVC_ERR_NULL,
+ *   KVC_ERR_HIP. */
+kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32_t budget, int32_t sinks,
+                             int32_t *idx, void *stream);
 
 /* ------------------------------------------------------------------ quantize
  * Prompt compression into an empty cache (MiniKV Alg. 1 prefill: heavy

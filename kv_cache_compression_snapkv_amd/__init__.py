@@ -8,5 +8,5 @@ by ``python kv_cache_compression_snapkv_amd/build.py`` (or ``__graft_entry__.bui
 """
 
 from ._lib import (Cache, KvcError, LIB_PATH, decode_ws_bytes, kvc_budget, kvc_budget_weighted,  # noqa: F401
-                   kvc_decode_attn, kvc_quantize, kvc_select, kvc_topk, kvc_window_scores, select_ws_bytes,
-                   topk_ws_bytes, window_scores_ws_bytes)
+                   kvc_decode_attn, kvc_quantize, kvc_select, kvc_select_recent, kvc_topk, kvc_window_scores,
+                   select_ws_bytes, topk_ws_bytes, window_scores_ws_bytes)

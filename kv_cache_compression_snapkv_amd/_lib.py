@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 KVC_F32, KVC_BF16 = 0, 1
 STATUS = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_BITS",
           5: "KVC_ERR_CAPACITY", 6: "KVC_ERR_WORKSPACE", 7: "KVC_ERR_HIP"}
-EXPORTS = ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_quantize",
-           "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error", "kvc_status_string")
+EXPORTS = ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
+           "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error", "kvc_status_string")
 
 
 class KvcError(RuntimeError):
@@ -60,13 +60,14 @@ def _load():
     lib.kvc_select.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_window_scores.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_topk.argtypes = [P, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    lib.kvc_select_recent.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
     lib.kvc_quantize.argtypes = [P, P, I32, I32, P, I32, I32, ctypes.POINTER(CacheStruct), P]
     lib.kvc_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P, SZ, P]
     lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_status_string.argtypes = [I32]
     lib.kvc_status_string.restype = ctypes.c_char_p
-    for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_quantize",
-              "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error"):
+    for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
+              "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -186,6 +187,18 @@ def kvc_topk(raw, pool, budget, want_scores=False, ws=None, idx=None, scores=Non
                                     _ptr(scores) if want_scores else None, _ptr(ws), ctypes.byref(wsb),
                                     _stream(stream)))
     return (idx, scores) if want_scores else idx
+
+
+def kvc_select_recent(B, Hkv, n, W, budget, sinks, idx=None, device="cuda", stream=None):
+    """Sinks plus the recent window (sliding window if sinks == 0): idx [B][Hkv][k'] int32."""
+    kk = (n - W) if budget < 0 else min(budget, n - W)
+    if idx is None:
+        idx = torch.empty(B, Hkv, max(kk, 0), dtype=torch.int32, device=device)
+    elif idx.dtype != torch.int32 or tuple(idx.shape) != (B, Hkv, kk):
+        raise ValueError("idx must be int32 [B][Hkv][k']")
+    _contig(idx)
+    _check("kvc_select_recent", lib.kvc_select_recent(B, Hkv, n, W, budget, sinks, _ptr(idx), _stream(stream)))
+    return idx
 
 
 def select_ws_bytes(dtype, B, Hq, Hkv, n, D, W, pool, budget):

@@ -1101,6 +1101,19 @@ kvc_status run_topk(const TopArgs& t, int B, hipStream_t st) {
   return check_launch();
 }
 
+// Position-only selection, the same for every (b, KV head): entry e of a row
+// is e for the s leading sinks, else the candidate N - k' + e (the last k' - s
+// candidates).  Grid-stride over the rows * k' entries.
+constexpr int kRecentThreads = 256;
+__global__ __launch_bounds__(kRecentThreads) void recent_kernel(int32_t* idx, size_t total, int kk, int s,
+                                                                int base) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kRecentThreads + threadIdx.x; i < total;
+       i += static_cast<size_t>(gridDim.x) * kRecentThreads) {
+    const int e = static_cast<int>(i % static_cast<size_t>(kk));
+    idx[i] = e < s ? e : base + e;
+  }
+}
+
 // Population variance over the N scores of each (b, KV head): one pass of
 // float64 sums of x and x^2 (var = (sum x^2 - (sum x)^2 / N) / N), reduced in
 // a fixed order (deterministic).  One 1024-thread workgroup per (b, j).
@@ -1284,4 +1297,19 @@ extern "C" kvc_status kvc_topk(const float* raw, int32_t B, int32_t Hkv, int32_t
   if (N == 0) return KVC_OK;
   const TopArgs t = top_args(raw, Hkv, N, kk, pool, tw, static_cast<char*>(ws), idx, scores);
   return run_topk(t, B, static_cast<hipStream_t>(stream));
+}
+
+extern "C" kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32_t budget, int32_t sinks,
+                                        int32_t* idx, void* stream) {
+  using namespace kvc;
+  if (B < 1 || Hkv < 1 || W < 1 || W > n || sinks < 0) return KVC_ERR_SHAPE;
+  const int N = n - W;
+  const int kk = budget < 0 ? N : std::min(budget, N);
+  if (kk == 0) return KVC_OK;
+  if (!idx) return KVC_ERR_NULL;
+  const size_t total = static_cast<size_t>(B) * Hkv * kk;
+  const size_t blocks = std::min<size_t>((total + kRecentThreads - 1) / kRecentThreads, 4096);
+  hipLaunchKernelGGL(recent_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRecentThreads), 0,
+                     static_cast<hipStream_t>(stream), idx, total, kk, std::min(sinks, kk), N - kk);
+  return check_launch();
 }

@@ -208,3 +208,16 @@ def test_cache_sizes():
     assert L.lib.kvc_cache_sizes(2, 3, 128, 3, 64, 160, out) == 4
     assert L.lib.kvc_cache_sizes(2, 3, 128, 2, 65, 160, out) == 2
     assert L.lib.kvc_status_string(5).decode().startswith("cache capacity")
+
+
+def test_select_recent_validation():
+    """Argument checks of the position-only selector; none of these launches."""
+    f = _lib().lib.kvc_select_recent
+    assert f(0, 2, 100, 8, 10, 4, None, None) == 2       # B < 1
+    assert f(1, 0, 100, 8, 10, 4, None, None) == 2       # Hkv < 1
+    assert f(1, 2, 100, 0, 10, 4, None, None) == 2       # W < 1
+    assert f(1, 2, 100, 101, 10, 4, None, None) == 2     # W > n
+    assert f(1, 2, 100, 8, 10, -1, None, None) == 2      # sinks < 0
+    assert f(1, 2, 100, 8, 10, 4, None, None) == 1       # idx NULL with k' > 0
+    assert f(1, 2, 100, 8, 0, 4, None, None) == 0        # k' == 0: nothing to write
+    assert f(1, 2, 100, 100, 10, 4, None, None) == 0     # no candidates

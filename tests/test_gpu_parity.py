@@ -237,3 +237,43 @@ def test_tiny_config_end_to_end():
     for j in range(cfg.kv_heads):
         gu.assert_cache_equal(gu.gpu_head_cache(cache, 0, j), ref[j], f"j{j}")
     gu.assert_decode_close(out[0], o_ref, "tiny end-to-end")
+
+
+@pytest.mark.parametrize("B,Hkv,n,W,budget,sinks", [
+    (2, 3, 300, 8, 100, 4), (2, 2, 300, 8, 100, 0), (1, 1, 50, 10, 100, 4), (2, 2, 300, 8, -1, 7),
+    (2, 2, 300, 8, 5, 9), (3, 2, 64, 64, 10, 4), (2, 2, 300, 8, 0, 4),
+    (8, 8, 40000, 32, 20000, 4)])   # 1.28M entries: several grid-stride passes
+def test_select_recent_parity(B, Hkv, n, W, budget, sinks):
+    kvc = _kvc()
+    idx = kvc.kvc_select_recent(B, Hkv, n, W, budget, sinks)
+    torch.cuda.synchronize()
+    want = torch.from_numpy(oselect.recent_select(n, W, budget, sinks))
+    assert tuple(idx.shape) == (B, Hkv, len(want))
+    assert torch.equal(idx.cpu(), want.expand(B, Hkv, -1))
+
+
+def test_recent_selection_end_to_end():
+    """Sinks + recent window through quantize and two decode steps (with the
+    appended tokens), against the oracle on the same kept positions."""
+    kvc = _kvc()
+    B, Hkv, G, D, n, W, budget, sinks, bits, R = 2, 2, 4, 128, 500, 16, 150, 4, 2, 32
+    k, v = _case(41, B, Hkv, n, D, "bf16")
+    idx = kvc.kvc_select_recent(B, Hkv, n, W, budget, sinks)
+    T = budget + W
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=T + 64, device="cuda")
+    kvc.kvc_quantize(k, v, cache, idx=idx, W=W)
+    kf, vf = gu.as_f32(k), gu.as_f32(v)
+    kept = oquant.kept_positions(n, W, oselect.recent_select(n, W, budget, sinks))
+    assert list(kept[:sinks]) == list(range(sinks)) and list(kept[sinks:]) == list(range(n - (T - sinks), n))
+    ref = [[oquant.build_head_cache(kf[b, j], vf[b, j], kept, R, bits) for j in range(Hkv)] for b in range(B)]
+    for s in range(2):
+        q = synth.random_tensor(300 + s, (B, Hkv * G, D), "bf16", tag="q").cuda()
+        kn = synth.random_tensor(400 + s, (B, Hkv, D), "bf16", tag="kn").cuda()
+        vn = synth.random_tensor(500 + s, (B, Hkv, D), "bf16", tag="vn").cuda()
+        out = kvc.kvc_decode_attn(cache, q, kn, vn).cpu().numpy()
+        qf = gu.as_f32(q).astype(np.float64)
+        for b in range(B):
+            o_ref, ref[b] = odecode.decode_step(ref[b], qf[b], gu.bf16_bits(kn)[b], gu.bf16_bits(vn)[b], R, bits)
+            gu.assert_decode_close(out[b], o_ref, f"step {s} b{b}")
+            for j in range(Hkv):
+                gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[b][j], f"step {s} b{b} j{j}")
