@@ -79,8 +79,21 @@ def counted_traffic(workload, bits):
     return int(m.group(1))
 
 
-def cpu_baseline(cfg, bits, layers_budget, budget_s=20.0):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def _timed(fn, share_s, max_reps):
+    """Mean seconds per call of fn, repeated until share_s has passed (at least once)."""
+    reps, t = 0, 0.0
+    while reps < max_reps and (reps == 0 or t < share_s):
+        t0 = time.perf_counter()
+        out = fn()
+        t += time.perf_counter() - t0
+        reps += 1
+    return t / reps, reps, out
+
+
+def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: one
+    (batch row, KV head) of layer 0, each stage repeated until its share of
+    budget_s (selection 1/4, quantization 1/4, one decode step 1/2) is spent."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -97,27 +110,20 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=20.0):
         kf = p["k"].float().numpy()[:1, :1]
         vf = p["v"].float().numpy()[:1, :1]
         n, W = cfg.prompt, cfg.window
-        t0 = time.perf_counter()
         if cfg.budget >= 0:
-            idx, _ = oselect.select(qw, kf, W, cfg.pool, layers_budget[0])
+            t_sel, r_sel, (idx, _) = _timed(lambda: oselect.select(qw, kf, W, cfg.pool, layers_budget[0]),
+                                            budget_s / 4, 1000)
             kept = oquant.kept_positions(n, W, idx[0, 0])
         else:
-            kept = np.arange(n)
-        t_sel = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        c = oquant.build_head_cache(kf[0, 0], vf[0, 0], kept, cfg.residual, bits)
-        t_q = time.perf_counter() - t0
+            t_sel, r_sel, kept = 0.0, 0, np.arange(n)
+        t_q, r_q, c = _timed(lambda: oquant.build_head_cache(kf[0, 0], vf[0, 0], kept, cfg.residual, bits),
+                             budget_s / 4, 1000)
         d = synth.decode_inputs(cfg, 0, 0, "cpu")
         q = d["q"].double().numpy()[0, : cfg.group]
         kn = oquant.bf16_bits(d["k_new"].float().numpy()[0, :1])
         vn = oquant.bf16_bits(d["v_new"].float().numpy()[0, :1])
-        reps, t_dec = 0, 0.0
-        while reps < 3 and t_dec + t_sel + t_q < budget_s:
-            t0 = time.perf_counter()
-            odecode.decode_step([c], q, kn, vn, cfg.residual, bits)
-            t_dec += time.perf_counter() - t0
-            reps += 1
-        t_dec /= reps
+        t_dec, reps, _ = _timed(lambda: odecode.decode_step([c], q, kn, vn, cfg.residual, bits), budget_s / 2,
+                                10000)
     torch.set_num_threads(os.cpu_count() or 1)
     L, B, Hkv = cfg.layers, cfg.batch, cfg.kv_heads
     step_s = t_dec * Hkv * L  # one decode step of one sequence, all layers and heads
@@ -126,9 +132,10 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=20.0):
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"layer 0, batch row 0, KV head 0 of {cfg.name}: select {t_sel:.2f}s, quantize {t_q:.2f}s, "
-                   f"decode step {t_dec:.2f}s ({reps} reps, {cfg.group} query heads); scaled by "
-                   f"{Hkv} KV heads x {L} layers per sequence-token"),
+        "sample": (f"layer 0, batch row 0, KV head 0 of {cfg.name} ({cfg.group} query heads), mean per call: "
+                   f"select {t_sel * 1e3:.3g} ms ({r_sel} reps), quantize {t_q * 1e3:.3g} ms ({r_q} reps), "
+                   f"decode step {t_dec * 1e3:.3g} ms ({reps} reps); scaled by {Hkv} KV heads x {L} layers "
+                   f"per sequence-token"),
         "select_quantize_ms_per_prompt": (t_sel + t_q) * Hkv * L * 1e3,
     }
 
