@@ -377,8 +377,11 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   // tile t (codes, meta) is consumed one iteration before its value part, so
   // its slot frees earlier.  A slot is refilled as soon as it frees, so key
   // loads lead their use by NK-1 whole iterations and value loads by NV-1.
-  constexpr int NK = (NWV == 8 && KS <= 4) ? 4 : 2;
-  constexpr int NV = (NWV == 8 && KS <= 4) ? 4 : 2;
+  // Each slot is a separate copy of the loop body (slots are compile-time), and
+  // a short run executes most of its code once: two slots beat four there
+  // (less code to fetch), and one slot exposes the load latency.
+  constexpr int NK = 2;
+  constexpr int NV = 2;
   constexpr int NPER = NK == NV ? NK : NK * NV;  // loop period (ring slots are compile-time)
   // Long runs stream each packed tile once; short runs share tiles between the
   // head workgroups of a unit through L2, so they keep the default policy.
