@@ -337,25 +337,6 @@ __device__ __forceinline__ int hist_split(int w, int NWT, int NTh, int nA, float
   return min(NTh, static_cast<int>(c + 0.5f));
 }
 
-// n / d and n % d for 0 <= n < 2^22, d >= 1, from rcp within a few ulps of 1/d:
-// the truncated float quotient is off by at most one, which the remainder test
-// corrects.
-struct QR {
-  int q, r;
-};
-__device__ __forceinline__ QR small_divmod(int n, int d, float rcp) {
-  int q = static_cast<int>(static_cast<float>(n) * rcp);
-  int r = n - q * d;
-  if (r < 0) {
-    --q;
-    r += d;
-  } else if (r >= d) {
-    ++q;
-    r -= d;
-  }
-  return QR{q, r};
-}
-
 // Resident workgroups per CU that the register budget allows (the occupancy
 // the planner assumes): 4-wave groups at up to 168 VGPRs fit three per CU.
 template <int BITS, int KS, int NWV, int HBS> constexpr int min_blocks() {

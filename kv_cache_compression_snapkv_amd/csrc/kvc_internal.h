@@ -20,6 +20,25 @@ inline bool dtype_ok(kvc_dtype d) { return d == KVC_F32 || d == KVC_BF16; }
 inline bool head_dim_ok(int D) { return D >= 32 && D <= 256 && D % 32 == 0; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// n / d and n % d for 0 <= n < 2^22, d >= 1, from rcp within a few ulps of 1/d:
+// the truncated float quotient is off by at most one, which the remainder test
+// corrects (cheaper than an integer division by a runtime divisor).
+struct QR {
+  int q, r;
+};
+__device__ __forceinline__ QR small_divmod(int n, int d, float rcp) {
+  int q = static_cast<int>(static_cast<float>(n) * rcp);
+  int r = n - q * d;
+  if (r < 0) {
+    --q;
+    r += d;
+  } else if (r >= d) {
+    ++q;
+    r -= d;
+  }
+  return QR{q, r};
+}
+
 // ---------------------------------------------------------------- number formats
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

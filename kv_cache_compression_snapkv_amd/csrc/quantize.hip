@@ -73,35 +73,61 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0
   const int tid = threadIdx.x;
   const float qmax = static_cast<float>((1 << BITS) - 1);
   const int ngv = D / kGroup;
-  // key groups: one channel over the 32 tokens
-  for (int c = tid; c < D; c += kThreads) {
-    float lo = as_f32(L.k[0][c]), hi = lo;
-    for (int t = 1; t < kGroup; ++t) {
-      lo = fminf(lo, as_f32(L.k[t][c]));
-      hi = fmaxf(hi, as_f32(L.k[t][c]));
-    }
-    const GroupQ g = make_group(lo, hi, qmax);
-    L.kq[c] = make_float2(g.z, g.inv);
-    k_meta[static_cast<size_t>(q0 / kGroup) * D + c] = g.meta;
-  }
-  // value groups: one token over 32 channels (a row segment)
-  for (int e = tid; e < kGroup * ngv; e += kThreads) {
-    const int t = e / ngv, j = e % ngv;
-    const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][j * kGroup]);
-    float lo = as_f32(L.v[t][j * kGroup]), hi = lo;  // the same fold as a walk from element 0
+  // Extremes are exact in any order, so the groups' walks are split over lanes
+  // and combined with lane shuffles; 2D and 64*ngv are multiples of 64, so
+  // every wave in these loops is whole.
+  // key groups: lanes 4p..4p+3 walk channels 2p, 2p+1 over the tokens of one
+  // residue mod 4 each; lane 4p+k (k = 0, 1) then makes channel 2p+k's group
+  for (int e = tid; e < 2 * D; e += kThreads) {
+    const int p = e >> 2, qt = e & 3;
+    float2 x = pair_f32(&L.k[qt][2 * p]);
+    float lo0 = x.x, hi0 = x.x, lo1 = x.y, hi1 = x.y;
 #pragma unroll
-    for (int p = 0; p < kGroup / VEC; ++p) {
-      float f[VEC];
-      unpack16(seg[p], f);
+    for (int i = 1; i < kGroup / 4; ++i) {
+      x = pair_f32(&L.k[qt + 4 * i][2 * p]);
+      lo0 = fminf(lo0, x.x);
+      hi0 = fmaxf(hi0, x.x);
+      lo1 = fminf(lo1, x.y);
+      hi1 = fmaxf(hi1, x.y);
+    }
+#pragma unroll
+    for (int o = 1; o <= 2; o <<= 1) {
+      lo0 = fminf(lo0, __shfl_xor(lo0, o));
+      hi0 = fmaxf(hi0, __shfl_xor(hi0, o));
+      lo1 = fminf(lo1, __shfl_xor(lo1, o));
+      hi1 = fmaxf(hi1, __shfl_xor(hi1, o));
+    }
+    if (qt < 2) {
+      const int c = 2 * p + qt;
+      const GroupQ g = make_group(qt ? lo1 : lo0, qt ? hi1 : hi0, qmax);
+      L.kq[c] = make_float2(g.z, g.inv);
+      k_meta[static_cast<size_t>(q0 / kGroup) * D + c] = g.meta;
+    }
+  }
+  // value groups: lane e walks half h of group j of token t (e = 64j + 32h + t);
+  // lanes e and e^32 combine and the h = 0 lane makes the group
+  for (int e = tid; e < 64 * ngv; e += kThreads) {
+    const int t = e & 31, j = e >> 6, h = (e >> 5) & 1;
+    const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][j * kGroup + 16 * h]);
+    float f[VEC];
+    unpack16(seg[0], f);
+    float lo = f[0], hi = f[0];
+#pragma unroll
+    for (int p = 0; p < 16 / VEC; ++p) {
+      if (p) unpack16(seg[p], f);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         lo = fminf(lo, f[i]);
         hi = fmaxf(hi, f[i]);
       }
     }
-    const GroupQ g = make_group(lo, hi, qmax);
-    L.vq[t][j] = make_float2(g.z, g.inv);
-    v_meta[static_cast<size_t>(q0 + t) * ngv + j] = g.meta;
+    lo = fminf(lo, __shfl_xor(lo, 32));
+    hi = fmaxf(hi, __shfl_xor(hi, 32));
+    if (h == 0) {
+      const GroupQ g = make_group(lo, hi, qmax);
+      L.vq[t][j] = make_float2(g.z, g.inv);
+      v_meta[static_cast<size_t>(q0 + t) * ngv + j] = g.meta;
+    }
   }
   __syncthreads();
   constexpr int per = 32 / BITS;
@@ -130,8 +156,10 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0
   // value words: word row r of channel c holds tokens r*per..; a thread takes
   // the channel pair c, c+1 (same group, same parameters)
   constexpr int rows = kGroup / per;  // value word rows per block
+  const float rcp_pairs = __builtin_amdgcn_rcpf(static_cast<float>(D / 2));
   for (int e = tid; e < rows * (D / 2); e += kThreads) {
-    const int r = e / (D / 2), c = (e % (D / 2)) * 2, j = c / kGroup;
+    const QR rc = small_divmod(e, D / 2, rcp_pairs);
+    const int r = rc.q, c = rc.r * 2, j = c / kGroup;
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) {
@@ -180,19 +208,23 @@ __device__ void stage_rows(QuantLds<T, DM>& L, const QuantArgs& a, int bj, int t
   const T* k = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
   const T* v = static_cast<const T*>(a.v) + static_cast<size_t>(bj) * a.n * D;
   const int tid = threadIdx.x;
-  int pos[MAXV];
+  const float rcp_ppr = __builtin_amdgcn_rcpf(static_cast<float>(ppr));
+  int pos[MAXV], tt[MAXV], cc[MAXV];  // piece e: row tt, element cc
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    const int e = tid + i * kThreads, t = e / ppr;
-    pos[i] = (e < total && t < count) ? kept_pos(a, bj, t_first + t) : 0;
+    const int e = tid + i * kThreads;
+    const QR rc = small_divmod(e, ppr, rcp_ppr);
+    tt[i] = rc.q;
+    cc[i] = rc.r * VEC;
+    pos[i] = (e < total && tt[i] < count) ? kept_pos(a, bj, t_first + tt[i]) : 0;
   }
   uint4 kv[MAXV], vv[MAXV];
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int e = tid + i * kThreads;
-    const size_t src = static_cast<size_t>(pos[i]) * D + (e % ppr) * VEC;
+    const size_t src = static_cast<size_t>(pos[i]) * D + cc[i];
     kv[i] = vv[i] = make_uint4(0, 0, 0, 0);
-    if (e < total && e / ppr < count) {
+    if (e < total && tt[i] < count) {
       kv[i] = *reinterpret_cast<const uint4*>(k + src);
       vv[i] = *reinterpret_cast<const uint4*>(v + src);
     }
@@ -201,9 +233,8 @@ __device__ void stage_rows(QuantLds<T, DM>& L, const QuantArgs& a, int bj, int t
   for (int i = 0; i < MAXV; ++i) {
     const int e = tid + i * kThreads;
     if (e < total) {
-      const int t = e / ppr, c = (e % ppr) * VEC;
-      *reinterpret_cast<uint4*>(&L.k[t][c]) = kv[i];
-      *reinterpret_cast<uint4*>(&L.v[t][c]) = vv[i];
+      *reinterpret_cast<uint4*>(&L.k[tt[i]][cc[i]]) = kv[i];
+      *reinterpret_cast<uint4*>(&L.v[tt[i]][cc[i]]) = vv[i];
     }
   }
 }
