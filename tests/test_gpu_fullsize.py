@@ -100,3 +100,39 @@ def test_fullsize_workload(name, bits, layer):
         gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[(b, j)], f"after decode b{b} j{j}")
     print(f"[fullsize] {name} layer {layer}: q_len {cache.q_len} r_len {cache.r_len}, {flushes} flushes, "
           f"worst normalized decode error {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name,layer", [("llama3_8b", 0), ("long_context", 0)])
+def test_fullsize_variance_budget_path(name, layer):
+    """Prompt compression of the variance budget policies at full size, in the
+    calls the benchmark makes for them: kvc_window_scores (raw window scores and
+    their variance per head), then kvc_topk at the layer's budget.  Every head:
+    the variance against the oracle's on the GPU's own scores, the pooled scores
+    and indices exact on those scores, and the same indices as kvc_select;
+    sampled heads: the raw scores against the oracle's window scores."""
+    gu.need_gpu()
+    import kv_cache_compression_snapkv_amd as kvc
+
+    cfg = synth.CONFIGS[name]
+    B, Hkv, D, n, W, G = cfg.batch, cfg.kv_heads, cfg.head_dim, cfg.prompt, cfg.window, cfg.group
+    budgets, _ = kvc.kvc_budget(cfg.layers, Hkv, D, n, W, cfg.decode_steps, cfg.budget, cfg.pyramid, cfg.beta,
+                                bits=cfg.bits[0], group=32, meta_bits=16, residual=cfg.residual)
+    kb = budgets[layer]
+    print(f"[fullsize] variance path {name} layer {layer} budget {kb}", flush=True)
+    p = synth.prompt_layer(cfg, layer, "cuda")
+    raw, var = kvc.kvc_window_scores(p["q_win"], p["k"], W)
+    idx, pooled = kvc.kvc_topk(raw, cfg.pool, kb, want_scores=True)
+    idx_fused = kvc.kvc_select(p["q_win"], p["k"], W, cfg.pool, kb)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_fused)
+    r, v, pc, ix = raw.cpu().numpy(), var.cpu().numpy(), pooled.cpu().numpy(), idx.cpu().numpy()
+    np.testing.assert_allclose(v, oselect.score_variance(r), rtol=1e-6)
+    np.testing.assert_array_equal(pc, oselect.max_pool(r.astype(np.float64), cfg.pool).astype(np.float32))
+    for b in range(B):
+        for j in range(Hkv):
+            np.testing.assert_array_equal(ix[b, j], oselect.top_k(pc[b, j], ix.shape[-1]), f"b{b} j{j}")
+    for b, j in _sampled_heads(cfg):
+        qw = gu.as_f32(p["q_win"][b:b + 1, j * G:(j + 1) * G])
+        kh = gu.as_f32(p["k"][b:b + 1, j:j + 1])
+        ref = oselect.window_scores(qw, kh, W)[0, 0]
+        np.testing.assert_array_less(np.abs(r[b, j] - ref), gu.SCORE_TOL * (np.abs(ref) + ref.max()) + 1e-30)
