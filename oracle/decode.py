@@ -15,8 +15,9 @@ def head_keys_values(cache, bits):
     bf16 residual follows, oldest first (MiniKV Alg. 1: concatenation of the
     dequantized history and the residual R_K, R_V).
     """
-    Kq = quant.unpack_keys(cache["k_codes"], cache["k_meta"], bits)
-    Vq = quant.unpack_values(cache["v_codes"], cache["v_meta"], bits)
+    g = cache.get("group", quant.GROUP)
+    Kq = quant.unpack_keys(cache["k_codes"], cache["k_meta"], bits, g)
+    Vq = quant.unpack_values(cache["v_codes"], cache["v_meta"], bits, g)
     Kr = quant.bf16_to_f32(cache["k_res"])
     Vr = quant.bf16_to_f32(cache["v_res"])
     K = np.concatenate([Kq, Kr], axis=0).astype(np.float64)

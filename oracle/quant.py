@@ -1,17 +1,19 @@
 """Oracle: group quantization, bit packing, the kept-cache builder and the
 residual flush.  Test infrastructure (see the package docstring).
 
-Cache layout (both sides use it, so "bit-exact packed codes" is well defined):
+Cache layout (both sides use it, so "bit-exact packed codes" is well defined),
+for a group size g (32 by default; MiniKV's own setting is 16):
   k_codes [Q][D*b/32] uint32  word w of token t: channel (32/b)*w+i at bits b*i
-  k_meta  [Q/32][D]   uint32  group g (tokens 32g..32g+31), channel c
+  k_meta  [Q/g][D]    uint32  group q (tokens gq..gq+g-1), channel c
   v_codes [Q*b/32][D] uint32  word row w, channel c: token (32/b)*w+i at bits b*i
-  v_meta  [Q][D/32]   uint32  token t, channel group j (channels 32j..32j+31)
+  v_meta  [Q][D/g]    uint32  token t, channel group j (channels gj..gj+g-1)
   meta word = fp16 scale bits | (fp16 zero bits << 16)
   k_res, v_res [r][D] uint16  bfloat16 bits, oldest token first
-Keys are grouped per channel over 32 tokens and values per token over 32
+Keys are grouped per channel over g tokens and values per token over g
 channels (blog, "Quantization: keep each token in fewer bits": KIVI's grouping;
-MiniKV Sec. 4.1).  Codes are packed LSB-first, 16 (2-bit) or 8 (4-bit) per
-32-bit word (MiniKV Sec. 4.4, INT2 quantization kernel).
+MiniKV Sec. 4.1, and Sec. 5.1 for its group size 16).  Codes are packed
+LSB-first, 16 (2-bit) or 8 (4-bit) per 32-bit word (MiniKV Sec. 4.4, INT2
+quantization kernel); the packing does not depend on g.
 """
 
 import numpy as np
@@ -43,9 +45,9 @@ def f16_to_f32(bits):
 
 # ---------------------------------------------------------------- groups
 def quantize_groups(X, bits):
-    """Asymmetric min/max quantization of groups of 32 float32 values.
+    """Asymmetric min/max quantization of groups of float32 values.
 
-    X: float32 [..., 32], one group per row of the last axis.
+    X: float32 [..., g], one group per row of the last axis (g = 32 or 16).
     Blog, "Measured on a real model", ``round_to``: lo/hi per group, step
     (hi-lo)/(2^b-1), codes round((x-lo)/step).  MiniKV Sec. 4.4: zero-point and
     scale are stored as FP16.  Reading fixed for bit-exactness: scale and zero
@@ -55,7 +57,7 @@ def quantize_groups(X, bits):
     codes 0.  Every arithmetic step is one IEEE float32 operation per element
     (numpy float32 array arithmetic), so rows are independent of each other.
 
-    Returns (scale_bits uint16 [...], zero_bits uint16 [...], codes uint32 [..., 32]).
+    Returns (scale_bits uint16 [...], zero_bits uint16 [...], codes uint32 [..., g]).
     """
     X = np.asarray(X, dtype=np.float32)
     qmax = np.float32(2 ** bits - 1)
@@ -75,7 +77,7 @@ def quantize_groups(X, bits):
 
 
 def quantize_group(x, bits):
-    """One group of 32 values (``quantize_groups`` on a single row)."""
+    """One group of values (``quantize_groups`` on a single row)."""
     s_bits, z_bits, codes = quantize_groups(np.asarray(x, dtype=np.float32)[None], bits)
     return s_bits[0], z_bits[0], codes[0]
 
@@ -112,43 +114,44 @@ def unpack_words(words, bits):
     return (np.asarray(words, dtype=np.uint32)[..., None] >> shifts) & np.uint32((1 << bits) - 1)
 
 
-def quantize_tokens(Kt, Vt, bits):
-    """Quantize a whole number of 32-token groups of kept keys/values.
+def quantize_tokens(Kt, Vt, bits, group=GROUP):
+    """Quantize a whole number of g-token groups of kept keys/values.
 
-    Kt, Vt: float32 [Q][D] (Q a multiple of 32).  Keys: one group per (32-token
-    block, channel); values: one group per (token, 32-channel block).
+    Kt, Vt: float32 [Q][D] (Q a multiple of g = group).  Keys: one group per
+    (g-token block, channel); values: one group per (token, g-channel block).
     Returns k_codes, k_meta, v_codes, v_meta in the layout of the module doc.
     """
     Q, D = Kt.shape
-    assert Q % GROUP == 0 and D % GROUP == 0
+    g = group
     per = 32 // bits
-    # keys: group (g, c) = Kt[32g:32g+32, c]
-    kg = np.ascontiguousarray(Kt.reshape(Q // GROUP, GROUP, D).transpose(0, 2, 1))  # [Q/32][D][32]
+    assert Q % g == 0 and D % g == 0 and Q % per == 0
+    # keys: group (q, c) = Kt[gq:gq+g, c]
+    kg = np.ascontiguousarray(Kt.reshape(Q // g, g, D).transpose(0, 2, 1))  # [Q/g][D][g]
     ks, kz, kcodes = quantize_groups(kg, bits)
-    k_meta = meta_word(ks, kz)                                        # [Q/32][D]
+    k_meta = meta_word(ks, kz)                                        # [Q/g][D]
     kc = kcodes.transpose(0, 2, 1).reshape(Q, D)                      # code of (token, channel)
-    # values: group (t, j) = Vt[t, 32j:32j+32]
-    vs, vz, vcodes = quantize_groups(Vt.reshape(Q, D // GROUP, GROUP), bits)
-    v_meta = meta_word(vs, vz)                                        # [Q][D/32]
+    # values: group (t, j) = Vt[t, gj:gj+g]
+    vs, vz, vcodes = quantize_groups(Vt.reshape(Q, D // g, g), bits)
+    v_meta = meta_word(vs, vz)                                        # [Q][D/g]
     vc = vcodes.reshape(Q, D)
     k_codes = pack_words(kc.reshape(Q, D // per, per), bits)          # channels of a token
     v_codes = pack_words(vc.reshape(Q // per, per, D).transpose(0, 2, 1), bits)  # tokens of a channel
     return k_codes, k_meta, v_codes, v_meta
 
 
-def unpack_keys(k_codes, k_meta, bits):
+def unpack_keys(k_codes, k_meta, bits, group=GROUP):
     """Dequantized keys float32 [Q][D] from the packed layout."""
     Q, nw = k_codes.shape
     codes = unpack_words(k_codes, bits).reshape(Q, nw * (32 // bits))  # [Q][D]
-    m = np.repeat(np.asarray(k_meta, dtype=np.uint32), GROUP, axis=0)  # meta of (t // 32, c)
+    m = np.repeat(np.asarray(k_meta, dtype=np.uint32), group, axis=0)  # meta of (t // g, c)
     return dequant(codes, (m & 0xFFFF).astype(np.uint16), (m >> 16).astype(np.uint16))
 
 
-def unpack_values(v_codes, v_meta, bits):
+def unpack_values(v_codes, v_meta, bits, group=GROUP):
     """Dequantized values float32 [Q][D] from the packed layout."""
     nrow, D = v_codes.shape
     codes = unpack_words(v_codes, bits).transpose(0, 2, 1).reshape(nrow * (32 // bits), D)  # [Q][D]
-    m = np.repeat(np.asarray(v_meta, dtype=np.uint32), GROUP, axis=1)      # meta of (t, c // 32)
+    m = np.repeat(np.asarray(v_meta, dtype=np.uint32), group, axis=1)      # meta of (t, c // g)
     return dequant(codes, (m & 0xFFFF).astype(np.uint16), (m >> 16).astype(np.uint16))
 
 
@@ -167,22 +170,22 @@ def kept_positions(n, W, idx_row):
     return np.concatenate([np.asarray(idx_row, dtype=np.int64), np.arange(n - W, n)])
 
 
-def build_head_cache(k_head, v_head, kept, residual, bits):
+def build_head_cache(k_head, v_head, kept, residual, bits, group=GROUP):
     """Prompt compression of one (batch, KV head): gather, quantize, residual.
 
     MiniKV Alg. 1 prefill (heavy hitters, then Quant); blog "Quantization":
     the most recent tokens stay in full precision until a group fills.  Reading:
-    Q = 32*floor(max(T-R,0)/32) oldest kept tokens are quantized, the last T-Q
-    (R <= T-Q < R+32 when T >= R) stay as bf16.
-    k_head, v_head: float32 [n][D].  Returns a dict.
+    Q = g*floor(max(T-R,0)/g) oldest kept tokens are quantized (g = group), the
+    last T-Q (R <= T-Q < R+g when T >= R) stay as bf16.
+    k_head, v_head: float32 [n][D].  Returns a dict (its "group" is g).
     """
     T = len(kept)
-    Q = GROUP * (max(T - residual, 0) // GROUP)
+    Q = group * (max(T - residual, 0) // group)
     Kk = k_head[kept].astype(np.float32)
     Vk = v_head[kept].astype(np.float32)
-    kc, km, vc, vm = quantize_tokens(Kk[:Q], Vk[:Q], bits)
+    kc, km, vc, vm = quantize_tokens(Kk[:Q], Vk[:Q], bits, group)
     return {
-        "q_len": Q, "r_len": T - Q,
+        "group": group, "q_len": Q, "r_len": T - Q,
         "k_codes": kc, "k_meta": km, "v_codes": vc, "v_meta": vm,
         "k_res": bf16_bits(Kk[Q:]), "v_res": bf16_bits(Vk[Q:]),
     }
@@ -193,24 +196,26 @@ def append_and_flush(cache, k_new_bits, v_new_bits, residual, bits):
 
     MiniKV Alg. 1 decoding: the new key/value join the fp residual; when it
     reaches its limit it is quantized and concatenated to the packed history.
-    Reading: the residual holds R..R+31 tokens; when an append makes it R+32 the
-    oldest 32 are quantized (the arithmetic of ``quantize_group``) and appended
-    as one group.  k_new_bits/v_new_bits: bf16 bits [D].  Returns a new dict.
+    Reading: the residual holds R..R+g-1 tokens (g = the cache's group); when an
+    append makes it R+g the oldest g are quantized (the arithmetic of
+    ``quantize_group``) and appended as one group.  k_new_bits/v_new_bits: bf16
+    bits [D].  Returns a new dict.
     """
+    g = cache.get("group", GROUP)
     c = dict(cache)
     c["k_res"] = np.concatenate([cache["k_res"], k_new_bits[None, :]], axis=0)
     c["v_res"] = np.concatenate([cache["v_res"], v_new_bits[None, :]], axis=0)
     c["r_len"] = cache["r_len"] + 1
-    if c["r_len"] == residual + GROUP:
-        Kf = bf16_to_f32(c["k_res"][:GROUP])
-        Vf = bf16_to_f32(c["v_res"][:GROUP])
-        kc, km, vc, vm = quantize_tokens(Kf, Vf, bits)
+    if c["r_len"] == residual + g:
+        Kf = bf16_to_f32(c["k_res"][:g])
+        Vf = bf16_to_f32(c["v_res"][:g])
+        kc, km, vc, vm = quantize_tokens(Kf, Vf, bits, g)
         c["k_codes"] = np.concatenate([cache["k_codes"], kc], axis=0)
         c["k_meta"] = np.concatenate([cache["k_meta"], km], axis=0)
         c["v_codes"] = np.concatenate([cache["v_codes"], vc], axis=0)
         c["v_meta"] = np.concatenate([cache["v_meta"], vm], axis=0)
-        c["k_res"] = c["k_res"][GROUP:]
-        c["v_res"] = c["v_res"][GROUP:]
-        c["q_len"] = cache["q_len"] + GROUP
-        c["r_len"] -= GROUP
+        c["k_res"] = c["k_res"][g:]
+        c["v_res"] = c["v_res"][g:]
+        c["q_len"] = cache["q_len"] + g
+        c["r_len"] -= g
     return c

@@ -35,15 +35,16 @@ def _sdpa(q, K, V):
     return o[:, 0, :].numpy()
 
 
+@pytest.mark.parametrize("group", [32, 16])
 @pytest.mark.parametrize("bits", [2, 4])
-def test_decode_matches_torch_sdpa(bits):
+def test_decode_matches_torch_sdpa(bits, group):
     n, D, Hkv, G, R = 150, 64, 2, 2, 16
     caches, Ks, Vs = [], [], []
     for j in range(Hkv):
         k, v = _head(j, n, D)
         kept = np.sort(np.random.default_rng(j).choice(n - 8, 70, replace=False))
         kept = np.concatenate([kept, np.arange(n - 8, n)])
-        caches.append(quant.build_head_cache(k, v, kept, R, bits))
+        caches.append(quant.build_head_cache(k, v, kept, R, bits, group))
     rng = np.random.default_rng(11)
     q = rng.standard_normal((Hkv * G, D))
     kn = quant.bf16_bits(rng.standard_normal((Hkv, D)).astype(np.float32))
@@ -102,22 +103,23 @@ def test_blog_masked_hook_semantics():
     np.testing.assert_allclose(decode.attend(q, K, V), ref.numpy(), rtol=1e-12)
 
 
+@pytest.mark.parametrize("group", [32, 16])
 @pytest.mark.parametrize("T,R,steps", [(72, 16, 70), (44, 128, 130), (300, 128, 40)])
-def test_incremental_flush_equals_batch_quantization(T, R, steps):
-    n, D, bits = T, 64, 2
+def test_incremental_flush_equals_batch_quantization(T, R, steps, group):
+    n, D, bits, g = T, 64, 2, group
     k, v = _head(T, n + steps, D)
-    c = quant.build_head_cache(k[:n], v[:n], np.arange(n), R, bits)
+    c = quant.build_head_cache(k[:n], v[:n], np.arange(n), R, bits, g)
     flushes = 0
     for s in range(steps):
         before = c["q_len"]
         c = quant.append_and_flush(c, quant.bf16_bits(k[n + s]), quant.bf16_bits(v[n + s]), R, bits)
         flushes += c["q_len"] != before
-        assert R <= c["r_len"] < R + 32 or (c["q_len"] == 0 and c["r_len"] < R + 32)
-    ref = quant.build_head_cache(k, v, np.arange(n + steps), R, bits)
+        assert R <= c["r_len"] < R + g or (c["q_len"] == 0 and c["r_len"] < R + g)
+    ref = quant.build_head_cache(k, v, np.arange(n + steps), R, bits, g)
     assert c["q_len"] == ref["q_len"] and c["r_len"] == ref["r_len"]
     for key in ("k_codes", "k_meta", "v_codes", "v_meta", "k_res", "v_res"):
         np.testing.assert_array_equal(c[key], ref[key])
-    assert flushes == (ref["q_len"] - quant.build_head_cache(k[:n], v[:n], np.arange(n), R, bits)["q_len"]) // 32
+    assert flushes == (ref["q_len"] - quant.build_head_cache(k[:n], v[:n], np.arange(n), R, bits, g)["q_len"]) // g
 
 
 def test_residual_split_rule():
@@ -128,3 +130,15 @@ def test_residual_split_rule():
         assert c["q_len"] == 32 * (max(T - R, 0) // 32)
     c = quant.build_head_cache(k, v, np.arange(72), 16, 2)
     assert (c["q_len"], c["r_len"]) == (32, 40)
+
+
+def test_residual_split_rule_group16():
+    """MiniKV's group of 16 (Sec. 5.1): Q = 16*floor(max(T-R,0)/16), so the
+    residual holds R..R+15 tokens."""
+    k, v = _head(0, 600, 32)
+    for T, R, want in [(72, 16, (48, 24)), (276, 128, (144, 132)), (44, 128, (0, 44)), (544, 128, (416, 128)),
+                       (16, 0, (16, 0)), (175, 128, (32, 143))]:
+        c = quant.build_head_cache(k, v, np.arange(T), R, 2, 16)
+        assert (c["q_len"], c["r_len"]) == want, (T, R)
+        assert c["k_meta"].shape == (want[0] // 16, 32) and c["v_meta"].shape == (want[0], 2)
+

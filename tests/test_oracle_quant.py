@@ -144,3 +144,43 @@ def test_bf16_rounding():
     got = quant.bf16_to_f32(quant.bf16_bits(x))
     ref = torch.tensor(x).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_group16_layout_through_packing(bits):
+    """Keys grouped per channel over 16 tokens and values per token over 16
+    channels (MiniKV's group size), read back through the packed layout: every
+    element is within half a step of its own 16-group's scale (plus the fp16
+    zero's rounding).  Blocks of 16 tokens and of 16 channels sit at offsets 0
+    and 100 alternately, so metadata indexed by 32-wide groups (or by the wrong
+    axis) would miss the bound by two orders of magnitude."""
+    rng = np.random.default_rng(5 + bits)
+    Q, D, g = 64, 64, 16
+    K = rng.standard_normal((Q, D)).astype(np.float32) + 100.0 * ((np.arange(Q) // g) % 2)[:, None]
+    V = rng.standard_normal((Q, D)).astype(np.float32) + 100.0 * ((np.arange(D) // g) % 2)[None, :]
+    kc, km, vc, vm = quant.quantize_tokens(K, V, bits, g)
+    assert km.shape == (Q // g, D) and vm.shape == (Q, D // g)
+    Kh = quant.unpack_keys(kc, km, bits, g)
+    Vh = quant.unpack_values(vc, vm, bits, g)
+    qmax = 2 ** bits - 1
+    for t in range(Q):
+        for c in range(D):
+            kb = K[g * (t // g):g * (t // g) + g, c]
+            vb = V[t, g * (c // g):g * (c // g) + g]
+            for x, xh, blk in ((K[t, c], Kh[t, c], kb), (V[t, c], Vh[t, c], vb)):
+                lo, hi = float(blk.min()), float(blk.max())
+                s = float(quant.f16_to_f32(quant.f16_bits((hi - lo) / qmax)))
+                z = float(quant.f16_to_f32(quant.f16_bits(lo)))
+                assert abs(float(x) - float(xh)) <= s * (0.5 + 2 ** -16) + abs(z - lo) + 1e-4 * max(abs(x), 1.0)
+
+
+def test_group16_integer_groups_exact():
+    """Integer-valued 16-groups quantize exactly (scale 1, zero the minimum)."""
+    K = np.tile(np.array([0, 1, 2, 3] * 4, np.float32)[:, None], (2, 32)) + np.repeat([0.0, 8.0], 16)[:, None]
+    V = np.tile(np.array([5, 6, 7, 8] * 4, np.float32)[None, :], (32, 2))
+    kc, km, vc, vm = quant.quantize_tokens(K.astype(np.float32), V.astype(np.float32), 2, 16)
+    np.testing.assert_array_equal(quant.unpack_keys(kc, km, 2, 16), K)
+    np.testing.assert_array_equal(quant.unpack_values(vc, vm, 2, 16), V)
+    assert set((km & 0xFFFF).ravel().tolist()) == {0x3C00} and set(((km >> 16) & 0xFFFF).ravel().tolist()) == {0, 0x4800}
+    assert set((vm & 0xFFFF).ravel().tolist()) == {0x3C00} and set((vm >> 16).ravel().tolist()) == {0x4500}
+
