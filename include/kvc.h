@@ -90,21 +90,26 @@ typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
  * is the state after the enqueued work completes (stream order). */
 typedef struct {
   int32_t batch, kv_heads, head_dim; /* B, Hkv, D                              */
-  int32_t bits;                      /* 2 or 4; group size is fixed at 32      */
+  int32_t bits;                      /* 2 or 4                                 */
   int32_t residual;                  /* R: recent tokens kept in bf16          */
-  int32_t q_cap, q_len;              /* packed history, tokens (multiples of 32)*/
-  int32_t r_cap, r_len;              /* bf16 residual, tokens; r_cap >= R + 32,
+  int32_t q_cap, q_len;              /* packed history, tokens: q_cap a multiple
+                                        of 32, q_len a multiple of the group   */
+  int32_t r_cap, r_len;              /* bf16 residual, tokens; r_cap >= R + g,
                                         r_cap a multiple of 8                  */
   int32_t r_start;                   /* ring row of the oldest residual token
                                         (a multiple of 8, < r_cap)             */
+  int32_t group;                     /* g, the quantization group: 32 (0 also
+                                        means 32) or 16 (MiniKV Sec. 5.1: keys
+                                        per channel over 16 tokens, values per
+                                        token over 16 channels)                */
   uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;
 } kvc_cache;
 
 /* Byte sizes of the six cache arrays for given capacities (host-only helper):
- * out[0..5] = k_codes, k_meta, v_codes, v_meta, k_res, v_res.
- * q_cap must be a multiple of 32. */
-kvc_status kvc_cache_sizes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t bits,
+ * out[0..5] = k_codes, k_meta, v_codes, v_meta, k_res, v_res; group as in
+ * kvc_cache (0, 16 or 32; else KVC_ERR_BITS).  q_cap must be a multiple of 32. */
+kvc_status kvc_cache_sizes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t bits, int32_t group,
                            int32_t q_cap, int32_t r_cap, size_t out[6]);
 
 /* ------------------------------------------------------------------ budget

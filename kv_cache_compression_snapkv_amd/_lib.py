@@ -31,6 +31,7 @@ class CacheStruct(ctypes.Structure):
                 ("bits", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("q_cap", ctypes.c_int32), ("q_len", ctypes.c_int32),
                 ("r_cap", ctypes.c_int32), ("r_len", ctypes.c_int32), ("r_start", ctypes.c_int32),
+                ("group", ctypes.c_int32),
                 ("k_codes", ctypes.c_void_p), ("k_meta", ctypes.c_void_p),
                 ("v_codes", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
                 ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p)]
@@ -63,7 +64,7 @@ def _load():
     lib.kvc_select_recent.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
     lib.kvc_quantize.argtypes = [P, P, I32, I32, P, I32, I32, ctypes.POINTER(CacheStruct), P]
     lib.kvc_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P, SZ, P]
-    lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_status_string.argtypes = [I32]
     lib.kvc_status_string.restype = ctypes.c_char_p
     for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
@@ -236,19 +237,19 @@ def kvc_select(q_win, k, W, pool, budget, want_scores=False, ws=None, idx=None, 
 class Cache:
     """One layer's compressed cache: caller-owned torch buffers + the C struct."""
 
-    def __init__(self, batch, kv_heads, head_dim, bits, residual, q_cap, r_cap=None, device="cuda"):
+    def __init__(self, batch, kv_heads, head_dim, bits, residual, q_cap, r_cap=None, device="cuda", group=32):
         if r_cap is None:
-            r_cap = residual + 32
+            r_cap = residual + group
         r_cap = 8 * ((r_cap + 7) // 8)
         q_cap = 32 * ((q_cap + 31) // 32)
         sizes = (ctypes.c_size_t * 6)()
-        _check("kvc_cache_sizes", lib.kvc_cache_sizes(batch, kv_heads, head_dim, bits, q_cap, r_cap, sizes))
+        _check("kvc_cache_sizes", lib.kvc_cache_sizes(batch, kv_heads, head_dim, bits, group, q_cap, r_cap, sizes))
         u32 = lambda nbytes: torch.zeros(max(nbytes // 4, 1), dtype=torch.int32, device=device)
         u16 = lambda nbytes: torch.zeros(max(nbytes // 2, 1), dtype=torch.int16, device=device)
         self.k_codes, self.k_meta = u32(sizes[0]), u32(sizes[1])
         self.v_codes, self.v_meta = u32(sizes[2]), u32(sizes[3])
         self.k_res, self.v_res = u16(sizes[4]), u16(sizes[5])
-        self.s = CacheStruct(batch, kv_heads, head_dim, bits, residual, q_cap, 0, r_cap, 0, 0,
+        self.s = CacheStruct(batch, kv_heads, head_dim, bits, residual, q_cap, 0, r_cap, 0, 0, group,
                              self.k_codes.data_ptr(), self.k_meta.data_ptr(), self.v_codes.data_ptr(),
                              self.v_meta.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr())
         self._ws = None
@@ -275,14 +276,14 @@ class Cache:
         """Logical views of the stored state (for tests): codes/meta/residual per (b, j)."""
         s = self.s
         B, H, D, b = s.batch, s.kv_heads, s.head_dim, s.bits
-        qc, rc = s.q_cap, s.r_cap
+        qc, rc, g = s.q_cap, s.r_cap, (s.group or 32)
         # residual ring rows, oldest first
         rows = (s.r_start + torch.arange(s.r_len, device=self.k_res.device)) % max(rc, 1)
         return {
             "k_codes": self.k_codes.view(B, H, qc, D * b // 32)[:, :, : s.q_len],
-            "k_meta": self.k_meta.view(B, H, qc // 32, D)[:, :, : s.q_len // 32],
+            "k_meta": self.k_meta.view(B, H, qc // g, D)[:, :, : s.q_len // g],
             "v_codes": self.v_codes.view(B, H, qc * b // 32, D)[:, :, : s.q_len * b // 32],
-            "v_meta": self.v_meta.view(B, H, qc, D // 32)[:, :, : s.q_len],
+            "v_meta": self.v_meta.view(B, H, qc, D // g)[:, :, : s.q_len],
             "k_res": self.k_res.view(B, H, rc, D).index_select(2, rows),
             "v_res": self.v_res.view(B, H, D, rc).index_select(3, rows).transpose(-1, -2),
         }

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvc.so")
-SOURCES = ["budget.cpp", "quantize.hip", "decode.hip", "select.hip"]
+SOURCES = ["budget.cpp", "quantize.hip", "decode.hip", "decode_g16.hip", "select.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

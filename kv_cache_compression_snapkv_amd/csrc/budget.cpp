@@ -39,18 +39,19 @@ extern "C" const char* kvc_status_string(kvc_status s) {
 }
 
 extern "C" kvc_status kvc_cache_sizes(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t bits,
-                                      int32_t q_cap, int32_t r_cap, size_t out[6]) {
+                                      int32_t group, int32_t q_cap, int32_t r_cap, size_t out[6]) {
   if (!out) return KVC_ERR_NULL;
-  if (bits != 2 && bits != 4) return KVC_ERR_BITS;
+  if ((bits != 2 && bits != 4) || !kvc::group_ok(group)) return KVC_ERR_BITS;
+  const size_t g = group == 0 ? kvc::kGroup : group;
   if (batch < 1 || kv_heads < 1 || !kvc::head_dim_ok(head_dim) || q_cap < 0 || r_cap < 0 ||
       q_cap % kvc::kGroup != 0)
     return KVC_ERR_SHAPE;
   const size_t bh = static_cast<size_t>(batch) * kv_heads;
   const size_t D = head_dim, qc = q_cap, rc = r_cap;
   out[0] = bh * qc * (D * bits / 32) * 4;  // k_codes
-  out[1] = bh * (qc / 32) * D * 4;         // k_meta
+  out[1] = bh * (qc / g) * D * 4;          // k_meta
   out[2] = bh * (qc * bits / 32) * D * 4;  // v_codes
-  out[3] = bh * qc * (D / 32) * 4;         // v_meta
+  out[3] = bh * qc * (D / g) * 4;          // v_meta
   out[4] = bh * rc * D * 2;                // k_res
   out[5] = bh * rc * D * 2;                // v_res
   return KVC_OK;

@@ -38,6 +38,8 @@ kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new
                         hipStream_t st);
 bool cache_ok(const kvc_cache* c);
 kvc_status cache_shape_status(const kvc_cache* c);
+kvc_status launch_decode_g16(const kvc_cache* c, const void* q, const void* k_new, const void* v_new, kvc_dtype dt,
+                             int Hq, int r_total, int r_new, float* out, hipStream_t st);
 
 namespace {
 
@@ -1337,9 +1339,10 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   if (!q || !k_new || !v_new || !out) return KVC_ERR_NULL;
   if (*ws_bytes < W.total) return KVC_ERR_WORKSPACE;
   const int R = cache->residual;
+  const int g = cache_group(cache);
   if (cache->r_len + 1 > cache->r_cap) return KVC_ERR_CAPACITY;
-  const bool flush = (cache->r_len + 1 == R + kGroup);
-  if (flush && cache->q_len + kGroup > cache->q_cap) return KVC_ERR_CAPACITY;
+  const bool flush = (cache->r_len + 1 == R + g);
+  if (flush && cache->q_len + g > cache->q_cap) return KVC_ERR_CAPACITY;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   DecArgs a;
@@ -1349,9 +1352,9 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   if (flush) {
     s = launch_flush(cache, k_new, v_new, dtype, st);
     if (s != KVC_OK) return s;
-    cache->q_len += kGroup;
+    cache->q_len += g;
     cache->r_len = R;
-    cache->r_start = (cache->r_start + kGroup) % cache->r_cap;
+    cache->r_start = (cache->r_start + g) % cache->r_cap;
     a.r_total = R;
     a.r_new = -1;
   } else {
@@ -1359,6 +1362,7 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
     a.r_total = cache->r_len + 1;
     cache->r_len += 1;
   }
+  if (g != kGroup) return launch_decode_g16(cache, q, k_new, v_new, dtype, Hq, a.r_total, a.r_new, out, st);
   a.k_codes = cache->k_codes;
   a.k_meta = cache->k_meta;
   a.v_codes = cache->v_codes;

@@ -1,0 +1,186 @@
+// Single-query decode attention over a cache quantized in groups of 16 (MiniKV
+// Sec. 5.1's group size; Alg. 1 decoding: one softmax over the dequantized
+// history followed by the bf16 residual, the appended token included).
+//
+// One workgroup per (query head, batch row).  Tokens are scored in chunks of
+// kChunk, one token per thread, with the history dequantized in float32 as
+// stored (zero + code * scale, each rounded); a running maximum and sum give one
+// online softmax over the chunks; the values are accumulated one channel per
+// thread.  This path is deliberately plain: with 16-token key groups every MFMA
+// column tile of the group-32 kernel would need its own scaled query operand,
+// so the group-16 layout gets a direct kernel of its own.
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kG16 = 16;
+constexpr int kChunk = 256;  // threads per workgroup = tokens per chunk; D <= 256 channels
+
+struct G16Args {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
+  uint16_t *k_res, *v_res;
+  float* out;
+  int Hq, Hkv, G, D, q_len, q_cap, r_total, r_new, r_start, r_cap;
+  float scale;  // 1/sqrt(D)
+};
+
+// Block-wide maximum / sum of one value per thread (every thread gets it).
+__device__ __forceinline__ float block_reduce(float x, float* sh, bool is_max) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float y = __shfl_xor(x, o);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w] = x;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kChunk / 64; ++i) r = is_max ? fmaxf(r, sh[i]) : r + sh[i];
+  __syncthreads();  // sh is reused by the next reduction
+  return r;
+}
+
+// Dequantized value of a code: zero + code * scale, in float32 (two roundings).
+__device__ __forceinline__ float dq(uint32_t code, uint32_t meta) {
+  return __fadd_rn(f16_bits_to_f32(meta >> 16), __fmul_rn(static_cast<float>(code), f16_bits_to_f32(meta & 0xFFFFu)));
+}
+
+template <typename T, int BITS>
+__global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
+  __shared__ float qs[256];
+  __shared__ float ps[kChunk];
+  __shared__ float red[kChunk / 64];
+  constexpr int per = 32 / BITS;  // codes per word
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int D = a.D;
+  const size_t bj = static_cast<size_t>(b) * a.Hkv + h / a.G;
+  const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.Hq + h) * D;
+  const T* knp = static_cast<const T*>(a.k_new) + bj * D;
+  const T* vnp = static_cast<const T*>(a.v_new) + bj * D;
+  if (tid < D) qs[tid] = load_f32(qp, tid);
+  __syncthreads();
+  const int nkw = D / per;   // key words per token
+  const int ngv = D / kG16;  // value groups per token
+  const uint32_t* kc = a.k_codes + bj * a.q_cap * nkw;
+  const uint32_t* km = a.k_meta + bj * (a.q_cap / kG16) * D;
+  const uint32_t* vc = a.v_codes + bj * (a.q_cap / per) * D;
+  const uint32_t* vm = a.v_meta + bj * a.q_cap * ngv;
+  const uint16_t* kr = a.k_res + bj * a.r_cap * D;  // [r_cap][D], token-major
+  const uint16_t* vr = a.v_res + bj * D * a.r_cap;  // [D][r_cap], channel-major
+  auto ring = [&](int t) {
+    const int p = a.r_start + t;
+    return p >= a.r_cap ? p - a.r_cap : p;
+  };
+  const int NT = a.q_len + a.r_total;  // tokens attended to
+  float m = -INFINITY, l = 0.0f, o = 0.0f;  // o: channel tid
+  for (int t0 = 0; t0 < NT; t0 += kChunk) {
+    const int t = t0 + tid;
+    float s = -INFINITY;
+    if (t < NT) {
+      float acc = 0.0f;
+      if (t < a.q_len) {
+        const uint32_t* kw = kc + static_cast<size_t>(t) * nkw;
+        const uint32_t* mrow = km + static_cast<size_t>(t / kG16) * D;
+        for (int w = 0; w < nkw; ++w) {
+          const uint32_t word = kw[w];
+#pragma unroll
+          for (int i = 0; i < per; ++i) {
+            const int c = w * per + i;
+            acc = fmaf(qs[c], dq((word >> (BITS * i)) & mask, mrow[c]), acc);
+          }
+        }
+      } else {
+        const int tr = t - a.q_len;
+        if (tr == a.r_new) {
+          for (int c = 0; c < D; ++c) acc = fmaf(qs[c], bf16_to_f32(f32_to_bf16(load_f32(knp, c))), acc);
+        } else {
+          const uint16_t* row = kr + static_cast<size_t>(ring(tr)) * D;
+          for (int c = 0; c < D; ++c) acc = fmaf(qs[c], bf16_to_f32(row[c]), acc);
+        }
+      }
+      s = acc * a.scale;
+    }
+    // every chunk holds a token (t0 < NT), so the maximum is finite
+    const float mn = fmaxf(m, block_reduce(s, red, true));
+    const float alpha = __expf(m - mn);  // 0 for the first chunk
+    const float p = t < NT ? __expf(s - mn) : 0.0f;
+    ps[tid] = p;
+    l = l * alpha + block_reduce(p, red, false);  // its barriers also publish ps
+    m = mn;
+    if (tid < D) {
+      const int c = tid;
+      float acc = o * alpha;
+      const int tn = min(kChunk, NT - t0);
+      for (int i = 0; i < tn; ++i) {
+        const int tt = t0 + i;
+        float vh;
+        if (tt < a.q_len) {
+          const uint32_t word = vc[static_cast<size_t>(tt / per) * D + c];
+          vh = dq((word >> (BITS * (tt % per))) & mask, vm[static_cast<size_t>(tt) * ngv + c / kG16]);
+        } else {
+          const int tr = tt - a.q_len;
+          vh = tr == a.r_new ? bf16_to_f32(f32_to_bf16(load_f32(vnp, c)))
+                             : bf16_to_f32(vr[static_cast<size_t>(c) * a.r_cap + ring(tr)]);
+        }
+        acc = fmaf(ps[i], vh, acc);
+      }
+      o = acc;
+    }
+    __syncthreads();  // ps is rewritten by the next chunk
+  }
+  if (tid < D) a.out[(static_cast<size_t>(b) * a.Hq + h) * D + tid] = o / l;
+  // the appended token joins the ring (written by the first query head of its
+  // KV head; no workgroup reads that row in this call)
+  if (a.r_new >= 0 && h % a.G == 0 && tid < D) {
+    const int p = ring(a.r_new);
+    a.k_res[(bj * a.r_cap + p) * D + tid] = f32_to_bf16(load_f32(knp, tid));
+    a.v_res[(bj * D + tid) * a.r_cap + p] = f32_to_bf16(load_f32(vnp, tid));
+  }
+}
+
+}  // namespace
+
+// Launch for a cache whose group is 16, after the host has appended the new
+// token (r_total, r_new as for the group-32 kernel: r_new = -1 after a flush).
+kvc_status launch_decode_g16(const kvc_cache* c, const void* q, const void* k_new, const void* v_new, kvc_dtype dt,
+                             int Hq, int r_total, int r_new, float* out, hipStream_t st) {
+  G16Args a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_codes = c->k_codes;
+  a.k_meta = c->k_meta;
+  a.v_codes = c->v_codes;
+  a.v_meta = c->v_meta;
+  a.k_res = c->k_res;
+  a.v_res = c->v_res;
+  a.out = out;
+  a.Hq = Hq;
+  a.Hkv = c->kv_heads;
+  a.G = Hq / c->kv_heads;
+  a.D = c->head_dim;
+  a.q_len = c->q_len;
+  a.q_cap = c->q_cap;
+  a.r_total = r_total;
+  a.r_new = r_new;
+  a.r_start = c->r_start;
+  a.r_cap = c->r_cap;
+  a.scale = 1.0f / sqrtf(static_cast<float>(c->head_dim));
+  const dim3 grid(Hq, c->batch);
+  if (dt == KVC_F32) {
+    if (c->bits == 2) hipLaunchKernelGGL((decode_g16_kernel<float, 2>), grid, dim3(kChunk), 0, st, a);
+    else hipLaunchKernelGGL((decode_g16_kernel<float, 4>), grid, dim3(kChunk), 0, st, a);
+  } else {
+    if (c->bits == 2) hipLaunchKernelGGL((decode_g16_kernel<uint16_t, 2>), grid, dim3(kChunk), 0, st, a);
+    else hipLaunchKernelGGL((decode_g16_kernel<uint16_t, 4>), grid, dim3(kChunk), 0, st, a);
+  }
+  return check_launch();
+}
+
+}  // namespace kvc

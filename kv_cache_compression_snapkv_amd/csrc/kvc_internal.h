@@ -9,7 +9,11 @@
 
 namespace kvc {
 
-constexpr int kGroup = 32;  // quantization group (tokens for keys, channels for values)
+constexpr int kGroup = 32;  // default quantization group (tokens for keys, channels for values)
+
+// The cache's group size: 32 (also for 0) or 16.
+inline bool group_ok(int g) { return g == 0 || g == 16 || g == 32; }
+inline int cache_group(const kvc_cache* c) { return c->group == 0 ? kGroup : c->group; }
 
 // ---------------------------------------------------------------- host side
 void set_last_hip_error(hipError_t e);

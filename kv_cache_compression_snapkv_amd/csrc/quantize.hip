@@ -6,7 +6,8 @@
 // Alg. 1 (prefill Quant; decoding flush of the streaming residual); blog
 // "Quantization" (KIVI grouping; recent tokens kept exact until a group fills).
 //
-// One workgroup owns one 32-token block of one (batch, KV head): the block's
+// One workgroup owns one G-token block of one (batch, KV head), G the group size
+// (32, or MiniKV's 16): the block's
 // gathered keys and values are staged in LDS (bfloat16 inputs as they are,
 // float32 inputs as float32; the layout is sized by a bound DM >= D so that
 // small heads take little LDS), the per-channel key
@@ -26,12 +27,12 @@ __device__ __forceinline__ float as_f32(uint16_t x) { return bf16_to_f32(x); }
 
 // S: staged element type, DM: head-dim bound.  Rows are 16 bytes longer than
 // DM elements (16-byte aligned rows; a column walk changes bank every row).
-template <typename S, int DM> struct QuantLds {
+template <typename S, int DM, int G> struct QuantLds {
   static constexpr int LD = DM + 16 / sizeof(S);
-  S k[kGroup][LD];
-  S v[kGroup][LD];
-  float2 kq[DM];                  // per key channel: (zero, 1/scale), 1/scale = 0 for a zero scale
-  float2 vq[kGroup][DM / kGroup];  // per value token group
+  S k[G][LD];
+  S v[G][LD];
+  float2 kq[DM];        // per key channel: (zero, 1/scale), 1/scale = 0 for a zero scale
+  float2 vq[G][DM / G];  // per value token group
 };
 
 // The 16 / sizeof(S) elements of a 16-byte LDS piece as float32.
@@ -63,19 +64,19 @@ __device__ __forceinline__ uint32_t code_q(float x, float2 q, float qmax) {
   return static_cast<uint32_t>(fminf(fmaxf(__builtin_rintf(t), 0.0f), qmax));
 }
 
-// Quantize the 32 tokens staged in L and write them at token offset q0 of the
+// Quantize the G tokens staged in L and write them at token offset q0 of the
 // (batch, KV head) slice whose base pointers are given.  Row segments and the
 // group parameters are read as 16-byte LDS vectors.
-template <int BITS, typename S, int DM>
-__device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0, uint32_t* k_codes, uint32_t* k_meta,
+template <int BITS, typename S, int DM, int G>
+__device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int q0, uint32_t* k_codes, uint32_t* k_meta,
                                uint32_t* v_codes, uint32_t* v_meta) {
   constexpr int VEC = 16 / sizeof(S);
   const int tid = threadIdx.x;
   const float qmax = static_cast<float>((1 << BITS) - 1);
-  const int ngv = D / kGroup;
+  const int ngv = D / G;
   // Extremes are exact in any order, so the groups' walks are split over lanes
-  // and combined with lane shuffles; 2D and 64*ngv are multiples of 64, so
-  // every wave in these loops is whole.
+  // and combined with lane shuffles; both loops run over 2D items, a multiple of
+  // 64, so every wave in them is whole.
   // key groups: lanes 4p..4p+3 walk channels 2p, 2p+1 over the tokens of one
   // residue mod 4 each; lane 4p+k (k = 0, 1) then makes channel 2p+k's group
   for (int e = tid; e < 2 * D; e += kThreads) {
@@ -83,7 +84,7 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0
     float2 x = pair_f32(&L.k[qt][2 * p]);
     float lo0 = x.x, hi0 = x.x, lo1 = x.y, hi1 = x.y;
 #pragma unroll
-    for (int i = 1; i < kGroup / 4; ++i) {
+    for (int i = 1; i < G / 4; ++i) {
       x = pair_f32(&L.k[qt + 4 * i][2 * p]);
       lo0 = fminf(lo0, x.x);
       hi0 = fmaxf(hi0, x.x);
@@ -101,19 +102,19 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0
       const int c = 2 * p + qt;
       const GroupQ g = make_group(qt ? lo1 : lo0, qt ? hi1 : hi0, qmax);
       L.kq[c] = make_float2(g.z, g.inv);
-      k_meta[static_cast<size_t>(q0 / kGroup) * D + c] = g.meta;
+      k_meta[static_cast<size_t>(q0 / G) * D + c] = g.meta;
     }
   }
-  // value groups: lane e walks half h of group j of token t (e = 64j + 32h + t);
-  // lanes e and e^32 combine and the h = 0 lane makes the group
-  for (int e = tid; e < 64 * ngv; e += kThreads) {
-    const int t = e & 31, j = e >> 6, h = (e >> 5) & 1;
-    const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][j * kGroup + 16 * h]);
+  // value groups: lane e walks half h of group j of token t (e = 2Gj + Gh + t);
+  // lanes e and e^G combine and the h = 0 lane makes the group
+  for (int e = tid; e < 2 * G * ngv; e += kThreads) {
+    const int t = e & (G - 1), j = e / (2 * G), h = (e / G) & 1;
+    const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][j * G + (G / 2) * h]);
     float f[VEC];
     unpack16(seg[0], f);
     float lo = f[0], hi = f[0];
 #pragma unroll
-    for (int p = 0; p < 16 / VEC; ++p) {
+    for (int p = 0; p < (G / 2) / VEC; ++p) {
       if (p) unpack16(seg[p], f);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
@@ -121,8 +122,8 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0
         hi = fmaxf(hi, f[i]);
       }
     }
-    lo = fminf(lo, __shfl_xor(lo, 32));
-    hi = fmaxf(hi, __shfl_xor(hi, 32));
+    lo = fminf(lo, __shfl_xor(lo, G));
+    hi = fmaxf(hi, __shfl_xor(hi, G));
     if (h == 0) {
       const GroupQ g = make_group(lo, hi, qmax);
       L.vq[t][j] = make_float2(g.z, g.inv);
@@ -134,8 +135,8 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0
   const int nw = D / per;  // key words per token
   // key words: word w of token t holds channels w*per.. of t; the lanes of a
   // wave share w (their parameter reads are broadcasts)
-  for (int e = tid; e < kGroup * nw; e += kThreads) {
-    const int w = e / kGroup, t = e % kGroup;
+  for (int e = tid; e < G * nw; e += kThreads) {
+    const int w = e / G, t = e % G;
     const uint4* xs = reinterpret_cast<const uint4*>(&L.k[t][w * per]);
     const uint4* qs = reinterpret_cast<const uint4*>(&L.kq[w * per]);
     uint32_t word = 0;
@@ -155,11 +156,11 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM>& L, int D, int q0
   }
   // value words: word row r of channel c holds tokens r*per..; a thread takes
   // the channel pair c, c+1 (same group, same parameters)
-  constexpr int rows = kGroup / per;  // value word rows per block
+  constexpr int rows = G / per;  // value word rows per block
   const float rcp_pairs = __builtin_amdgcn_rcpf(static_cast<float>(D / 2));
   for (int e = tid; e < rows * (D / 2); e += kThreads) {
     const QR rc = small_divmod(e, D / 2, rcp_pairs);
-    const int r = rc.q, c = rc.r * 2, j = c / kGroup;
+    const int r = rc.q, c = rc.r * 2, j = c / G;
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) {
@@ -197,14 +198,14 @@ __device__ __forceinline__ int kept_pos(const QuantArgs& a, int bj, int t) {
 }
 
 // Stage `count` kept tokens starting at kept index t_first (rows beyond count
-// are zero) as float32 rows of L.k / L.v.  Every 16-byte load of the 32 rows is
+// are zero) as float32 rows of L.k / L.v.  Every 16-byte load of the G rows is
 // issued before the first LDS store: one memory round trip for the positions,
 // one for the data.
-template <typename T, int DM>
-__device__ void stage_rows(QuantLds<T, DM>& L, const QuantArgs& a, int bj, int t_first, int count) {
+template <typename T, int DM, int G>
+__device__ void stage_rows(QuantLds<T, DM, G>& L, const QuantArgs& a, int bj, int t_first, int count) {
   constexpr int VEC = 16 / sizeof(T);                      // elements per 16 bytes
-  constexpr int MAXV = (kGroup * DM / VEC + kThreads - 1) / kThreads;  // pieces per thread at D = DM
-  const int D = a.D, ppr = D / VEC, total = kGroup * ppr;  // pieces per row, per tensor
+  constexpr int MAXV = (G * DM / VEC + kThreads - 1) / kThreads;  // pieces per thread at D = DM
+  const int D = a.D, ppr = D / VEC, total = G * ppr;       // pieces per row, per tensor
   const T* k = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
   const T* v = static_cast<const T*>(a.v) + static_cast<size_t>(bj) * a.n * D;
   const int tid = threadIdx.x;
@@ -239,28 +240,28 @@ __device__ void stage_rows(QuantLds<T, DM>& L, const QuantArgs& a, int bj, int t
   }
 }
 
-template <typename T, int BITS, int DM>
+template <typename T, int BITS, int DM, int G>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ __attribute__((aligned(16))) QuantLds<T, DM> L;
+  __shared__ __attribute__((aligned(16))) QuantLds<T, DM, G> L;
   const int blk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int bj = b * a.Hkv + j;
   const int D = a.D;
   const int tid = threadIdx.x;
-  const int nqb = a.Q / kGroup;
+  const int nqb = a.Q / G;
   if (blk < nqb) {
-    const int t0 = blk * kGroup;
-    stage_rows<T, DM>(L, a, bj, t0, kGroup);
+    const int t0 = blk * G;
+    stage_rows<T, DM, G>(L, a, bj, t0, G);
     __syncthreads();
     const size_t qc = a.q_cap;
     quantize_block<BITS>(L, D, t0, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
-                         a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D,
+                         a.k_meta + static_cast<size_t>(bj) * (qc / G) * D,
                          a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
-                         a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
+                         a.v_meta + static_cast<size_t>(bj) * qc * (D / G));
   } else {
     // residual: kept tokens [Q, T) -> bf16 ring rows 0..T-Q-1
-    const int r0 = (blk - nqb) * kGroup;
-    const int nr = min(kGroup, a.T - a.Q - r0);
-    stage_rows<T, DM>(L, a, bj, a.Q + r0, nr);
+    const int r0 = (blk - nqb) * G;
+    const int nr = min(G, a.T - a.Q - r0);
+    stage_rows<T, DM, G>(L, a, bj, a.Q + r0, nr);
     __syncthreads();
     uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
     uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
@@ -304,16 +305,16 @@ struct FlushArgs {
   uint16_t *k_res, *v_res;
 };
 
-// Decode-step flush: the residual ring held r_old = R+31 tokens; the new token
-// makes it R+32.  Quantize the oldest 32 (the new token is among them only when
+// Decode-step flush: the residual ring held r_old = R+G-1 tokens; the new token
+// makes it R+G.  Quantize the oldest G (the new token is among them only when
 // R == 0) and append them to the packed history at q_len; the new token takes
-// ring row r_start + r_old.  The host then advances r_start by 32.  Keys are
+// ring row r_start + r_old.  The host then advances r_start by G.  Keys are
 // staged with 16-byte row loads, values with 16-byte loads of 8 consecutive
 // ring rows of one channel (r_start and r_cap are multiples of 8, so such a
 // chunk never wraps).
-template <typename T, int BITS, int DM>
+template <typename T, int BITS, int DM, int G>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
-  __shared__ __attribute__((aligned(16))) QuantLds<uint16_t, DM> L;  // the ring holds bf16
+  __shared__ __attribute__((aligned(16))) QuantLds<uint16_t, DM, G> L;  // the ring holds bf16
   const int j = blockIdx.x, b = blockIdx.y;
   const int bj = b * a.Hkv + j;
   const int D = a.D;
@@ -327,12 +328,12 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     return p >= a.r_cap ? p - a.r_cap : p;
   };
   const int cpr = D / 8;  // 16-byte chunks per key row
-  for (int e = tid; e < kGroup * cpr; e += kThreads) {
+  for (int e = tid; e < G * cpr; e += kThreads) {
     const int t = e / cpr, c8 = (e % cpr) * 8;
     *reinterpret_cast<uint4*>(&L.k[t][c8]) = *reinterpret_cast<const uint4*>(kr + static_cast<size_t>(ring(t)) * D + c8);
   }
-  for (int e = tid; e < D * (kGroup / 8); e += kThreads) {
-    const int c = e / (kGroup / 8), t8 = (e % (kGroup / 8)) * 8;
+  for (int e = tid; e < D * (G / 8); e += kThreads) {
+    const int c = e / (G / 8), t8 = (e % (G / 8)) * 8;
     const uint4 w = *reinterpret_cast<const uint4*>(vr + static_cast<size_t>(c) * a.r_cap + ring(t8));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   // the new token: quantized with the group when R == 0, else kept in the ring
   for (int c = tid; c < D; c += kThreads) {
     const uint16_t kb = f32_to_bf16(load_f32(kn, c)), vb = f32_to_bf16(load_f32(vn, c));
-    if (a.r_old < kGroup) {
+    if (a.r_old < G) {
       L.k[a.r_old][c] = kb;
       L.v[a.r_old][c] = vb;
     } else {
@@ -357,27 +358,33 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   __syncthreads();
   const size_t qc = a.q_cap;
   quantize_block<BITS>(L, D, a.q_len, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
-                       a.k_meta + static_cast<size_t>(bj) * (qc / kGroup) * D,
+                       a.k_meta + static_cast<size_t>(bj) * (qc / G) * D,
                        a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
-                       a.v_meta + static_cast<size_t>(bj) * qc * (D / kGroup));
+                       a.v_meta + static_cast<size_t>(bj) * qc * (D / G));
 }
 
 // Head-dim bound of the LDS layout.
 int dm_for(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : 256; }
 
-template <typename T>
-kvc_status launch_quantize(const QuantArgs& a, int bits, int B, hipStream_t st) {
-  const int nblk = a.Q / kGroup + (a.T - a.Q + kGroup - 1) / kGroup;
-  if (nblk == 0) return KVC_OK;
-  dim3 grid(nblk, a.Hkv, B);
+template <typename T, int G>
+void launch_quantize_g(const QuantArgs& a, int bits, dim3 grid, hipStream_t st) {
   const int dm = dm_for(a.D);
-#define KVC_Q(B_, DM_) hipLaunchKernelGGL((quantize_kernel<T, B_, DM_>), grid, dim3(kThreads), 0, st, a)
+#define KVC_Q(B_, DM_) hipLaunchKernelGGL((quantize_kernel<T, B_, DM_, G>), grid, dim3(kThreads), 0, st, a)
   if (bits == 2) {
     if (dm == 64) KVC_Q(2, 64); else if (dm == 128) KVC_Q(2, 128); else KVC_Q(2, 256);
   } else {
     if (dm == 64) KVC_Q(4, 64); else if (dm == 128) KVC_Q(4, 128); else KVC_Q(4, 256);
   }
 #undef KVC_Q
+}
+
+template <typename T>
+kvc_status launch_quantize(const QuantArgs& a, int bits, int group, int B, hipStream_t st) {
+  const int nblk = a.Q / group + (a.T - a.Q + group - 1) / group;
+  if (nblk == 0) return KVC_OK;
+  dim3 grid(nblk, a.Hkv, B);
+  if (group == 16) launch_quantize_g<T, 16>(a, bits, grid, st);
+  else launch_quantize_g<T, kGroup>(a, bits, grid, st);
   return check_launch();
 }
 
@@ -404,11 +411,17 @@ kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new
   a.v_res = c->v_res;
   dim3 grid(c->kv_heads, c->batch);
   const int dm = dm_for(a.D);
-#define KVC_F(T_, B_)                                                                                        \
-  do {                                                                                                       \
-    if (dm == 64) hipLaunchKernelGGL((flush_kernel<T_, B_, 64>), grid, dim3(kThreads), 0, st, a);          \
-    else if (dm == 128) hipLaunchKernelGGL((flush_kernel<T_, B_, 128>), grid, dim3(kThreads), 0, st, a);   \
-    else hipLaunchKernelGGL((flush_kernel<T_, B_, 256>), grid, dim3(kThreads), 0, st, a);                  \
+  const bool g16 = cache_group(c) == 16;
+#define KVC_FG(T_, B_, G_)                                                                                     \
+  do {                                                                                                         \
+    if (dm == 64) hipLaunchKernelGGL((flush_kernel<T_, B_, 64, G_>), grid, dim3(kThreads), 0, st, a);        \
+    else if (dm == 128) hipLaunchKernelGGL((flush_kernel<T_, B_, 128, G_>), grid, dim3(kThreads), 0, st, a); \
+    else hipLaunchKernelGGL((flush_kernel<T_, B_, 256, G_>), grid, dim3(kThreads), 0, st, a);                \
+  } while (0)
+#define KVC_F(T_, B_)                     \
+  do {                                    \
+    if (g16) KVC_FG(T_, B_, 16);          \
+    else KVC_FG(T_, B_, kGroup);          \
   } while (0)
   if (dt == KVC_F32) {
     if (c->bits == 2) KVC_F(float, 2); else KVC_F(float, 4);
@@ -416,6 +429,7 @@ kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new
     if (c->bits == 2) KVC_F(uint16_t, 2); else KVC_F(uint16_t, 4);
   }
 #undef KVC_F
+#undef KVC_FG
   return check_launch();
 }
 
@@ -424,13 +438,14 @@ bool cache_ok(const kvc_cache* c) {
 }
 
 kvc_status cache_shape_status(const kvc_cache* c) {
-  if (c->bits != 2 && c->bits != 4) return KVC_ERR_BITS;
+  if ((c->bits != 2 && c->bits != 4) || !group_ok(c->group)) return KVC_ERR_BITS;
+  const int g = cache_group(c);
   if (c->batch < 1 || c->kv_heads < 1 || !head_dim_ok(c->head_dim) || c->residual < 0 ||
       c->q_cap < 0 || c->q_cap % kGroup != 0 || c->r_cap < 0 || c->r_cap % 8 != 0 || c->q_len < 0 || c->r_len < 0 ||
-      c->q_len % kGroup != 0)
+      c->q_len % g != 0)
     return KVC_ERR_SHAPE;
   if (c->r_start < 0 || c->r_start % 8 != 0 || (c->r_cap > 0 && c->r_start >= c->r_cap)) return KVC_ERR_SHAPE;
-  if (c->q_len > c->q_cap || c->r_len > c->r_cap || c->r_cap < c->residual + kGroup)
+  if (c->q_len > c->q_cap || c->r_len > c->r_cap || c->r_cap < c->residual + g)
     return KVC_ERR_CAPACITY;
   return KVC_OK;
 }
@@ -455,7 +470,8 @@ extern "C" kvc_status kvc_quantize(const void* k, const void* v, kvc_dtype dtype
   }
   if (cache->q_len != 0 || cache->r_len != 0) return KVC_ERR_CAPACITY;
   const int R = cache->residual;
-  const int Q = kGroup * (std::max(T - R, 0) / kGroup);
+  const int g = cache_group(cache);
+  const int Q = g * (std::max(T - R, 0) / g);
   if (Q > cache->q_cap || T - Q > cache->r_cap) return KVC_ERR_CAPACITY;
   QuantArgs a;
   a.k = k;
@@ -477,8 +493,8 @@ extern "C" kvc_status kvc_quantize(const void* k, const void* v, kvc_dtype dtype
   a.k_res = cache->k_res;
   a.v_res = cache->v_res;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  s = dtype == KVC_F32 ? launch_quantize<float>(a, cache->bits, cache->batch, st)
-                       : launch_quantize<uint16_t>(a, cache->bits, cache->batch, st);
+  s = dtype == KVC_F32 ? launch_quantize<float>(a, cache->bits, g, cache->batch, st)
+                       : launch_quantize<uint16_t>(a, cache->bits, g, cache->batch, st);
   if (s != KVC_OK) return s;
   cache->q_len = Q;
   cache->r_len = T - Q;

@@ -162,7 +162,7 @@ def test_select_validation_and_ws_query():
 
 def _cache(**kw):
     L = _lib()
-    c = L.CacheStruct(1, 4, 64, 2, 16, 64, 0, 48, 0, 0, 16, 16, 16, 16, 16, 16)
+    c = L.CacheStruct(1, 4, 64, 2, 16, 64, 0, 48, 0, 0, 0, 16, 16, 16, 16, 16, 16)
     for k, v in kw.items():
         setattr(c, k, v)
     return c
@@ -183,6 +183,10 @@ def test_quantize_and_decode_validation():
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_cap=52)), None) == 2    # r_cap % 8
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_start=4)), None) == 2   # ring start % 8
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(r_start=48)), None) == 2  # ring start >= r_cap
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(group=8)), None) == 4     # group not 16/32
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(group=16, r_cap=24)), None) == 5  # r_cap < R+16
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(group=16, q_len=16)), None) == 5  # not empty
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(q_len=16)), None) == 2    # q_len % 32
     d = L.lib.kvc_decode_attn
     need = ctypes.c_size_t(0)
     assert d(ctypes.byref(_cache()), None, None, None, 1, 4, None, None, ctypes.byref(need), None) == 0
@@ -201,12 +205,17 @@ def test_quantize_and_decode_validation():
 def test_cache_sizes():
     L = _lib()
     out = (ctypes.c_size_t * 6)()
-    assert L.lib.kvc_cache_sizes(2, 3, 128, 2, 64, 160, out) == 0
     bh = 6
-    assert list(out) == [bh * 64 * 8 * 4, bh * 2 * 128 * 4, bh * 4 * 128 * 4, bh * 64 * 4 * 4,
+    for g in (0, 32):
+        assert L.lib.kvc_cache_sizes(2, 3, 128, 2, g, 64, 160, out) == 0
+        assert list(out) == [bh * 64 * 8 * 4, bh * 2 * 128 * 4, bh * 4 * 128 * 4, bh * 64 * 4 * 4,
+                             bh * 160 * 128 * 2, bh * 160 * 128 * 2]
+    assert L.lib.kvc_cache_sizes(2, 3, 128, 4, 16, 64, 160, out) == 0
+    assert list(out) == [bh * 64 * 16 * 4, bh * 4 * 128 * 4, bh * 8 * 128 * 4, bh * 64 * 8 * 4,
                          bh * 160 * 128 * 2, bh * 160 * 128 * 2]
-    assert L.lib.kvc_cache_sizes(2, 3, 128, 3, 64, 160, out) == 4
-    assert L.lib.kvc_cache_sizes(2, 3, 128, 2, 65, 160, out) == 2
+    assert L.lib.kvc_cache_sizes(2, 3, 128, 3, 32, 64, 160, out) == 4
+    assert L.lib.kvc_cache_sizes(2, 3, 128, 2, 8, 64, 160, out) == 4
+    assert L.lib.kvc_cache_sizes(2, 3, 128, 2, 32, 65, 160, out) == 2
     assert L.lib.kvc_status_string(5).decode().startswith("cache capacity")
 
 

@@ -277,3 +277,68 @@ def test_recent_selection_end_to_end():
             gu.assert_decode_close(out[b], o_ref, f"step {s} b{b}")
             for j in range(Hkv):
                 gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[b][j], f"step {s} b{b} j{j}")
+
+
+# ---------------------------------------------------------------- group size 16
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("D,with_idx", [(64, True), (128, False), (256, True)])
+def test_quantize_parity_group16(dtype, bits, D, with_idx):
+    """MiniKV's group of 16 (keys per channel over 16 tokens, values per token
+    over 16 channels): packed codes, metadata and residual bit-exact against the
+    oracle, with and without a selection."""
+    kvc = _kvc()
+    B, Hkv, n, W, R = 2, 2, 300, 8, 16
+    k, v = _case(11, B, Hkv, n, D, dtype)
+    idx, k_sel = None, 0
+    if with_idx:
+        g = torch.Generator().manual_seed(12)
+        k_sel = 123
+        idx = torch.stack([torch.stack([torch.sort(torch.randperm(n - W, generator=g)[:k_sel]).values
+                                        for _ in range(Hkv)]) for _ in range(B)]).to(torch.int32).cuda()
+    T = k_sel + W if with_idx else n
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=T + 64, device="cuda", group=16)
+    kvc.kvc_quantize(k, v, cache, idx=idx, W=W)
+    torch.cuda.synchronize()
+    kf, vf = gu.as_f32(k), gu.as_f32(v)
+    for b in range(B):
+        for j in range(Hkv):
+            kept = oquant.kept_positions(n, W, idx[b, j].cpu().numpy() if with_idx else None)
+            ref = oquant.build_head_cache(kf[b, j], vf[b, j], kept, R, bits, 16)
+            gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref, f"b{b} j{j}")
+
+
+@pytest.mark.parametrize("dtype,bits,G,D,R,n", [
+    ("bf16", 2, 4, 128, 16, 300), ("bf16", 4, 2, 64, 0, 200), ("f32", 2, 1, 256, 24, 130),
+    ("bf16", 4, 8, 32, 40, 160), ("bf16", 2, 2, 128, 128, 700)])
+def test_decode_parity_group16_multi_step(dtype, bits, G, D, R, n):
+    """Decode over group-16 caches for 40 steps (several 16-token flushes, the
+    residual ring wrapping): outputs within the decode tolerance and the cache
+    bit-exact against the oracle stepping its own cache."""
+    kvc = _kvc()
+    B, Hkv, steps = 2, 2, 40
+    Hq = Hkv * G
+    k, v = _case(13, B, Hkv, n, D, dtype)
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=n + steps + 32, device="cuda", group=16)
+    kvc.kvc_quantize(k, v, cache)
+    kf, vf = gu.as_f32(k), gu.as_f32(v)
+    ref = [[oquant.build_head_cache(kf[b, j], vf[b, j], np.arange(n), R, bits, 16) for j in range(Hkv)]
+           for b in range(B)]
+    flushes = 0
+    for s in range(steps):
+        q = synth.random_tensor(400 + s, (B, Hq, D), dtype, tag="q").cuda()
+        kn = synth.random_tensor(500 + s, (B, Hkv, D), dtype, tag="kn").cuda()
+        vn = synth.random_tensor(600 + s, (B, Hkv, D), dtype, tag="vn").cuda()
+        ql = cache.q_len
+        out = kvc.kvc_decode_attn(cache, q, kn, vn).cpu().numpy()
+        flushes += cache.q_len != ql
+        qf = gu.as_f32(q).astype(np.float64)
+        knb, vnb = gu.bf16_bits(kn), gu.bf16_bits(vn)
+        for b in range(B):
+            o_ref, ref[b] = odecode.decode_step(ref[b], qf[b], knb[b], vnb[b], R, bits)
+            gu.assert_decode_close(out[b], o_ref, f"step {s} b{b}")
+    torch.cuda.synchronize()
+    for b in range(B):
+        for j in range(Hkv):
+            gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[b][j], f"after steps b{b} j{j}")
+    assert flushes >= 2
