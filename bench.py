@@ -47,15 +47,17 @@ def parse():
                     help="prompt selection: observation-window scores (kvc_select), or position-only with "
                          "kvc_select_recent: --sinks leading tokens plus the recent window, or the sliding window")
     ap.add_argument("--sinks", type=int, default=4)
+    ap.add_argument("--group", type=int, default=32, choices=(32, 16),
+                    help="quantization group: 32, or MiniKV's 16 (its own decode kernel)")
     a = ap.parse_args()
     if a.selector != "snapkv" and a.budget_policy != "workload":
         ap.error("--budget-policy var-prop/var-inv needs the window scores of --selector snapkv")
     return a
 
 
-def decode_call_bytes(B, Hq, Hkv, D, bits, q_len, r_total, in_bytes):
+def decode_call_bytes(B, Hq, Hkv, D, bits, q_len, r_total, in_bytes, group=32):
     """Algorithmic HBM bytes of one kvc_decode_attn call (one layer)."""
-    hist = q_len * D * bits // 8 * 2 + (q_len // 32) * D * 4 + q_len * (D // 32) * 4
+    hist = q_len * D * bits // 8 * 2 + (q_len // group) * D * 4 + q_len * (D // group) * 4
     resid = r_total * D * 2 * 2
     io = B * Hq * D * in_bytes + 2 * B * Hkv * D * in_bytes + B * Hq * D * 4 + 2 * B * Hkv * D * 2
     return B * Hkv * (hist + resid) + io
@@ -140,7 +142,7 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0):
     }
 
 
-def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", selector="snapkv", sinks=4):
+def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", selector="snapkv", sinks=4, group=32):
     """Time `steps` graph-replayed steps of the whole path on one workload.
 
     policy var-prop / var-inv: prompt compression runs kvc_window_scores for
@@ -158,7 +160,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     dev = "cuda"
     L, B, Hq, Hkv, D, n, W = cfg.layers, cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.prompt, cfg.window
     budgets, fp = kvc.kvc_budget(L, Hkv, D, n, W, cfg.decode_steps, cfg.budget, cfg.pyramid, cfg.beta,
-                                 bits=bits, group=32, meta_bits=16, residual=cfg.residual)
+                                 bits=bits, group=group, meta_bits=16, residual=cfg.residual)
     in_bytes = 4 if cfg.dtype == "f32" else 2
     if layers is not None:
         L = min(L, layers)
@@ -177,14 +179,15 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         score = [max(float(v.double().mean()), 1e-300) for v in lvars]
         weights = score if policy == "var-prop" else [1.0 / x for x in score]
         budgets, fp = kvc.kvc_budget_weighted(L, Hkv, D, n, W, cfg.decode_steps, cfg.budget, weights, bits=bits,
-                                              group=32, meta_bits=16, residual=cfg.residual)
+                                              group=group, meta_bits=16, residual=cfg.residual)
         tk_ws = torch.empty(max(kvc.topk_ws_bytes(B, Hkv, N, cfg.pool, b) for b in budgets), dtype=torch.uint8,
                             device=dev)
     dec = [[synth.decode_inputs(cfg, l, s, dev) for l in range(L)] for s in range(cfg.decode_steps)]
     caches, idxs = [], []
     for l in range(L):
         T = (budgets[l] + W) if cfg.budget >= 0 else n
-        caches.append(kvc.Cache(B, Hkv, D, bits, cfg.residual, q_cap=T + cfg.decode_steps + 32, device=dev))
+        caches.append(kvc.Cache(B, Hkv, D, bits, cfg.residual, q_cap=T + cfg.decode_steps + 32, device=dev,
+                                group=group))
         idxs.append(torch.empty(B, Hkv, budgets[l], dtype=torch.int32, device=dev) if cfg.budget >= 0 else None)
     sel_ws = torch.empty(max(kvc.select_ws_bytes(1 if in_bytes == 2 else 0, B, Hq, Hkv, n, D, W, cfg.pool, b)
                              for b in budgets) if cfg.budget >= 0 else 1, dtype=torch.uint8, device=dev)
@@ -219,7 +222,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
                 c, d = caches[l], dec[s][l]
                 kvc.kvc_decode_attn(c, d["q"], d["k_new"], d["v_new"], out=out, ws=dec_ws)
                 if nbytes is not None:
-                    nbytes.append(decode_call_bytes(B, Hq, Hkv, D, bits, c.q_len, c.r_len, in_bytes))
+                    nbytes.append(decode_call_bytes(B, Hq, Hkv, D, bits, c.q_len, c.r_len, in_bytes, group))
 
     # eager pass, then capture one step into two HIP graphs (prompt compression;
     # all decode steps of all layers) so the timed replays run without host gaps
@@ -263,15 +266,16 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     desc = (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
             f"prompt {n}, {cfg.dtype} inputs, W={W}, {sel}pool {cfg.pool}, budget "
             f"{'all' if cfg.budget < 0 else (policy + ' avg ' if varp else 'pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
-            f"{bits}-bit g32 fp16 scale/zero, residual {cfg.residual}, {cfg.decode_steps} decode steps")
+            f"{bits}-bit g{group} fp16 scale/zero, residual {cfg.residual}, {cfg.decode_steps} decode steps")
     res = {
         "desc": desc, "budgets": budgets, "footprint": fp,
         "tokens_per_s": B * cfg.decode_steps / (dec_ms * 1e-3),
         "step_ms": step_ms, "pre_ms": pre_ms, "dec_ms": dec_ms, "wall": wall,
         "roofline": {
-            "kernel": "decode_kernel (+ merge_kernel; flush_kernel on 1 step in 32), per kvc_decode_attn call",
+            "kernel": ("decode_kernel (+ merge_kernel; flush_kernel on 1 step in 32), per kvc_decode_attn call"
+                       if group == 32 else "decode_g16_kernel (flush_kernel on 1 step in 16), per kvc_decode_attn call"),
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(cfg.name, bits),
+            "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(cfg.name, bits) if group == 32 else None,
             "avg_call_us": dec_ms * 1e3 / ncalls, "algorithmic_bytes_per_call": sum(call_bytes) / ncalls,
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated), "
                             "profiles/decode_<workload>_<bits>bit_hbm_counters.md; null if decode.hip changed since",
@@ -295,7 +299,7 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     bits = args.bits or cfg.bits[0]
     r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers,
-            policy=args.budget_policy, selector=args.selector, sinks=args.sinks)
+            policy=args.budget_policy, selector=args.selector, sinks=args.sinks, group=args.group)
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s (% peak); select+quantize ms/prompt",
         "value": r["tokens_per_s"],
@@ -311,7 +315,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": r["desc"], "batch": cfg.batch, "prompt": cfg.prompt, "layers": cfg.layers,
                    "bits": bits, "decode_steps": cfg.decode_steps, "budget_policy": args.budget_policy,
-                   "selector": args.selector},
+                   "selector": args.selector, "group": args.group},
         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
         "decode_ms_per_token_all_layers": r["dec_ms"] / cfg.decode_steps,
         "decode_hbm_GBs": r["roofline"]["achieved"],

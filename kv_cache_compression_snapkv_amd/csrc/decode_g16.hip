@@ -55,6 +55,9 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
   __shared__ float qs[256];
   __shared__ float ps[kChunk];
   __shared__ float red[kChunk / 64];
+  __shared__ uint32_t kms[kChunk / kG16][256];        // key meta of the chunk's 16 groups
+  __shared__ uint32_t vcs[kChunk * BITS / 32][256];   // value code word rows of the chunk
+  __shared__ uint32_t vms[kChunk][256 / kG16];        // value meta of the chunk's tokens
   constexpr int per = 32 / BITS;  // codes per word
   constexpr uint32_t mask = (1u << BITS) - 1u;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -81,12 +84,26 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
   float m = -INFINITY, l = 0.0f, o = 0.0f;  // o: channel tid
   for (int t0 = 0; t0 < NT; t0 += kChunk) {
     const int t = t0 + tid;
+    // packed tokens of this chunk: [t0, t0 + np), whole groups (t0 and q_len are
+    // multiples of 16); their key meta, value code rows and value meta go to LDS
+    // with coalesced loads, all issued before the first use
+    const int np = max(0, min(kChunk, a.q_len - t0));
+    for (int e = tid; e < (np / kG16) * D; e += kChunk) {
+      const int gi = e / D, c = e - gi * D;
+      kms[gi][c] = km[static_cast<size_t>(t0 / kG16 + gi) * D + c];
+    }
+    for (int e = tid; e < (np / per) * D; e += kChunk) {
+      const int r = e / D, c = e - r * D;
+      vcs[r][c] = vc[static_cast<size_t>(t0 / per + r) * D + c];
+    }
+    for (int e = tid; e < np * ngv; e += kChunk) vms[e / ngv][e % ngv] = vm[static_cast<size_t>(t0) * ngv + e];
+    __syncthreads();
     float s = -INFINITY;
     if (t < NT) {
       float acc = 0.0f;
       if (t < a.q_len) {
         const uint32_t* kw = kc + static_cast<size_t>(t) * nkw;
-        const uint32_t* mrow = km + static_cast<size_t>(t / kG16) * D;
+        const uint32_t* mrow = kms[tid / kG16];
         for (int w = 0; w < nkw; ++w) {
           const uint32_t word = kw[w];
 #pragma unroll
@@ -117,18 +134,28 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
       const int c = tid;
       float acc = o * alpha;
       const int tn = min(kChunk, NT - t0);
-      for (int i = 0; i < tn; ++i) {
-        const int tt = t0 + i;
-        float vh;
-        if (tt < a.q_len) {
-          const uint32_t word = vc[static_cast<size_t>(tt / per) * D + c];
-          vh = dq((word >> (BITS * (tt % per))) & mask, vm[static_cast<size_t>(tt) * ngv + c / kG16]);
-        } else {
-          const int tr = tt - a.q_len;
-          vh = tr == a.r_new ? bf16_to_f32(f32_to_bf16(load_f32(vnp, c)))
-                             : bf16_to_f32(vr[static_cast<size_t>(c) * a.r_cap + ring(tr)]);
+      // packed tokens, from the staged rows
+      const int jc = c / kG16;
+      for (int i0 = 0; i0 < np; i0 += per) {
+        const uint32_t word = vcs[i0 / per][c];
+#pragma unroll
+        for (int u = 0; u < per; ++u)
+          acc = fmaf(ps[i0 + u], dq((word >> (BITS * u)) & mask, vms[i0 + u][jc]), acc);
+      }
+      // residual tokens, 8 loads in flight
+      for (int i0 = np; i0 < tn; i0 += 8) {
+        float vh[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int tr = t0 + i0 + u - a.q_len;
+          vh[u] = 0.0f;
+          if (i0 + u < tn)
+            vh[u] = tr == a.r_new ? bf16_to_f32(f32_to_bf16(load_f32(vnp, c)))
+                                  : bf16_to_f32(vr[static_cast<size_t>(c) * a.r_cap + ring(tr)]);
         }
-        acc = fmaf(ps[i], vh, acc);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u < tn) acc = fmaf(ps[i0 + u], vh[u], acc);
       }
       o = acc;
     }
