@@ -39,7 +39,8 @@ kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new
 bool cache_ok(const kvc_cache* c);
 kvc_status cache_shape_status(const kvc_cache* c);
 kvc_status launch_decode_g16(const kvc_cache* c, const void* q, const void* k_new, const void* v_new, kvc_dtype dt,
-                             int Hq, int r_total, int r_new, float* out, hipStream_t st);
+                             int Hq, int r_total, int r_new, float* out, void* ws, hipStream_t st);
+size_t g16_ws_bytes(const kvc_cache* c, int Hq);
 
 namespace {
 
@@ -1332,14 +1333,15 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   const Occupancy oc = occupancy(dtype, cache->bits, KS, G);
   if (oc.cus == 0) return KVC_ERR_HIP;
   const WsLayout W = ws_layout(cache, G, oc);
+  const int g = cache_group(cache);
+  const size_t need = g == kGroup ? W.total : std::max(W.total, g16_ws_bytes(cache, Hq));
   if (!ws) {
-    *ws_bytes = W.total;
+    *ws_bytes = need;
     return KVC_OK;
   }
   if (!q || !k_new || !v_new || !out) return KVC_ERR_NULL;
-  if (*ws_bytes < W.total) return KVC_ERR_WORKSPACE;
+  if (*ws_bytes < need) return KVC_ERR_WORKSPACE;
   const int R = cache->residual;
-  const int g = cache_group(cache);
   if (cache->r_len + 1 > cache->r_cap) return KVC_ERR_CAPACITY;
   const bool flush = (cache->r_len + 1 == R + g);
   if (flush && cache->q_len + g > cache->q_cap) return KVC_ERR_CAPACITY;
@@ -1362,7 +1364,7 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
     a.r_total = cache->r_len + 1;
     cache->r_len += 1;
   }
-  if (g != kGroup) return launch_decode_g16(cache, q, k_new, v_new, dtype, Hq, a.r_total, a.r_new, out, st);
+  if (g != kGroup) return launch_decode_g16(cache, q, k_new, v_new, dtype, Hq, a.r_total, a.r_new, out, ws, st);
   a.k_codes = cache->k_codes;
   a.k_meta = cache->k_meta;
   a.v_codes = cache->v_codes;

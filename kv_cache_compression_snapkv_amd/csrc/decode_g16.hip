@@ -2,13 +2,16 @@
 // Sec. 5.1's group size; Alg. 1 decoding: one softmax over the dequantized
 // history followed by the bf16 residual, the appended token included).
 //
-// One workgroup per (query head, batch row).  Tokens are scored in chunks of
+// One workgroup per (query head, batch row, split of the token range; the
+// splits' partial softmax states are merged by merge_g16_kernel).  Tokens are scored in chunks of
 // kChunk, one token per thread, with the history dequantized in float32 as
 // stored (zero + code * scale, each rounded); a running maximum and sum give one
 // online softmax over the chunks; the values are accumulated one channel per
 // thread.  This path is deliberately plain: with 16-token key groups every MFMA
 // column tile of the group-32 kernel would need its own scaled query operand,
 // so the group-16 layout gets a direct kernel of its own.
+#include <algorithm>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -24,8 +27,11 @@ struct G16Args {
   const uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;
   float* out;
+  float2* part_ml;  // [B][Hq][S] running (max, sum) of each split (S > 1)
+  float* part_o;    // [B][Hq][S][D] its unnormalized output
   int Hq, Hkv, G, D, q_len, q_cap, r_total, r_new, r_start, r_cap;
-  float scale;  // 1/sqrt(D)
+  int span;         // tokens per split, a multiple of kChunk
+  float scale;      // 1/sqrt(D)
 };
 
 // Block-wide maximum / sum of one value per thread (every thread gets it).
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
   __shared__ uint32_t vms[kChunk][256 / kG16];        // value meta of the chunk's tokens
   constexpr int per = 32 / BITS;  // codes per word
   constexpr uint32_t mask = (1u << BITS) - 1u;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y, sp = blockIdx.z, tid = threadIdx.x;
   const int D = a.D;
   const size_t bj = static_cast<size_t>(b) * a.Hkv + h / a.G;
   const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.Hq + h) * D;
@@ -80,9 +86,9 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
     const int p = a.r_start + t;
     return p >= a.r_cap ? p - a.r_cap : p;
   };
-  const int NT = a.q_len + a.r_total;  // tokens attended to
+  const int NT = min(a.q_len + a.r_total, (sp + 1) * a.span);  // end of this split's tokens
   float m = -INFINITY, l = 0.0f, o = 0.0f;  // o: channel tid
-  for (int t0 = 0; t0 < NT; t0 += kChunk) {
+  for (int t0 = sp * a.span; t0 < NT; t0 += kChunk) {
     const int t = t0 + tid;
     // packed tokens of this chunk: [t0, t0 + np), whole groups (t0 and q_len are
     // multiples of 16); their key meta, value code rows and value meta go to LDS
@@ -117,8 +123,16 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
         if (tr == a.r_new) {
           for (int c = 0; c < D; ++c) acc = fmaf(qs[c], bf16_to_f32(f32_to_bf16(load_f32(knp, c))), acc);
         } else {
-          const uint16_t* row = kr + static_cast<size_t>(ring(tr)) * D;
-          for (int c = 0; c < D; ++c) acc = fmaf(qs[c], bf16_to_f32(row[c]), acc);
+          const uint4* row = reinterpret_cast<const uint4*>(kr + static_cast<size_t>(ring(tr)) * D);
+          for (int c8 = 0; c8 < D / 8; ++c8) {
+            const uint4 w = row[c8];
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc = fmaf(qs[8 * c8 + 2 * i], __uint_as_float(u[i] << 16), acc);
+              acc = fmaf(qs[8 * c8 + 2 * i + 1], __uint_as_float(u[i] & 0xFFFF0000u), acc);
+            }
+          }
         }
       }
       s = acc * a.scale;
@@ -142,41 +156,81 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
         for (int u = 0; u < per; ++u)
           acc = fmaf(ps[i0 + u], dq((word >> (BITS * u)) & mask, vms[i0 + u][jc]), acc);
       }
-      // residual tokens, 8 loads in flight
+      // residual tokens, 8 at a time: the first is a multiple of 8 from the
+      // ring start (q_len and t0 are multiples of 16), and r_start and r_cap are
+      // multiples of 8, so the 8 ring rows of a channel are one 16-byte load
+      // (rows past the residual are read but not used)
+      const float vnew = bf16_to_f32(f32_to_bf16(load_f32(vnp, c)));
       for (int i0 = np; i0 < tn; i0 += 8) {
-        float vh[8];
+        const int tr0 = t0 + i0 - a.q_len;
+        const uint4 w = *reinterpret_cast<const uint4*>(vr + static_cast<size_t>(c) * a.r_cap + ring(tr0));
+        const uint32_t u4[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int tr = t0 + i0 + u - a.q_len;
-          vh[u] = 0.0f;
-          if (i0 + u < tn)
-            vh[u] = tr == a.r_new ? bf16_to_f32(f32_to_bf16(load_f32(vnp, c)))
-                                  : bf16_to_f32(vr[static_cast<size_t>(c) * a.r_cap + ring(tr)]);
+          const float x = (tr0 + u == a.r_new) ? vnew : __uint_as_float(u & 1 ? u4[u >> 1] & 0xFFFF0000u : u4[u >> 1] << 16);
+          if (i0 + u < tn) acc = fmaf(ps[i0 + u], x, acc);
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (i0 + u < tn) acc = fmaf(ps[i0 + u], vh[u], acc);
       }
       o = acc;
     }
     __syncthreads();  // ps is rewritten by the next chunk
   }
-  if (tid < D) a.out[(static_cast<size_t>(b) * a.Hq + h) * D + tid] = o / l;
-  // the appended token joins the ring (written by the first query head of its
-  // KV head; no workgroup reads that row in this call)
-  if (a.r_new >= 0 && h % a.G == 0 && tid < D) {
+  const size_t bh = static_cast<size_t>(b) * a.Hq + h;
+  if (gridDim.z == 1) {
+    if (tid < D) a.out[bh * D + tid] = o / l;
+  } else {
+    const size_t ps_i = bh * gridDim.z + sp;
+    if (tid < D) a.part_o[ps_i * D + tid] = o;
+    if (tid == 0) a.part_ml[ps_i] = make_float2(m, l);
+  }
+  // the appended token joins the ring (written by split 0 of the first query
+  // head of its KV head; no workgroup reads that row in this call)
+  if (a.r_new >= 0 && h % a.G == 0 && sp == 0 && tid < D) {
     const int p = ring(a.r_new);
     a.k_res[(bj * a.r_cap + p) * D + tid] = f32_to_bf16(load_f32(knp, tid));
     a.v_res[(bj * D + tid) * a.r_cap + p] = f32_to_bf16(load_f32(vnp, tid));
   }
 }
 
+// The S splits of (b, h) merged: with M = max_s m_s, out = sum_s e^(m_s - M) o_s
+// / sum_s e^(m_s - M) l_s (every split holds at least one token).
+__global__ __launch_bounds__(kChunk) void merge_g16_kernel(const float2* part_ml, const float* part_o, float* out,
+                                                           int Hq, int D, int S) {
+  const size_t bh = static_cast<size_t>(blockIdx.y) * Hq + blockIdx.x;
+  const int c = threadIdx.x;
+  if (c >= D) return;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[bh * S + s].x);
+  float L = 0.0f, acc = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float2 ml = part_ml[bh * S + s];
+    const float w = __expf(ml.x - M);
+    L += w * ml.y;
+    acc += w * part_o[(bh * S + s) * D + c];
+  }
+  out[bh * D + c] = acc / L;
+}
+
 }  // namespace
+
+// Splits of the token range for a call: enough workgroups to fill the GPU
+// (about 2048), at least one chunk each.  Bounded by the capacities so that the
+// workspace query and the call agree.
+int g16_splits(int B, int Hq, int tokens) {
+  const int chunks = std::max(1, (tokens + kChunk - 1) / kChunk);
+  return std::max(1, std::min(chunks, (2048 + B * Hq - 1) / (B * Hq)));
+}
+size_t g16_ws_bytes(const kvc_cache* c, int Hq) {
+  const int S = g16_splits(c->batch, Hq, c->q_cap + c->r_cap);
+  if (S == 1) return 0;
+  const size_t n = static_cast<size_t>(c->batch) * Hq * S;
+  return align_up(n * sizeof(float2), 256) + n * c->head_dim * sizeof(float);
+}
 
 // Launch for a cache whose group is 16, after the host has appended the new
 // token (r_total, r_new as for the group-32 kernel: r_new = -1 after a flush).
 kvc_status launch_decode_g16(const kvc_cache* c, const void* q, const void* k_new, const void* v_new, kvc_dtype dt,
-                             int Hq, int r_total, int r_new, float* out, hipStream_t st) {
+                             int Hq, int r_total, int r_new, float* out, void* ws, hipStream_t st) {
   G16Args a;
   a.q = q;
   a.k_new = k_new;
@@ -199,7 +253,17 @@ kvc_status launch_decode_g16(const kvc_cache* c, const void* q, const void* k_ne
   a.r_start = c->r_start;
   a.r_cap = c->r_cap;
   a.scale = 1.0f / sqrtf(static_cast<float>(c->head_dim));
-  const dim3 grid(Hq, c->batch);
+  // splits: at most the capacity-bound count (the workspace is sized for it),
+  // trimmed so that none is empty
+  const int NT = c->q_len + r_total;
+  const int smax = g16_splits(c->batch, Hq, c->q_cap + c->r_cap);
+  int S = std::min(smax, g16_splits(c->batch, Hq, NT));
+  a.span = kChunk * (((NT + S - 1) / S + kChunk - 1) / kChunk);
+  S = (NT + a.span - 1) / a.span;
+  const size_t n = static_cast<size_t>(c->batch) * Hq * smax;
+  a.part_ml = static_cast<float2*>(ws);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(n * sizeof(float2), 256));
+  const dim3 grid(Hq, c->batch, S);
   if (dt == KVC_F32) {
     if (c->bits == 2) hipLaunchKernelGGL((decode_g16_kernel<float, 2>), grid, dim3(kChunk), 0, st, a);
     else hipLaunchKernelGGL((decode_g16_kernel<float, 4>), grid, dim3(kChunk), 0, st, a);
@@ -207,6 +271,10 @@ kvc_status launch_decode_g16(const kvc_cache* c, const void* q, const void* k_ne
     if (c->bits == 2) hipLaunchKernelGGL((decode_g16_kernel<uint16_t, 2>), grid, dim3(kChunk), 0, st, a);
     else hipLaunchKernelGGL((decode_g16_kernel<uint16_t, 4>), grid, dim3(kChunk), 0, st, a);
   }
+  kvc_status s = check_launch();
+  if (s != KVC_OK || S == 1) return s;
+  hipLaunchKernelGGL(merge_g16_kernel, dim3(Hq, c->batch), dim3(kChunk), 0, st, a.part_ml, a.part_o, out, Hq,
+                     c->head_dim, S);
   return check_launch();
 }
 
