@@ -291,8 +291,8 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by (batch, KV head); see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the path shards by "
+              "(batch, KV head), so each GPU would run the same kernels on its own heads)", file=sys.stderr)
         sys.exit(2)
     import synth
 

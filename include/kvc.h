@@ -6,7 +6,7 @@
  *                   every earlier prompt position, the scores are max-pooled and
  *                   the top-k positions per KV head are kept.
  *   kvc_quantize    KIVI/MiniKV group quantization of the kept tokens (keys per
- *                   channel, values per token, group 32, 2 or 4 bits, fp16
+ *                   channel, values per token, groups of g = 32 or 16, 2 or 4 bits, fp16
  *                   scale and zero-point) into a packed cache plus a bf16
  *                   residual of the most recent tokens.
  *   kvc_decode_attn one decode step: append the new token, flush a full group of
@@ -46,19 +46,19 @@
  * Cache layout (one layer; C-contiguous, capacities are the strides):
  *   k_codes [B][Hkv][q_cap][D*bits/32]  uint32: word w of token t holds
  *                                       channel (32/bits)*w+i at bits bits*i
- *   k_meta  [B][Hkv][q_cap/32][D]       uint32: group g = tokens 32g..32g+31,
- *                                       channel c
+ *   k_meta  [B][Hkv][q_cap/g][D]        uint32: group q = tokens gq..gq+g-1,
+ *                                       channel c (g = the cache's group)
  *   v_codes [B][Hkv][q_cap*bits/32][D]  uint32: word row w, channel c holds
  *                                       token (32/bits)*w+i at bits bits*i
- *   v_meta  [B][Hkv][q_cap][D/32]       uint32: token t, channels 32j..32j+31
+ *   v_meta  [B][Hkv][q_cap][D/g]        uint32: token t, channels gj..gj+g-1
  *   meta word = fp16 scale bits | (fp16 zero-point bits << 16)
  *   k_res [B][Hkv][r_cap][D]            uint16 bfloat16 keys, token-major
  *   v_res [B][Hkv][D][r_cap]            uint16 bfloat16 values, channel-major
  *                                       (a decode step reads 8 consecutive
  *                                       tokens of one channel per load)
  *   The residual is a ring: its i-th oldest token (i < r_len) is row
- *   (r_start + i) % r_cap of every (b, head).  A flush quantizes the 32 oldest
- *   and advances r_start by 32, so no residual data is ever moved.
+ *   (r_start + i) % r_cap of every (b, head).  A flush quantizes the g oldest
+ *   and advances r_start by g, so no residual data is ever moved.
  * Codes are LSB-first (MiniKV Sec. 4.4: 16 INT2 values shifted into one INT32).
  * Dequantized value = zero + code * scale.
  */
@@ -231,8 +231,8 @@ kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32
  * "Quantization": keys per channel, values per token, recent tokens in full
  * precision until a group fills).  The kept tokens of each (b, KV head) are
  * idx[b][j][0..k_sel) followed by the window n-W..n-1 (T = k_sel + W), or all n
- * prompt tokens when idx == NULL (T = n).  The oldest Q = 32*floor(max(T-R,0)/32)
- * are quantized: per group of 32 values, lo/hi -> scale = fp16((hi-lo)/(2^b-1)),
+ * prompt tokens when idx == NULL (T = n).  The oldest Q = g*floor(max(T-R,0)/g)
+ * are quantized: per group of g values, lo/hi -> scale = fp16((hi-lo)/(2^b-1)),
  * zero = fp16(lo), code = clamp(rint((x - zero) * (1/scale)), 0, 2^b-1) in IEEE
  * float32 (scale 0 -> codes 0); the last T-Q go to the residual as bf16.
  *   k, v [B][Hkv][n][D] dtype; idx [B][Hkv][k_sel] int32 (ascending, < n-W) or
@@ -241,22 +241,24 @@ kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32
  *   cache->r_start = 0.
  * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_BITS, KVC_ERR_SHAPE,
  *   KVC_ERR_CAPACITY (cache not empty, Q > q_cap, T-Q > r_cap or
- *   r_cap < R+32), KVC_ERR_HIP. */
+ *   r_cap < R+g), KVC_ERR_HIP.  KVC_ERR_BITS also for a group not in {0, 16, 32}. */
 kvc_status kvc_quantize(const void *k, const void *v, kvc_dtype dtype, int32_t n, const int32_t *idx,
                         int32_t k_sel, int32_t W, kvc_cache *cache, void *stream);
 
 /* ------------------------------------------------------------------ decode
  * One decode step (MiniKV Eq. 1 and Alg. 1 decoding; blog attention hook):
  * k_new/v_new are appended to the bf16 residual; if the residual then holds
- * R+32 tokens its oldest 32 are quantized (same arithmetic as kvc_quantize)
+ * R+g tokens its oldest g are quantized (same arithmetic as kvc_quantize)
  * and appended to the packed history; then for every query head h (KV head
  * h / (Hq/Hkv)) out = softmax(q K^T / sqrt(D)) V over the q_len dequantized
  * history tokens and the r_len residual tokens, one softmax over both.
  *   q [B][Hq][D], k_new, v_new [B][Hkv][D] in dtype; out [B][Hq][D] float32.
+ * Group-32 caches run the MFMA kernel; group-16 caches a direct kernel whose
+ *   token range is split over workgroups and merged.
  * Workspace: *ws_bytes (ws == NULL query) is sized for q_len == q_cap, so one
  *   buffer serves every step of this cache.
  * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_BITS, KVC_ERR_SHAPE,
- *   KVC_ERR_CAPACITY (r_len+1 > r_cap, or a flush with q_len+32 > q_cap),
+ *   KVC_ERR_CAPACITY (r_len+1 > r_cap, or a flush with q_len+g > q_cap),
  *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
 kvc_status kvc_decode_attn(kvc_cache *cache, const void *q, const void *k_new, const void *v_new,
                            kvc_dtype dtype, int32_t Hq, float *out, void *ws, size_t *ws_bytes,
