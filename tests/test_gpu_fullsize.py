@@ -26,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     ("llama3_8b", 2, 0),
+    ("llama3_8b", 2, 0, 16),   # MiniKV's group size
     ("mistral_pyramid", 2, 0),
     ("mistral_pyramid", 2, 31),
     ("llama2_13b_mha", 4, 0),
@@ -39,8 +40,10 @@ def _sampled_heads(cfg):
     return sorted({(0, 0), (cfg.batch - 1, cfg.kv_heads - 1)})
 
 
-@pytest.mark.parametrize("name,bits,layer", CASES)
-def test_fullsize_workload(name, bits, layer):
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fullsize_workload(case):
+    name, bits, layer = case[:3]
+    group = case[3] if len(case) > 3 else 32
     gu.need_gpu()
     import kv_cache_compression_snapkv_amd as kvc
 
@@ -50,7 +53,7 @@ def test_fullsize_workload(name, bits, layer):
     budgets, _ = kvc.kvc_budget(cfg.layers, Hkv, D, n, W, cfg.decode_steps, cfg.budget, cfg.pyramid, cfg.beta,
                                 bits=bits, group=32, meta_bits=16, residual=R)
     kb = budgets[layer]
-    print(f"[fullsize] {name} layer {layer} bits {bits} budget {kb}", flush=True)
+    print(f"[fullsize] {name} layer {layer} bits {bits} group {group} budget {kb}", flush=True)
     p = synth.prompt_layer(cfg, layer, "cuda")
     heads = _sampled_heads(cfg)
 
@@ -71,13 +74,13 @@ def test_fullsize_workload(name, bits, layer):
 
     # ---- quantization, in the benchmark's capacities
     T = kb + W if cfg.budget >= 0 else n
-    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=T + cfg.decode_steps + 32, device="cuda")
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=T + cfg.decode_steps + 32, device="cuda", group=group)
     kvc.kvc_quantize(p["k"], p["v"], cache, idx=idx, W=W)
     torch.cuda.synchronize()
     ref = {}
     for b, j in heads:
         kept = oquant.kept_positions(n, W, idx[b, j].cpu().numpy() if idx is not None else None)
-        ref[(b, j)] = oquant.build_head_cache(gu.as_f32(p["k"][b, j]), gu.as_f32(p["v"][b, j]), kept, R, bits)
+        ref[(b, j)] = oquant.build_head_cache(gu.as_f32(p["k"][b, j]), gu.as_f32(p["v"][b, j]), kept, R, bits, group)
         gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[(b, j)], f"prefill b{b} j{j}")
     del p
 

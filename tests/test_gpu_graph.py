@@ -12,7 +12,8 @@ import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_equal_eager():
+@pytest.mark.parametrize("group", [32, 16])
+def test_graph_replays_equal_eager(group):
     gu.need_gpu()
     import kv_cache_compression_snapkv_amd as kvc
 
@@ -26,7 +27,7 @@ def test_graph_replays_equal_eager():
     T = budget + W
 
     def make_cache():
-        return kvc.Cache(B, Hkv, D, bits, R, q_cap=T + steps + 32, device="cuda")
+        return kvc.Cache(B, Hkv, D, bits, R, q_cap=T + steps + 32, device="cuda", group=group)
 
     sel_ws = torch.empty(kvc.select_ws_bytes(1, B, Hq, Hkv, n, D, W, pool, budget), dtype=torch.uint8,
                          device="cuda")
@@ -45,7 +46,7 @@ def test_graph_replays_equal_eager():
     outs0 = [torch.empty(B, Hq, D, dtype=torch.float32, device="cuda") for _ in range(steps)]
     run(c0, idx0, ws0, outs0)
     torch.cuda.synchronize()
-    assert c0.q_len > 32 * ((T - R) // 32), "the run must include a flush"
+    assert c0.q_len > group * ((T - R) // group), "the run must include a flush"
     ref = [o.clone() for o in outs0]
     ref_cache = {key: t.clone() for key, t in c0.views().items()}
 
