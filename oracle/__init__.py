@@ -9,13 +9,14 @@ method's arithmetic.
 
 Sources (cited by page title and section in each function):
   * "KV Cache Compression: Eviction and Quantization" (blog): the budget
-    script and table, the ``round_to`` quantizer, the ``attention()`` hook.
+    script and table, the eviction rules (sliding window, attention sinks), the
+    ``round_to`` quantizer, the ``attention()`` hook.
   * "PyramidKV: Dynamic KV Cache Compression based on Pyramidal Information
     Funneling": budget allocation and SnapKV-style selection.
   * "MiniKV: Pushing the Limits of LLM Inference via 2-Bit Layer-Discriminative
-    KV Cache": problem statement (Eq. 1, Def. 2.1), the pyramid policy (Sec. 4.2),
-    the INT2 kernels and streaming residual (Sec. 4.4), Algorithm 1, the KV-size
-    analysis.
+    KV Cache": problem statement (Eq. 1, Def. 2.1), the pyramid and variance
+    policies (Sec. 4.2), the INT2 kernels and streaming residual (Sec. 4.4),
+    Algorithm 1, the group size of Sec. 5.1, the KV-size analysis.
   * "CSKV: Training-Efficient Channel Shrinking for KV Cache in Long-Context
     Scenarios": the footprint claim of the introduction.
 
@@ -27,11 +28,14 @@ Parity status of each function (pins live in ``tests/test_oracle_*.py``):
   budget.*            pinned (blog table, MiniKV example, CSKV/PyramidKV claims,
                       pyramid invariants, weighted-budget closed forms)
   select.*            pinned (torch softmax/max_pool1d, brute force, invariants,
-                      variance closed forms)
+                      variance closed forms; recent_select: the blog's sink/window
+                      configurations, PyramidKV's split, a top-k route)
   quant.*             pinned (error bound, exact-nearest brute force, integer
-                      groups, blog round_to, pack round trip)
+                      groups, blog round_to, pack round trip; group 16: layout
+                      through packing, integer groups, residual closed forms)
   decode.*            pinned (torch SDPA, dense special case, convex hull, blog
-                      attention hook semantics, incremental flush == batch)
+                      attention hook semantics, incremental flush == batch, at
+                      groups 32 and 16)
 """
 
 from . import budget, select, quant, decode  # noqa: F401
