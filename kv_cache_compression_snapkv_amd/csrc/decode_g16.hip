@@ -87,7 +87,11 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
     return p >= a.r_cap ? p - a.r_cap : p;
   };
   const int NT = min(a.q_len + a.r_total, (sp + 1) * a.span);  // end of this split's tokens
-  float m = -INFINITY, l = 0.0f, o = 0.0f;  // o: channel tid
+  // values: tpc threads per channel, each with its own share of the tokens and
+  // its own partial output (all scaled alike), summed at the end
+  const int tpc = kChunk / D;  // >= 1 (D <= 256)
+  const int c = tid % D, part = tid / D;
+  float m = -INFINITY, l = 0.0f, o = 0.0f;  // o: this thread's part of channel c
   for (int t0 = sp * a.span; t0 < NT; t0 += kChunk) {
     const int t = t0 + tid;
     // packed tokens of this chunk: [t0, t0 + np), whole groups (t0 and q_len are
@@ -144,13 +148,12 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
     ps[tid] = p;
     l = l * alpha + block_reduce(p, red, false);  // its barriers also publish ps
     m = mn;
-    if (tid < D) {
-      const int c = tid;
+    if (part < tpc) {
       float acc = o * alpha;
       const int tn = min(kChunk, NT - t0);
-      // packed tokens, from the staged rows
+      // packed tokens, from the staged rows (words part, part + tpc, ...)
       const int jc = c / kG16;
-      for (int i0 = 0; i0 < np; i0 += per) {
+      for (int i0 = part * per; i0 < np; i0 += tpc * per) {
         const uint32_t word = vcs[i0 / per][c];
 #pragma unroll
         for (int u = 0; u < per; ++u)
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
       // multiples of 8, so the 8 ring rows of a channel are one 16-byte load
       // (rows past the residual are read but not used)
       const float vnew = bf16_to_f32(f32_to_bf16(load_f32(vnp, c)));
-      for (int i0 = np; i0 < tn; i0 += 8) {
+      for (int i0 = np + 8 * part; i0 < tn; i0 += 8 * tpc) {
         const int tr0 = t0 + i0 - a.q_len;
         const uint4 w = *reinterpret_cast<const uint4*>(vr + static_cast<size_t>(c) * a.r_cap + ring(tr0));
         const uint32_t u4[4] = {w.x, w.y, w.z, w.w};
@@ -174,6 +177,13 @@ __global__ __launch_bounds__(kChunk) void decode_g16_kernel(G16Args a) {
       o = acc;
     }
     __syncthreads();  // ps is rewritten by the next chunk
+  }
+  // sum the parts of each channel (ps is free after the last chunk's barrier)
+  if (part < tpc) ps[part * D + c] = o;
+  __syncthreads();
+  if (tid < D) {
+    o = 0.0f;
+    for (int p2 = 0; p2 < tpc; ++p2) o += ps[p2 * D + tid];
   }
   const size_t bh = static_cast<size_t>(b) * a.Hq + h;
   if (gridDim.z == 1) {
