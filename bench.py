@@ -92,7 +92,7 @@ def _timed(fn, share_s, max_reps):
     return t / reps, reps, out
 
 
-def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0):
+def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32):
     """The oracle, as it stands, on a bounded sample of the same workload: one
     (batch row, KV head) of layer 0, each stage repeated until its share of
     budget_s (selection 1/4, quantization 1/4, one decode step 1/2) is spent."""
@@ -118,7 +118,7 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0):
             kept = oquant.kept_positions(n, W, idx[0, 0])
         else:
             t_sel, r_sel, kept = 0.0, 0, np.arange(n)
-        t_q, r_q, c = _timed(lambda: oquant.build_head_cache(kf[0, 0], vf[0, 0], kept, cfg.residual, bits),
+        t_q, r_q, c = _timed(lambda: oquant.build_head_cache(kf[0, 0], vf[0, 0], kept, cfg.residual, bits, group),
                              budget_s / 4, 1000)
         d = synth.decode_inputs(cfg, 0, 0, "cpu")
         q = d["q"].double().numpy()[0, : cfg.group]
@@ -334,7 +334,7 @@ def main():
                                       "quantize_ms_per_prompt": h["pre_ms"] / hc.batch, "steps": 2, "warmup": 1,
                                       "roofline": h["roofline"]})
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"])
+        res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"], group=args.group)
     print(json.dumps(res))
 
 
