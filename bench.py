@@ -47,6 +47,9 @@ def parse():
                     help="prompt selection: observation-window scores (kvc_select), or position-only with "
                          "kvc_select_recent: --sinks leading tokens plus the recent window, or the sliding window")
     ap.add_argument("--sinks", type=int, default=4)
+    ap.add_argument("--streams", type=int, default=1,
+                    help="prompt compression runs the layers round-robin on this many streams (they are "
+                         "independent); decode stays on one stream, layer after layer")
     ap.add_argument("--group", type=int, default=32, choices=(32, 16),
                     help="quantization group: 32, or MiniKV's 16 (its own decode kernel)")
     a = ap.parse_args()
@@ -142,7 +145,8 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32):
     }
 
 
-def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", selector="snapkv", sinks=4, group=32):
+def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", selector="snapkv", sinks=4, group=32,
+        streams=1):
     """Time `steps` graph-replayed steps of the whole path on one workload.
 
     policy var-prop / var-inv: prompt compression runs kvc_window_scores for
@@ -194,27 +198,56 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     dec_ws = torch.zeros(max(kvc.decode_ws_bytes(c, Hq) for c in caches), dtype=torch.uint8, device=dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    # prompt compression: the layers are independent, so they run round-robin on
+    # side streams (default priority), each stream with its own workspaces
+    ns = max(1, streams)
+    side = [torch.cuda.Stream(device=dev) for _ in range(ns)] if ns > 1 else []
+    sel_wss = [sel_ws] + [torch.empty_like(sel_ws) for _ in range(ns - 1)]
+    if varp:
+        sc_wss = [sc_ws] + [torch.empty_like(sc_ws) for _ in range(ns - 1)]
+        tk_wss = [tk_ws] + [torch.empty_like(tk_ws) for _ in range(ns - 1)]
+
+    def on_streams(work):
+        """work(l, k) for every layer l, on side stream k = l % ns (forked from
+        and joined back to the current stream, also under graph capture)."""
+        if not side:
+            for l in range(L):
+                work(l, 0)
+            return
+        cur = torch.cuda.current_stream()
+        for sd in side:
+            sd.wait_stream(cur)
+        for l in range(L):
+            with torch.cuda.stream(side[l % ns]):
+                work(l, l % ns)
+        for sd in side:
+            cur.wait_stream(sd)
 
     def prefill():
         for c in caches:
             c.reset()
         if varp:
-            for l in range(L):
-                kvc.kvc_window_scores(prompts[l]["q_win"], prompts[l]["k"], W, ws=sc_ws, raw=raws[l], var=lvars[l])
-            for l in range(L):
-                kvc.kvc_topk(raws[l], cfg.pool, budgets[l], ws=tk_ws, idx=idxs[l])
+            # the same layer -> stream mapping orders each layer's scores before its top-k
+            on_streams(lambda l, k: kvc.kvc_window_scores(prompts[l]["q_win"], prompts[l]["k"], W, ws=sc_wss[k],
+                                                          raw=raws[l], var=lvars[l]))
+
+            def top_quant(l, k):
+                kvc.kvc_topk(raws[l], cfg.pool, budgets[l], ws=tk_wss[k], idx=idxs[l])
                 kvc.kvc_quantize(prompts[l]["k"], prompts[l]["v"], caches[l], idx=idxs[l], W=W)
+            on_streams(top_quant)
             return
-        for l in range(L):
+
+        def one(l, k):
             p = prompts[l]
             if cfg.budget >= 0 and selector != "snapkv":
                 kvc.kvc_select_recent(B, Hkv, n, W, budgets[l], sinks if selector == "sinks" else 0, idx=idxs[l])
                 kvc.kvc_quantize(p["k"], p["v"], caches[l], idx=idxs[l], W=W)
             elif cfg.budget >= 0:
-                kvc.kvc_select(p["q_win"], p["k"], W, cfg.pool, budgets[l], ws=sel_ws, idx=idxs[l])
+                kvc.kvc_select(p["q_win"], p["k"], W, cfg.pool, budgets[l], ws=sel_wss[k], idx=idxs[l])
                 kvc.kvc_quantize(p["k"], p["v"], caches[l], idx=idxs[l], W=W)
             else:
                 kvc.kvc_quantize(p["k"], p["v"], caches[l])
+        on_streams(one)
 
     def decode_all(nbytes=None):
         for s in range(cfg.decode_steps):
@@ -281,9 +314,9 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
                             "profiles/decode_<workload>_<bits>bit_hbm_counters.md; null if decode.hip changed since",
         },
     }
-    del prompts, dec, caches, idxs, sel_ws, dec_ws, g_pre, g_dec
+    del prompts, dec, caches, idxs, sel_ws, sel_wss, dec_ws, g_pre, g_dec, side
     if varp:
-        del raws, lvars, sc_ws, tk_ws
+        del raws, lvars, sc_ws, tk_ws, sc_wss, tk_wss
     torch.cuda.empty_cache()
     return res
 
@@ -299,7 +332,8 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     bits = args.bits or cfg.bits[0]
     r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers,
-            policy=args.budget_policy, selector=args.selector, sinks=args.sinks, group=args.group)
+            policy=args.budget_policy, selector=args.selector, sinks=args.sinks, group=args.group,
+            streams=args.streams)
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s (% peak); select+quantize ms/prompt",
         "value": r["tokens_per_s"],
@@ -315,7 +349,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": r["desc"], "batch": cfg.batch, "prompt": cfg.prompt, "layers": cfg.layers,
                    "bits": bits, "decode_steps": cfg.decode_steps, "budget_policy": args.budget_policy,
-                   "selector": args.selector, "group": args.group},
+                   "selector": args.selector, "group": args.group, "prefill_streams": args.streams},
         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
         "decode_ms_per_token_all_layers": r["dec_ms"] / cfg.decode_steps,
         "decode_hbm_GBs": r["roofline"]["achieved"],
