@@ -230,3 +230,13 @@ def test_select_recent_validation():
     assert f(1, 2, 100, 8, 10, 4, None, None) == 1       # idx NULL with k' > 0
     assert f(1, 2, 100, 8, 0, 4, None, None) == 0        # k' == 0: nothing to write
     assert f(1, 2, 100, 100, 10, 4, None, None) == 0     # no candidates
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; --gpus N > 1 exits non-zero with a message
+    (before anything touches a GPU)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
