@@ -170,22 +170,24 @@ def kept_positions(n, W, idx_row):
     return np.concatenate([np.asarray(idx_row, dtype=np.int64), np.arange(n - W, n)])
 
 
-def build_head_cache(k_head, v_head, kept, residual, bits, group=GROUP):
+def build_head_cache(k_head, v_head, kept, residual, bits, group=GROUP, flush_all=False):
     """Prompt compression of one (batch, KV head): gather, quantize, residual.
 
     MiniKV Alg. 1 prefill (heavy hitters, then Quant); blog "Quantization":
     the most recent tokens stay in full precision until a group fills.  Reading:
     Q = g*floor(max(T-R,0)/g) oldest kept tokens are quantized (g = group), the
-    last T-Q (R <= T-Q < R+g when T >= R) stay as bf16.
+    last T-Q (R <= T-Q < R+g when T >= R) stay as bf16.  With flush_all (MiniKV
+    Alg. 1 as printed: the prefill quantizes the kept cache, the residual only
+    collects decoded tokens) Q = g*floor(T/g), so fewer than g tokens remain.
     k_head, v_head: float32 [n][D].  Returns a dict (its "group" is g).
     """
     T = len(kept)
-    Q = group * (max(T - residual, 0) // group)
+    Q = group * (T // group) if flush_all else group * (max(T - residual, 0) // group)
     Kk = k_head[kept].astype(np.float32)
     Vk = v_head[kept].astype(np.float32)
     kc, km, vc, vm = quantize_tokens(Kk[:Q], Vk[:Q], bits, group)
     return {
-        "group": group, "q_len": Q, "r_len": T - Q,
+        "group": group, "flush_all": flush_all, "q_len": Q, "r_len": T - Q,
         "k_codes": kc, "k_meta": km, "v_codes": vc, "v_meta": vm,
         "k_res": bf16_bits(Kk[Q:]), "v_res": bf16_bits(Vk[Q:]),
     }
@@ -198,11 +200,30 @@ def append_and_flush(cache, k_new_bits, v_new_bits, residual, bits):
     reaches its limit it is quantized and concatenated to the packed history.
     Reading: the residual holds R..R+g-1 tokens (g = the cache's group); when an
     append makes it R+g the oldest g are quantized (the arithmetic of
-    ``quantize_group``) and appended as one group.  k_new_bits/v_new_bits: bf16
-    bits [D].  Returns a new dict.
+    ``quantize_group``) and appended as one group.  With the cache's flush_all
+    (MiniKV Alg. 1 as printed) the residual is instead quantized whole, in
+    groups of g, when it reaches R tokens.  k_new_bits/v_new_bits: bf16 bits
+    [D].  Returns a new dict.
     """
     g = cache.get("group", GROUP)
     c = dict(cache)
+    if cache.get("flush_all", False):
+        # MiniKV Alg. 1 decoding: the residual is quantized whole once it holds
+        # n_r = R tokens (R a multiple of g), in groups of g, oldest first
+        c["k_res"] = np.concatenate([cache["k_res"], k_new_bits[None, :]], axis=0)
+        c["v_res"] = np.concatenate([cache["v_res"], v_new_bits[None, :]], axis=0)
+        c["r_len"] = cache["r_len"] + 1
+        if c["r_len"] == residual:
+            kc, km, vc, vm = quantize_tokens(bf16_to_f32(c["k_res"]), bf16_to_f32(c["v_res"]), bits, g)
+            c["k_codes"] = np.concatenate([cache["k_codes"], kc], axis=0)
+            c["k_meta"] = np.concatenate([cache["k_meta"], km], axis=0)
+            c["v_codes"] = np.concatenate([cache["v_codes"], vc], axis=0)
+            c["v_meta"] = np.concatenate([cache["v_meta"], vm], axis=0)
+            c["k_res"] = c["k_res"][:0]
+            c["v_res"] = c["v_res"][:0]
+            c["q_len"] = cache["q_len"] + residual
+            c["r_len"] = 0
+        return c
     c["k_res"] = np.concatenate([cache["k_res"], k_new_bits[None, :]], axis=0)
     c["v_res"] = np.concatenate([cache["v_res"], v_new_bits[None, :]], axis=0)
     c["r_len"] = cache["r_len"] + 1

@@ -142,3 +142,52 @@ def test_residual_split_rule_group16():
         assert (c["q_len"], c["r_len"]) == want, (T, R)
         assert c["k_meta"].shape == (want[0] // 16, 32) and c["v_meta"].shape == (want[0], 2)
 
+
+
+def test_flush_all_prefill_split_closed_forms():
+    """MiniKV Alg. 1 as printed: the prefill quantizes every complete group of
+    the kept cache (Q = g*floor(T/g)), so fewer than g tokens stay in bf16."""
+    k, v = _head(1, 600, 32)
+    for T, g, want in [(72, 32, (64, 8)), (44, 32, (32, 12)), (72, 16, (64, 8)), (31, 32, (0, 31)), (160, 16, (160, 0))]:
+        c = quant.build_head_cache(k, v, np.arange(T), 128, 2, g, flush_all=True)
+        assert (c["q_len"], c["r_len"]) == want, (T, g)
+
+
+@pytest.mark.parametrize("group,R", [(32, 64), (16, 48), (16, 16)])
+def test_flush_all_incremental_equals_batch_quantization(group, R):
+    """Whole-residual flushes: the residual cycles through 0..R-1 tokens, each
+    flush quantizes R (a multiple of g) at a group boundary, so the packed
+    history always equals the batch quantization of the same token prefix and
+    the residual holds the rest."""
+    n, D, bits, steps = 100, 64, 2, 150
+    k, v = _head(7, n + steps, D)
+    c = quant.build_head_cache(k[:n], v[:n], np.arange(n), R, bits, group, flush_all=True)
+    flushes = 0
+    for s in range(steps):
+        before = c["q_len"]
+        c = quant.append_and_flush(c, quant.bf16_bits(k[n + s]), quant.bf16_bits(v[n + s]), R, bits)
+        if c["q_len"] != before:
+            flushes += 1
+            assert c["q_len"] - before == R and c["r_len"] == 0
+        assert 0 <= c["r_len"] < max(R, (n % group) + 1 + s)
+        total = n + s + 1
+        assert c["q_len"] + c["r_len"] == total
+        kc, km, vc, vm = quant.quantize_tokens(k[:c["q_len"]], v[:c["q_len"]], bits, group)
+        for key, ref in (("k_codes", kc), ("k_meta", km), ("v_codes", vc), ("v_meta", vm)):
+            np.testing.assert_array_equal(c[key], ref, f"step {s} {key}")
+        np.testing.assert_array_equal(c["k_res"], quant.bf16_bits(k[c["q_len"]:total]))
+    assert flushes == (steps + n % group) // R
+
+
+def test_flush_all_decode_matches_torch_sdpa():
+    n, D, Hkv, G, R, bits = 90, 64, 2, 2, 32, 4
+    caches = [quant.build_head_cache(*_head(20 + j, n, D), np.arange(n), R, bits, 16, flush_all=True)
+              for j in range(Hkv)]
+    rng = np.random.default_rng(21)
+    for s in range(40):
+        q = rng.standard_normal((Hkv * G, D))
+        kn = quant.bf16_bits(rng.standard_normal((Hkv, D)).astype(np.float32))
+        vn = quant.bf16_bits(rng.standard_normal((Hkv, D)).astype(np.float32))
+        out, caches = decode.decode_step(caches, q, kn, vn, R, bits)
+        Ks, Vs = zip(*(decode.head_keys_values(c, bits) for c in caches))
+        np.testing.assert_allclose(out, _sdpa(q, np.stack(Ks), np.stack(Vs)), rtol=1e-12, atol=1e-14)
