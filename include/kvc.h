@@ -102,6 +102,14 @@ typedef struct {
                                         means 32) or 16 (MiniKV Sec. 5.1: keys
                                         per channel over 16 tokens, values per
                                         token over 16 channels)                */
+  int32_t flush_all;                 /* residual policy.  0: a decode step
+                                        flushes the oldest g tokens when the
+                                        residual reaches R+g, and the prefill
+                                        keeps R..R+g-1 tokens in bf16.  1:
+                                        MiniKV Alg. 1 as printed: the prefill
+                                        quantizes every complete group, and the
+                                        residual is quantized whole when it
+                                        reaches R (R a positive multiple of g) */
   uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;
 } kvc_cache;
@@ -232,6 +240,7 @@ kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32
  * precision until a group fills).  The kept tokens of each (b, KV head) are
  * idx[b][j][0..k_sel) followed by the window n-W..n-1 (T = k_sel + W), or all n
  * prompt tokens when idx == NULL (T = n).  The oldest Q = g*floor(max(T-R,0)/g)
+ * (g*floor(T/g) with flush_all)
  * are quantized: per group of g values, lo/hi -> scale = fp16((hi-lo)/(2^b-1)),
  * zero = fp16(lo), code = clamp(rint((x - zero) * (1/scale)), 0, 2^b-1) in IEEE
  * float32 (scale 0 -> codes 0); the last T-Q go to the residual as bf16.
@@ -248,7 +257,8 @@ kvc_status kvc_quantize(const void *k, const void *v, kvc_dtype dtype, int32_t n
 /* ------------------------------------------------------------------ decode
  * One decode step (MiniKV Eq. 1 and Alg. 1 decoding; blog attention hook):
  * k_new/v_new are appended to the bf16 residual; if the residual then holds
- * R+g tokens its oldest g are quantized (same arithmetic as kvc_quantize)
+ * R+g tokens its oldest g are quantized (with flush_all: once it holds R tokens
+ * all of them are, in groups of g; same arithmetic as kvc_quantize)
  * and appended to the packed history; then for every query head h (KV head
  * h / (Hq/Hkv)) out = softmax(q K^T / sqrt(D)) V over the q_len dequantized
  * history tokens and the r_len residual tokens, one softmax over both.
@@ -258,7 +268,7 @@ kvc_status kvc_quantize(const void *k, const void *v, kvc_dtype dtype, int32_t n
  * Workspace: *ws_bytes (ws == NULL query) is sized for q_len == q_cap, so one
  *   buffer serves every step of this cache.
  * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_BITS, KVC_ERR_SHAPE,
- *   KVC_ERR_CAPACITY (r_len+1 > r_cap, or a flush with q_len+g > q_cap),
+ *   KVC_ERR_CAPACITY (r_len+1 > r_cap, or a flush past q_cap),
  *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
 kvc_status kvc_decode_attn(kvc_cache *cache, const void *q, const void *k_new, const void *v_new,
                            kvc_dtype dtype, int32_t Hq, float *out, void *ws, size_t *ws_bytes,

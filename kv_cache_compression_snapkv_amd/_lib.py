@@ -31,7 +31,7 @@ class CacheStruct(ctypes.Structure):
                 ("bits", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("q_cap", ctypes.c_int32), ("q_len", ctypes.c_int32),
                 ("r_cap", ctypes.c_int32), ("r_len", ctypes.c_int32), ("r_start", ctypes.c_int32),
-                ("group", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("flush_all", ctypes.c_int32),
                 ("k_codes", ctypes.c_void_p), ("k_meta", ctypes.c_void_p),
                 ("v_codes", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
                 ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p)]
@@ -237,7 +237,8 @@ def kvc_select(q_win, k, W, pool, budget, want_scores=False, ws=None, idx=None, 
 class Cache:
     """One layer's compressed cache: caller-owned torch buffers + the C struct."""
 
-    def __init__(self, batch, kv_heads, head_dim, bits, residual, q_cap, r_cap=None, device="cuda", group=32):
+    def __init__(self, batch, kv_heads, head_dim, bits, residual, q_cap, r_cap=None, device="cuda", group=32,
+                 flush_all=False):
         if r_cap is None:
             r_cap = residual + group
         r_cap = 8 * ((r_cap + 7) // 8)
@@ -249,7 +250,7 @@ class Cache:
         self.k_codes, self.k_meta = u32(sizes[0]), u32(sizes[1])
         self.v_codes, self.v_meta = u32(sizes[2]), u32(sizes[3])
         self.k_res, self.v_res = u16(sizes[4]), u16(sizes[5])
-        self.s = CacheStruct(batch, kv_heads, head_dim, bits, residual, q_cap, 0, r_cap, 0, 0, group,
+        self.s = CacheStruct(batch, kv_heads, head_dim, bits, residual, q_cap, 0, r_cap, 0, 0, group, int(flush_all),
                              self.k_codes.data_ptr(), self.k_meta.data_ptr(), self.v_codes.data_ptr(),
                              self.v_meta.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr())
         self._ws = None

@@ -1343,8 +1343,11 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   if (*ws_bytes < need) return KVC_ERR_WORKSPACE;
   const int R = cache->residual;
   if (cache->r_len + 1 > cache->r_cap) return KVC_ERR_CAPACITY;
-  const bool flush = (cache->r_len + 1 == R + g);
-  if (flush && cache->q_len + g > cache->q_cap) return KVC_ERR_CAPACITY;
+  // tokens a flush moves into the packed history: one group, or with flush_all
+  // the whole residual of R tokens (R/g groups, the appended token last)
+  const int moved = cache->flush_all ? R : g;
+  const bool flush = (cache->r_len + 1 == R + (cache->flush_all ? 0 : g));
+  if (flush && cache->q_len + moved > cache->q_cap) return KVC_ERR_CAPACITY;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   DecArgs a;
@@ -1352,12 +1355,21 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   a.k_new = k_new;
   a.v_new = v_new;
   if (flush) {
-    s = launch_flush(cache, k_new, v_new, dtype, st);
-    if (s != KVC_OK) return s;
-    cache->q_len += g;
-    cache->r_len = R;
-    cache->r_start = (cache->r_start + g) % cache->r_cap;
-    a.r_total = R;
+    // group i of the flushed tokens: the ring's oldest g after i groups left;
+    // the appended token joins the last group (its index in that launch's
+    // residual, r_len - i*g, is then below g)
+    for (int i = 0; i < moved / g; ++i) {
+      kvc_cache ci = *cache;
+      ci.r_len = cache->r_len - i * g;
+      ci.r_start = (cache->r_start + i * g) % cache->r_cap;
+      ci.q_len = cache->q_len + i * g;
+      s = launch_flush(&ci, k_new, v_new, dtype, st);
+      if (s != KVC_OK) return s;
+    }
+    cache->q_len += moved;
+    cache->r_len = cache->r_len + 1 - moved;
+    cache->r_start = (cache->r_start + moved) % cache->r_cap;
+    a.r_total = cache->r_len;
     a.r_new = -1;
   } else {
     a.r_new = cache->r_len;

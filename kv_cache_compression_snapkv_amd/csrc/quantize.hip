@@ -445,6 +445,7 @@ kvc_status cache_shape_status(const kvc_cache* c) {
       c->q_len % g != 0)
     return KVC_ERR_SHAPE;
   if (c->r_start < 0 || c->r_start % 8 != 0 || (c->r_cap > 0 && c->r_start >= c->r_cap)) return KVC_ERR_SHAPE;
+  if (c->flush_all != 0 && (c->flush_all != 1 || c->residual < g || c->residual % g != 0)) return KVC_ERR_SHAPE;
   if (c->q_len > c->q_cap || c->r_len > c->r_cap || c->r_cap < c->residual + g)
     return KVC_ERR_CAPACITY;
   return KVC_OK;
@@ -471,7 +472,7 @@ extern "C" kvc_status kvc_quantize(const void* k, const void* v, kvc_dtype dtype
   if (cache->q_len != 0 || cache->r_len != 0) return KVC_ERR_CAPACITY;
   const int R = cache->residual;
   const int g = cache_group(cache);
-  const int Q = g * (std::max(T - R, 0) / g);
+  const int Q = cache->flush_all ? g * (T / g) : g * (std::max(T - R, 0) / g);
   if (Q > cache->q_cap || T - Q > cache->r_cap) return KVC_ERR_CAPACITY;
   QuantArgs a;
   a.k = k;

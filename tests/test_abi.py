@@ -162,7 +162,7 @@ def test_select_validation_and_ws_query():
 
 def _cache(**kw):
     L = _lib()
-    c = L.CacheStruct(1, 4, 64, 2, 16, 64, 0, 48, 0, 0, 0, 16, 16, 16, 16, 16, 16)
+    c = L.CacheStruct(1, 4, 64, 2, 16, 64, 0, 48, 0, 0, 0, 0, 16, 16, 16, 16, 16, 16)
     for k, v in kw.items():
         setattr(c, k, v)
     return c
@@ -187,6 +187,9 @@ def test_quantize_and_decode_validation():
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(group=16, r_cap=24)), None) == 5  # r_cap < R+16
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(group=16, q_len=16)), None) == 5  # not empty
     assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(q_len=16)), None) == 2    # q_len % 32
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(flush_all=2)), None) == 2  # policy not 0/1
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(flush_all=1)), None) == 2  # R=16 not a multiple of 32
+    assert q(P, P, 1, 64, None, 0, 0, ctypes.byref(_cache(flush_all=1, group=16, r_len=1)), None) == 5  # not empty
     d = L.lib.kvc_decode_attn
     need = ctypes.c_size_t(0)
     assert d(ctypes.byref(_cache()), None, None, None, 1, 4, None, None, ctypes.byref(need), None) == 0

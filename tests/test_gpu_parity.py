@@ -342,3 +342,44 @@ def test_decode_parity_group16_multi_step(dtype, bits, G, D, R, n):
         for j in range(Hkv):
             gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[b][j], f"after steps b{b} j{j}")
     assert flushes >= 2
+
+
+# ---------------------------------------------------------------- whole-residual flush
+@pytest.mark.parametrize("group,R,bits,G,D", [(32, 64, 2, 4, 128), (16, 48, 4, 2, 64), (16, 16, 2, 1, 128)])
+def test_decode_parity_flush_all(group, R, bits, G, D):
+    """MiniKV's whole-residual policy (flush_all): the prefill quantizes every
+    complete group, the residual is quantized whole (R/g groups, the appended
+    token last) when it reaches R; 100 steps with several such flushes, outputs
+    within the decode tolerance and the cache bit-exact against the oracle."""
+    kvc = _kvc()
+    B, Hkv, n, steps = 2, 2, 300, 100
+    Hq = Hkv * G
+    k, v = _case(17, B, Hkv, n, D, "bf16")
+    cache = kvc.Cache(B, Hkv, D, bits, R, q_cap=n + steps + 64, device="cuda", group=group, flush_all=True)
+    kvc.kvc_quantize(k, v, cache)
+    kf, vf = gu.as_f32(k), gu.as_f32(v)
+    ref = [[oquant.build_head_cache(kf[b, j], vf[b, j], np.arange(n), R, bits, group, flush_all=True)
+            for j in range(Hkv)] for b in range(B)]
+    torch.cuda.synchronize()
+    for b in range(B):
+        for j in range(Hkv):
+            gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[b][j], f"prefill b{b} j{j}")
+    flushes = 0
+    for s in range(steps):
+        q = synth.random_tensor(700 + s, (B, Hq, D), "bf16", tag="q").cuda()
+        kn = synth.random_tensor(800 + s, (B, Hkv, D), "bf16", tag="kn").cuda()
+        vn = synth.random_tensor(900 + s, (B, Hkv, D), "bf16", tag="vn").cuda()
+        ql = cache.q_len
+        out = kvc.kvc_decode_attn(cache, q, kn, vn).cpu().numpy()
+        flushes += cache.q_len != ql
+        qf = gu.as_f32(q).astype(np.float64)
+        knb, vnb = gu.bf16_bits(kn), gu.bf16_bits(vn)
+        for b in range(B):
+            o_ref, ref[b] = odecode.decode_step(ref[b], qf[b], knb[b], vnb[b], R, bits)
+            gu.assert_decode_close(out[b], o_ref, f"step {s} b{b}")
+        if cache.q_len != ql:
+            torch.cuda.synchronize()
+            for b in range(B):
+                for j in range(Hkv):
+                    gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref[b][j], f"flush step {s} b{b} j{j}")
+    assert flushes == (n % group + steps) // R >= 1
