@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--streams", type=int, default=1,
                     help="prompt compression runs the layers round-robin on this many streams (they are "
                          "independent); decode stays on one stream, layer after layer")
+    ap.add_argument("--flush-all", action="store_true",
+                    help="MiniKV's residual policy: the prefill quantizes every complete group and the residual "
+                         "is quantized whole when it reaches R")
     ap.add_argument("--group", type=int, default=32, choices=(32, 16),
                     help="quantization group: 32, or MiniKV's 16 (its own decode kernel)")
     a = ap.parse_args()
@@ -146,7 +149,7 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32):
 
 
 def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", selector="snapkv", sinks=4, group=32,
-        streams=1):
+        streams=1, flush_all=False):
     """Time `steps` graph-replayed steps of the whole path on one workload.
 
     policy var-prop / var-inv: prompt compression runs kvc_window_scores for
@@ -191,7 +194,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     for l in range(L):
         T = (budgets[l] + W) if cfg.budget >= 0 else n
         caches.append(kvc.Cache(B, Hkv, D, bits, cfg.residual, q_cap=T + cfg.decode_steps + 32, device=dev,
-                                group=group))
+                                group=group, flush_all=flush_all))
         idxs.append(torch.empty(B, Hkv, budgets[l], dtype=torch.int32, device=dev) if cfg.budget >= 0 else None)
     sel_ws = torch.empty(max(kvc.select_ws_bytes(1 if in_bytes == 2 else 0, B, Hq, Hkv, n, D, W, cfg.pool, b)
                              for b in budgets) if cfg.budget >= 0 else 1, dtype=torch.uint8, device=dev)
@@ -299,7 +302,8 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     desc = (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
             f"prompt {n}, {cfg.dtype} inputs, W={W}, {sel}pool {cfg.pool}, budget "
             f"{'all' if cfg.budget < 0 else (policy + ' avg ' if varp else 'pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
-            f"{bits}-bit g{group} fp16 scale/zero, residual {cfg.residual}, {cfg.decode_steps} decode steps")
+            f"{bits}-bit g{group} fp16 scale/zero, residual {cfg.residual}"
+            f"{' (whole-residual flush)' if flush_all else ''}, {cfg.decode_steps} decode steps")
     res = {
         "desc": desc, "budgets": budgets, "footprint": fp,
         "tokens_per_s": B * cfg.decode_steps / (dec_ms * 1e-3),
@@ -333,7 +337,7 @@ def main():
     bits = args.bits or cfg.bits[0]
     r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers,
             policy=args.budget_policy, selector=args.selector, sinks=args.sinks, group=args.group,
-            streams=args.streams)
+            streams=args.streams, flush_all=args.flush_all)
     res = {
         "metric": "decode attn tokens/s + achieved HBM GB/s (% peak); select+quantize ms/prompt",
         "value": r["tokens_per_s"],
@@ -349,7 +353,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": r["desc"], "batch": cfg.batch, "prompt": cfg.prompt, "layers": cfg.layers,
                    "bits": bits, "decode_steps": cfg.decode_steps, "budget_policy": args.budget_policy,
-                   "selector": args.selector, "group": args.group, "prefill_streams": args.streams},
+                   "selector": args.selector, "group": args.group, "prefill_streams": args.streams,
+                   "flush_all": args.flush_all},
         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
         "decode_ms_per_token_all_layers": r["dec_ms"] / cfg.decode_steps,
         "decode_hbm_GBs": r["roofline"]["achieved"],
