@@ -6,15 +6,17 @@ for every layer, kvc_select (window scorer + pool + top-k) and kvc_quantize
 kvc_decode_attn (append, flush, attention) on every layer.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--bits B]
-                    [--no-cpu-baseline] [--no-hbm-stress]
+                    [--no-cpu-baseline] [--no-sub]
 
 Prints one JSON line.  value = decode-attention tokens/s (batch * decode steps /
-time of the decode part); the selection+quantization time per prompt is
-reported beside it.  Inputs are generated on the GPU before timing (seeded).
-By default the line also carries `hbm_stress`: the decode-only, no-eviction
-Llama-2-13B-shaped case (40 layers x 0.5 GB (2-bit) or 0.85 GB (4-bit) of packed
-cache per step), the one large enough to be bound by HBM rather than by launch
-latency, at 2 and at 4 bits.
+time of the decode part) of the headline workload, by default the largest one:
+the Llama-2-13B-shaped MHA cache with no eviction at 2 bits (40 layers x 32k
+tokens x 4 sequences, 0.51 GB of packed cache per layer per step, the case bound
+by HBM rather than by launch latency); the selection+quantization time per
+prompt is reported beside it.  Inputs are generated on the GPU before timing
+(seeded).  By default the line also carries `sub_workloads`: the same figures
+for every other workload and width (the 13B shape at 4 bits, the Llama-3-8B,
+Mistral pyramid and 128k long-context shapes), each timed the same way.
 """
 
 import argparse
@@ -34,10 +36,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama3_8b")
-    ap.add_argument("--bits", type=int, default=None)
+    ap.add_argument("--workload", default="llama2_13b_mha")
+    ap.add_argument("--bits", type=int, default=None, help="default: 2 if the workload has it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-hbm-stress", action="store_true")
+    ap.add_argument("--no-sub", action="store_true", help="headline workload only")
+    ap.add_argument("--sub-steps", type=int, default=10, help="timed steps of each sub-workload (at most --steps)")
     ap.add_argument("--no-graph", action="store_true", help="eager launches (for counter collection)")
     ap.add_argument("--layers", type=int, default=None, help="run only the first N layers")
     ap.add_argument("--budget-policy", default="workload", choices=("workload", "var-prop", "var-inv"),
@@ -69,12 +72,15 @@ def decode_call_bytes(B, Hq, Hkv, D, bits, q_len, r_total, in_bytes, group=32):
     return B * Hkv * (hist + resid) + io
 
 
-def counted_traffic(workload, bits):
+def counted_traffic(workload, bits, flush_all=False, group=32):
     """HBM bytes per kvc_decode_attn call from the committed rocprofv3 counter
-    summary of this workload, or None when the decode source has changed since
-    the counters were taken (or no summary exists)."""
+    summary of this workload (default residual policy, group 32), or None when
+    the decode source has changed since the counters were taken, no summary
+    exists, or the run uses another policy or group."""
     import hashlib
     import re
+    if flush_all or group != 32:
+        return None
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_{bits}bit_hbm_counters.md")
     src = os.path.join(ROOT, "kv_cache_compression_snapkv_amd", "csrc", "decode.hip")
     if not os.path.exists(path):
@@ -98,7 +104,27 @@ def _timed(fn, share_s, max_reps):
     return t / reps, reps, out
 
 
-def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32):
+def host_info():
+    """Host cores available to this process, CPU model, BLAS threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = {i.get("internal_api", "?"): i.get("num_threads") for i in threadpool_info()}
+    except Exception:  # noqa: BLE001 -- informational only
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model, "blas_threads_default": blas}
+
+
+def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32, flush_all=False):
     """The oracle, as it stands, on a bounded sample of the same workload: one
     (batch row, KV head) of layer 0, each stage repeated until its share of
     budget_s (selection 1/4, quantization 1/4, one decode step 1/2) is spent."""
@@ -111,12 +137,16 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32):
     from oracle import quant as oquant
     from oracle import select as oselect
 
+    info = host_info()
     with threadpool_limits(limits=1):
         torch.set_num_threads(1)
-        p = synth.prompt_layer(cfg, 0, "cpu")
-        qw = p["q_win"].float().numpy()[:1, : cfg.group]
-        kf = p["k"].float().numpy()[:1, :1]
-        vf = p["v"].float().numpy()[:1, :1]
+        # the layer is drawn where it is fastest (the GPU when there is one); only
+        # the sampled (batch row, KV head) comes to the host
+        p = synth.prompt_layer(cfg, 0, "cuda" if torch.cuda.is_available() else "cpu")
+        qw = p["q_win"][:1, : cfg.group].float().cpu().numpy()
+        kf = p["k"][:1, :1].float().cpu().numpy()
+        vf = p["v"][:1, :1].float().cpu().numpy()
+        del p
         n, W = cfg.prompt, cfg.window
         if cfg.budget >= 0:
             t_sel, r_sel, (idx, _) = _timed(lambda: oselect.select(qw, kf, W, cfg.pool, layers_budget[0]),
@@ -124,9 +154,10 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32):
             kept = oquant.kept_positions(n, W, idx[0, 0])
         else:
             t_sel, r_sel, kept = 0.0, 0, np.arange(n)
-        t_q, r_q, c = _timed(lambda: oquant.build_head_cache(kf[0, 0], vf[0, 0], kept, cfg.residual, bits, group),
+        t_q, r_q, c = _timed(lambda: oquant.build_head_cache(kf[0, 0], vf[0, 0], kept, cfg.residual, bits, group,
+                                                             flush_all=flush_all),
                              budget_s / 4, 1000)
-        d = synth.decode_inputs(cfg, 0, 0, "cpu")
+        d = synth.decode_inputs(cfg, 0, 0, "cpu")  # small
         q = d["q"].double().numpy()[0, : cfg.group]
         kn = oquant.bf16_bits(d["k_new"].float().numpy()[0, :1])
         vn = oquant.bf16_bits(d["v_new"].float().numpy()[0, :1])
@@ -140,10 +171,12 @@ def cpu_baseline(cfg, bits, layers_budget, budget_s=12.0, group=32):
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
+        "host": info,
+        "threads_used": "1 (numpy BLAS and torch limited to one thread)",
         "sample": (f"layer 0, batch row 0, KV head 0 of {cfg.name} ({cfg.group} query heads), mean per call: "
                    f"select {t_sel * 1e3:.3g} ms ({r_sel} reps), quantize {t_q * 1e3:.3g} ms ({r_q} reps), "
                    f"decode step {t_dec * 1e3:.3g} ms ({reps} reps); scaled by {Hkv} KV heads x {L} layers "
-                   f"per sequence-token"),
+                   f"per sequence-token{' (whole-residual policy)' if flush_all else ''}"),
         "select_quantize_ms_per_prompt": (t_sel + t_q) * Hkv * L * 1e3,
     }
 
@@ -165,6 +198,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     import synth
 
     dev = "cuda"
+    print(f"[bench] {cfg.name} {bits}-bit: generating inputs", file=sys.stderr, flush=True)
     L, B, Hq, Hkv, D, n, W = cfg.layers, cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.prompt, cfg.window
     budgets, fp = kvc.kvc_budget(L, Hkv, D, n, W, cfg.decode_steps, cfg.budget, cfg.pyramid, cfg.beta,
                                  bits=bits, group=group, meta_bits=16, residual=cfg.residual)
@@ -198,7 +232,8 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         idxs.append(torch.empty(B, Hkv, budgets[l], dtype=torch.int32, device=dev) if cfg.budget >= 0 else None)
     sel_ws = torch.empty(max(kvc.select_ws_bytes(1 if in_bytes == 2 else 0, B, Hq, Hkv, n, D, W, cfg.pool, b)
                              for b in budgets) if cfg.budget >= 0 else 1, dtype=torch.uint8, device=dev)
-    dec_ws = torch.zeros(max(kvc.decode_ws_bytes(c, Hq) for c in caches), dtype=torch.uint8, device=dev)
+    dec_ws = torch.zeros(max(kvc.decode_ws_bytes(c, Hq, 1 if in_bytes == 2 else 0) for c in caches),
+                         dtype=torch.uint8, device=dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     # prompt compression: the layers are independent, so they run round-robin on
@@ -277,6 +312,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     else:
         g_pre = g_dec = None
         run_pre, run_dec = prefill, decode_all
+    print(f"[bench] {cfg.name} {bits}-bit: {warmup} warm-up and {steps} timed steps", file=sys.stderr, flush=True)
     for _ in range(warmup):
         run_pre()
         run_dec()
@@ -309,10 +345,12 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         "tokens_per_s": B * cfg.decode_steps / (dec_ms * 1e-3),
         "step_ms": step_ms, "pre_ms": pre_ms, "dec_ms": dec_ms, "wall": wall,
         "roofline": {
-            "kernel": ("decode_kernel (+ merge_kernel; flush_kernel on 1 step in 32), per kvc_decode_attn call"
-                       if group == 32 else "decode_g16_kernel (flush_kernel on 1 step in 16), per kvc_decode_attn call"),
+            "kernel": ((("decode_kernel (+ merge_kernel" if group == 32 else "decode_g16_kernel (+ merge_g16_kernel")
+                        + (f"; flush_kernel of {cfg.residual // group} groups on 1 step in {cfg.residual})"
+                           if flush_all else f"; flush_kernel on 1 step in {group})"))
+                       + ", per kvc_decode_attn call"),
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(cfg.name, bits) if group == 32 else None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(cfg.name, bits, flush_all, group),
             "avg_call_us": dec_ms * 1e3 / ncalls, "algorithmic_bytes_per_call": sum(call_bytes) / ncalls,
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated), "
                             "profiles/decode_<workload>_<bits>bit_hbm_counters.md; null if decode.hip changed since",
@@ -325,6 +363,18 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     return res
 
 
+SUB_WORKLOADS = (("llama2_13b_mha", 4), ("llama2_13b_mha", 2), ("llama3_8b", 2), ("mistral_pyramid", 2),
+                 ("long_context", 2))
+
+
+def entry(r, cfg, bits, steps, warmup):
+    """The figures of one workload run (a sub-workload line)."""
+    return {"workload": r["desc"], "bits": bits, "decode_tokens_per_s": r["tokens_per_s"],
+            "avg_call_us": r["roofline"]["avg_call_us"], "ms_per_step": r["step_ms"],
+            "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch, "steps": steps, "warmup": warmup,
+            "roofline": r["roofline"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -334,7 +384,7 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.workload]
-    bits = args.bits or cfg.bits[0]
+    bits = args.bits or (2 if 2 in cfg.bits else cfg.bits[0])
     r = run(cfg, bits, args.steps, args.warmup, graph=not args.no_graph, layers=args.layers,
             policy=args.budget_policy, selector=args.selector, sinks=args.sinks, group=args.group,
             streams=args.streams, flush_all=args.flush_all)
@@ -362,18 +412,18 @@ def main():
         "wall_s_timed": r["wall"],
         "footprint_bytes_per_prompt_token": r["footprint"]["bytes_per_prompt_token"],
     }
-    if not args.no_hbm_stress and args.workload != "llama2_13b_mha":
-        # the HBM-bound decode case: no eviction, full 32k cache of 40 layers,
-        # at each of its quantization widths
-        hc = synth.CONFIGS["llama2_13b_mha"]
-        res["hbm_stress"] = []
-        for hb in sorted(hc.bits):
-            h = run(hc, hb, 2, 1)
-            res["hbm_stress"].append({"workload": h["desc"], "bits": hb, "decode_tokens_per_s": h["tokens_per_s"],
-                                      "quantize_ms_per_prompt": h["pre_ms"] / hc.batch, "steps": 2, "warmup": 1,
-                                      "roofline": h["roofline"]})
+    if not args.no_sub:
+        # every other workload and width, each timed the same way (fewer steps)
+        sub_steps, sub_warm = max(1, min(args.steps, args.sub_steps)), max(1, min(args.warmup, 2))
+        res["sub_workloads"] = []
+        for name, sb in SUB_WORKLOADS:
+            if (name, sb) == (args.workload, bits):
+                continue
+            sc = synth.CONFIGS[name]
+            h = run(sc, sb, sub_steps, sub_warm)
+            res["sub_workloads"].append(entry(h, sc, sb, sub_steps, sub_warm))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"], group=args.group)
+        res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"], group=args.group, flush_all=args.flush_all)
     print(json.dumps(res))
 
 

@@ -299,9 +299,11 @@ def kvc_quantize(k, v, cache, idx=None, W=0, stream=None):
     return cache
 
 
-def decode_ws_bytes(cache, Hq):
+def decode_ws_bytes(cache, Hq, dtype=KVC_BF16):
+    """Workspace bytes of kvc_decode_attn on this cache with Hq query heads (the
+    size covers every step up to the cache's capacities)."""
     need = ctypes.c_size_t(0)
-    _check("kvc_decode_attn", lib.kvc_decode_attn(ctypes.byref(cache.s), None, None, None, KVC_BF16, Hq,
+    _check("kvc_decode_attn", lib.kvc_decode_attn(ctypes.byref(cache.s), None, None, None, dtype, Hq,
                                                   None, None, ctypes.byref(need), None))
     return need.value
 
@@ -311,8 +313,9 @@ def kvc_decode_attn(cache, q, k_new, v_new, out=None, ws=None, stream=None):
     _contig(q, k_new, v_new)
     B, Hq, D = q.shape
     if ws is None:
-        if cache._ws is None:
-            cache._ws = torch.zeros(decode_ws_bytes(cache, Hq), dtype=torch.uint8, device=q.device)
+        need = decode_ws_bytes(cache, Hq, _dtype(q))
+        if cache._ws is None or cache._ws.numel() < need:
+            cache._ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
         ws = cache._ws
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)

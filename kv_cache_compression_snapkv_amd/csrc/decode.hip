@@ -34,7 +34,7 @@
 
 namespace kvc {
 
-kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new, kvc_dtype dt,
+kvc_status launch_flush(const kvc_cache* c, int ngroups, const void* k_new, const void* v_new, kvc_dtype dt,
                         hipStream_t st);
 bool cache_ok(const kvc_cache* c);
 kvc_status cache_shape_status(const kvc_cache* c);
@@ -1208,40 +1208,38 @@ const void* kernel_for(int dt, int bits, int KS, int nwv, int hbs) {
 int hbs_kernel(int hbs) { return hbs == 1 ? 1 : kHB; }
 
 // Workgroups of the 4-wave long-run kernel resident per CU, and the CU count of
-// the current device (queried once per device and instantiation).  Long runs
-// put min(kHB, G) heads in a workgroup.
+// the current device, queried on every call that plans a long run (no state is
+// kept between calls).  Long runs put min(kHB, G) heads in a workgroup.
 struct Occupancy {
   int per_cu, cus;
 };
-Occupancy occupancy(int dt, int bits, int KS, int G) {
-  static int cache[8][2][2][9][2] = {};  // [device][dtype][bits][KS][one head]: per_cu * 4096 + cus
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) dev = 0;
-  const int hk = hbs_kernel(std::min(kHB, G));
-  int& c = cache[dev][dt == KVC_F32 ? 0 : 1][bits == 2 ? 0 : 1][KS][hk == 1 ? 1 : 0];
-  if (c == 0) {
-    // allow the dynamic LDS of every workgroup shape, then ask for the occupancy
-    const int shapes[3][2] = {{8, 1}, {4, 1}, {4, kHB}};
-    for (const auto& sh : shapes) {
-      const void* k = kernel_for(dt, bits, KS, sh[0], sh[1]);
-      const int bytes = kernel_lds(bits, KS, sh[0], sh[1]).total;
-      if (k && bytes > 65536) {
-        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-        if (e != hipSuccess) {
-          set_last_hip_error(e);
-          return Occupancy{0, 0};
-        }
-      }
-    }
-    int per_cu = 0, cus = 0;
-    const void* k = kernel_for(dt, bits, KS, 4, hk);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, kernel_lds(bits, KS, 4, hk).total) != hipSuccess ||
-        per_cu < 1)
-      per_cu = 1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    c = per_cu * 4096 + cus;
+// Allows a kernel's dynamic LDS above the 64 KB default (idempotent).
+kvc_status allow_lds(const void* k, int bytes) {
+  if (!k || bytes <= 65536) return KVC_OK;
+  const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) {
+    set_last_hip_error(e);
+    return KVC_ERR_HIP;
   }
-  return Occupancy{c / 4096, c % 4096};
+  return KVC_OK;
+}
+kvc_status occupancy(int dt, int bits, int KS, int G, Occupancy* oc) {
+  int dev = 0, per_cu = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_last_hip_error(e);
+    return KVC_ERR_HIP;
+  }
+  const int hk = hbs_kernel(std::min(kHB, G));
+  const void* k = kernel_for(dt, bits, KS, 4, hk);
+  const int bytes = kernel_lds(bits, KS, 4, hk).total;
+  const kvc_status s = allow_lds(k, bytes);
+  if (s != KVC_OK) return s;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, bytes) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  oc->per_cu = per_cu;
+  oc->cus = cus;
+  return KVC_OK;
 }
 
 // Heads per workgroup: long runs take all kHB heads of a group (the packed cache
@@ -1253,7 +1251,7 @@ bool is_short(int NT, int KS) {
   const int nwv_short = KS <= 6 ? 8 : 4;
   return (NT + nwv_short - 1) / nwv_short <= kShortTilesPerWave;
 }
-Plan plan(int NT, int BH, int G, int KS, const Occupancy& oc) {
+Plan plan(int NT, int BH, int G, int KS, const Occupancy& oc) {  // oc is read for long runs only
   Plan p;
   const bool sh = is_short(NT, KS);
   p.hbs = heads_per_block(G, sh);
@@ -1273,27 +1271,27 @@ Plan plan(int NT, int BH, int G, int KS, const Occupancy& oc) {
   return p;
 }
 
+// Workspace of the split runs: (m, l) and o[D] for kHB heads per workgroup
+// slot.  Sized without the device: the splits of a long run are at most
+// min(kMaxNb, ceil(NT / (4 * kMinTilesPerWave))) whatever the occupancy, and that
+// bound grows with NT, so the capacity's tile count gives the largest run.
 struct WsLayout {
   size_t part_ml, part_o, total;
-  int nb_max;
 };
-WsLayout ws_layout(const kvc_cache* c, int G, const Occupancy& oc) {
-  const int BH = c->batch * c->kv_heads;
-  const int NTmax = c->q_cap / kGroup + (c->r_cap + kGroup - 1) / kGroup;
-  size_t slots = 1;  // workgroup partial slots: units * nb, maximized over every possible length
-  int nmax = 1;
-  for (int nt = 1; nt <= NTmax; ++nt) {
-    const Plan p = plan(nt, BH, G, c->head_dim / 32, oc);
-    const size_t units = static_cast<size_t>(BH) * ((G + p.hbs - 1) / p.hbs);
-    slots = std::max(slots, units * p.nb);
-    nmax = std::max(nmax, p.nb);
-  }
+WsLayout ws_layout_for(size_t slots, int D) {
   WsLayout w;
-  w.nb_max = nmax;
   w.part_ml = 0;
   w.part_o = align_up(slots * kHB * sizeof(float2), 256);
-  w.total = w.part_o + slots * kHB * c->head_dim * sizeof(float);
+  w.total = w.part_o + slots * kHB * D * sizeof(float);
   return w;
+}
+size_t max_slots(const kvc_cache* c, int G) {
+  const int KS = c->head_dim / 32;
+  const int NTmax = c->q_cap / kGroup + (c->r_cap + kGroup - 1) / kGroup;
+  if (is_short(NTmax, KS)) return 0;  // every run fits one workgroup per unit
+  const size_t units = static_cast<size_t>(c->batch) * c->kv_heads * ((G + kHB - 1) / kHB);
+  const int nb = std::min(kMaxNb, (NTmax + 4 * kMinTilesPerWave - 1) / (4 * kMinTilesPerWave));
+  return units * static_cast<size_t>(nb);
 }
 
 kvc_status launch_decode(const DecArgs& a, int dt, int bits, int KS, int nwv, int B, hipStream_t st) {
@@ -1301,6 +1299,8 @@ kvc_status launch_decode(const DecArgs& a, int dt, int bits, int KS, int nwv, in
   const void* k = kernel_for(dt, bits, KS, nwv, hk);
   if (!k) return KVC_ERR_SHAPE;
   const int bytes = kernel_lds(bits, KS, nwv, hk).total;
+  kvc_status s = allow_lds(k, bytes);
+  if (s != KVC_OK) return s;
   dim3 grid(a.nb, a.Hkv * a.HB, B);
   void* args[] = {const_cast<DecArgs*>(&a)};
   hipError_t e = hipLaunchKernel(k, grid, dim3(64 * nwv), args, bytes, st);
@@ -1308,11 +1308,66 @@ kvc_status launch_decode(const DecArgs& a, int dt, int bits, int KS, int nwv, in
     set_last_hip_error(e);
     return KVC_ERR_HIP;
   }
-  kvc_status st2 = check_launch();
-  if (st2 != KVC_OK || a.nb == 1) return st2;
+  s = check_launch();
+  if (s != KVC_OK || a.nb == 1) return s;
   hipLaunchKernelGGL(merge_kernel, dim3(a.Hkv * a.HB, B), dim3(kMergeThreads), 0, st, a.part_o, a.part_ml, a.out,
                      a.Hq, a.Hkv, a.G, a.HB, a.hbs, 32 * KS, a.nb);
   return check_launch();
+}
+
+// Workspace bytes of a decode call on this cache with G query heads per KV
+// head: the split partials (group 32) or the group-16 kernel's; never zero, so
+// that a caller's buffer pointer is never NULL.
+size_t decode_ws_need(const kvc_cache* c, int G) {
+  const size_t w = cache_group(c) == kGroup ? ws_layout_for(max_slots(c, G), c->head_dim).total
+                                            : g16_ws_bytes(c, G * c->kv_heads);
+  return std::max<size_t>(w, 256);
+}
+
+// The group-32 attention launch for a cache whose state already includes this
+// step's append (a.r_total, a.r_new set; a.q, a.k_new, a.v_new set).
+kvc_status decode_g32(const kvc_cache& c, DecArgs& a, kvc_dtype dtype, int Hq, float* out, void* ws, hipStream_t st) {
+  const int Hkv = c.kv_heads, G = Hq / Hkv, KS = c.head_dim / 32;
+  a.k_codes = c.k_codes;
+  a.k_meta = c.k_meta;
+  a.v_codes = c.v_codes;
+  a.v_meta = c.v_meta;
+  a.k_res = c.k_res;
+  a.v_res = c.v_res;
+  a.B = c.batch;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.q_cap = c.q_cap;
+  a.r_cap = c.r_cap;
+  a.r_start = c.r_start;
+  a.q_len = c.q_len;
+  const int NT = a.q_len / kGroup + (a.r_total + kGroup - 1) / kGroup;
+  Occupancy oc{1, 256};
+  if (!is_short(NT, KS)) {
+    const kvc_status s = occupancy(dtype, c.bits, KS, G, &oc);
+    if (s != KVC_OK) return s;
+  }
+  const Plan p = plan(NT, c.batch * Hkv, G, KS, oc);
+  a.hbs = p.hbs;
+  a.HB = (G + p.hbs - 1) / p.hbs;
+  a.nb = p.nb;
+  const WsLayout W = ws_layout_for(max_slots(&c, G), c.head_dim);
+  char* w = static_cast<char*>(ws);
+  a.part_ml = reinterpret_cast<float2*>(w + W.part_ml);
+  a.part_o = reinterpret_cast<float*>(w + W.part_o);
+  a.out = out;
+  a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(c.head_dim));
+  a.rcp_hkv = 1.0f / static_cast<float>(Hkv);
+  a.rcp_hb = 1.0f / static_cast<float>(a.HB);
+  a.rcp_xhb = 1.0f / static_cast<float>(kXcds * a.HB);
+  const int NWT = p.nb * p.nwv;
+  const SplitParams sp = split_params(NWT, a.q_len / kGroup, (a.r_total + kGroup - 1) / kGroup);
+  a.split_nA = sp.nA;
+  a.split_hA = sp.hA;
+  a.split_hB = sp.hB;
+  a.sp_new = a.r_new >= 0 ? NWT - 1 - (a.r_new / kGroup) % NWT : -1;
+  return launch_decode(a, dtype, c.bits, KS, p.nwv, c.batch, st);
 }
 
 }  // namespace
@@ -1330,11 +1385,8 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   if (Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return KVC_ERR_SHAPE;
   const int G = Hq / Hkv;
   const int KS = cache->head_dim / 32;
-  const Occupancy oc = occupancy(dtype, cache->bits, KS, G);
-  if (oc.cus == 0) return KVC_ERR_HIP;
-  const WsLayout W = ws_layout(cache, G, oc);
   const int g = cache_group(cache);
-  const size_t need = g == kGroup ? W.total : std::max(W.total, g16_ws_bytes(cache, Hq));
+  const size_t need = decode_ws_need(cache, G);
   if (!ws) {
     *ws_bytes = need;
     return KVC_OK;
@@ -1350,66 +1402,33 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
   if (flush && cache->q_len + moved > cache->q_cap) return KVC_ERR_CAPACITY;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
+  // The state after this step goes to *cache only once every launch has been
+  // enqueued: the flush and the attention kernel write past the current
+  // lengths only (codes at q_len.., the appended token's ring row), so a failed
+  // call leaves the cache as it was.
+  kvc_cache nc = *cache;
   DecArgs a;
   a.q = q;
   a.k_new = k_new;
   a.v_new = v_new;
   if (flush) {
-    // group i of the flushed tokens: the ring's oldest g after i groups left;
-    // the appended token joins the last group (its index in that launch's
-    // residual, r_len - i*g, is then below g)
-    for (int i = 0; i < moved / g; ++i) {
-      kvc_cache ci = *cache;
-      ci.r_len = cache->r_len - i * g;
-      ci.r_start = (cache->r_start + i * g) % cache->r_cap;
-      ci.q_len = cache->q_len + i * g;
-      s = launch_flush(&ci, k_new, v_new, dtype, st);
-      if (s != KVC_OK) return s;
-    }
-    cache->q_len += moved;
-    cache->r_len = cache->r_len + 1 - moved;
-    cache->r_start = (cache->r_start + moved) % cache->r_cap;
-    a.r_total = cache->r_len;
+    s = launch_flush(cache, moved / g, k_new, v_new, dtype, st);
+    if (s != KVC_OK) return s;
+    nc.q_len += moved;
+    nc.r_len = cache->r_len + 1 - moved;
+    nc.r_start = (cache->r_start + moved) % cache->r_cap;
+    a.r_total = nc.r_len;
     a.r_new = -1;
   } else {
     a.r_new = cache->r_len;
     a.r_total = cache->r_len + 1;
-    cache->r_len += 1;
+    nc.r_len += 1;
   }
-  if (g != kGroup) return launch_decode_g16(cache, q, k_new, v_new, dtype, Hq, a.r_total, a.r_new, out, ws, st);
-  a.k_codes = cache->k_codes;
-  a.k_meta = cache->k_meta;
-  a.v_codes = cache->v_codes;
-  a.v_meta = cache->v_meta;
-  a.k_res = cache->k_res;
-  a.v_res = cache->v_res;
-  a.B = cache->batch;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.G = G;
-
-  a.q_cap = cache->q_cap;
-  a.r_cap = cache->r_cap;
-  a.r_start = cache->r_start;
-  a.q_len = cache->q_len;
-  const int NT = a.q_len / kGroup + (a.r_total + kGroup - 1) / kGroup;
-  const Plan p = plan(NT, cache->batch * Hkv, G, KS, oc);
-  a.hbs = p.hbs;
-  a.HB = (G + p.hbs - 1) / p.hbs;
-  a.nb = p.nb;
-  char* w = static_cast<char*>(ws);
-  a.part_ml = reinterpret_cast<float2*>(w + W.part_ml);
-  a.part_o = reinterpret_cast<float*>(w + W.part_o);
-  a.out = out;
-  a.scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(cache->head_dim));
-  a.rcp_hkv = 1.0f / static_cast<float>(Hkv);
-  a.rcp_hb = 1.0f / static_cast<float>(a.HB);
-  a.rcp_xhb = 1.0f / static_cast<float>(kXcds * a.HB);
-  const int NWT = p.nb * p.nwv;
-  const SplitParams sp = split_params(NWT, a.q_len / kGroup, (a.r_total + kGroup - 1) / kGroup);
-  a.split_nA = sp.nA;
-  a.split_hA = sp.hA;
-  a.split_hB = sp.hB;
-  a.sp_new = a.r_new >= 0 ? NWT - 1 - (a.r_new / kGroup) % NWT : -1;
-  return launch_decode(a, dtype, cache->bits, KS, p.nwv, cache->batch, st);
+  if (g != kGroup) {
+    s = launch_decode_g16(&nc, q, k_new, v_new, dtype, Hq, a.r_total, a.r_new, out, ws, st);
+  } else {
+    s = decode_g32(nc, a, dtype, Hq, out, ws, st);
+  }
+  if (s == KVC_OK) *cache = nc;
+  return s;
 }

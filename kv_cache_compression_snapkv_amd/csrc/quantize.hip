@@ -301,40 +301,47 @@ struct FlushArgs {
   const void* k_new;
   const void* v_new;
   int D, Hkv, R, r_old, r_start, q_len, q_cap, r_cap;
+  int store_new;  // the appended token stays in the ring (it is in no flushed group)
   uint32_t *k_codes, *k_meta, *v_codes, *v_meta;
   uint16_t *k_res, *v_res;
 };
 
-// Decode-step flush: the residual ring held r_old = R+G-1 tokens; the new token
-// makes it R+G.  Quantize the oldest G (the new token is among them only when
-// R == 0) and append them to the packed history at q_len; the new token takes
-// ring row r_start + r_old.  The host then advances r_start by G.  Keys are
-// staged with 16-byte row loads, values with 16-byte loads of 8 consecutive
-// ring rows of one channel (r_start and r_cap are multiples of 8, so such a
-// chunk never wraps).
+// Decode-step flush of gridDim.z groups: the residual ring held r_old tokens
+// and the appended token makes it r_old+1.  Group i (blockIdx.z) quantizes ring
+// tokens i*G .. i*G+G-1 (the appended token, from the inputs, when it falls in
+// that range) and appends them to the packed history at q_len + i*G.  With one
+// group (the default policy) the ring held R+G-1 and the appended token takes
+// ring row r_start + r_old unless R == 0; with R/G groups (the whole-residual
+// policy) the appended token is the last group's last token.  The host then
+// advances r_start by G times the group count.  Keys are staged with 16-byte
+// row loads, values with 16-byte loads of 8 consecutive ring rows of one channel
+// (r_start and r_cap are multiples of 8, so such a chunk never wraps).
 template <typename T, int BITS, int DM, int G>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   __shared__ __attribute__((aligned(16))) QuantLds<uint16_t, DM, G> L;  // the ring holds bf16
-  const int j = blockIdx.x, b = blockIdx.y;
+  const int j = blockIdx.x, b = blockIdx.y, grp = blockIdx.z;
   const int bj = b * a.Hkv + j;
   const int D = a.D;
   const int tid = threadIdx.x;
+  const int t_first = grp * G;          // first residual token of this group
+  const int r_new = a.r_old - t_first;  // the appended token's index inside this group's tokens
   const T* kn = static_cast<const T*>(a.k_new) + static_cast<size_t>(bj) * D;
   const T* vn = static_cast<const T*>(a.v_new) + static_cast<size_t>(bj) * D;
   uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
   uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
-  auto ring = [&](int t) {
+  auto ring = [&](int t) {  // residual token t (t < r_cap) -> ring row
     const int p = a.r_start + t;
     return p >= a.r_cap ? p - a.r_cap : p;
   };
   const int cpr = D / 8;  // 16-byte chunks per key row
   for (int e = tid; e < G * cpr; e += kThreads) {
     const int t = e / cpr, c8 = (e % cpr) * 8;
-    *reinterpret_cast<uint4*>(&L.k[t][c8]) = *reinterpret_cast<const uint4*>(kr + static_cast<size_t>(ring(t)) * D + c8);
+    *reinterpret_cast<uint4*>(&L.k[t][c8]) =
+        *reinterpret_cast<const uint4*>(kr + static_cast<size_t>(ring(t_first + t)) * D + c8);
   }
   for (int e = tid; e < D * (G / 8); e += kThreads) {
     const int c = e / (G / 8), t8 = (e % (G / 8)) * 8;
-    const uint4 w = *reinterpret_cast<const uint4*>(vr + static_cast<size_t>(c) * a.r_cap + ring(t8));
+    const uint4 w = *reinterpret_cast<const uint4*>(vr + static_cast<size_t>(c) * a.r_cap + ring(t_first + t8));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -343,21 +350,24 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     }
   }
   __syncthreads();
-  // the new token: quantized with the group when R == 0, else kept in the ring
-  for (int c = tid; c < D; c += kThreads) {
-    const uint16_t kb = f32_to_bf16(load_f32(kn, c)), vb = f32_to_bf16(load_f32(vn, c));
-    if (a.r_old < G) {
-      L.k[a.r_old][c] = kb;
-      L.v[a.r_old][c] = vb;
-    } else {
-      const int p = ring(a.r_old);
-      kr[static_cast<size_t>(p) * D + c] = kb;
-      vr[static_cast<size_t>(c) * a.r_cap + p] = vb;
+  // the appended token: quantized with the group it falls in, or stored in the
+  // ring (by the first group only)
+  if (r_new < G || (a.store_new && grp == 0)) {
+    for (int c = tid; c < D; c += kThreads) {
+      const uint16_t kb = f32_to_bf16(load_f32(kn, c)), vb = f32_to_bf16(load_f32(vn, c));
+      if (r_new < G) {
+        L.k[r_new][c] = kb;
+        L.v[r_new][c] = vb;
+      } else {
+        const int p = ring(a.r_old);
+        kr[static_cast<size_t>(p) * D + c] = kb;
+        vr[static_cast<size_t>(c) * a.r_cap + p] = vb;
+      }
     }
   }
   __syncthreads();
   const size_t qc = a.q_cap;
-  quantize_block<BITS>(L, D, a.q_len, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
+  quantize_block<BITS>(L, D, a.q_len + t_first, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
                        a.k_meta + static_cast<size_t>(bj) * (qc / G) * D,
                        a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
                        a.v_meta + static_cast<size_t>(bj) * qc * (D / G));
@@ -390,7 +400,9 @@ kvc_status launch_quantize(const QuantArgs& a, int bits, int group, int B, hipSt
 
 }  // namespace
 
-kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new, kvc_dtype dt,
+// Flush of ngroups groups of the cache's group size (1, or R/g with the
+// whole-residual policy) in one launch; c is the state before the decode step.
+kvc_status launch_flush(const kvc_cache* c, int ngroups, const void* k_new, const void* v_new, kvc_dtype dt,
                         hipStream_t st) {
   FlushArgs a;
   a.k_new = k_new;
@@ -409,7 +421,8 @@ kvc_status launch_flush(const kvc_cache* c, const void* k_new, const void* v_new
   a.v_meta = c->v_meta;
   a.k_res = c->k_res;
   a.v_res = c->v_res;
-  dim3 grid(c->kv_heads, c->batch);
+  a.store_new = c->r_len - (ngroups - 1) * cache_group(c) >= cache_group(c);
+  dim3 grid(c->kv_heads, c->batch, ngroups);
   const int dm = dm_for(a.D);
   const bool g16 = cache_group(c) == 16;
 #define KVC_FG(T_, B_, G_)                                                                                     \

@@ -641,7 +641,7 @@ __device__ __forceinline__ void select_digit_wide(const int* cnt, int krem, int*
 }
 
 struct TopArgs {
-  const float* raw;  // [B][Hkv][N]
+  const float* raw;  // [B][Hkv] rows of N scores, ld apart
   uint32_t* keys;    // [B][Hkv][NP] (chunked path)
   float* scores;     // pooled scores out, or null
   int32_t* idx;      // [B][Hkv][kk]
@@ -650,6 +650,7 @@ struct TopArgs {
   uint32_t* sel;     // [B][Hkv][kSelSlots]: (prefix, remaining k) after passes 1, 2 and 3
   int2* cnt;         // [B][Hkv][nch] (keys above the threshold, keys equal to it) per chunk
   int Hkv, N, kk, pool, NP, nch;
+  int ld;  // row stride of raw (>= N)
 };
 
 // Long score rows: the candidates are split into chunks of kChunk, one
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
   const int tid = threadIdx.x, w = tid >> 6;
   const int N = a.N, h = a.pool / 2, c0 = ch * kChunk;
-  const float* raw = a.raw + bj * N;
+  const float* raw = a.raw + bj * a.ld;
   for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
   if (ch == 0)  // the counts of passes 2 and 3 are accumulated by later launches
     for (int i = tid; i < 2 * kWideBins; i += kTopThreads) a.ghist[bj * 2 * kWideBins + i] = 0;
@@ -890,7 +891,7 @@ __global__ __launch_bounds__(kTopThreads) void pool_topk_lds_kernel(TopArgs a) {
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
   const int tid = threadIdx.x, w = tid >> 6;
   const int N = a.N, h = a.pool / 2;
-  const float* raw = a.raw + bj * N;
+  const float* raw = a.raw + bj * a.ld;
   int32_t* idx = a.idx + bj * a.kk;
   {
     float v[KPT];
@@ -1034,14 +1035,12 @@ template <int KS, int PASS, int TPW>
 kvc_status launch_pipe(const ScoreArgs& a, int B, hipStream_t st) {
   const void* k = reinterpret_cast<const void*>(&score_pipe_kernel<KS, PASS, TPW>);
   constexpr int bytes = PipeGeom<KS>::LDS;
-  static bool lds_set = false;  // one attribute call per instantiation (idempotent)
-  if (bytes > 65536 && !lds_set) {
+  if (bytes > 65536) {  // idempotent; made on every launch (no state kept between calls)
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) {
       set_last_hip_error(e);
       return KVC_ERR_HIP;
     }
-    lds_set = true;
   }
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -1218,6 +1217,7 @@ TopArgs top_args(const float* raw, int Hkv, int N, int kk, int pool, const TopWs
   t.pool = pool;
   t.nch = tw.nch;
   t.NP = tw.nch * kChunk;
+  t.ld = N;
   return t;
 }
 bool score_shape_ok(int B, int Hq, int Hkv, int n, int D, int W) {

@@ -46,6 +46,26 @@ def gpu_head_cache(cache, b, j):
     }
 
 
+def gpu_all_caches(cache):
+    """Every unit's logical cache state, copied to the host once: a dict of numpy
+    arrays [B][Hkv][...] plus q_len / r_len (for unit_cache)."""
+    v = cache.views()
+    out = {"q_len": cache.q_len, "r_len": cache.r_len}
+    for key in ("k_codes", "k_meta", "v_codes", "v_meta"):
+        out[key] = u32(v[key])
+    for key in ("k_res", "v_res"):
+        out[key] = u16(v[key])
+    return out
+
+
+def unit_cache(allc, b, j):
+    """One unit's cache from gpu_all_caches, in the layout of gpu_head_cache."""
+    d = {"q_len": allc["q_len"], "r_len": allc["r_len"]}
+    for key in ("k_codes", "k_meta", "v_codes", "v_meta", "k_res", "v_res"):
+        d[key] = allc[key][b, j]
+    return d
+
+
 def assert_cache_equal(gpu, ref, where=""):
     assert gpu["q_len"] == ref["q_len"] and gpu["r_len"] == ref["r_len"], where
     for key in ("k_codes", "k_meta", "v_codes", "v_meta", "k_res", "v_res"):

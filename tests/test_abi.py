@@ -243,3 +243,68 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_workspace_queries_from_many_threads():
+    """The workspace queries keep no state between calls: eight host threads
+    querying at once get the sizes a single thread gets, for every call and
+    cache shape (decode sizes do not depend on the device or the dtype)."""
+    import concurrent.futures
+    L = _lib()
+
+    def dec(args):
+        B, H, D, bits, R, q_cap, r_cap, G, group, dt = args
+        c = L.CacheStruct(B, H, D, bits, R, q_cap, 0, r_cap, 0, 0, group, 0, 16, 16, 16, 16, 16, 16)
+        need = ctypes.c_size_t(0)
+        st = L.lib.kvc_decode_attn(ctypes.byref(c), None, None, None, dt, H * G, None, None, ctypes.byref(need),
+                                   None)
+        return st, need.value
+
+    def sel(args):
+        return L.select_ws_bytes(*args)
+
+    dec_cases = [(B, H, D, bits, R, q_cap, r_cap, G, group, dt)
+                 for (B, H, G) in ((1, 8, 4), (4, 40, 1), (8, 8, 4), (1, 1, 16))
+                 for D in (64, 128, 256) for bits in (2, 4) for group in (32, 16)
+                 for (R, q_cap, r_cap) in ((128, 32768, 160), (16, 64, 48), (256, 4096, 288))
+                 for dt in (0, 1)]
+    sel_cases = [(1, B, Hq, Hkv, n, 128, W, 7, bud) for (B, Hq, Hkv) in ((1, 32, 8), (8, 32, 8), (4, 40, 40))
+                 for n in (512, 8192, 131072) for (W, bud) in ((32, 512), (64, 2048))]
+    serial_dec = [dec(c) for c in dec_cases]
+    serial_sel = [sel(c) for c in sel_cases]
+    assert all(st == 0 and need > 0 for st, need in serial_dec)
+    # the decode size is the same for both dtypes
+    for i in range(0, len(dec_cases), 2):
+        assert serial_dec[i] == serial_dec[i + 1]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        for _ in range(3):
+            assert list(ex.map(dec, dec_cases)) == serial_dec
+            assert list(ex.map(sel, sel_cases)) == serial_sel
+
+
+def test_decode_workspace_closed_form():
+    """The decode workspace equals its closed form: split partials only when
+    the capacity's tile count exceeds what one workgroup per unit covers (eight
+    waves of six tiles, four waves at D > 192), then units * min(64,
+    ceil(tiles / 12)) slots of four heads' (m, l) and o[D]."""
+    L = _lib()
+
+    def need(B, H, D, R, q_cap, r_cap, G):
+        c = L.CacheStruct(B, H, D, 2, R, q_cap, 0, r_cap, 0, 0, 32, 0, 16, 16, 16, 16, 16, 16)
+        n = ctypes.c_size_t(0)
+        assert L.lib.kvc_decode_attn(ctypes.byref(c), None, None, None, 1, H * G, None, None, ctypes.byref(n),
+                                     None) == 0
+        return n.value
+
+    def closed(B, H, D, R, q_cap, r_cap, G):
+        nt = q_cap // 32 + (r_cap + 31) // 32
+        waves = 8 if D <= 192 else 4
+        if -(-nt // waves) <= 6:
+            return 256
+        slots = B * H * (-(-G // 4)) * min(64, -(-nt // 12))
+        ml = -(-(slots * 4 * 8) // 256) * 256
+        return max(256, ml + slots * 4 * D * 4)
+
+    for args in ((4, 40, 128, 128, 32768, 160, 1), (1, 8, 128, 256, 4096, 288, 4), (8, 8, 128, 128, 608, 160, 4),
+                 (1, 1, 256, 16, 1600, 48, 16), (2, 3, 64, 16, 64, 48, 2), (1, 8, 128, 128, 8192, 160, 4)):
+        assert need(*args) == closed(*args), args

@@ -61,7 +61,9 @@ def test_quantize_parity(dtype, bits, D, with_idx):
 @pytest.mark.parametrize("dtype,bits,G,D,R,n", [
     ("bf16", 2, 4, 128, 16, 300), ("bf16", 4, 1, 128, 16, 300), ("f32", 2, 1, 64, 16, 250),
     ("bf16", 2, 2, 64, 0, 200), ("bf16", 4, 8, 32, 40, 160), ("f32", 4, 3, 256, 24, 130),
-    ("bf16", 2, 16, 64, 16, 100)])
+    ("bf16", 2, 16, 64, 16, 100),
+    # histories long enough for the split runs (several workgroups per unit, merged)
+    ("f32", 2, 1, 128, 16, 3000), ("f32", 4, 4, 128, 128, 2600), ("bf16", 2, 4, 128, 128, 4000)])
 def test_decode_parity_multi_step(dtype, bits, G, D, R, n):
     kvc = _kvc()
     B, Hkv = 2, 2

@@ -180,3 +180,27 @@ def test_weighted_invariants(seed):
 
 def test_weighted_layer_budgets_cap():
     assert budget.weighted_layer_budgets([1.0, 9.0], 100, prompt_len=150, window=20) == [20, 130]
+
+
+@pytest.mark.parametrize("name,bits", [("llama3_8b", 2), ("llama3_8b", 4), ("mistral_pyramid", 2),
+                                       ("long_context", 2), ("long_context", 4)])
+def test_layout_bytes_equal_the_built_cache(name, bits):
+    """footprint()['bytes_layout'] with a residual and with eviction equals the
+    bytes of the arrays oracle.quant.build_head_cache returns for each layer's
+    kept tokens (T = budget + W), summed over layers, times the KV heads: the
+    packed codes, the fp16 scale/zero words and the bf16 residual of the
+    blog's accounting ("The budget"), laid out as quant.py states."""
+    import synth
+    from oracle import quant
+
+    cfg = synth.CONFIGS[name]
+    L, Hkv, D, n, W, R = cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.prompt, cfg.window, cfg.residual
+    fp = budget.footprint(L, Hkv, D, n, W, 0, cfg.budget, cfg.pyramid, cfg.beta, bits, 32, 16, R)
+    rng = np.random.default_rng(5)
+    total = 0
+    for k in budget.layer_budgets(L, cfg.budget, cfg.pyramid, cfg.beta, n, W):
+        T = k + W
+        x = rng.standard_normal((T, D)).astype(np.float32)
+        c = quant.build_head_cache(x, x, np.arange(T), R, bits)
+        total += sum(c[key].nbytes for key in ("k_codes", "k_meta", "v_codes", "v_meta", "k_res", "v_res"))
+    assert fp["bytes_layout"] == float(total * Hkv)
