@@ -19,6 +19,9 @@ Sources (cited by page title and section in each function):
     Algorithm 1, the group size of Sec. 5.1, the KV-size analysis.
   * "CSKV: Training-Efficient Channel Shrinking for KV Cache in Long-Context
     Scenarios": the footprint claim of the introduction.
+  * MiniKV Sec. 4.3 "Selective KV Compatible Attention Kernels" (Fig. 9): the
+    prefill attention that also returns the attention each key accumulates;
+    blog "Eviction" and PyramidKV "Baselines": H2O heavy hitters.
 
 Precision: scores and attention in float64; the quantizer in exact IEEE float32
 with float16 scale/zero (numpy float32 ops and float16 casts round to nearest
@@ -36,6 +39,10 @@ Parity status of each function (pins live in ``tests/test_oracle_*.py``):
   decode.*            pinned (torch SDPA, dense special case, convex hull, blog
                       attention hook semantics, incremental flush == batch, at
                       groups 32 and 16)
+  prefill.*           pinned (torch SDPA for the output, pure-Python brute force
+                      and the harmonic closed form for the column sums, the
+                      row-mass invariant, the last W rows == window scores,
+                      H2O selection by brute-force sort, variance closed forms)
 """
 
-from . import budget, select, quant, decode  # noqa: F401
+from . import budget, select, quant, decode, prefill  # noqa: F401
