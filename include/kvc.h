@@ -22,6 +22,10 @@
  *   kvc_select_recent
  *                   position-only selection: attention sinks plus the recent
  *                   window, or the sliding window alone.
+ *   kvc_prefill_attn
+ *                   the prefill's causal attention that also returns the
+ *                   attention each key accumulates (MiniKV's selective
+ *                   flash-attention); kvc_select_h2o: heavy hitters on it.
  *
  * Conventions shared by every call
  *   Memory:   every device buffer is allocated and owned by the caller; the
@@ -232,6 +236,44 @@ kvc_status kvc_topk(const float *raw, int32_t B, int32_t Hkv, int32_t N, int32_t
  *   KVC_ERR_HIP. */
 kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32_t budget, int32_t sinks,
                              int32_t *idx, void *stream);
+
+/* ------------------------------------------------------------------ prefill
+ * Causal prefill attention with the attention accumulated by each key (MiniKV
+ * Sec. 4.3 "Selective KV Compatible Attention Kernels", Fig. 9: FlashAttention
+ * that also returns A_cumul along each key column, O(l_key) extra memory).
+ * For query head h (KV head j = h / (Hq/Hkv)) and row r:
+ *   out[b][h][r] = softmax over keys c <= r of q_r . k_c / sqrt(D), times V;
+ *   acc[b][j][c] = sum over the Hq/Hkv heads of KV head j and the rows r >= c
+ *                  of that softmax's probability of key c (the normalized
+ *                  probabilities: H2O's accumulated attention, blog
+ *                  "Eviction"; MiniKV's kernel omits the row normalization to
+ *                  save the per-row state, kept here as the workspace);
+ *   var[b][j]    = population variance of acc[b][j][0..n) (MiniKV Sec. 4.2 and
+ *                  Fig. 7: Var(A_cumul)), float64 sums as kvc_window_scores.
+ *   q [B][Hq][n][D], k, v [B][Hkv][n][D] in dtype (post-RoPE); out
+ *   [B][Hq][n][D] float32; acc [B][Hkv][n] float32 or NULL (no column sums);
+ *   var [B][Hkv] float32 or NULL (needs acc).  D in {32, 64, 128}.
+ * Workspace: the per-row log-sum-exp, B*Hq*n floats (ws == NULL: size query).
+ * acc is written in a fixed order (no atomics): the same inputs give the same
+ * bits.
+ * Errors: KVC_ERR_NULL (q, k, v or out NULL, var without acc), KVC_ERR_DTYPE,
+ *   KVC_ERR_SHAPE (B, Hq, Hkv, n < 1, Hq % Hkv, D not 32/64/128),
+ *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
+kvc_status kvc_prefill_attn(const void *q, const void *k, const void *v, kvc_dtype dtype, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t n, int32_t D, float *out, float *acc, float *var, void *ws,
+                            size_t *ws_bytes, void *stream);
+
+/* kvc_select_h2o: heavy-hitter selection (blog "Eviction: keep fewer tokens":
+ * H2O keeps the tokens with the largest accumulated attention plus a recent
+ * window; PyramidKV "Baselines").  As kvc_select, the window [n-W, n) is always
+ * kept and the k' = min(budget, n-W) largest of acc[b][j][0..n-W) are taken
+ * (ties to the lower position, no pooling), ascending, into idx [B][Hkv][k']
+ * int32; budget < 0 keeps all n-W.  acc [B][Hkv][n] float32 as written by
+ * kvc_prefill_attn (rows n apart).  idx may be NULL if k' == 0.
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE (B, Hkv < 1, W < 1, W > n),
+ *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
+kvc_status kvc_select_h2o(const float *acc, int32_t B, int32_t Hkv, int32_t n, int32_t W, int32_t budget,
+                          int32_t *idx, void *ws, size_t *ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ quantize
  * Prompt compression into an empty cache (MiniKV Alg. 1 prefill: heavy

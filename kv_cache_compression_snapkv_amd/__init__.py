@@ -7,6 +7,7 @@ the thin Python binding (same entry-point names); it needs ``libkvc.so``, built
 by ``python kv_cache_compression_snapkv_amd/build.py`` (or ``__graft_entry__.build()``).
 """
 
-from ._lib import (Cache, KvcError, LIB_PATH, decode_ws_bytes, kvc_budget, kvc_budget_weighted,  # noqa: F401
-                   kvc_decode_attn, kvc_quantize, kvc_select, kvc_select_recent, kvc_topk, kvc_window_scores,
-                   select_ws_bytes, topk_ws_bytes, window_scores_ws_bytes)
+from ._lib import (Cache, KvcError, LIB_PATH, decode_ws_bytes, h2o_ws_bytes, kvc_budget,  # noqa: F401
+                   kvc_budget_weighted, kvc_decode_attn, kvc_prefill_attn, kvc_quantize, kvc_select, kvc_select_h2o,
+                   kvc_select_recent, kvc_topk, kvc_window_scores, prefill_ws_bytes, select_ws_bytes, topk_ws_bytes,
+                   window_scores_ws_bytes)

@@ -17,7 +17,8 @@ KVC_F32, KVC_BF16 = 0, 1
 STATUS = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_BITS",
           5: "KVC_ERR_CAPACITY", 6: "KVC_ERR_WORKSPACE", 7: "KVC_ERR_HIP"}
 EXPORTS = ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
-           "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error", "kvc_status_string")
+           "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
+           "kvc_last_hip_error", "kvc_status_string")
 
 
 class KvcError(RuntimeError):
@@ -62,13 +63,16 @@ def _load():
     lib.kvc_window_scores.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_topk.argtypes = [P, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_select_recent.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
+    lib.kvc_prefill_attn.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, SZ, P]
+    lib.kvc_select_h2o.argtypes = [P, I32, I32, I32, I32, I32, P, P, SZ, P]
     lib.kvc_quantize.argtypes = [P, P, I32, I32, P, I32, I32, ctypes.POINTER(CacheStruct), P]
     lib.kvc_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P, SZ, P]
     lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_status_string.argtypes = [I32]
     lib.kvc_status_string.restype = ctypes.c_char_p
     for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
-              "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes", "kvc_last_hip_error"):
+              "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
+              "kvc_last_hip_error"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -231,6 +235,64 @@ def kvc_select(q_win, k, W, pool, budget, want_scores=False, ws=None, idx=None, 
                                         _ptr(idx), _ptr(scores) if want_scores else None, _ptr(ws),
                                         ctypes.byref(wsb), _stream(stream)))
     return (idx, scores) if want_scores else idx
+
+
+# ---------------------------------------------------------------- prefill
+def prefill_ws_bytes(dtype, B, Hq, Hkv, n, D):
+    need = ctypes.c_size_t(0)
+    _check("kvc_prefill_attn", lib.kvc_prefill_attn(None, None, None, dtype, B, Hq, Hkv, n, D, None, None, None,
+                                                    None, ctypes.byref(need), None))
+    return need.value
+
+
+def kvc_prefill_attn(q, k, v, want_acc=True, want_var=False, ws=None, out=None, acc=None, var=None, stream=None):
+    """Causal prefill attention: out [B][Hq][n][D] float32, plus the attention
+    each key accumulates, acc [B][Hkv][n] float32, and its variance [B][Hkv]."""
+    _contig(q, k, v)
+    B, Hq, n, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, n, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q [B][Hq][n][D], k and v [B][Hkv][n][D], one dtype")
+    dt = _dtype(q)
+    need = prefill_ws_bytes(dt, B, Hq, Hkv, n, D)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, Hq, n, D, dtype=torch.float32, device=q.device)
+    if (want_acc or want_var) and acc is None:
+        acc = torch.empty(B, Hkv, n, dtype=torch.float32, device=q.device)
+    if want_var and var is None:
+        var = torch.empty(B, Hkv, dtype=torch.float32, device=q.device)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("kvc_prefill_attn", lib.kvc_prefill_attn(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, n, D, _ptr(out),
+                                                    _ptr(acc) if (want_acc or want_var) else None,
+                                                    _ptr(var) if want_var else None, _ptr(ws), ctypes.byref(wsb),
+                                                    _stream(stream)))
+    return out, (acc if (want_acc or want_var) else None), (var if want_var else None)
+
+
+def h2o_ws_bytes(B, Hkv, n, W, budget):
+    need = ctypes.c_size_t(0)
+    _check("kvc_select_h2o", lib.kvc_select_h2o(None, B, Hkv, n, W, budget, None, None, ctypes.byref(need), None))
+    return need.value
+
+
+def kvc_select_h2o(acc, W, budget, ws=None, idx=None, stream=None):
+    """Heavy hitters of acc [B][Hkv][n] among [0, n-W): idx [B][Hkv][k'] int32."""
+    _contig(acc)
+    if acc.dtype != torch.float32:
+        raise TypeError("accumulated attention is float32")
+    B, Hkv, n = acc.shape
+    kk = (n - W) if budget < 0 else min(budget, n - W)
+    need = h2o_ws_bytes(B, Hkv, n, W, budget)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=acc.device)
+    if idx is None:
+        idx = torch.empty(B, Hkv, max(kk, 0), dtype=torch.int32, device=acc.device)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("kvc_select_h2o", lib.kvc_select_h2o(_ptr(acc), B, Hkv, n, W, budget, _ptr(idx), _ptr(ws), ctypes.byref(wsb),
+                                                _stream(stream)))
+    return idx
 
 
 # ---------------------------------------------------------------- cache

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvc.so")
-SOURCES = ["budget.cpp", "quantize.hip", "decode.hip", "decode_g16.hip", "select.hip"]
+SOURCES = ["budget.cpp", "quantize.hip", "decode.hip", "decode_g16.hip", "select.hip", "prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -29,10 +29,10 @@ FLAGS = [
 ]
 
 
-# Per-source extras.  decode.hip and select.hip: their values are never NaN for
+# Per-source extras.  decode.hip, select.hip and prefill.hip: their values are never NaN for
 # finite inputs (logits, softmax weights, -inf masks), so fmax needs no
 # canonicalization and the 16-lane DPP max folds into v_max_f32_dpp.
-EXTRA = {"decode.hip": ["-fno-honor-nans"], "select.hip": ["-fno-honor-nans"]}
+EXTRA = {"decode.hip": ["-fno-honor-nans"], "select.hip": ["-fno-honor-nans"], "prefill.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src):

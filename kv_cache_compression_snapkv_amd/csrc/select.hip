@@ -1225,6 +1225,13 @@ bool score_shape_ok(int B, int Hq, int Hkv, int n, int D, int W) {
 }
 
 }  // namespace
+
+// Population variance of each of `rows` rows of N floats (variance_kernel).
+kvc_status launch_variance(const float* raw, int rows, int N, float* var, hipStream_t st) {
+  hipLaunchKernelGGL(variance_kernel, dim3(rows), dim3(kVarThreads), 0, st, raw, N, var);
+  return check_launch();
+}
+
 }  // namespace kvc
 
 extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dtype, int32_t B, int32_t Hq,
@@ -1277,8 +1284,7 @@ extern "C" kvc_status kvc_window_scores(const void* q_win, const void* k, kvc_dt
   const ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, static_cast<char*>(ws), raw);
   kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st) : run_scores<uint16_t>(a, D / 32, B, st);
   if (s != KVC_OK || !var) return s;
-  hipLaunchKernelGGL(variance_kernel, dim3(B * Hkv), dim3(kVarThreads), 0, st, raw, N, var);
-  return check_launch();
+  return launch_variance(raw, B * Hkv, N, var, st);
 }
 
 extern "C" kvc_status kvc_topk(const float* raw, int32_t B, int32_t Hkv, int32_t N, int32_t pool, int32_t budget,
@@ -1312,4 +1318,25 @@ extern "C" kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32
   hipLaunchKernelGGL(recent_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRecentThreads), 0,
                      static_cast<hipStream_t>(stream), idx, total, kk, std::min(sinks, kk), N - kk);
   return check_launch();
+}
+
+extern "C" kvc_status kvc_select_h2o(const float* acc, int32_t B, int32_t Hkv, int32_t n, int32_t W, int32_t budget,
+                                     int32_t* idx, void* ws, size_t* ws_bytes, void* stream) {
+  using namespace kvc;
+  if (!ws_bytes) return KVC_ERR_NULL;
+  if (B < 1 || Hkv < 1 || W < 1 || W > n) return KVC_ERR_SHAPE;
+  const int N = n - W;
+  const TopWs tw = top_ws(B, Hkv, N);
+  if (!ws) {
+    *ws_bytes = tw.total;
+    return KVC_OK;
+  }
+  const int kk = budget < 0 ? N : std::min(budget, N);
+  if ((N > 0 && !acc) || (kk > 0 && !idx)) return KVC_ERR_NULL;
+  if (*ws_bytes < tw.total) return KVC_ERR_WORKSPACE;
+  if (N == 0) return KVC_OK;
+  // the first n - W entries of each accumulated-attention row, no pooling
+  TopArgs t = top_args(acc, Hkv, N, kk, 1, tw, static_cast<char*>(ws), idx, nullptr);
+  t.ld = n;
+  return run_topk(t, B, static_cast<hipStream_t>(stream));
 }

@@ -133,6 +133,21 @@ def prompt_layer(cfg, layer, device="cpu"):
     return {"q_win": q_win.to(dt), "k": k.to(dt), "v": v.to(dt)}
 
 
+def prefill_layer(cfg, layer, device="cpu", n=None):
+    """Prompt tensors of one layer with the queries of every prompt row:
+    q [B][Hq][n][D] (its last W rows are prompt_layer's q_win), k, v
+    [B][Hkv][n][D] as prompt_layer (same key model, heavy hitters and sinks).
+    n < cfg.prompt takes the first n positions of a config shortened to n."""
+    if n is not None and n != cfg.prompt:
+        from dataclasses import replace
+        cfg = replace(cfg, prompt=n, name=f"{cfg.name}@{n}")
+    p = prompt_layer(cfg, layer, device)
+    B, Hq, D, n, W = cfg.batch, cfg.q_heads, cfg.head_dim, cfg.prompt, cfg.window
+    q_rest = torch.randn(B, Hq, n - W, D, generator=_gen(device, cfg.seed, cfg.name, layer, "q_rest"),
+                         device=device, dtype=torch.float32).to(torch_dtype(cfg))
+    return {"q": torch.cat([q_rest, p["q_win"]], dim=2).contiguous(), "k": p["k"], "v": p["v"]}
+
+
 def decode_inputs(cfg, layer, step, device="cpu"):
     """Decode-step tensors of one layer: q [B][Hq][D], k_new, v_new [B][Hkv][D]."""
     B, Hq, Hkv, D = cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim
