@@ -30,7 +30,9 @@
  * Conventions shared by every call
  *   Memory:   every device buffer is allocated and owned by the caller; the
  *             library allocates no device memory and keeps no global mutable
- *             state besides a thread-local last-HIP-error code.  Scratch space
+ *             state besides a thread-local last-HIP-error code (and, for
+ *             kvc_decode_attn_noalloc only, its per-device scratch array and
+ *             that array's address, set once per device).  Scratch space
  *             comes from a caller workspace: pass ws == NULL to have the
  *             required size written to *ws_bytes (nothing is launched).
  *   Streams:  device work is only enqueued on `stream` (a hipStream_t passed as
@@ -315,6 +317,21 @@ kvc_status kvc_quantize(const void *k, const void *v, kvc_dtype dtype, int32_t n
 kvc_status kvc_decode_attn(kvc_cache *cache, const void *q, const void *k_new, const void *v_new,
                            kvc_dtype dtype, int32_t Hq, float *out, void *ws, size_t *ws_bytes,
                            void *stream);
+
+/* The same decode step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the scratch that kvc_decode_attn takes from `ws` comes from a
+ * static device array inside the library, one per device, 16 MiB, reached
+ * through hipGetSymbolAddress once per device.  No allocating call is made; the
+ * caller still passes q, k_new, v_new and out.  Results and cache updates are
+ * those of kvc_decode_attn.  Calls that overlap on one device share the array
+ * and race (serialize them, e.g. on one stream); nothing in it needs clearing
+ * between calls.
+ * Errors: as kvc_decode_attn, with KVC_ERR_WORKSPACE when this call's split
+ *   partials (units x splits x 4 heads x (D + 2) floats) exceed 16 MiB; the
+ *   per-device address lookup failing gives KVC_ERR_HIP. */
+kvc_status kvc_decode_attn_noalloc(kvc_cache *cache, const void *q, const void *k_new, const void *v_new,
+                                   kvc_dtype dtype, int32_t Hq, float *out, void *stream);
 
 /* hipError_t of the last failed HIP call on this thread (0 if none). */
 int kvc_last_hip_error(void);

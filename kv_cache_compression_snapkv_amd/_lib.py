@@ -17,8 +17,8 @@ KVC_F32, KVC_BF16 = 0, 1
 STATUS = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_BITS",
           5: "KVC_ERR_CAPACITY", 6: "KVC_ERR_WORKSPACE", 7: "KVC_ERR_HIP"}
 EXPORTS = ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
-           "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
-           "kvc_last_hip_error", "kvc_status_string")
+           "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_decode_attn_noalloc",
+           "kvc_cache_sizes", "kvc_last_hip_error", "kvc_status_string")
 
 
 class KvcError(RuntimeError):
@@ -67,12 +67,13 @@ def _load():
     lib.kvc_select_h2o.argtypes = [P, I32, I32, I32, I32, I32, P, P, SZ, P]
     lib.kvc_quantize.argtypes = [P, P, I32, I32, P, I32, I32, ctypes.POINTER(CacheStruct), P]
     lib.kvc_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P, SZ, P]
+    lib.kvc_decode_attn_noalloc.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P]
     lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_status_string.argtypes = [I32]
     lib.kvc_status_string.restype = ctypes.c_char_p
     for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
-              "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_cache_sizes",
-              "kvc_last_hip_error"):
+              "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_decode_attn_noalloc",
+              "kvc_cache_sizes", "kvc_last_hip_error"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -385,4 +386,15 @@ def kvc_decode_attn(cache, q, k_new, v_new, out=None, ws=None, stream=None):
     _check("kvc_decode_attn", lib.kvc_decode_attn(ctypes.byref(cache.s), _ptr(q), _ptr(k_new), _ptr(v_new),
                                                   _dtype(q), Hq, _ptr(out), _ptr(ws), ctypes.byref(wsb),
                                                   _stream(stream)))
+    return out
+
+
+def kvc_decode_attn_noalloc(cache, q, k_new, v_new, out, stream=None):
+    """kvc_decode_attn with the library's static per-device scratch instead of a
+    workspace (no device allocation inside the call; `out` is the caller's)."""
+    _contig(q, k_new, v_new, out)
+    B, Hq, D = q.shape
+    _check("kvc_decode_attn_noalloc", lib.kvc_decode_attn_noalloc(ctypes.byref(cache.s), _ptr(q), _ptr(k_new),
+                                                                  _ptr(v_new), _dtype(q), Hq, _ptr(out),
+                                                                  _stream(stream)))
     return out

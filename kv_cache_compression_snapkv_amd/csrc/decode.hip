@@ -29,6 +29,7 @@
 //           and the lanes of a group are summed once at the end of the run.
 //   residual: B = bf16 keys/values as stored, A = q or p split in two.
 #include <algorithm>
+#include <mutex>
 
 #include "kvc_internal.h"
 
@@ -1324,10 +1325,68 @@ size_t decode_ws_need(const kvc_cache* c, int G) {
   return std::max<size_t>(w, 256);
 }
 
-// The group-32 attention launch for a cache whose state already includes this
-// step's append (a.r_total, a.r_new set; a.q, a.k_new, a.v_new set).
-kvc_status decode_g32(const kvc_cache& c, DecArgs& a, kvc_dtype dtype, int Hq, float* out, void* ws, hipStream_t st) {
+// One decode step, planned before anything is launched: the cache state after
+// the step (append, flush), the attention launch shape and the workspace bytes
+// this call uses.
+struct Step {
+  kvc_cache nc;        // state after the step
+  bool flush;
+  int ngroups;         // flushed groups (1, or R/g for the whole-residual policy)
+  int r_total, r_new;  // residual tokens attended; the appended token's index (-1: flushed)
+  Plan plan;           // group-32 launch shape
+  size_t used;         // workspace bytes this call uses
+};
+kvc_status plan_step(const kvc_cache* cache, int dtype, int Hq, Step* sp) {
+  const int R = cache->residual, g = cache_group(cache);
+  const int G = Hq / cache->kv_heads, KS = cache->head_dim / 32;
+  if (cache->r_len + 1 > cache->r_cap) return KVC_ERR_CAPACITY;
+  // tokens a flush moves into the packed history: one group, or with flush_all
+  // the whole residual of R tokens (R/g groups, the appended token last)
+  const int moved = cache->flush_all ? R : g;
+  sp->flush = (cache->r_len + 1 == R + (cache->flush_all ? 0 : g));
+  if (sp->flush && cache->q_len + moved > cache->q_cap) return KVC_ERR_CAPACITY;
+  sp->nc = *cache;
+  sp->ngroups = moved / g;
+  if (sp->flush) {
+    sp->nc.q_len += moved;
+    sp->nc.r_len = cache->r_len + 1 - moved;
+    sp->nc.r_start = (cache->r_start + moved) % cache->r_cap;
+    sp->r_total = sp->nc.r_len;
+    sp->r_new = -1;
+  } else {
+    sp->r_new = cache->r_len;
+    sp->r_total = cache->r_len + 1;
+    sp->nc.r_len += 1;
+  }
+  if (g != kGroup) {
+    sp->used = g16_ws_bytes(cache, Hq);
+    return KVC_OK;
+  }
+  const int NT = sp->nc.q_len / kGroup + (sp->r_total + kGroup - 1) / kGroup;
+  Occupancy oc{1, 256};
+  if (!is_short(NT, KS)) {
+    const kvc_status s = occupancy(dtype, cache->bits, KS, G, &oc);
+    if (s != KVC_OK) return s;
+  }
+  sp->plan = plan(NT, cache->batch * cache->kv_heads, G, KS, oc);
+  const size_t units = static_cast<size_t>(cache->batch) * cache->kv_heads * ((G + sp->plan.hbs - 1) / sp->plan.hbs);
+  sp->used = sp->plan.nb > 1 ? ws_layout_for(units * sp->plan.nb, cache->head_dim).total : 0;
+  return KVC_OK;
+}
+
+// The group-32 attention launch of a planned step (split partials laid out in
+// ws for this call's slots).
+kvc_status decode_g32(const Step& sp, const void* q, const void* k_new, const void* v_new, kvc_dtype dtype, int Hq,
+                      float* out, void* ws, hipStream_t st) {
+  const kvc_cache& c = sp.nc;
+  const Plan& p = sp.plan;
   const int Hkv = c.kv_heads, G = Hq / Hkv, KS = c.head_dim / 32;
+  DecArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.r_total = sp.r_total;
+  a.r_new = sp.r_new;
   a.k_codes = c.k_codes;
   a.k_meta = c.k_meta;
   a.v_codes = c.v_codes;
@@ -1342,17 +1401,11 @@ kvc_status decode_g32(const kvc_cache& c, DecArgs& a, kvc_dtype dtype, int Hq, f
   a.r_cap = c.r_cap;
   a.r_start = c.r_start;
   a.q_len = c.q_len;
-  const int NT = a.q_len / kGroup + (a.r_total + kGroup - 1) / kGroup;
-  Occupancy oc{1, 256};
-  if (!is_short(NT, KS)) {
-    const kvc_status s = occupancy(dtype, c.bits, KS, G, &oc);
-    if (s != KVC_OK) return s;
-  }
-  const Plan p = plan(NT, c.batch * Hkv, G, KS, oc);
   a.hbs = p.hbs;
   a.HB = (G + p.hbs - 1) / p.hbs;
   a.nb = p.nb;
-  const WsLayout W = ws_layout_for(max_slots(&c, G), c.head_dim);
+  const size_t slots = static_cast<size_t>(c.batch) * Hkv * a.HB * p.nb;
+  const WsLayout W = ws_layout_for(slots, c.head_dim);
   char* w = static_cast<char*>(ws);
   a.part_ml = reinterpret_cast<float2*>(w + W.part_ml);
   a.part_o = reinterpret_cast<float*>(w + W.part_o);
@@ -1362,12 +1415,43 @@ kvc_status decode_g32(const kvc_cache& c, DecArgs& a, kvc_dtype dtype, int Hq, f
   a.rcp_hb = 1.0f / static_cast<float>(a.HB);
   a.rcp_xhb = 1.0f / static_cast<float>(kXcds * a.HB);
   const int NWT = p.nb * p.nwv;
-  const SplitParams sp = split_params(NWT, a.q_len / kGroup, (a.r_total + kGroup - 1) / kGroup);
-  a.split_nA = sp.nA;
-  a.split_hA = sp.hA;
-  a.split_hB = sp.hB;
+  const SplitParams spl = split_params(NWT, a.q_len / kGroup, (a.r_total + kGroup - 1) / kGroup);
+  a.split_nA = spl.nA;
+  a.split_hA = spl.hA;
+  a.split_hB = spl.hB;
   a.sp_new = a.r_new >= 0 ? NWT - 1 - (a.r_new / kGroup) % NWT : -1;
   return launch_decode(a, dtype, c.bits, KS, p.nwv, c.batch, st);
+}
+
+// Validation shared by both decode entry points (before anything else).
+kvc_status decode_args_status(const kvc_cache* cache, kvc_dtype dtype, int Hq) {
+  if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
+  const kvc_status s = cache_shape_status(cache);
+  if (s != KVC_OK) return s;
+  const int Hkv = cache->kv_heads;
+  if (Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return KVC_ERR_SHAPE;
+  return KVC_OK;
+}
+
+// Enqueue a planned step (flush, then attention) and commit the host state.
+// The state goes to *cache only once every launch has been enqueued: the flush
+// and the attention kernel write past the current lengths only (codes at
+// q_len.., the appended token's ring row), so a failed call leaves the cache as
+// it was.
+kvc_status run_step(kvc_cache* cache, const Step& sp, const void* q, const void* k_new, const void* v_new,
+                    kvc_dtype dtype, int Hq, float* out, void* ws, hipStream_t st) {
+  kvc_status s = KVC_OK;
+  if (sp.flush) {
+    s = launch_flush(cache, sp.ngroups, k_new, v_new, dtype, st);
+    if (s != KVC_OK) return s;
+  }
+  if (cache_group(cache) != kGroup) {
+    s = launch_decode_g16(&sp.nc, q, k_new, v_new, dtype, Hq, sp.r_total, sp.r_new, out, ws, st);
+  } else {
+    s = decode_g32(sp, q, k_new, v_new, dtype, Hq, out, ws, st);
+  }
+  if (s == KVC_OK) *cache = sp.nc;
+  return s;
 }
 
 }  // namespace
@@ -1378,57 +1462,79 @@ extern "C" kvc_status kvc_decode_attn(kvc_cache* cache, const void* q, const voi
                                       void* ws, size_t* ws_bytes, void* stream) {
   using namespace kvc;
   if (!cache_ok(cache) || !ws_bytes) return KVC_ERR_NULL;
-  if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
-  kvc_status s = cache_shape_status(cache);
+  kvc_status s = decode_args_status(cache, dtype, Hq);
   if (s != KVC_OK) return s;
-  const int Hkv = cache->kv_heads;
-  if (Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return KVC_ERR_SHAPE;
-  const int G = Hq / Hkv;
-  const int KS = cache->head_dim / 32;
-  const int g = cache_group(cache);
-  const size_t need = decode_ws_need(cache, G);
+  const size_t need = decode_ws_need(cache, Hq / cache->kv_heads);
   if (!ws) {
     *ws_bytes = need;
     return KVC_OK;
   }
   if (!q || !k_new || !v_new || !out) return KVC_ERR_NULL;
   if (*ws_bytes < need) return KVC_ERR_WORKSPACE;
-  const int R = cache->residual;
-  if (cache->r_len + 1 > cache->r_cap) return KVC_ERR_CAPACITY;
-  // tokens a flush moves into the packed history: one group, or with flush_all
-  // the whole residual of R tokens (R/g groups, the appended token last)
-  const int moved = cache->flush_all ? R : g;
-  const bool flush = (cache->r_len + 1 == R + (cache->flush_all ? 0 : g));
-  if (flush && cache->q_len + moved > cache->q_cap) return KVC_ERR_CAPACITY;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  Step sp;
+  s = plan_step(cache, dtype, Hq, &sp);
+  if (s != KVC_OK) return s;
+  return run_step(cache, sp, q, k_new, v_new, dtype, Hq, out, ws, static_cast<hipStream_t>(stream));
+}
 
-  // The state after this step goes to *cache only once every launch has been
-  // enqueued: the flush and the attention kernel write past the current
-  // lengths only (codes at q_len.., the appended token's ring row), so a failed
-  // call leaves the cache as it was.
-  kvc_cache nc = *cache;
-  DecArgs a;
-  a.q = q;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  if (flush) {
-    s = launch_flush(cache, moved / g, k_new, v_new, dtype, st);
-    if (s != KVC_OK) return s;
-    nc.q_len += moved;
-    nc.r_len = cache->r_len + 1 - moved;
-    nc.r_start = (cache->r_start + moved) % cache->r_cap;
-    a.r_total = nc.r_len;
-    a.r_new = -1;
-  } else {
-    a.r_new = cache->r_len;
-    a.r_total = cache->r_len + 1;
-    nc.r_len += 1;
+// ---------------------------------------------------------------- no-allocation variant
+// kvc_decode_attn_noalloc takes its scratch (the split partials) from this
+// file-scope device array instead of a caller workspace.  Each device holds its
+// own copy for the life of the process; host code reaches it only through the
+// address hipGetSymbolAddress returns for that device (the symbol's name is a
+// host-side stand-in, not a device address).  No kernel needs it cleared: every
+// slot a merge reads was written by the same call.  Calls that overlap on one
+// device share it and race.
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kScratchDevices = 64;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// The device address of `scratch` on the current device, looked up once per
+// device (std::call_once) -- the library's only process-wide state besides the
+// thread-local error code.
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kScratchDevices];
+
+kvc_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    kvc::set_last_hip_error(e);
+    return KVC_ERR_HIP;
   }
-  if (g != kGroup) {
-    s = launch_decode_g16(&nc, q, k_new, v_new, dtype, Hq, a.r_total, a.r_new, out, ws, st);
-  } else {
-    s = decode_g32(nc, a, dtype, Hq, out, ws, st);
+  if (dev < 0 || dev >= kScratchDevices) return KVC_ERR_SHAPE;
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&sl] { sl.err = hipGetSymbolAddress(&sl.ptr, HIP_SYMBOL(scratch)); });
+  if (sl.err != hipSuccess || !sl.ptr) {
+    kvc::set_last_hip_error(sl.err != hipSuccess ? sl.err : hipErrorInvalidSymbol);
+    return KVC_ERR_HIP;
   }
-  if (s == KVC_OK) *cache = nc;
-  return s;
+  *out = sl.ptr;
+  return KVC_OK;
+}
+}  // namespace
+
+extern "C" kvc_status kvc_decode_attn_noalloc(kvc_cache* cache, const void* q, const void* k_new,
+                                              const void* v_new, kvc_dtype dtype, int32_t Hq, float* out,
+                                              void* stream) {
+  using namespace kvc;
+  if (!cache_ok(cache)) return KVC_ERR_NULL;
+  kvc_status s = decode_args_status(cache, dtype, Hq);
+  if (s != KVC_OK) return s;
+  if (!q || !k_new || !v_new || !out) return KVC_ERR_NULL;
+  Step sp;
+  s = plan_step(cache, dtype, Hq, &sp);
+  if (s != KVC_OK) return s;
+  if (sp.used > kScratchBytes) return KVC_ERR_WORKSPACE;
+  void* ws = nullptr;
+  s = scratch_ptr(&ws);
+  if (s != KVC_OK) return s;
+  return run_step(cache, sp, q, k_new, v_new, dtype, Hq, out, ws, static_cast<hipStream_t>(stream));
 }
