@@ -46,9 +46,11 @@ def parse():
     ap.add_argument("--budget-policy", default="workload", choices=("workload", "var-prop", "var-inv"),
                     help="per-layer budgets: the workload's (uniform or pyramid), or proportional to the variance "
                          "of each layer's window scores or to its reciprocal (scores, budgets, then top-k)")
-    ap.add_argument("--selector", default="snapkv", choices=("snapkv", "sinks", "window"),
-                    help="prompt selection: observation-window scores (kvc_select), or position-only with "
-                         "kvc_select_recent: --sinks leading tokens plus the recent window, or the sliding window")
+    ap.add_argument("--selector", default="snapkv", choices=("snapkv", "sinks", "window", "h2o"),
+                    help="prompt selection: observation-window scores (kvc_select); position-only with "
+                         "kvc_select_recent: --sinks leading tokens plus the recent window, or the sliding window; "
+                         "h2o: the prefill attention of every prompt row with accumulated column attention "
+                         "(kvc_prefill_attn), then heavy hitters plus the window (kvc_select_h2o)")
     ap.add_argument("--sinks", type=int, default=4)
     ap.add_argument("--streams", type=int, default=1,
                     help="prompt compression runs the layers round-robin on this many streams (they are "
@@ -59,8 +61,8 @@ def parse():
     ap.add_argument("--group", type=int, default=32, choices=(32, 16),
                     help="quantization group: 32, or MiniKV's 16 (its own decode kernel)")
     a = ap.parse_args()
-    if a.selector != "snapkv" and a.budget_policy != "workload":
-        ap.error("--budget-policy var-prop/var-inv needs the window scores of --selector snapkv")
+    if a.selector in ("sinks", "window") and a.budget_policy != "workload":
+        ap.error("--budget-policy var-prop/var-inv needs attention scores (--selector snapkv or h2o)")
     return a
 
 
@@ -191,7 +193,10 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     from an untimed pass over the same prompts), then kvc_topk and kvc_quantize
     run per layer.  selector sinks / window: kvc_select_recent replaces
     kvc_select (first `sinks` prompt tokens plus the most recent; none for the
-    sliding window)."""
+    sliding window).  selector h2o: kvc_prefill_attn (the causal attention of
+    every prompt row and the attention each key accumulates; its variance for
+    the variance policies) then kvc_select_h2o replace kvc_select; the prefill
+    attention alone is also timed, for its MFMA roofline."""
     import torch
 
     import kv_cache_compression_snapkv_amd as kvc
@@ -206,10 +211,26 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     if layers is not None:
         L = min(L, layers)
     varp = policy != "workload" and cfg.budget >= 0
+    h2o = selector == "h2o" and cfg.budget >= 0
 
     # inputs resident in HBM before timing
-    prompts = [synth.prompt_layer(cfg, l, dev) for l in range(L)]
-    if varp:
+    prompts = [(synth.prefill_layer if h2o else synth.prompt_layer)(cfg, l, dev) for l in range(L)]
+    if h2o:
+        dt_code = 1 if in_bytes == 2 else 0
+        accs = [torch.empty(B, Hkv, n, dtype=torch.float32, device=dev) for _ in range(L)]
+        lvars = [torch.empty(B, Hkv, dtype=torch.float32, device=dev) for _ in range(L)]
+        attn_out = torch.empty(B, Hq, n, D, dtype=torch.float32, device=dev)
+        pf_ws = torch.empty(kvc.prefill_ws_bytes(dt_code, B, Hq, Hkv, n, D), dtype=torch.uint8, device=dev)
+        if varp:
+            for l in range(L):
+                kvc.kvc_prefill_attn(prompts[l]["q"], prompts[l]["k"], prompts[l]["v"], want_var=True, ws=pf_ws,
+                                     out=attn_out, acc=accs[l], var=lvars[l])
+            score = [max(float(v.double().mean()), 1e-300) for v in lvars]
+            weights = score if policy == "var-prop" else [1.0 / x for x in score]
+            budgets, fp = kvc.kvc_budget_weighted(L, Hkv, D, n, W, cfg.decode_steps, cfg.budget, weights, bits=bits,
+                                                  group=group, meta_bits=16, residual=cfg.residual)
+        h2o_ws = torch.empty(max(kvc.h2o_ws_bytes(B, Hkv, n, W, b) for b in budgets), dtype=torch.uint8, device=dev)
+    elif varp:
         N = n - W
         raws = [torch.empty(B, Hkv, N, dtype=torch.float32, device=dev) for _ in range(L)]
         lvars = [torch.empty(B, Hkv, dtype=torch.float32, device=dev) for _ in range(L)]
@@ -231,7 +252,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
                                 group=group, flush_all=flush_all))
         idxs.append(torch.empty(B, Hkv, budgets[l], dtype=torch.int32, device=dev) if cfg.budget >= 0 else None)
     sel_ws = torch.empty(max(kvc.select_ws_bytes(1 if in_bytes == 2 else 0, B, Hq, Hkv, n, D, W, cfg.pool, b)
-                             for b in budgets) if cfg.budget >= 0 else 1, dtype=torch.uint8, device=dev)
+                             for b in budgets) if cfg.budget >= 0 and not h2o else 1, dtype=torch.uint8, device=dev)
     dec_ws = torch.zeros(max(kvc.decode_ws_bytes(c, Hq, 1 if in_bytes == 2 else 0) for c in caches),
                          dtype=torch.uint8, device=dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
@@ -241,7 +262,11 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     ns = max(1, streams)
     side = [torch.cuda.Stream(device=dev) for _ in range(ns)] if ns > 1 else []
     sel_wss = [sel_ws] + [torch.empty_like(sel_ws) for _ in range(ns - 1)]
-    if varp:
+    if h2o:
+        pf_wss = [pf_ws] + [torch.empty_like(pf_ws) for _ in range(ns - 1)]
+        h2o_wss = [h2o_ws] + [torch.empty_like(h2o_ws) for _ in range(ns - 1)]
+        attn_outs = [attn_out] + [torch.empty_like(attn_out) for _ in range(ns - 1)]
+    elif varp:
         sc_wss = [sc_ws] + [torch.empty_like(sc_ws) for _ in range(ns - 1)]
         tk_wss = [tk_ws] + [torch.empty_like(tk_ws) for _ in range(ns - 1)]
 
@@ -261,9 +286,23 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         for sd in side:
             cur.wait_stream(sd)
 
+    def attn_all():
+        """The prefill attention (with column sums) of every layer."""
+        for l in range(L):
+            p = prompts[l]
+            kvc.kvc_prefill_attn(p["q"], p["k"], p["v"], ws=pf_ws, out=attn_out, acc=accs[l])
+
     def prefill():
         for c in caches:
             c.reset()
+        if h2o:
+            def h2o_one(l, k):
+                p = prompts[l]
+                kvc.kvc_prefill_attn(p["q"], p["k"], p["v"], ws=pf_wss[k], out=attn_outs[k], acc=accs[l])
+                kvc.kvc_select_h2o(accs[l], W, budgets[l], ws=h2o_wss[k], idx=idxs[l])
+                kvc.kvc_quantize(p["k"], p["v"], caches[l], idx=idxs[l], W=W)
+            on_streams(h2o_one)
+            return
         if varp:
             # the same layer -> stream mapping orders each layer's scores before its top-k
             on_streams(lambda l, k: kvc.kvc_window_scores(prompts[l]["q_win"], prompts[l]["k"], W, ws=sc_wss[k],
@@ -334,7 +373,39 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     step_ms = sum(e0.elapsed_time(e2) for e0, _, e2 in recs) / steps
     ncalls = len(call_bytes)
     achieved = sum(call_bytes) / (dec_ms * 1e-3) / 1e9
-    sel = {"snapkv": "", "sinks": f"{sinks} sinks + recent window, ", "window": "sliding window, "}[selector]
+    attn = None
+    if h2o:
+        # the prefill attention alone (every layer), for its MFMA roofline
+        if graph:
+            g_attn = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_attn):
+                attn_all()
+            run_attn = g_attn.replay
+        else:
+            run_attn = attn_all
+        run_attn()
+        torch.cuda.synchronize()
+        ea = []
+        for _ in range(max(1, min(steps, 5))):
+            a0, a1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            a0.record(stream)
+            run_attn()
+            a1.record(stream)
+            ea.append((a0, a1))
+        torch.cuda.synchronize()
+        attn_ms = sum(a0.elapsed_time(a1) for a0, a1 in ea) / len(ea)
+        flops = 4.0 * D * Hq * B * n * (n + 1) / 2 * L
+        peak = 2500.0 if in_bytes == 2 else 157.3
+        tf = flops / (attn_ms * 1e-3) / 1e12
+        attn = {"kernel": "fa_fwd_kernel + colsum_kernel (kvc_prefill_attn), every layer", "bound": "mfma",
+                "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak, "traffic": None,
+                "ms_per_layer": attn_ms / L, "algorithmic_flops_per_layer": flops / L,
+                "flops_note": "4*D*Hq*B*n(n+1)/2 per layer: Q K^T and P V over the causal half; the column-sum pass "
+                              "recomputes Q K^T and is not counted"}
+        if graph:
+            del g_attn
+    sel = {"snapkv": "", "sinks": f"{sinks} sinks + recent window, ", "window": "sliding window, ",
+           "h2o": "H2O heavy hitters on the prefill's accumulated attention, "}[selector]
     desc = (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
             f"prompt {n}, {cfg.dtype} inputs, W={W}, {sel}pool {cfg.pool}, budget "
             f"{'all' if cfg.budget < 0 else (policy + ' avg ' if varp else 'pyramid avg ' if cfg.pyramid else '') + str(cfg.budget)}, "
@@ -343,7 +414,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     res = {
         "desc": desc, "budgets": budgets, "footprint": fp,
         "tokens_per_s": B * cfg.decode_steps / (dec_ms * 1e-3),
-        "step_ms": step_ms, "pre_ms": pre_ms, "dec_ms": dec_ms, "wall": wall,
+        "step_ms": step_ms, "pre_ms": pre_ms, "dec_ms": dec_ms, "wall": wall, "prefill_attention": attn,
         "roofline": {
             "kernel": ((("decode_kernel (+ merge_kernel" if group == 32 else "decode_g16_kernel (+ merge_g16_kernel")
                         + (f"; flush_kernel of {cfg.residual // group} groups on 1 step in {cfg.residual})"
@@ -357,22 +428,28 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         },
     }
     del prompts, dec, caches, idxs, sel_ws, sel_wss, dec_ws, g_pre, g_dec, side
-    if varp:
+    if h2o:
+        del accs, lvars, attn_out, attn_outs, pf_ws, pf_wss, h2o_ws, h2o_wss
+    elif varp:
         del raws, lvars, sc_ws, tk_ws, sc_wss, tk_wss
     torch.cuda.empty_cache()
     return res
 
 
-SUB_WORKLOADS = (("llama2_13b_mha", 4), ("llama2_13b_mha", 2), ("llama3_8b", 2), ("mistral_pyramid", 2),
-                 ("long_context", 2))
+# (workload, bits, selector): every other workload and width, and the H2O path
+SUB_WORKLOADS = (("llama2_13b_mha", 4, "snapkv"), ("llama2_13b_mha", 2, "snapkv"), ("llama3_8b", 2, "snapkv"),
+                 ("mistral_pyramid", 2, "snapkv"), ("long_context", 2, "snapkv"), ("llama3_8b", 2, "h2o"))
 
 
-def entry(r, cfg, bits, steps, warmup):
+def entry(r, cfg, bits, steps, warmup, selector):
     """The figures of one workload run (a sub-workload line)."""
-    return {"workload": r["desc"], "bits": bits, "decode_tokens_per_s": r["tokens_per_s"],
-            "avg_call_us": r["roofline"]["avg_call_us"], "ms_per_step": r["step_ms"],
-            "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch, "steps": steps, "warmup": warmup,
-            "roofline": r["roofline"]}
+    e = {"workload": r["desc"], "bits": bits, "selector": selector, "decode_tokens_per_s": r["tokens_per_s"],
+         "avg_call_us": r["roofline"]["avg_call_us"], "ms_per_step": r["step_ms"],
+         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch, "steps": steps, "warmup": warmup,
+         "roofline": r["roofline"]}
+    if r["prefill_attention"] is not None:
+        e["prefill_attention"] = r["prefill_attention"]
+    return e
 
 
 def main():
@@ -412,16 +489,18 @@ def main():
         "wall_s_timed": r["wall"],
         "footprint_bytes_per_prompt_token": r["footprint"]["bytes_per_prompt_token"],
     }
+    if r["prefill_attention"] is not None:
+        res["prefill_attention"] = r["prefill_attention"]
     if not args.no_sub:
         # every other workload and width, each timed the same way (fewer steps)
         sub_steps, sub_warm = max(1, min(args.steps, args.sub_steps)), max(1, min(args.warmup, 2))
         res["sub_workloads"] = []
-        for name, sb in SUB_WORKLOADS:
-            if (name, sb) == (args.workload, bits):
+        for name, sb, ssel in SUB_WORKLOADS:
+            if (name, sb, ssel) == (args.workload, bits, args.selector):
                 continue
             sc = synth.CONFIGS[name]
-            h = run(sc, sb, sub_steps, sub_warm)
-            res["sub_workloads"].append(entry(h, sc, sb, sub_steps, sub_warm))
+            h = run(sc, sb, sub_steps, sub_warm, selector=ssel)
+            res["sub_workloads"].append(entry(h, sc, sb, sub_steps, sub_warm, ssel))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"], group=args.group, flush_all=args.flush_all)
     print(json.dumps(res))

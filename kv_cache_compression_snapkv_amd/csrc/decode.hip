@@ -719,8 +719,10 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
       for (int i = 0; i < 2 * NGV; ++i) {
         oacc[i][0] *= alpha[0];
         oacc[i][1] *= alpha[0];
-        oacc[i][2] *= alpha[1];
-        oacc[i][3] *= alpha[1];
+        if constexpr (HBS > 1) {  // rows 2-3 of a lane quarter hold the second head
+          oacc[i][2] *= alpha[1];
+          oacc[i][3] *= alpha[1];
+        }
       }
       // per-head factors for the value corrections (lanes of quarter h/2 hold head h)
 #pragma unroll
@@ -875,7 +877,9 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
           VRegs vcur;
           slot_k(slot, kn);
           slot_v(slot, vcur);
-          if (nxt) k_stage(kn);
+          // unconditional: the last iteration's key part is a clamped copy of
+          // an existing tile, and its operand rows are never read
+          k_stage(kn);
           v_stage(vcur);
           wave_sync();
           float x[2][2];
@@ -906,7 +910,7 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
       VRegs& vcur = vring[u % NV];
       if (tt < th_end) {
         const bool nxt = tt + 1 < th_end;
-        if (nxt) k_stage(kn);
+        k_stage(kn);  // unconditional, as above
         v_stage(vcur);
         wave_sync();
         float x[2][2];
@@ -1124,43 +1128,54 @@ __global__ __launch_bounds__(64 * NWV, (min_blocks<BITS, KS, NWV, HBS>())) void 
   }
 }
 
-// Combine the per-block partials of each (batch, KV head, head block): the
-// split weights 2^(m_s - M)/L per head go to LDS first, then every output is an
-// independent-load weighted sum over the splits.
+// Combine the per-block partials of each (batch, KV head, head block).  Every
+// output element's thread reads the (m, l) of all splits of its head and its o
+// values, all requested before any is used (one memory round trip), and forms
+// M = max m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s in split
+// order.  Splits with l = 0 (no tokens) have weight 0.
 constexpr int kMaxNb = 64;
 constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 8;  // splits whose loads are in flight together
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* part_o, const float2* part_ml, float* out,
                                                               int Hq, int Hkv, int G, int HB, int hbs, int D, int nb) {
-  __shared__ float wgt[kHB][kMaxNb];
   const int jh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int j = jh / HB, hb = jh % HB, h0 = hb * hbs;
   const int Gb = min(hbs, G - h0);
   const size_t base = ((static_cast<size_t>(b) * Hkv + j) * HB + hb) * nb;
-  // one 64-lane wave per head: lane s holds split s
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int h = wave; h < Gb; h += kMergeThreads / 64) {
-    const float2 ml = lane < nb ? part_ml[(base + lane) * kHB + h] : make_float2(-INFINITY, 0.0f);
-    float M = ml.x;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = ml.y > 0.0f ? __builtin_amdgcn_exp2f(ml.x - M) : 0.0f;
-    float Lsum = f * ml.y;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) Lsum += __shfl_xor(Lsum, o);
-    if (lane < nb) wgt[h][lane] = f / Lsum;
-  }
-  __syncthreads();
   for (int e = tid; e < Gb * D; e += kMergeThreads) {
     const int h = e / D, c = e % D;
+    const float2* ml = part_ml + base * kHB + h;
     const float* po = part_o + (base * kHB + h) * D + c;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 4 <= nb; s += 4) {
+    float M = -INFINITY, Lsum = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < nb; s0 += kMergeBatch) {
+      const int cnt = min(kMergeBatch, nb - s0);
+      float2 m[kMergeBatch];
+      float o[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += wgt[h][s + u] * po[static_cast<size_t>(s + u) * kHB * D];
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (u < cnt) {
+          m[u] = ml[static_cast<size_t>(s0 + u) * kHB];
+          o[u] = po[static_cast<size_t>(s0 + u) * kHB * D];
+        }
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u)
+        if (u < cnt && m[u].y > 0.0f) Mb = fmaxf(Mb, m[u].x);
+      const float r = Mb == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mb);  // rescale the running sums
+      Lsum *= r;
+      acc *= r;
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (u < cnt && m[u].y > 0.0f) {
+          const float f = __builtin_amdgcn_exp2f(m[u].x - Mb);
+          Lsum += f * m[u].y;
+          acc += f * o[u];
+        }
+      }
+      M = Mb;
     }
-    for (; s < nb; ++s) acc[0] += wgt[h][s] * po[static_cast<size_t>(s) * kHB * D];
-    out[(static_cast<size_t>(b) * Hq + j * G + h0 + h) * D + c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    out[(static_cast<size_t>(b) * Hq + j * G + h0 + h) * D + c] = acc / Lsum;
   }
 }
 
