@@ -59,7 +59,7 @@ def parse():
                     help="MiniKV's residual policy: the prefill quantizes every complete group and the residual "
                          "is quantized whole when it reaches R")
     ap.add_argument("--group", type=int, default=32, choices=(32, 16),
-                    help="quantization group: 32, or MiniKV's 16 (its own decode kernel)")
+                    help="quantization group: 32, or MiniKV's 16 (the decode kernel's group-16 instantiation)")
     a = ap.parse_args()
     if a.selector in ("sinks", "window") and a.budget_policy != "workload":
         ap.error("--budget-policy var-prop/var-inv needs attention scores (--selector snapkv or h2o)")
@@ -74,22 +74,36 @@ def decode_call_bytes(B, Hq, Hkv, D, bits, q_len, r_total, in_bytes, group=32):
     return B * Hkv * (hist + resid) + io
 
 
+DECODE_SOURCES = ("decode_kernel.h", "decode.hip", "decode_g16.hip")
+
+
+def decode_src_sha256():
+    """First 16 hex digits of the sha256 of the decode sources, concatenated in
+    DECODE_SOURCES order (what `cat decode_kernel.h decode.hip decode_g16.hip |
+    sha256sum` prints in csrc/)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, "kv_cache_compression_snapkv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def counted_traffic(workload, bits, flush_all=False, group=32):
     """HBM bytes per kvc_decode_attn call from the committed rocprofv3 counter
-    summary of this workload (default residual policy, group 32), or None when
-    the decode source has changed since the counters were taken, no summary
-    exists, or the run uses another policy or group."""
-    import hashlib
+    summary of this workload (default residual policy; group 32, or group 16 in
+    the summary named with _g16), or None when the decode sources have changed
+    since the counters were taken, no summary exists, or the run uses the
+    whole-residual policy."""
     import re
-    if flush_all or group != 32:
+    if flush_all:
         return None
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_{bits}bit_hbm_counters.md")
-    src = os.path.join(ROOT, "kv_cache_compression_snapkv_amd", "csrc", "decode.hip")
+    tag = "" if group == 32 else f"_g{group}"
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_{bits}bit{tag}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"traffic: bytes_per_call=(\d+) workload=(\S+) bits=(\d+) decode_src_sha256=([0-9a-f]+)",
                   open(path).read())
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = decode_src_sha256()
     if not m or m.group(2) != workload or int(m.group(3)) != bits or m.group(4) != sha:
         return None
     return int(m.group(1))
@@ -416,7 +430,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         "tokens_per_s": B * cfg.decode_steps / (dec_ms * 1e-3),
         "step_ms": step_ms, "pre_ms": pre_ms, "dec_ms": dec_ms, "wall": wall, "prefill_attention": attn,
         "roofline": {
-            "kernel": ((("decode_kernel (+ merge_kernel" if group == 32 else "decode_g16_kernel (+ merge_g16_kernel")
+            "kernel": ((f"decode_kernel<GS={group}> (+ merge_kernel"
                         + (f"; flush_kernel of {cfg.residual // group} groups on 1 step in {cfg.residual})"
                            if flush_all else f"; flush_kernel on 1 step in {group})"))
                        + ", per kvc_decode_attn call"),
@@ -424,7 +438,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
             "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(cfg.name, bits, flush_all, group),
             "avg_call_us": dec_ms * 1e3 / ncalls, "algorithmic_bytes_per_call": sum(call_bytes) / ncalls,
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated), "
-                            "profiles/decode_<workload>_<bits>bit_hbm_counters.md; null if decode.hip changed since",
+                            "profiles/decode_<workload>_<bits>bit[_g16]_hbm_counters.md; null if the decode sources changed since",
         },
     }
     del prompts, dec, caches, idxs, sel_ws, sel_wss, dec_ws, g_pre, g_dec, side

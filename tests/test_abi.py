@@ -284,27 +284,32 @@ def test_workspace_queries_from_many_threads():
 
 def test_decode_workspace_closed_form():
     """The decode workspace equals its closed form: split partials only when
-    the capacity's tile count exceeds what one workgroup per unit covers (eight
-    waves of six tiles, four waves at D > 192), then units * min(64,
-    ceil(tiles / 12)) slots of four heads' (m, l) and o[D]."""
+    the capacity's tile count (32-token tiles, whatever the group size) exceeds
+    what one workgroup per unit covers (eight waves of six tiles, four waves at
+    D > 192), then units * min(64, ceil(tiles / 12)) slots of four heads' (m, l)
+    and o[D].  A unit is up to four query heads of a KV head, or one head where
+    the four-head kernel's LDS would exceed a CU's 160 KB (group 16 at D = 256)."""
     L = _lib()
 
-    def need(B, H, D, R, q_cap, r_cap, G):
-        c = L.CacheStruct(B, H, D, 2, R, q_cap, 0, r_cap, 0, 0, 32, 0, 16, 16, 16, 16, 16, 16)
+    def need(B, H, D, R, q_cap, r_cap, G, group):
+        c = L.CacheStruct(B, H, D, 2, R, q_cap, 0, r_cap, 0, 0, group, 0, 16, 16, 16, 16, 16, 16)
         n = ctypes.c_size_t(0)
         assert L.lib.kvc_decode_attn(ctypes.byref(c), None, None, None, 1, H * G, None, None, ctypes.byref(n),
                                      None) == 0
         return n.value
 
-    def closed(B, H, D, R, q_cap, r_cap, G):
+    def closed(B, H, D, R, q_cap, r_cap, G, group):
         nt = q_cap // 32 + (r_cap + 31) // 32
         waves = 8 if D <= 192 else 4
         if -(-nt // waves) <= 6:
             return 256
-        slots = B * H * (-(-G // 4)) * min(64, -(-nt // 12))
+        hbs = 1 if (group == 16 and D == 256) else 4
+        slots = B * H * (-(-G // hbs)) * min(64, -(-nt // 12))
         ml = -(-(slots * 4 * 8) // 256) * 256
         return max(256, ml + slots * 4 * D * 4)
 
-    for args in ((4, 40, 128, 128, 32768, 160, 1), (1, 8, 128, 256, 4096, 288, 4), (8, 8, 128, 128, 608, 160, 4),
-                 (1, 1, 256, 16, 1600, 48, 16), (2, 3, 64, 16, 64, 48, 2), (1, 8, 128, 128, 8192, 160, 4)):
-        assert need(*args) == closed(*args), args
+    for group in (32, 16):
+        for args in ((4, 40, 128, 128, 32768, 160, 1), (1, 8, 128, 256, 4096, 288, 4), (8, 8, 128, 128, 608, 160, 4),
+                     (1, 1, 256, 16, 1600, 48, 16), (2, 3, 64, 16, 64, 48, 2), (1, 8, 128, 128, 8192, 160, 4),
+                     (2, 2, 256, 64, 8192, 96, 4), (2, 2, 224, 64, 8192, 96, 4)):
+            assert need(*args, group) == closed(*args, group), (args, group)

@@ -312,7 +312,12 @@ def test_quantize_parity_group16(dtype, bits, D, with_idx):
 
 @pytest.mark.parametrize("dtype,bits,G,D,R,n", [
     ("bf16", 2, 4, 128, 16, 300), ("bf16", 4, 2, 64, 0, 200), ("f32", 2, 1, 256, 24, 130),
-    ("bf16", 4, 8, 32, 40, 160), ("bf16", 2, 2, 128, 128, 700)])
+    ("bf16", 4, 8, 32, 40, 160), ("bf16", 2, 2, 128, 128, 700),
+    # split runs: one head per workgroup with staged tiles, four heads per
+    # workgroup, and f32 inputs; the history alternates between an even and an
+    # odd number of 16-token groups (a half-full last tile)
+    ("bf16", 2, 1, 128, 16, 4000), ("bf16", 4, 4, 128, 128, 2600), ("f32", 2, 1, 128, 16, 3000),
+    ("bf16", 2, 1, 64, 16, 5000)])
 def test_decode_parity_group16_multi_step(dtype, bits, G, D, R, n):
     """Decode over group-16 caches for 40 steps (several 16-token flushes, the
     residual ring wrapping): outputs within the decode tolerance and the cache
