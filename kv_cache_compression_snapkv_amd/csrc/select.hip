@@ -564,23 +564,13 @@ __device__ int block_exclusive_scan(int x, int* sh, int* total) {
   return res;
 }
 
-// Add one vote per active lane to hist[bin] (bin < 2^NBITS) with one atomic per
-// distinct bin in the wave (scores share their leading key bytes, so plain
-// per-lane atomics on one address would serialize).  The lanes with this lane's
-// bin are found with one ballot per bin bit, at a cost that does not depend on
-// how many distinct bins the wave holds.
-template <int NBITS = 8>
-__device__ __forceinline__ void wave_hist_add(int* hist, bool valid, uint32_t bin) {
-  uint64_t peers = __ballot(valid);
-  if (peers == 0) return;  // wave-uniform: no lane votes (later radix passes, most waves)
-#pragma unroll
-  for (int bit = 0; bit < NBITS; ++bit) {
-    const bool set = (bin >> bit) & 1u;
-    const uint64_t ones = __ballot(set);
-    peers &= set ? ones : ~ones;
-  }
-  const int lane = threadIdx.x & 63;
-  if (valid && __builtin_ctzll(peers) == lane) atomicAdd(&hist[bin], __popcll(peers));
+// One vote per active lane to an LDS histogram.  The LDS resolves lanes that hit
+// one address in hardware; that is cheaper than grouping the lanes of a bin
+// first (one ballot and about four VALU instructions per bin bit and key:
+// measured 10 us slower per layer at the 8B shape, although scores share their
+// leading key bytes and so collide).
+__device__ __forceinline__ void hist_add(int* hist, bool valid, uint32_t bin) {
+  if (valid) atomicAdd(&hist[bin], 1);
 }
 
 // Digit selection of one radix pass: the largest d with sum_{d' >= d} cnt[d'] >=
@@ -671,13 +661,13 @@ __device__ __forceinline__ uint32_t key_at(const uint4& k, int i) { return i == 
 
 __global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
   __shared__ float rs[kChunk + 2 * kMaxPoolHalf];  // raw[c0 - kMaxPoolHalf + i]
-  __shared__ int hist[kTopThreads / 64][256];
+  __shared__ int hist[256];
   const int ch = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x;
   const int N = a.N, h = a.pool / 2, c0 = ch * kChunk;
   const float* raw = a.raw + bj * a.ld;
-  for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
+  if (tid < 256) hist[tid] = 0;
   if (ch == 0)  // the counts of passes 2 and 3 are accumulated by later launches
     for (int i = tid; i < 2 * kWideBins; i += kTopThreads) a.ghist[bj * 2 * kWideBins + i] = 0;
   for (int i = tid; i < kChunk + 2 * kMaxPoolHalf; i += kTopThreads) {
@@ -723,13 +713,9 @@ __global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
   *reinterpret_cast<uint4*>(a.keys + bj * a.NP + cb) = make_uint4(key[0], key[1], key[2], key[3]);
   if (a.kk == 0) return;
 #pragma unroll
-  for (int i = 0; i < kChunkKpt; ++i) wave_hist_add(hist[w], cb + i < N, key[i] >> 24);
+  for (int i = 0; i < kChunkKpt; ++i) hist_add(hist, cb + i < N, key[i] >> 24);
   __syncthreads();
-  if (tid < 256) {
-    int s = 0;
-    for (int i = 0; i < kTopThreads / 64; ++i) s += hist[i][tid];
-    a.hist1[(bj * a.nch + ch) * 256 + tid] = s;
-  }
+  if (tid < 256) a.hist1[(bj * a.nch + ch) * 256 + tid] = hist[tid];
 }
 
 // PASS 2: digit 1 from the per-chunk byte counts, then counts of key bits
@@ -781,7 +767,7 @@ __global__ __launch_bounds__(kTopThreads) void chunk_hist_kernel(TopArgs a) {
 #pragma unroll
   for (int i = 0; i < kChunkKpt; ++i) {
     const uint32_t key = key_at(k4, i);
-    wave_hist_add<12>(hist, cb + i < a.N && (key & pmask) == prefix, (key >> shift) & (kWideBins - 1));
+    hist_add(hist, cb + i < a.N && (key & pmask) == prefix, (key >> shift) & (kWideBins - 1));
   }
   __syncthreads();
   int* g = a.ghist + (bj * 2 + (PASS - 2)) * kWideBins;
@@ -884,12 +870,12 @@ __global__ __launch_bounds__(kTopThreads) void chunk_emit_kernel(TopArgs a) {
 template <int KPT>
 __global__ __launch_bounds__(kTopThreads) void pool_topk_lds_kernel(TopArgs a) {
   extern __shared__ __attribute__((aligned(16))) float rs[];  // [N] raw scores
-  __shared__ int hist[kTopThreads / 64][256];
+  __shared__ int hist[256];
   __shared__ int scan_sh[kTopThreads / 64 + 1];
   __shared__ uint32_t sel_sh[2];
   const int j = blockIdx.x, b = blockIdx.y;
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x;
   const int N = a.N, h = a.pool / 2;
   const float* raw = a.raw + bj * a.ld;
   int32_t* idx = a.idx + bj * a.kk;
@@ -949,26 +935,21 @@ __global__ __launch_bounds__(kTopThreads) void pool_topk_lds_kernel(TopArgs a) {
   }
   uint32_t prefix = 0, pmask = 0;
   int krem = a.kk;
+  // per pass: the histogram is cleared (its readers passed the barrier after
+  // the previous digit selection), filled, and its digit selected; sel_sh is
+  // read before the next selection, two barriers later
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < (kTopThreads / 64) * 256; i += kTopThreads) (&hist[0][0])[i] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      wave_hist_add(hist[w], cb + i < N && (key[i] & pmask) == prefix, (key[i] >> shift) & 255u);
+    for (int i = 0; i < KPT; ++i) hist_add(hist, cb + i < N && (key[i] & pmask) == prefix, (key[i] >> shift) & 255u);
     __syncthreads();
-    if (tid < 256) {
-      int s2 = 0;
-      for (int i = 0; i < kTopThreads / 64; ++i) s2 += hist[i][tid];
-      hist[0][tid] = s2;
-    }
-    __syncthreads();
-    select_digit(hist[0], krem, scan_sh, sel_sh);
+    select_digit(hist, krem, scan_sh, sel_sh);
     __syncthreads();
     prefix |= sel_sh[0] << shift;
     pmask |= 255u << shift;
     krem = static_cast<int>(sel_sh[1]);
-    __syncthreads();
   }
   // prefix is the k'-th largest key: take every larger key and the krem
   // lowest-index keys equal to it, in index order
