@@ -16,7 +16,9 @@ by HBM rather than by launch latency); the selection+quantization time per
 prompt is reported beside it.  Inputs are generated on the GPU before timing
 (seeded).  By default the line also carries `sub_workloads`: the same figures
 for every other workload and width (the 13B shape at 4 bits, the Llama-3-8B,
-Mistral pyramid and 128k long-context shapes), each timed the same way.
+Mistral pyramid and 128k long-context shapes, the 8B shape with H2O selection on
+the prefill's accumulated attention, and the 13B and 8B shapes at MiniKV's group
+size of 16), each timed the same way.
 """
 
 import argparse
@@ -451,13 +453,17 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
 
 
 # (workload, bits, selector): every other workload and width, and the H2O path
-SUB_WORKLOADS = (("llama2_13b_mha", 4, "snapkv"), ("llama2_13b_mha", 2, "snapkv"), ("llama3_8b", 2, "snapkv"),
-                 ("mistral_pyramid", 2, "snapkv"), ("long_context", 2, "snapkv"), ("llama3_8b", 2, "h2o"))
+# (workload, bits, selector, group)
+SUB_WORKLOADS = (("llama2_13b_mha", 4, "snapkv", 32), ("llama2_13b_mha", 2, "snapkv", 32),
+                 ("llama3_8b", 2, "snapkv", 32), ("mistral_pyramid", 2, "snapkv", 32),
+                 ("long_context", 2, "snapkv", 32), ("llama3_8b", 2, "h2o", 32),
+                 ("llama2_13b_mha", 2, "snapkv", 16), ("llama3_8b", 2, "snapkv", 16))
 
 
-def entry(r, cfg, bits, steps, warmup, selector):
+def entry(r, cfg, bits, steps, warmup, selector, group=32):
     """The figures of one workload run (a sub-workload line)."""
-    e = {"workload": r["desc"], "bits": bits, "selector": selector, "decode_tokens_per_s": r["tokens_per_s"],
+    e = {"workload": r["desc"], "bits": bits, "selector": selector, "group": group,
+         "decode_tokens_per_s": r["tokens_per_s"],
          "avg_call_us": r["roofline"]["avg_call_us"], "ms_per_step": r["step_ms"],
          "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch, "steps": steps, "warmup": warmup,
          "roofline": r["roofline"]}
@@ -509,12 +515,12 @@ def main():
         # every other workload and width, each timed the same way (fewer steps)
         sub_steps, sub_warm = max(1, min(args.steps, args.sub_steps)), max(1, min(args.warmup, 2))
         res["sub_workloads"] = []
-        for name, sb, ssel in SUB_WORKLOADS:
-            if (name, sb, ssel) == (args.workload, bits, args.selector):
+        for name, sb, ssel, sg in SUB_WORKLOADS:
+            if (name, sb, ssel, sg) == (args.workload, bits, args.selector, args.group):
                 continue
             sc = synth.CONFIGS[name]
-            h = run(sc, sb, sub_steps, sub_warm, selector=ssel)
-            res["sub_workloads"].append(entry(h, sc, sb, sub_steps, sub_warm, ssel))
+            h = run(sc, sb, sub_steps, sub_warm, selector=ssel, group=sg)
+            res["sub_workloads"].append(entry(h, sc, sb, sub_steps, sub_warm, ssel, sg))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, bits, r["budgets"], group=args.group, flush_all=args.flush_all)
     print(json.dumps(res))
