@@ -190,7 +190,9 @@ kvc_status kvc_budget_weighted(const kvc_budget_args *args, const double *weight
  *   k      [B][Hkv][n][D]  prompt keys (post-RoPE), dtype
  *   idx    [B][Hkv][k']    int32 output, ascending, in [0, n-W) (may be NULL if k' == 0)
  *   scores [B][Hkv][n-W]   float32 output of the pooled scores, or NULL
- *   budget < 0 keeps every candidate.
+ *   budget < 0 keeps every candidate.  When every candidate is kept and scores
+ *   is NULL, the ranking decides nothing: idx = 0, 1, ..., n-W-1 is written and
+ *   no score is computed.
  * Errors: KVC_ERR_NULL, KVC_ERR_DTYPE, KVC_ERR_SHAPE (W < 1, W > n, pool even
  *   or < 1, shapes above), KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
 kvc_status kvc_select(const void *q_win, const void *k, kvc_dtype dtype, int32_t B, int32_t Hq,

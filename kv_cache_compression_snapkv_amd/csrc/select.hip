@@ -1207,6 +1207,18 @@ bool score_shape_ok(int B, int Hq, int Hkv, int n, int D, int W) {
 
 }  // namespace
 
+// idx rows of kk entries: the first s positions, then base + e (recent_kernel);
+// with s = kk every row is 0, 1, ..., kk-1.
+kvc_status launch_recent(int32_t* idx, size_t total, int kk, int s, int base, hipStream_t st) {
+  const size_t blocks = std::min<size_t>((total + kRecentThreads - 1) / kRecentThreads, 4096);
+  hipLaunchKernelGGL(recent_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRecentThreads), 0, st, idx, total,
+                     kk, s, base);
+  return check_launch();
+}
+kvc_status launch_identity(int32_t* idx, size_t total, int kk, hipStream_t st) {
+  return launch_recent(idx, total, kk, kk, 0, st);
+}
+
 // Population variance of each of `rows` rows of N floats (variance_kernel).
 kvc_status launch_variance(const float* raw, int rows, int N, float* var, hipStream_t st) {
   hipLaunchKernelGGL(variance_kernel, dim3(rows), dim3(kVarThreads), 0, st, raw, N, var);
@@ -1236,6 +1248,7 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   if (*ws_bytes < need) return KVC_ERR_WORKSPACE;
   if (N == 0) return KVC_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kk == N && !scores) return launch_identity(idx, static_cast<size_t>(B) * Hkv * N, N, st);
   char* w = static_cast<char*>(ws);
   float* raw = reinterpret_cast<float*>(w + sw.total);
   const ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, w, raw);
@@ -1294,11 +1307,8 @@ extern "C" kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32
   const int kk = budget < 0 ? N : std::min(budget, N);
   if (kk == 0) return KVC_OK;
   if (!idx) return KVC_ERR_NULL;
-  const size_t total = static_cast<size_t>(B) * Hkv * kk;
-  const size_t blocks = std::min<size_t>((total + kRecentThreads - 1) / kRecentThreads, 4096);
-  hipLaunchKernelGGL(recent_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRecentThreads), 0,
-                     static_cast<hipStream_t>(stream), idx, total, kk, std::min(sinks, kk), N - kk);
-  return check_launch();
+  return launch_recent(idx, static_cast<size_t>(B) * Hkv * kk, kk, std::min(sinks, kk), N - kk,
+                       static_cast<hipStream_t>(stream));
 }
 
 extern "C" kvc_status kvc_select_h2o(const float* acc, int32_t B, int32_t Hkv, int32_t n, int32_t W, int32_t budget,

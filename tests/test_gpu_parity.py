@@ -127,6 +127,26 @@ def test_select_parity(dtype, B, G, Hkv, n, D, W, pool, budget):
             gu.check_selection(ix[b, j], sc[b, j], pooled[b, j], budget)
 
 
+@pytest.mark.parametrize("budget", [-1, 280, 5000])
+def test_select_keep_all_without_scores(budget):
+    """Keeping every candidate needs no ranking: without scores kvc_select
+    writes 0..n-W-1 per (b, KV head) (no scorer launch), the same idx as the
+    scored call; a smaller budget still ranks."""
+    kvc = _kvc()
+    B, G, Hkv, n, D, W = 2, 4, 2, 300, 128, 20
+    k, _ = _case(8, B, Hkv, n, D, "bf16")
+    q_win = synth.random_tensor(9, (B, G * Hkv, W, D), "bf16", tag="qw").cuda()
+    idx = kvc.kvc_select(q_win, k, W, 7, budget)
+    idx_s, _ = kvc.kvc_select(q_win, k, W, 7, budget, want_scores=True)
+    torch.cuda.synchronize()
+    want = torch.arange(n - W, dtype=torch.int32).expand(B, Hkv, n - W)
+    assert torch.equal(idx.cpu(), want) and torch.equal(idx_s.cpu(), want)
+    idx2 = kvc.kvc_select(q_win, k, W, 7, n - W - 1)
+    idx2_s, _ = kvc.kvc_select(q_win, k, W, 7, n - W - 1, want_scores=True)
+    torch.cuda.synchronize()
+    assert idx2.shape == (B, Hkv, n - W - 1) and torch.equal(idx2.cpu(), idx2_s.cpu())
+
+
 @pytest.mark.parametrize("dtype,B,G,Hkv,n,D,W", [
     ("bf16", 2, 4, 2, 700, 128, 16), ("f32", 1, 1, 3, 300, 64, 8), ("bf16", 1, 8, 1, 1000, 256, 32),
     ("bf16", 1, 4, 1, 2000, 128, 64), ("bf16", 1, 2, 2, 37000, 64, 16)])
