@@ -29,10 +29,12 @@ FLAGS = [
 ]
 
 
-# Per-source extras.  decode.hip, select.hip and prefill.hip: their values are never NaN for
-# finite inputs (logits, softmax weights, -inf masks), so fmax needs no
-# canonicalization and the 16-lane DPP max folds into v_max_f32_dpp.
-EXTRA = {"decode.hip": ["-fno-honor-nans"], "select.hip": ["-fno-honor-nans"], "prefill.hip": ["-fno-honor-nans"]}
+# Per-source extras.  The decode sources (both group sizes), select.hip and
+# prefill.hip: their values are never NaN for finite inputs (logits, softmax
+# weights, -inf masks), so fmax needs no canonicalization and the 16-lane DPP max
+# folds into v_max_f32_dpp.
+_NO_NANS = ["-fno-honor-nans"]
+EXTRA = {"decode.hip": _NO_NANS, "decode_g16.hip": _NO_NANS, "select.hip": _NO_NANS, "prefill.hip": _NO_NANS}
 
 
 def _compile(src):
