@@ -3,8 +3,8 @@
 // dequantized older ones; query head h reads KV head h / G).
 //
 // Work split.  The tokens of one (batch, KV head) are cut into 32-token tiles:
-// Q/32 packed-history tiles (one key group each) followed by the bf16 residual
-// tiles.  Every wavefront owns a contiguous run of tiles for up to 4 query heads
+// ceil(Q/32) packed-history tiles (one or two key groups each) followed by the
+// bf16 residual tiles.  Every wavefront owns a contiguous run of tiles for up to 4 query heads
 // of that KV head and keeps its own online-softmax state; the waves of a
 // workgroup merge through LDS, M = max m_w, o = sum_w 2^(m_w-M) o_w,
 // l = sum_w 2^(m_w-M) l_w (log2 units), and write the output directly when one
@@ -24,7 +24,7 @@
 //           MFMA of that operand against all -1 gives, per head, the exact sum
 //           of the A pieces (the 1.0 offset to remove) and the zero-point term.
 //   values: o[c] = sum_t A[t] B[t][c] with the same code encoding and
-//           A = p*scale*2^(7-pos) per (token, 32-channel group); each lane adds
+//           A = p*scale*2^(7-pos) per (token, value group); each lane adds
 //           p*zero - (hi + lo) for the pieces it wrote into a float32 register,
 //           and the lanes of a group are summed once at the end of the run.
 //   residual: B = bf16 keys/values as stored, A = q or p split in two.
