@@ -63,7 +63,8 @@ def test_quantize_parity(dtype, bits, D, with_idx):
     ("bf16", 2, 2, 64, 0, 200), ("bf16", 4, 8, 32, 40, 160), ("f32", 4, 3, 256, 24, 130),
     ("bf16", 2, 16, 64, 16, 100),
     # histories long enough for the split runs (several workgroups per unit, merged)
-    ("f32", 2, 1, 128, 16, 3000), ("f32", 4, 4, 128, 128, 2600), ("bf16", 2, 4, 128, 128, 4000)])
+    ("f32", 2, 1, 128, 16, 3000), ("f32", 4, 4, 128, 128, 2600), ("bf16", 2, 4, 128, 128, 4000),
+    ("bf16", 2, 4, 256, 16, 3000)])   # D = 256: four heads per workgroup in the split runs
 def test_decode_parity_multi_step(dtype, bits, G, D, R, n):
     kvc = _kvc()
     B, Hkv = 2, 2
@@ -337,7 +338,8 @@ def test_quantize_parity_group16(dtype, bits, D, with_idx):
     # workgroup, and f32 inputs; the history alternates between an even and an
     # odd number of 16-token groups (a half-full last tile)
     ("bf16", 2, 1, 128, 16, 4000), ("bf16", 4, 4, 128, 128, 2600), ("f32", 2, 1, 128, 16, 3000),
-    ("bf16", 2, 1, 64, 16, 5000)])
+    ("bf16", 2, 1, 64, 16, 5000),
+    ("bf16", 2, 4, 256, 16, 3000)])   # D = 256: one head per workgroup (four would not fit a CU's LDS)
 def test_decode_parity_group16_multi_step(dtype, bits, G, D, R, n):
     """Decode over group-16 caches for 40 steps (several 16-token flushes, the
     residual ring wrapping): outputs within the decode tolerance and the cache
