@@ -17,8 +17,9 @@ prompt is reported beside it.  Inputs are generated on the GPU before timing
 (seeded).  By default the line also carries `sub_workloads`: the same figures
 for every other workload and width (the 13B shape at 4 bits, the Llama-3-8B,
 Mistral pyramid and 128k long-context shapes, the 8B shape with H2O selection on
-the prefill's accumulated attention, and the 13B and 8B shapes at MiniKV's group
-size of 16), each timed the same way.
+the prefill's accumulated attention, the 13B and 8B shapes at MiniKV's group size
+of 16, and the 8B and 128k shapes with the window scores normalized by the
+prefill's log-sum-exp), each timed the same way.
 """
 
 import argparse
@@ -48,11 +49,13 @@ def parse():
     ap.add_argument("--budget-policy", default="workload", choices=("workload", "var-prop", "var-inv"),
                     help="per-layer budgets: the workload's (uniform or pyramid), or proportional to the variance "
                          "of each layer's window scores or to its reciprocal (scores, budgets, then top-k)")
-    ap.add_argument("--selector", default="snapkv", choices=("snapkv", "sinks", "window", "h2o"),
-                    help="prompt selection: observation-window scores (kvc_select); position-only with "
-                         "kvc_select_recent: --sinks leading tokens plus the recent window, or the sliding window; "
-                         "h2o: the prefill attention of every prompt row with accumulated column attention "
-                         "(kvc_prefill_attn), then heavy hitters plus the window (kvc_select_h2o)")
+    ap.add_argument("--selector", default="snapkv", choices=("snapkv", "snapkv-lse", "sinks", "window", "h2o"),
+                    help="prompt selection: observation-window scores (kvc_select); snapkv-lse: the same scores "
+                         "given each window row's log-sum-exp from the prompt's prefill attention (kvc_prefill_attn, "
+                         "run before timing as the model's prefill would), one pass over K (kvc_select_lse); "
+                         "position-only with kvc_select_recent: --sinks leading tokens plus the recent window, or "
+                         "the sliding window; h2o: the prefill attention of every prompt row with accumulated column "
+                         "attention (kvc_prefill_attn), then heavy hitters plus the window (kvc_select_h2o)")
     ap.add_argument("--sinks", type=int, default=4)
     ap.add_argument("--streams", type=int, default=1,
                     help="prompt compression runs the layers round-robin on this many streams (they are "
@@ -228,6 +231,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         L = min(L, layers)
     varp = policy != "workload" and cfg.budget >= 0
     h2o = selector == "h2o" and cfg.budget >= 0
+    use_lse = selector == "snapkv-lse" and cfg.budget >= 0 and not varp
 
     # inputs resident in HBM before timing
     prompts = [(synth.prefill_layer if h2o else synth.prompt_layer)(cfg, l, dev) for l in range(L)]
@@ -260,6 +264,21 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
                                               group=group, meta_bits=16, residual=cfg.residual)
         tk_ws = torch.empty(max(kvc.topk_ws_bytes(B, Hkv, N, cfg.pool, b) for b in budgets), dtype=torch.uint8,
                             device=dev)
+    if use_lse:
+        # each window row's log-sum-exp from the prompt's prefill attention (every
+        # row of the layer; its last W query rows are q_win), computed before
+        # timing as the model's own prefill would
+        dt_code = 1 if in_bytes == 2 else 0
+        lse_out = torch.empty(B, Hq, n, D, dtype=torch.float32, device=dev)
+        lse_full = torch.empty(B, Hq, n, dtype=torch.float32, device=dev)
+        lse_ws = torch.empty(kvc.prefill_ws_bytes(dt_code, B, Hq, Hkv, n, D), dtype=torch.uint8, device=dev)
+        lse_win = []
+        for l in range(L):
+            pf = synth.prefill_layer(cfg, l, dev)
+            kvc.kvc_prefill_attn(pf["q"], pf["k"], pf["v"], want_acc=False, ws=lse_ws, out=lse_out, lse=lse_full)
+            lse_win.append(lse_full[:, :, n - W:].contiguous())
+            del pf
+        del lse_out, lse_full, lse_ws
     dec = [[synth.decode_inputs(cfg, l, s, dev) for l in range(L)] for s in range(cfg.decode_steps)]
     caches, idxs = [], []
     for l in range(L):
@@ -332,8 +351,12 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
 
         def one(l, k):
             p = prompts[l]
-            if cfg.budget >= 0 and selector != "snapkv":
+            if cfg.budget >= 0 and selector in ("sinks", "window"):
                 kvc.kvc_select_recent(B, Hkv, n, W, budgets[l], sinks if selector == "sinks" else 0, idx=idxs[l])
+                kvc.kvc_quantize(p["k"], p["v"], caches[l], idx=idxs[l], W=W)
+            elif use_lse:
+                kvc.kvc_select_lse(p["q_win"], p["k"], lse_win[l], W, cfg.pool, budgets[l], ws=sel_wss[k],
+                                   idx=idxs[l])
                 kvc.kvc_quantize(p["k"], p["v"], caches[l], idx=idxs[l], W=W)
             elif cfg.budget >= 0:
                 kvc.kvc_select(p["q_win"], p["k"], W, cfg.pool, budgets[l], ws=sel_wss[k], idx=idxs[l])
@@ -420,7 +443,8 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
                               "recomputes Q K^T and is not counted"}
         if graph:
             del g_attn
-    sel = {"snapkv": "", "sinks": f"{sinks} sinks + recent window, ", "window": "sliding window, ",
+    sel = {"snapkv": "", "snapkv-lse": "window scores given the prefill's log-sum-exp (one pass over K), ",
+           "sinks": f"{sinks} sinks + recent window, ", "window": "sliding window, ",
            "h2o": "H2O heavy hitters on the prefill's accumulated attention, "}[selector]
     desc = (f"{cfg.name}: {L} layers, batch {B}, {Hq} query / {Hkv} KV heads, head dim {D}, "
             f"prompt {n}, {cfg.dtype} inputs, W={W}, {sel}pool {cfg.pool}, budget "
@@ -457,7 +481,8 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
 SUB_WORKLOADS = (("llama2_13b_mha", 4, "snapkv", 32), ("llama2_13b_mha", 2, "snapkv", 32),
                  ("llama3_8b", 2, "snapkv", 32), ("mistral_pyramid", 2, "snapkv", 32),
                  ("long_context", 2, "snapkv", 32), ("llama3_8b", 2, "h2o", 32),
-                 ("llama2_13b_mha", 2, "snapkv", 16), ("llama3_8b", 2, "snapkv", 16))
+                 ("llama2_13b_mha", 2, "snapkv", 16), ("llama3_8b", 2, "snapkv", 16),
+                 ("llama3_8b", 2, "snapkv-lse", 32), ("long_context", 2, "snapkv-lse", 32))
 
 
 def entry(r, cfg, bits, steps, warmup, selector, group=32):

@@ -199,6 +199,23 @@ kvc_status kvc_select(const void *q_win, const void *k, kvc_dtype dtype, int32_t
                       int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool, int32_t budget,
                       int32_t *idx, float *scores, void *ws, size_t *ws_bytes, void *stream);
 
+/* kvc_select_lse: kvc_select given each window row's softmax normalizer, as the
+ * prompt's own prefill attention computes it (FlashAttention keeps every row's
+ * log-sum-exp; MiniKV Sec. 4.3 fuses the selection scores into that prefill).
+ * The scores are the same column sums; with the normalizers known, the window
+ * scorer needs one pass over K instead of two (the first pass of kvc_select
+ * exists only to find them).
+ *   lse   float32, row w of query head h of batch row b at lse[(b*Hq + h) *
+ *         lse_stride + w]: the natural-log log-sum-exp of that window row's
+ *         causal logits q.k/sqrt(D) over keys 0..n-W+w (kvc_prefill_attn's lse
+ *         output from its row n-W on, with lse_stride = n).
+ *   lse_stride >= W.  Everything else as kvc_select (same workspace size).
+ * Errors: as kvc_select; KVC_ERR_NULL also for lse NULL, KVC_ERR_SHAPE for
+ *   lse_stride < W. */
+kvc_status kvc_select_lse(const void *q_win, const void *k, const float *lse, int32_t lse_stride, kvc_dtype dtype,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool,
+                          int32_t budget, int32_t *idx, float *scores, void *ws, size_t *ws_bytes, void *stream);
+
 /* The two halves of kvc_select, for callers that look at the scores before
  * choosing budgets (the variance policies of kvc_budget_weighted):
  *
@@ -257,6 +274,10 @@ kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32
  *   q [B][Hq][n][D], k, v [B][Hkv][n][D] in dtype (post-RoPE); out
  *   [B][Hq][n][D] float32; acc [B][Hkv][n] float32 or NULL (no column sums);
  *   var [B][Hkv] float32 or NULL (needs acc).  D in {32, 64, 128}.
+ *   lse [B][Hq][n] float32 or NULL: each row's log-sum-exp, natural log, of its
+ *                  causal logits q_r . k_c / sqrt(D) over c <= r (the softmax
+ *                  normalizer FlashAttention keeps; kvc_select_lse takes the
+ *                  last W rows of it).
  * Workspace: the per-row log-sum-exp, B*Hq*n floats (ws == NULL: size query).
  * acc is written in a fixed order (no atomics): the same inputs give the same
  * bits.
@@ -264,8 +285,8 @@ kvc_status kvc_select_recent(int32_t B, int32_t Hkv, int32_t n, int32_t W, int32
  *   KVC_ERR_SHAPE (B, Hq, Hkv, n < 1, Hq % Hkv, D not 32/64/128),
  *   KVC_ERR_WORKSPACE, KVC_ERR_HIP. */
 kvc_status kvc_prefill_attn(const void *q, const void *k, const void *v, kvc_dtype dtype, int32_t B, int32_t Hq,
-                            int32_t Hkv, int32_t n, int32_t D, float *out, float *acc, float *var, void *ws,
-                            size_t *ws_bytes, void *stream);
+                            int32_t Hkv, int32_t n, int32_t D, float *out, float *acc, float *var, float *lse,
+                            void *ws, size_t *ws_bytes, void *stream);
 
 /* kvc_select_h2o: heavy-hitter selection (blog "Eviction: keep fewer tokens":
  * H2O keeps the tokens with the largest accumulated attention plus a recent

@@ -9,6 +9,6 @@ by ``python kv_cache_compression_snapkv_amd/build.py`` (or ``__graft_entry__.bui
 
 from ._lib import (Cache, KvcError, LIB_PATH, decode_ws_bytes, h2o_ws_bytes, kvc_budget,  # noqa: F401
                    kvc_budget_weighted, kvc_decode_attn, kvc_decode_attn_noalloc, kvc_prefill_attn, kvc_quantize,
-                   kvc_select, kvc_select_h2o,
+                   kvc_select, kvc_select_h2o, kvc_select_lse,
                    kvc_select_recent, kvc_topk, kvc_window_scores, prefill_ws_bytes, select_ws_bytes, topk_ws_bytes,
                    window_scores_ws_bytes)

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 KVC_F32, KVC_BF16 = 0, 1
 STATUS = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_BITS",
           5: "KVC_ERR_CAPACITY", 6: "KVC_ERR_WORKSPACE", 7: "KVC_ERR_HIP"}
-EXPORTS = ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
+EXPORTS = ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_select_lse", "kvc_window_scores", "kvc_topk",
+           "kvc_select_recent",
            "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_decode_attn_noalloc",
            "kvc_cache_sizes", "kvc_last_hip_error", "kvc_status_string")
 
@@ -60,10 +61,11 @@ def _load():
     lib.kvc_budget_weighted.argtypes = [ctypes.POINTER(BudgetArgs), ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(I32), ctypes.POINTER(Footprint)]
     lib.kvc_select.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    lib.kvc_select_lse.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_window_scores.argtypes = [P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_topk.argtypes = [P, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     lib.kvc_select_recent.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
-    lib.kvc_prefill_attn.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, SZ, P]
+    lib.kvc_prefill_attn.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, P, SZ, P]
     lib.kvc_select_h2o.argtypes = [P, I32, I32, I32, I32, I32, P, P, SZ, P]
     lib.kvc_quantize.argtypes = [P, P, I32, I32, P, I32, I32, ctypes.POINTER(CacheStruct), P]
     lib.kvc_decode_attn.argtypes = [ctypes.POINTER(CacheStruct), P, P, P, I32, I32, P, P, SZ, P]
@@ -71,7 +73,8 @@ def _load():
     lib.kvc_cache_sizes.argtypes = [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_status_string.argtypes = [I32]
     lib.kvc_status_string.restype = ctypes.c_char_p
-    for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_window_scores", "kvc_topk", "kvc_select_recent",
+    for f in ("kvc_budget", "kvc_budget_weighted", "kvc_select", "kvc_select_lse", "kvc_window_scores", "kvc_topk",
+              "kvc_select_recent",
               "kvc_prefill_attn", "kvc_select_h2o", "kvc_quantize", "kvc_decode_attn", "kvc_decode_attn_noalloc",
               "kvc_cache_sizes", "kvc_last_hip_error"):
         getattr(lib, f).restype = I32
@@ -238,17 +241,50 @@ def kvc_select(q_win, k, W, pool, budget, want_scores=False, ws=None, idx=None, 
     return (idx, scores) if want_scores else idx
 
 
+def kvc_select_lse(q_win, k, lse, W, pool, budget, want_scores=False, ws=None, idx=None, scores=None, stream=None):
+    """kvc_select given each window row's log-sum-exp: lse float32 [B][Hq][L],
+    L >= W, whose last W entries are the window rows' (kvc_prefill_attn's lse,
+    L = n, or a compact [B][Hq][W]).  Same outputs as kvc_select."""
+    _contig(q_win, k, lse)
+    B, Hq, Wq, D = q_win.shape
+    _, Hkv, n, _ = k.shape
+    if Wq != W or k.dtype != q_win.dtype:
+        raise ValueError("q_win must be [B][Hq][W][D] with the dtype of k")
+    if lse.dtype != torch.float32 or lse.dim() != 3 or tuple(lse.shape[:2]) != (B, Hq) or lse.shape[2] < W:
+        raise ValueError("lse must be float32 [B][Hq][L] with L >= W")
+    dt = _dtype(k)
+    N = n - W
+    kk = N if budget < 0 else min(budget, N)
+    need = select_ws_bytes(dt, B, Hq, Hkv, n, D, W, pool, budget)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    if idx is None:
+        idx = torch.empty(B, Hkv, kk, dtype=torch.int32, device=k.device)
+    if want_scores and scores is None:
+        scores = torch.empty(B, Hkv, N, dtype=torch.float32, device=k.device)
+    L = lse.shape[2]
+    lse_w = lse.data_ptr() + (L - W) * 4  # the window rows: the last W of each row of lse
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("kvc_select_lse", lib.kvc_select_lse(_ptr(q_win), _ptr(k), ctypes.c_void_p(lse_w), L, dt, B, Hq, Hkv,
+                                                n, D, W, pool, budget, _ptr(idx),
+                                                _ptr(scores) if want_scores else None, _ptr(ws), ctypes.byref(wsb),
+                                                _stream(stream)))
+    return (idx, scores) if want_scores else idx
+
+
 # ---------------------------------------------------------------- prefill
 def prefill_ws_bytes(dtype, B, Hq, Hkv, n, D):
     need = ctypes.c_size_t(0)
     _check("kvc_prefill_attn", lib.kvc_prefill_attn(None, None, None, dtype, B, Hq, Hkv, n, D, None, None, None,
-                                                    None, ctypes.byref(need), None))
+                                                    None, None, ctypes.byref(need), None))
     return need.value
 
 
-def kvc_prefill_attn(q, k, v, want_acc=True, want_var=False, ws=None, out=None, acc=None, var=None, stream=None):
+def kvc_prefill_attn(q, k, v, want_acc=True, want_var=False, ws=None, out=None, acc=None, var=None, lse=None,
+                     stream=None):
     """Causal prefill attention: out [B][Hq][n][D] float32, plus the attention
-    each key accumulates, acc [B][Hkv][n] float32, and its variance [B][Hkv]."""
+    each key accumulates, acc [B][Hkv][n] float32, and its variance [B][Hkv].
+    lse (optional, float32 [B][Hq][n]) receives each row's log-sum-exp."""
     _contig(q, k, v)
     B, Hq, n, D = q.shape
     Hkv = k.shape[1]
@@ -264,11 +300,16 @@ def kvc_prefill_attn(q, k, v, want_acc=True, want_var=False, ws=None, out=None, 
         acc = torch.empty(B, Hkv, n, dtype=torch.float32, device=q.device)
     if want_var and var is None:
         var = torch.empty(B, Hkv, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _contig(lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, n):
+            raise ValueError("lse must be float32 [B][Hq][n]")
     wsb = ctypes.c_size_t(ws.numel())
     _check("kvc_prefill_attn", lib.kvc_prefill_attn(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, n, D, _ptr(out),
                                                     _ptr(acc) if (want_acc or want_var) else None,
-                                                    _ptr(var) if want_var else None, _ptr(ws), ctypes.byref(wsb),
-                                                    _stream(stream)))
+                                                    _ptr(var) if want_var else None,
+                                                    _ptr(lse) if lse is not None else None, _ptr(ws),
+                                                    ctypes.byref(wsb), _stream(stream)))
     return out, (acc if (want_acc or want_var) else None), (var if want_var else None)
 
 

@@ -131,6 +131,7 @@ struct PfArgs {
   const void *q, *k, *v;  // [B][Hq][n][D], [B][Hkv][n][D] x2
   float* out;             // [B][Hq][n][D]
   float* lse;             // [B][Hq][n] m + log2(l), log2 units
+  float* lse_out;         // [B][Hq][n] the same in natural-log units, or null
   float* acc;             // [B][Hkv][n]
   int B, Hq, Hkv, G, n, Gc, ngr, nrb, units;
   float scale2;           // log2(e)/sqrt(D)
@@ -356,7 +357,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
         const f32x4 v = oacc[c][rs] * inv;
         *reinterpret_cast<float4*>(o + 16 * c) = make_float4(v[0], v[1], v[2], v[3]);
       }
-      if (lq == 0) a.lse[qrow0 + row] = m_run[rs] + __log2f(l);
+      if (lq == 0) {
+        const float lse2 = m_run[rs] + __log2f(l);
+        a.lse[qrow0 + row] = lse2;
+        if (a.lse_out) a.lse_out[qrow0 + row] = lse2 * 0.6931471805599453f;  // ln 2
+      }
     }
   }
 }
@@ -479,7 +484,7 @@ bool prefill_dim_ok(int D) { return D == 32 || D == 64 || D == 128; }
 
 extern "C" kvc_status kvc_prefill_attn(const void* q, const void* k, const void* v, kvc_dtype dtype, int32_t B,
                                        int32_t Hq, int32_t Hkv, int32_t n, int32_t D, float* out, float* acc,
-                                       float* var, void* ws, size_t* ws_bytes, void* stream) {
+                                       float* var, float* lse, void* ws, size_t* ws_bytes, void* stream) {
   using namespace kvc;
   if (!ws_bytes) return KVC_ERR_NULL;
   if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
@@ -497,6 +502,7 @@ extern "C" kvc_status kvc_prefill_attn(const void* q, const void* k, const void*
   a.v = v;
   a.out = out;
   a.lse = static_cast<float*>(ws);
+  a.lse_out = lse;
   a.acc = acc;
   a.B = B;
   a.Hq = Hq;

@@ -529,6 +529,17 @@ __global__ __launch_bounds__(kThreads) void rowstat_kernel(ScoreArgs a) {
   if (lane == 0) a.rowstat[bj * a.R + r] = M + log2f(L);
 }
 
+// Pass 2's row statistics from given normalizers: rowstat[b][j][g*W + w] =
+// log2(e) * lse[(b*Hq + j*G + g)*stride + w] (the log2-unit M + log2 L that
+// rowstat_kernel would derive from pass 1).
+__global__ __launch_bounds__(kThreads) void lse_rowstat_kernel(ScoreArgs a, const float* lse, int stride) {
+  const int r = blockIdx.x * kThreads + threadIdx.x, j = blockIdx.y, b = blockIdx.z;
+  if (r >= a.R) return;
+  const int g = r / a.W, w = r - g * a.W;
+  a.rowstat[(static_cast<size_t>(b) * a.Hkv + j) * a.R + r] =
+      lse[(static_cast<size_t>(b) * a.Hq + j * a.G + g) * stride + w] * 1.4426950408889634f;
+}
+
 constexpr int kTopThreads = 1024;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -1047,13 +1058,23 @@ kvc_status launch_pipe_any(const ScoreArgs& a, int KS, int B, hipStream_t st) {
 }
 bool pipe_ok(int KS, int R) { return (KS == 1 || KS == 2 || KS == 4) && R <= 256; }
 
+// The window scores: pass 1 and rowstat_kernel find each row's normalizer, or
+// (lse given) lse_rowstat_kernel takes it; then pass 2.
 template <typename T>
-kvc_status run_scores(const ScoreArgs& a, int KS, int B, hipStream_t st) {
+kvc_status run_scores(const ScoreArgs& a, int KS, int B, hipStream_t st, const float* lse = nullptr,
+                      int lse_stride = 0) {
   constexpr int CH = ChunkCols<T>::value;
   const bool pipe = sizeof(T) == 2 && pipe_ok(KS, a.R);
-  kvc_status s = pipe ? launch_pipe_any<1>(a, KS, B, st) : launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
-  if (s != KVC_OK) return s;
-  hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.Hkv, B), dim3(kThreads), 0, st, a);
+  kvc_status s;
+  if (lse) {
+    hipLaunchKernelGGL(lse_rowstat_kernel, dim3((a.R + kThreads - 1) / kThreads, a.Hkv, B), dim3(kThreads), 0, st, a,
+                       lse, lse_stride);
+  } else {
+    s = pipe ? launch_pipe_any<1>(a, KS, B, st) : launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
+    if (s != KVC_OK) return s;
+    hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.Hkv, B), dim3(kThreads), 0,
+                       st, a);
+  }
   if ((s = check_launch()) != KVC_OK) return s;
   return pipe ? launch_pipe_any<2>(a, KS, B, st) : launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
 }
@@ -1227,10 +1248,12 @@ kvc_status launch_variance(const float* raw, int rows, int N, float* var, hipStr
 
 }  // namespace kvc
 
-extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dtype, int32_t B, int32_t Hq,
-                                 int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool, int32_t budget,
-                                 int32_t* idx, float* scores, void* ws, size_t* ws_bytes, void* stream) {
-  using namespace kvc;
+namespace kvc {
+namespace {
+// kvc_select and kvc_select_lse (lse NULL: the normalizers from pass 1).
+kvc_status select_impl(const void* q_win, const void* k, const float* lse, int lse_stride, kvc_dtype dtype,
+                       int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool,
+                       int32_t budget, int32_t* idx, float* scores, void* ws, size_t* ws_bytes, void* stream) {
   if (!ws_bytes) return KVC_ERR_NULL;
   if (!dtype_ok(dtype)) return KVC_ERR_DTYPE;
   if (!score_shape_ok(B, Hq, Hkv, n, D, W) || pool < 1 || pool % 2 == 0) return KVC_ERR_SHAPE;
@@ -1253,9 +1276,29 @@ extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dty
   float* raw = reinterpret_cast<float*>(w + sw.total);
   const ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, w, raw);
   const TopArgs t = top_args(raw, Hkv, N, kk, pool, tw, w + sw.total + sz_raw, idx, scores);
-  kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st) : run_scores<uint16_t>(a, D / 32, B, st);
+  kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st, lse, lse_stride)
+                                  : run_scores<uint16_t>(a, D / 32, B, st, lse, lse_stride);
   if (s != KVC_OK) return s;
   return run_topk(t, B, st);
+}
+}  // namespace
+}  // namespace kvc
+
+extern "C" kvc_status kvc_select(const void* q_win, const void* k, kvc_dtype dtype, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t n, int32_t D, int32_t W, int32_t pool, int32_t budget,
+                                 int32_t* idx, float* scores, void* ws, size_t* ws_bytes, void* stream) {
+  return kvc::select_impl(q_win, k, nullptr, 0, dtype, B, Hq, Hkv, n, D, W, pool, budget, idx, scores, ws, ws_bytes,
+                          stream);
+}
+
+extern "C" kvc_status kvc_select_lse(const void* q_win, const void* k, const float* lse, int32_t lse_stride,
+                                     kvc_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t D,
+                                     int32_t W, int32_t pool, int32_t budget, int32_t* idx, float* scores, void* ws,
+                                     size_t* ws_bytes, void* stream) {
+  if (!ws_bytes || (ws && !lse)) return KVC_ERR_NULL;
+  if (lse_stride < W) return KVC_ERR_SHAPE;
+  return kvc::select_impl(q_win, k, lse, lse_stride, dtype, B, Hq, Hkv, n, D, W, pool, budget, idx, scores, ws,
+                          ws_bytes, stream);
 }
 
 extern "C" kvc_status kvc_window_scores(const void* q_win, const void* k, kvc_dtype dtype, int32_t B, int32_t Hq,

@@ -160,6 +160,23 @@ def test_select_validation_and_ws_query():
     assert st == 1
 
 
+def test_select_lse_validation_and_ws_query():
+    """kvc_select_lse: the same workspace as kvc_select; a given workspace with
+    no lse, or a row stride below W, is rejected before any launch."""
+    L = _lib()
+    f = L.lib.kvc_select_lse
+    need = ctypes.c_size_t(0)
+    N = None
+    assert f(N, N, N, 8, 1, 1, 4, 4, 64, 64, 8, 5, 8, N, N, N, ctypes.byref(need), N) == 0
+    assert need.value == _call_select()[1]
+    assert f(N, N, N, 7, 1, 1, 4, 4, 64, 64, 8, 5, 8, N, N, N, ctypes.byref(need), N) == 2   # lse stride < W
+    assert f(N, N, N, 8, 1, 1, 6, 4, 64, 64, 8, 5, 8, N, N, N, ctypes.byref(need), N) == 2   # Hq % Hkv
+    P = ctypes.c_void_p(16)
+    big = ctypes.c_size_t(1 << 30)
+    assert f(P, P, N, 8, 1, 1, 4, 4, 64, 64, 8, 5, 8, P, N, P, ctypes.byref(big), N) == 1    # no lse
+    assert f(P, P, P, 8, 1, 1, 4, 4, 64, 64, 8, 5, 8, P, N, P, None, N) == 1                 # no ws_bytes
+
+
 def _cache(**kw):
     L = _lib()
     c = L.CacheStruct(1, 4, 64, 2, 16, 64, 0, 48, 0, 0, 0, 0, 16, 16, 16, 16, 16, 16)

@@ -128,6 +128,33 @@ def test_select_parity(dtype, B, G, Hkv, n, D, W, pool, budget):
             gu.check_selection(ix[b, j], sc[b, j], pooled[b, j], budget)
 
 
+@pytest.mark.parametrize("dtype,B,G,Hkv,n,D,W,pool,budget", [
+    ("bf16", 2, 4, 2, 700, 128, 16, 7, 100), ("f32", 1, 1, 4, 512, 64, 8, 5, 64),
+    ("bf16", 1, 8, 1, 1000, 128, 32, 7, 200),     # 256 window rows
+    ("bf16", 1, 3, 2, 333, 32, 5, 3, 40),
+    ("bf16", 1, 2, 2, 40000, 64, 16, 7, 1500)])   # rows above 32k candidates
+def test_select_lse_parity(dtype, B, G, Hkv, n, D, W, pool, budget):
+    """kvc_select_lse with the window rows' log-sum-exp from kvc_prefill_attn
+    (the prompt's own prefill, its last W query rows being q_win): the scores
+    and indices meet the same checks against the oracle as kvc_select's."""
+    kvc = _kvc()
+    Hq = G * Hkv
+    k, v = _case(21, B, Hkv, n, D, dtype)
+    q = synth.random_tensor(22, (B, Hq, n, D), dtype, tag="q").cuda()
+    q_win = q[:, :, n - W:].contiguous()
+    lse = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+    kvc.kvc_prefill_attn(q, k, v, want_acc=False, lse=lse)
+    idx, scores = kvc.kvc_select_lse(q_win, k, lse, W, pool, budget, want_scores=True)
+    idx2, _ = kvc.kvc_select_lse(q_win, k, lse[:, :, n - W:].contiguous(), W, pool, budget, want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)  # a compact [B][Hq][W] lse gives the same selection
+    pooled = oselect.max_pool(oselect.window_scores(gu.as_f32(q_win), gu.as_f32(k), W), pool)
+    sc, ix = scores.cpu().numpy(), idx.cpu().numpy()
+    for b in range(B):
+        for j in range(Hkv):
+            gu.check_selection(ix[b, j], sc[b, j], pooled[b, j], budget)
+
+
 @pytest.mark.parametrize("budget", [-1, 280, 5000])
 def test_select_keep_all_without_scores(budget):
     """Keeping every candidate needs no ranking: without scores kvc_select

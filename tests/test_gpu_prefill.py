@@ -95,14 +95,15 @@ def test_prefill_without_colsums_and_validation():
     need = ctypes.c_size_t(0)
     f = _lib.lib.kvc_prefill_attn
     P = ctypes.c_void_p(16)
-    assert f(None, None, None, 1, 1, 4, 2, 150, 96, None, None, None, None, ctypes.byref(need), None) == 2  # D
-    assert f(None, None, None, 1, 1, 6, 4, 150, 64, None, None, None, None, ctypes.byref(need), None) == 2  # Hq%Hkv
-    assert f(None, None, None, 4, 1, 4, 2, 150, 64, None, None, None, None, ctypes.byref(need), None) == 3
-    assert f(None, None, None, 1, 1, 4, 2, 150, 64, None, None, None, None, ctypes.byref(need), None) == 0
+    N = None
+    assert f(N, N, N, 1, 1, 4, 2, 150, 96, N, N, N, N, N, ctypes.byref(need), N) == 2  # D
+    assert f(N, N, N, 1, 1, 6, 4, 150, 64, N, N, N, N, N, ctypes.byref(need), N) == 2  # Hq % Hkv
+    assert f(N, N, N, 4, 1, 4, 2, 150, 64, N, N, N, N, N, ctypes.byref(need), N) == 3  # dtype
+    assert f(N, N, N, 1, 1, 4, 2, 150, 64, N, N, N, N, N, ctypes.byref(need), N) == 0
     big = ctypes.c_size_t(need.value)
-    assert f(P, P, P, 1, 1, 4, 2, 150, 64, P, None, P, P, ctypes.byref(big), None) == 1   # var without acc
+    assert f(P, P, P, 1, 1, 4, 2, 150, 64, P, N, P, N, P, ctypes.byref(big), N) == 1   # var without acc
     small = ctypes.c_size_t(need.value - 1)
-    assert f(P, P, P, 1, 1, 4, 2, 150, 64, P, P, None, P, ctypes.byref(small), None) == 6
+    assert f(P, P, P, 1, 1, 4, 2, 150, 64, P, P, N, N, P, ctypes.byref(small), N) == 6
 
 
 @pytest.mark.parametrize("n,W,budget", [(300, 8, 40), (300, 8, -1), (300, 300, 5), (300, 16, 0), (5000, 32, 600),
