@@ -42,7 +42,8 @@ Parity status of each function (pins live in ``tests/test_oracle_*.py``):
   prefill.*           pinned (torch SDPA for the output, pure-Python brute force
                       and the harmonic closed form for the column sums, the
                       row-mass invariant, the last W rows == window scores,
-                      H2O selection by brute-force sort, variance closed forms)
+                      H2O selection by brute-force sort, variance closed forms;
+                      row_lse: brute force, max/log bounds, equal-keys closed form)
 """
 
 from . import budget, select, quant, decode, prefill  # noqa: F401

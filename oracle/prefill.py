@@ -65,6 +65,27 @@ def attention_colsums(q, k, v, row_from=0, row_block=1024):
     return O, acc
 
 
+def row_lse(q, k):
+    """Each prompt row's log-sum-exp (natural log) of its causal logits
+    q_r . k_c / sqrt(D) over c <= r: the softmax normalizer the prefill's
+    FlashAttention keeps (MiniKV Sec. 4.3), which normalizes each row of
+    attention_colsums.  q [B][Hq][n][D], k [B][Hkv][n][D]; returns float64
+    [B][Hq][n]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Hq, n, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.empty((B, Hq, n))
+    mask = np.arange(n)[None, :] > np.arange(n)[:, None]
+    for b in range(B):
+        for h in range(Hq):
+            x = (q[b, h] @ k[b, h // G].T) / np.sqrt(D)
+            x[mask] = -np.inf
+            m = x.max(axis=1)
+            out[b, h] = m + np.log(np.exp(x - m[:, None]).sum(axis=1))
+    return out
+
+
 def h2o_select(acc_row, n, W, budget):
     """Heavy hitters plus the recent window for one (b, KV head).
 

@@ -5,6 +5,7 @@ through the C ABI, against oracle.prefill on the same inputs:
   * A_cumul within 1e-5 * (|a_ref| + max a_ref) per (b, KV head), and the
     row-mass invariant sum_c A_cumul = G * n;
   * the variance against the oracle's on the GPU's own A_cumul;
+  * each row's log-sum-exp within 1e-5 * max(1, |lse_ref|) of oracle.prefill.row_lse;
   * H2O indices exact on the GPU's own A_cumul, and the oracle's set up to
     near-ties; A_cumul bit-identical between two runs (no atomics).
 """
@@ -36,7 +37,7 @@ def _inputs(seed, B, Hq, Hkv, n, D, dtype):
     return q, k, v
 
 
-def check_prefill(q, k, v, out, acc, var, heads=None, where=""):
+def check_prefill(q, k, v, out, acc, var, heads=None, where="", lse=None):
     """Compare the GPU results with the oracle on (b, KV head) units `heads`
     (all by default); the row-mass invariant on every unit."""
     B, Hq, n, D = q.shape
@@ -57,6 +58,11 @@ def check_prefill(q, k, v, out, acc, var, heads=None, where=""):
         ar = a_ref[0, 0]
         np.testing.assert_array_less(np.abs(a[b, j] - ar), gu.SCORE_TOL * (np.abs(ar) + ar.max()) + 1e-30,
                                      err_msg=f"{where} acc b{b} j{j}")
+        if lse is not None:
+            lr = oprefill.row_lse(qf[b:b + 1, j * G:(j + 1) * G], kf[b:b + 1, j:j + 1])[0]
+            lg = lse[b, j * G:(j + 1) * G].cpu().numpy()
+            np.testing.assert_array_less(np.abs(lg - lr), 1e-5 * np.maximum(1.0, np.abs(lr)),
+                                         err_msg=f"{where} lse b{b} j{j}")
     return worst
 
 
@@ -72,9 +78,10 @@ def check_prefill(q, k, v, out, acc, var, heads=None, where=""):
 def test_prefill_parity(dtype, B, Hq, Hkv, n, D):
     kvc = _kvc()
     q, k, v = _inputs(1, B, Hq, Hkv, n, D, dtype)
-    out, acc, var = kvc.kvc_prefill_attn(q, k, v, want_var=True)
+    lse = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+    out, acc, var = kvc.kvc_prefill_attn(q, k, v, want_var=True, lse=lse)
     torch.cuda.synchronize()
-    check_prefill(q, k, v, out, acc, var, where=f"{dtype} B{B} Hq{Hq} Hkv{Hkv} n{n} D{D}")
+    check_prefill(q, k, v, out, acc, var, where=f"{dtype} B{B} Hq{Hq} Hkv{Hkv} n{n} D{D}", lse=lse)
     # deterministic: the same bits again
     _, acc2, _ = kvc.kvc_prefill_attn(q, k, v)
     torch.cuda.synchronize()

@@ -130,3 +130,45 @@ def test_variance_closed_forms():
     mu = sum(harm) / n
     ref = sum((x - mu) ** 2 for x in harm) / n
     assert prefill.acc_variance(harm[None, None])[0, 0] == pytest.approx(ref, rel=1e-12)
+
+
+def test_row_lse_brute_force_and_bounds():
+    """row_lse by plain loops with math.exp on a tiny case; in general
+    max_c x_rc <= lse_r <= max_c x_rc + log(r + 1), and with equal keys
+    lse_r = x + log(r + 1) exactly."""
+    q, k, _ = _case(9, 1, 4, 2, 9, 5)
+    lse = prefill.row_lse(q, k)
+    for h in range(4):
+        for r in range(9):
+            xs = [sum(q[0, h, r, d] * k[0, h // 2, c, d] for d in range(5)) / math.sqrt(5) for c in range(r + 1)]
+            assert lse[0, h, r] == pytest.approx(math.log(sum(math.exp(x) for x in xs)), rel=1e-12, abs=1e-12)
+    q, k, _ = _case(10, 2, 4, 2, 60, 16, key_scale=3.0)
+    lse = prefill.row_lse(q, k)
+    x = np.einsum("bhrd,bjcd->bhjrc", q, k)  # every head against every KV head; take its own below
+    for h in range(4):
+        xs = x[:, h, h // 2] / 4.0
+        xs = np.where(np.arange(60)[None, None, :] > np.arange(60)[None, :, None], -np.inf, xs)
+        mx = xs.max(axis=-1)
+        assert np.all(lse[:, h] >= mx - 1e-12) and np.all(lse[:, h] <= mx + np.log(np.arange(1, 61)) + 1e-12)
+    n, D = 20, 8
+    rng = np.random.default_rng(11)
+    kk = np.tile(rng.standard_normal(D), (1, 1, n, 1))
+    qq = rng.standard_normal((1, 2, n, D))
+    lse = prefill.row_lse(qq, kk)
+    xv = (qq[0] @ kk[0, 0, 0]) / np.sqrt(D)
+    np.testing.assert_allclose(lse[0], xv + np.log(np.arange(1, n + 1))[None, :], rtol=1e-13, atol=1e-13)
+
+
+def test_colsums_normalized_by_row_lse():
+    """attention_colsums' probabilities are exp(x - row_lse): rebuilding A_cumul
+    from row_lse gives the same columns."""
+    q, k, v = _case(12, 1, 4, 2, 40, 8, key_scale=2.0)
+    _, acc = prefill.attention_colsums(q, k, v)
+    lse = prefill.row_lse(q, k)
+    n, G = 40, 2
+    ref = np.zeros((1, 2, n))
+    for h in range(4):
+        x = (q[0, h] @ k[0, h // G].T) / np.sqrt(8)
+        x[np.arange(n)[None, :] > np.arange(n)[:, None]] = -np.inf
+        ref[0, h // G] += np.exp(x - lse[0, h][:, None]).sum(axis=0)
+    np.testing.assert_allclose(acc, ref, rtol=1e-12)
