@@ -36,6 +36,8 @@ struct ScoreArgs {
   float2* stats;      // pass 1: [B][Hkv][nc1][R] (max, sum) in log2 units
   float* rowstat;     // [B][Hkv][R] M + log2(L): 2^(x - it) is x's softmax weight
   float* raw;         // [B][Hkv][N] column sums
+  const float* lse;   // or null: window row w of head h at lse[(b*Hq + h)*lse_stride + w], natural log
+  int lse_stride;
   int Hq, Hkv, G, n, W, R, N, nc1;
   float scale2;
 };
@@ -213,16 +215,25 @@ __device__ __forceinline__ void score_rows(const ScoreArgs& a, int bj, int chunk
   }
 }
 
-// Pass 2's row statistics for the lane's eight rows.
+// Pass 2's row statistics for the lane's rows: from rowstat_kernel, or (lse
+// given) log2(e) times window row r % W of query head r / W of the KV head.
 template <int TPW>
 __device__ __forceinline__ void load_rowstat(const ScoreArgs& a, int bj, const int (&row0)[TPW], float (&st)[TPW][4]) {
   const int lq = (threadIdx.x & 63) >> 4;
+  const int b = bj / a.Hkv, j = bj - b * a.Hkv;
 #pragma unroll
   for (int u = 0; u < TPW; ++u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = row0[u] + 4 * lq + i;
-      st[u][i] = (r < a.R) ? a.rowstat[static_cast<size_t>(bj) * a.R + r] : INFINITY;
+      if (r >= a.R) {
+        st[u][i] = INFINITY;
+      } else if (a.lse) {
+        const int g = r / a.W, w = r - g * a.W;
+        st[u][i] = a.lse[(static_cast<size_t>(b) * a.Hq + j * a.G + g) * a.lse_stride + w] * 1.4426950408889634f;
+      } else {
+        st[u][i] = a.rowstat[static_cast<size_t>(bj) * a.R + r];
+      }
     }
 }
 
@@ -527,17 +538,6 @@ __global__ __launch_bounds__(kThreads) void rowstat_kernel(ScoreArgs a) {
   const float M = wave_max(m);
   const float L = wave_sum(m == -INFINITY ? 0.0f : l * exp2f(m - M));
   if (lane == 0) a.rowstat[bj * a.R + r] = M + log2f(L);
-}
-
-// Pass 2's row statistics from given normalizers: rowstat[b][j][g*W + w] =
-// log2(e) * lse[(b*Hq + j*G + g)*stride + w] (the log2-unit M + log2 L that
-// rowstat_kernel would derive from pass 1).
-__global__ __launch_bounds__(kThreads) void lse_rowstat_kernel(ScoreArgs a, const float* lse, int stride) {
-  const int r = blockIdx.x * kThreads + threadIdx.x, j = blockIdx.y, b = blockIdx.z;
-  if (r >= a.R) return;
-  const int g = r / a.W, w = r - g * a.W;
-  a.rowstat[(static_cast<size_t>(b) * a.Hkv + j) * a.R + r] =
-      lse[(static_cast<size_t>(b) * a.Hq + j * a.G + g) * stride + w] * 1.4426950408889634f;
 }
 
 constexpr int kTopThreads = 1024;
@@ -1058,24 +1058,19 @@ kvc_status launch_pipe_any(const ScoreArgs& a, int KS, int B, hipStream_t st) {
 }
 bool pipe_ok(int KS, int R) { return (KS == 1 || KS == 2 || KS == 4) && R <= 256; }
 
-// The window scores: pass 1 and rowstat_kernel find each row's normalizer, or
-// (lse given) lse_rowstat_kernel takes it; then pass 2.
+// The window scores: pass 1 and rowstat_kernel find each row's normalizer
+// (unless a.lse gives them: pass 2 reads those directly), then pass 2.
 template <typename T>
-kvc_status run_scores(const ScoreArgs& a, int KS, int B, hipStream_t st, const float* lse = nullptr,
-                      int lse_stride = 0) {
+kvc_status run_scores(const ScoreArgs& a, int KS, int B, hipStream_t st) {
   constexpr int CH = ChunkCols<T>::value;
   const bool pipe = sizeof(T) == 2 && pipe_ok(KS, a.R);
-  kvc_status s;
-  if (lse) {
-    hipLaunchKernelGGL(lse_rowstat_kernel, dim3((a.R + kThreads - 1) / kThreads, a.Hkv, B), dim3(kThreads), 0, st, a,
-                       lse, lse_stride);
-  } else {
-    s = pipe ? launch_pipe_any<1>(a, KS, B, st) : launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
+  if (!a.lse) {
+    kvc_status s = pipe ? launch_pipe_any<1>(a, KS, B, st) : launch_score<T, 1>(a, KS, dim3(a.nc1, a.Hkv, B), st);
     if (s != KVC_OK) return s;
     hipLaunchKernelGGL(rowstat_kernel, dim3((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.Hkv, B), dim3(kThreads), 0,
                        st, a);
+    if ((s = check_launch()) != KVC_OK) return s;
   }
-  if ((s = check_launch()) != KVC_OK) return s;
   return pipe ? launch_pipe_any<2>(a, KS, B, st) : launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
 }
 
@@ -1191,6 +1186,8 @@ ScoreArgs score_args(const void* q_win, const void* k, int Hq, int Hkv, int n, i
   a.stats = reinterpret_cast<float2*>(w);
   a.rowstat = reinterpret_cast<float*>(w + sw.stats);
   a.raw = raw;
+  a.lse = nullptr;
+  a.lse_stride = 0;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = Hq / Hkv;
@@ -1274,10 +1271,11 @@ kvc_status select_impl(const void* q_win, const void* k, const float* lse, int l
   if (kk == N && !scores) return launch_identity(idx, static_cast<size_t>(B) * Hkv * N, N, st);
   char* w = static_cast<char*>(ws);
   float* raw = reinterpret_cast<float*>(w + sw.total);
-  const ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, w, raw);
+  ScoreArgs a = score_args(q_win, k, Hq, Hkv, n, D, W, sw, w, raw);
+  a.lse = lse;
+  a.lse_stride = lse_stride;
   const TopArgs t = top_args(raw, Hkv, N, kk, pool, tw, w + sw.total + sz_raw, idx, scores);
-  kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st, lse, lse_stride)
-                                  : run_scores<uint16_t>(a, D / 32, B, st, lse, lse_stride);
+  kvc_status s = dtype == KVC_F32 ? run_scores<float>(a, D / 32, B, st) : run_scores<uint16_t>(a, D / 32, B, st);
   if (s != KVC_OK) return s;
   return run_topk(t, B, st);
 }
