@@ -548,66 +548,71 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-wide exclusive prefix sum of one int per thread; *total gets the sum.
-__device__ int block_exclusive_scan(int x, int* sh, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int inc = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) sh[w] = inc;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < kTopThreads / 64; ++i) {
-      const int t = sh[i];
-      sh[i] = run;
-      run += t;
-    }
-    sh[kTopThreads / 64] = run;
-  }
-  __syncthreads();
-  const int res = sh[w] + inc - x;
-  *total = sh[kTopThreads / 64];
-  __syncthreads();
-  return res;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4, 8 within each row of 16 lanes, then row 0's total into row 1 and row
+// 2's into row 3 (row_bcast:15), then rows 0-1's total into rows 2-3
+// (row_bcast:31).  Lanes without a source add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
 }
 
-// One vote per active lane to an LDS histogram.  The LDS resolves lanes that hit
-// one address in hardware; that is cheaper than grouping the lanes of a bin
-// first (one ballot and about four VALU instructions per bin bit and key:
-// measured 10 us slower per layer at the 8B shape, although scores share their
-// leading key bytes and so collide).
-__device__ __forceinline__ void hist_add(int* hist, bool valid, uint32_t bin) {
-  if (valid) atomicAdd(&hist[bin], 1);
+// Histogram votes of a thread's consecutive candidates: one LDS atomic per run
+// of valid keys with equal bins, adding the run length.  Neighbouring
+// candidates mostly share their leading key byte, so one vote per key would put
+// nearly every lane of a wave on one address in the first pass (the LDS
+// serializes those): measured 4.6 us of a 14 us top-k at the 8B shape.
+template <int KPT>
+__device__ __forceinline__ void hist_add_runs(int* hist, const bool (&valid)[KPT], const uint32_t (&bin)[KPT]) {
+  int run = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    run = valid[i] ? run + 1 : 0;
+    const bool cont = i + 1 < KPT && valid[i + 1] && bin[i + 1] == bin[i];
+    if (valid[i] && !cont) atomicAdd(&hist[bin[i]], run);
+    if (!cont) run = 0;
+  }
 }
 
-// Digit selection of one radix pass: the largest d with sum_{d' >= d} cnt[d'] >=
-// krem, by an inclusive scan over the 256 bins taken from the top (threads
-// 0..255, cnt of bin 255 - t); the owning thread writes (d, krem - above).
-__device__ __forceinline__ void select_digit(const int* cnt, int krem, int* wsum, uint32_t* sel) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int c = t < 256 ? cnt[255 - t] : 0;
-  int inc = c;
+// Digit selection of one radix pass by one wave (after the barrier that ends
+// the votes): lane l holds bins 255-4l .. 252-4l (counted from the top), one
+// wave scan of their sums, and the lane whose bin first reaches krem writes
+// (digit, krem - above).  It clears the 256 bins for the next pass (no one
+// reads them before the next barrier).
+__device__ __forceinline__ void select_digit_wave(int* hist, int krem, uint32_t* sel) {
+  const int lane = threadIdx.x & 63;
+  int4* h4 = reinterpret_cast<int4*>(hist) + 63 - lane;  // bins 252-4l .. 255-4l
+  const int4 w = *h4;
+  *h4 = make_int4(0, 0, 0, 0);
+  const int c[4] = {w.w, w.z, w.y, w.x};  // bins 255-4l, 254-4l, ...
+  const int tot = c[0] + c[1] + c[2] + c[3];
+  int above = wave_incl_scan(tot) - tot;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (t < 256 && lane == 63) wsum[w] = inc;
-  __syncthreads();
-  if (t < 256) {
-    int off = 0;
-    for (int i = 0; i < w; ++i) off += wsum[i];
-    inc += off;
-    const int above = inc - c;
-    if (inc >= krem && above < krem) {
-      sel[0] = static_cast<uint32_t>(255 - t);
+  for (int i = 0; i < 4; ++i) {
+    if (above < krem && above + c[i] >= krem) {
+      sel[0] = static_cast<uint32_t>(255 - 4 * lane - i);
       sel[1] = static_cast<uint32_t>(krem - above);
     }
+    above += c[i];
   }
+}
+
+// Block-wide exclusive prefix sum with one barrier; sh (kTopThreads/64 ints)
+// must not be written again before a later barrier.
+__device__ int block_exclusive_scan1(int x, int* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int inc = wave_incl_scan(x);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kTopThreads / 64; ++i) base += i < w ? sh[i] : 0;
+  return base + inc - x;
 }
 
 constexpr int kMaxPoolHalf = 4;  // pooling kernels up to 9 use the register window
@@ -629,8 +634,7 @@ __device__ __forceinline__ void select_digit_wide(const int* cnt, int krem, int*
     c[i] = cnt[NB - 1 - (t * BPT + i)];
     tot += c[i];
   }
-  int all;
-  int above = block_exclusive_scan(tot, scan_sh, &all);
+  int above = block_exclusive_scan1(tot, scan_sh);
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     if (above < krem && above + c[i] >= krem) {
@@ -671,7 +675,9 @@ __device__ __forceinline__ uint4 load_chunk_keys(const TopArgs& a, size_t bj, in
 __device__ __forceinline__ uint32_t key_at(const uint4& k, int i) { return i == 0 ? k.x : i == 1 ? k.y : i == 2 ? k.z : k.w; }
 
 __global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
-  __shared__ float rs[kChunk + 2 * kMaxPoolHalf];  // raw[c0 - kMaxPoolHalf + i]
+  // raw[c0 - kMaxPoolHalf + i], positions outside the row replaced by the
+  // nearest end value (the maximum of a window clipped to the row)
+  __shared__ __attribute__((aligned(16))) float rs[kChunk + 2 * kMaxPoolHalf];
   __shared__ int hist[256];
   const int ch = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
@@ -681,28 +687,31 @@ __global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
   if (tid < 256) hist[tid] = 0;
   if (ch == 0)  // the counts of passes 2 and 3 are accumulated by later launches
     for (int i = tid; i < 2 * kWideBins; i += kTopThreads) a.ghist[bj * 2 * kWideBins + i] = 0;
-  for (int i = tid; i < kChunk + 2 * kMaxPoolHalf; i += kTopThreads) {
-    const int c = c0 - kMaxPoolHalf + i;
-    if (c >= 0 && c < N) rs[i] = raw[c];
-  }
+  for (int i = tid; i < kChunk + 2 * kMaxPoolHalf; i += kTopThreads)
+    rs[i] = raw[min(max(c0 - kMaxPoolHalf + i, 0), N - 1)];
   __syncthreads();
   const int cb = c0 + tid * kChunkKpt;
   uint32_t key[kChunkKpt];
   if (h <= kMaxPoolHalf) {
-    // window [cb - h, cb + kChunkKpt + h) clamped to the row: every clamped
-    // position lies in the staged range
-    float win[kChunkKpt + 2 * kMaxPoolHalf];
+    // window positions cb - 4 .. cb + kChunkKpt + 3 through aligned 16-byte
+    // LDS reads (per-float reads of slots 4 floats apart conflict on the banks)
+    constexpr int NWIN = kChunkKpt + 2 * kMaxPoolHalf;
+    float win[NWIN];
+    const float4* w4 = reinterpret_cast<const float4*>(rs + tid * kChunkKpt);
 #pragma unroll
-    for (int i = 0; i < kChunkKpt + 2 * kMaxPoolHalf; ++i) {
-      const int c = min(max(cb - h + i, 0), N - 1);
-      win[i] = (i < kChunkKpt + 2 * h) ? rs[c - (c0 - kMaxPoolHalf)] : 0.0f;
+    for (int i = 0; i < NWIN / 4; ++i) {
+      const float4 x = w4[i];
+      win[4 * i] = x.x;
+      win[4 * i + 1] = x.y;
+      win[4 * i + 2] = x.z;
+      win[4 * i + 3] = x.w;
     }
 #pragma unroll
     for (int i = 0; i < kChunkKpt; ++i) {
-      float m = win[i];
+      float m = win[i + kMaxPoolHalf];
 #pragma unroll
-      for (int d = 1; d <= 2 * kMaxPoolHalf; ++d)
-        if (d <= 2 * h) m = fmaxf(m, win[i + d]);
+      for (int d = 1; d <= kMaxPoolHalf; ++d)
+        if (d <= h) m = fmaxf(m, fmaxf(win[i + kMaxPoolHalf - d], win[i + kMaxPoolHalf + d]));
       const int c = cb + i;
       key[i] = c < N ? order_key(m) : 0u;
       if (a.scores && c < N) a.scores[bj * N + c] = m;
@@ -723,8 +732,14 @@ __global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
   }
   *reinterpret_cast<uint4*>(a.keys + bj * a.NP + cb) = make_uint4(key[0], key[1], key[2], key[3]);
   if (a.kk == 0) return;
+  bool valid[kChunkKpt];
+  uint32_t bin[kChunkKpt];
 #pragma unroll
-  for (int i = 0; i < kChunkKpt; ++i) hist_add(hist, cb + i < N, key[i] >> 24);
+  for (int i = 0; i < kChunkKpt; ++i) {
+    valid[i] = cb + i < N;
+    bin[i] = key[i] >> 24;
+  }
+  hist_add_runs<kChunkKpt>(hist, valid, bin);
   __syncthreads();
   if (tid < 256) a.hist1[(bj * a.nch + ch) * 256 + tid] = hist[tid];
 }
@@ -734,7 +749,7 @@ __global__ __launch_bounds__(kTopThreads) void chunk_pool_kernel(TopArgs a) {
 // then counts of bits 0..11 among keys with that 20-bit prefix.
 template <int PASS>
 __global__ __launch_bounds__(kTopThreads) void chunk_hist_kernel(TopArgs a) {
-  __shared__ int hist[kWideBins];
+  __shared__ __attribute__((aligned(16))) int hist[kWideBins];
   __shared__ int scan_sh[kTopThreads / 64 + 1];
   __shared__ uint32_t sel_sh[2];
   const int ch = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -752,7 +767,7 @@ __global__ __launch_bounds__(kTopThreads) void chunk_hist_kernel(TopArgs a) {
       atomicAdd(&hist[bin], s);
     }
     __syncthreads();
-    select_digit(hist, a.kk, scan_sh, sel_sh);
+    if (tid < 64) select_digit_wave(hist, a.kk, sel_sh);
     __syncthreads();
     prefix = sel_sh[0] << 24;
     pmask = 0xFF000000u;
@@ -775,11 +790,15 @@ __global__ __launch_bounds__(kTopThreads) void chunk_hist_kernel(TopArgs a) {
   constexpr int shift = PASS == 2 ? 12 : 0;
   const int cb = ch * kChunk + tid * kChunkKpt;
   const uint4 k4 = load_chunk_keys(a, bj, cb);
+  bool valid[kChunkKpt];
+  uint32_t bin[kChunkKpt];
 #pragma unroll
   for (int i = 0; i < kChunkKpt; ++i) {
     const uint32_t key = key_at(k4, i);
-    hist_add(hist, cb + i < a.N && (key & pmask) == prefix, (key >> shift) & (kWideBins - 1));
+    valid[i] = cb + i < a.N && (key & pmask) == prefix;
+    bin[i] = (key >> shift) & (kWideBins - 1);
   }
+  hist_add_runs<kChunkKpt>(hist, valid, bin);
   __syncthreads();
   int* g = a.ghist + (bj * 2 + (PASS - 2)) * kWideBins;
   for (int i = tid; i < kWideBins; i += kTopThreads)
@@ -812,10 +831,16 @@ __global__ __launch_bounds__(kTopThreads) void chunk_count_kernel(TopArgs a) {
     gt += (ok && key > tau) ? 1 : 0;
     eq += (ok && key == tau) ? 1 : 0;
   }
-  int tg, te;
-  block_exclusive_scan(gt, scan_sh, &tg);
-  block_exclusive_scan(eq, scan_sh, &te);
-  if (tid == 0) a.cnt[bj * a.nch + ch] = make_int2(tg, te);
+  // both counts in 16-bit halves (at most kChunk = 4096 each)
+  const int inc = wave_incl_scan((gt << 16) | eq);
+  if ((tid & 63) == 63) scan_sh[tid >> 6] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < kTopThreads / 64; ++i) t += scan_sh[i];
+    a.cnt[bj * a.nch + ch] = make_int2(t >> 16, t & 0xFFFF);
+  }
 }
 
 // Chunk ch's keys above the threshold go after those of chunks 0..ch-1; of the
@@ -849,78 +874,91 @@ __global__ __launch_bounds__(kTopThreads) void chunk_emit_kernel(TopArgs a) {
   const int g_before = before[0], e_before = before[1];
   const int cb = ch * kChunk + tid * kChunkKpt;
   const uint4 k4 = load_chunk_keys(a, bj, cb);
-  int n_eq = 0;
+  // keys taken before this thread's: the larger ones plus min(krem, equal ones)
+  // before it, over this chunk and the chunks before it (one scan of both
+  // counts in 16-bit halves)
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
-  for (int i = 0; i < kChunkKpt; ++i) n_eq += (cb + i < a.N && key_at(k4, i) == tau) ? 1 : 0;
-  int tot;
-  int eq_rank = block_exclusive_scan(n_eq, scan_sh, &tot) + e_before;
-  bool take[kChunkKpt];
-  int n_take = 0;
+  for (int i = 0; i < kChunkKpt; ++i) {
+    const uint32_t key = key_at(k4, i);
+    const bool ok = cb + i < a.N;
+    n_gt += (ok && key > tau) ? 1 : 0;
+    n_eq += (ok && key == tau) ? 1 : 0;
+  }
+  const int bfr = block_exclusive_scan1((n_gt << 16) | n_eq, scan_sh);
+  int eq_rank = (bfr & 0xFFFF) + e_before;
+  int pos = g_before + (bfr >> 16) + min(krem, eq_rank);
+  int32_t* idx = a.idx + bj * a.kk;
 #pragma unroll
   for (int i = 0; i < kChunkKpt; ++i) {
     const uint32_t key = key_at(k4, i);
     const bool ok = cb + i < a.N;
     const bool eq = ok && key == tau;
-    take[i] = ok && (key > tau || (eq && eq_rank < krem));
+    const bool take = ok && (key > tau || (eq && eq_rank < krem));
     eq_rank += eq ? 1 : 0;
-    n_take += take[i] ? 1 : 0;
-  }
-  int pos = block_exclusive_scan(n_take, scan_sh, &tot) + g_before + min(krem, e_before);
-  int32_t* idx = a.idx + bj * a.kk;
-#pragma unroll
-  for (int i = 0; i < kChunkKpt; ++i) {
-    if (take[i] && pos < a.kk) idx[pos] = cb + i;
-    pos += take[i] ? 1 : 0;
+    if (take && pos < a.kk) idx[pos] = cb + i;
+    pos += take ? 1 : 0;
   }
 }
 
 // Short score rows (N <= KPT * 1024): the raw scores are staged in LDS once,
 // thread t owns the KPT consecutive candidates [t*KPT, t*KPT + KPT) and keeps
-// their pooled keys in registers for the four radix passes, and the index-order
-// emission needs two block scans in total.
+// their pooled keys in registers for the four radix passes (two barriers each),
+// and the index-order emission needs one block scan.
 template <int KPT>
 __global__ __launch_bounds__(kTopThreads) void pool_topk_lds_kernel(TopArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float rs[];  // [N] raw scores
-  __shared__ int hist[256];
+  // raw scores of positions -kMaxPoolHalf .. KPT*kTopThreads + kMaxPoolHalf - 1:
+  // the row, padded on both sides with copies of its end values
+  extern __shared__ __attribute__((aligned(16))) float rs_pad[];
+  __shared__ __attribute__((aligned(16))) int hist[256];
   __shared__ int scan_sh[kTopThreads / 64 + 1];
   __shared__ uint32_t sel_sh[2];
   const int j = blockIdx.x, b = blockIdx.y;
   const size_t bj = static_cast<size_t>(b) * a.Hkv + j;
   const int tid = threadIdx.x;
-  const int N = a.N, h = a.pool / 2;
+  const int N = a.N, h = a.pool / 2;  // N >= 1
   const float* raw = a.raw + bj * a.ld;
   int32_t* idx = a.idx + bj * a.kk;
+  float* rs = rs_pad + kMaxPoolHalf;
   {
     float v[KPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * kTopThreads;
-      v[i] = c < N ? raw[c] : 0.0f;
-    }
+    for (int i = 0; i < KPT; ++i) v[i] = raw[min(tid + i * kTopThreads, N - 1)];
+    float e = 0.0f;
+    if (tid < 2 * kMaxPoolHalf) e = raw[tid < kMaxPoolHalf ? 0 : N - 1];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * kTopThreads;
-      if (c < N) rs[c] = v[i];
-    }
+    for (int i = 0; i < KPT; ++i) rs[tid + i * kTopThreads] = v[i];
+    if (tid < kMaxPoolHalf) rs[tid - kMaxPoolHalf] = e;
+    else if (tid < 2 * kMaxPoolHalf) rs[KPT * kTopThreads + tid - kMaxPoolHalf] = e;
   }
+  if (tid < 256) hist[tid] = 0;
   __syncthreads();
   const int cb = tid * KPT;
   uint32_t key[KPT];
   if (h <= kMaxPoolHalf) {
-    // the thread's pooling window [cb - h, cb + KPT + h) in registers, clamped
-    // at the row ends (the same maximum as a window clipped to the row)
-    float win[KPT + 2 * kMaxPoolHalf];
+    // the thread's widest pooling window, positions cb - 4 .. cb + KPT + 3, in
+    // registers through aligned 16-byte LDS reads (one float per lane from
+    // slots 8 floats apart would conflict on the LDS banks); the padding
+    // repeats the end values, which gives the maximum of a window clipped to
+    // the row
+    constexpr int NWIN = KPT + 2 * kMaxPoolHalf;
+    float win[NWIN];
+    const float4* w4 = reinterpret_cast<const float4*>(rs + cb - kMaxPoolHalf);
 #pragma unroll
-    for (int i = 0; i < KPT + 2 * kMaxPoolHalf; ++i) {
-      const int c = min(max(cb - h + i, 0), N - 1);
-      win[i] = (i < KPT + 2 * h) ? rs[c] : 0.0f;
+    for (int i = 0; i < NWIN / 4; ++i) {
+      const float4 x = w4[i];
+      win[4 * i] = x.x;
+      win[4 * i + 1] = x.y;
+      win[4 * i + 2] = x.z;
+      win[4 * i + 3] = x.w;
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      float m = win[i];
+      // window of candidate cb + i: win[i + 4 - h .. i + 4 + h]
+      float m = win[i + kMaxPoolHalf];
 #pragma unroll
-      for (int d = 1; d <= 2 * kMaxPoolHalf; ++d)
-        if (d <= 2 * h) m = fmaxf(m, win[i + d]);
+      for (int d = 1; d <= kMaxPoolHalf; ++d)
+        if (d <= h) m = fmaxf(m, fmaxf(win[i + kMaxPoolHalf - d], win[i + kMaxPoolHalf + d]));
       const int c = cb + i;
       key[i] = c < N ? order_key(m) : 0u;
       if (a.scores && c < N) a.scores[bj * N + c] = m;
@@ -946,44 +984,48 @@ __global__ __launch_bounds__(kTopThreads) void pool_topk_lds_kernel(TopArgs a) {
   }
   uint32_t prefix = 0, pmask = 0;
   int krem = a.kk;
-  // per pass: the histogram is cleared (its readers passed the barrier after
-  // the previous digit selection), filled, and its digit selected; sel_sh is
-  // read before the next selection, two barriers later
+  // per pass: votes (the histogram was cleared before the previous barrier),
+  // a barrier, wave 0's digit selection (which clears the bins again), a
+  // barrier; sel_sh is read before wave 0 next writes it, one barrier later
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+    bool valid[KPT];
+    uint32_t bin[KPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) hist_add(hist, cb + i < N && (key[i] & pmask) == prefix, (key[i] >> shift) & 255u);
+    for (int i = 0; i < KPT; ++i) {
+      valid[i] = cb + i < N && (key[i] & pmask) == prefix;
+      bin[i] = (key[i] >> shift) & 255u;
+    }
+    hist_add_runs<KPT>(hist, valid, bin);
     __syncthreads();
-    select_digit(hist, krem, scan_sh, sel_sh);
+    if (tid < 64) select_digit_wave(hist, krem, sel_sh);
     __syncthreads();
     prefix |= sel_sh[0] << shift;
     pmask |= 255u << shift;
     krem = static_cast<int>(sel_sh[1]);
   }
   // prefix is the k'-th largest key: take every larger key and the krem
-  // lowest-index keys equal to it, in index order
-  int n_eq = 0;
+  // lowest-index keys equal to it, in index order.  The keys taken before this
+  // thread's are the larger ones plus min(krem, equal ones) before it: one scan
+  // of both counts, packed in 16-bit halves (N <= 32768).
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) n_eq += (cb + i < N && key[i] == prefix) ? 1 : 0;
-  int tot;
-  int eq_rank = block_exclusive_scan(n_eq, scan_sh, &tot);
-  int n_take = 0;
-  bool take[KPT];
+  for (int i = 0; i < KPT; ++i) {
+    const bool ok = cb + i < N;
+    n_gt += (ok && key[i] > prefix) ? 1 : 0;
+    n_eq += (ok && key[i] == prefix) ? 1 : 0;
+  }
+  const int before = block_exclusive_scan1((n_gt << 16) | n_eq, scan_sh);
+  int eq_rank = before & 0xFFFF;
+  int pos = (before >> 16) + min(eq_rank, krem);
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const bool ok = cb + i < N;
     const bool eq = ok && key[i] == prefix;
-    take[i] = ok && (key[i] > prefix || (eq && eq_rank < krem));
+    const bool take = ok && (key[i] > prefix || (eq && eq_rank < krem));
     eq_rank += eq ? 1 : 0;
-    n_take += take[i] ? 1 : 0;
-  }
-  int pos = block_exclusive_scan(n_take, scan_sh, &tot);
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if (take[i] && pos < a.kk) idx[pos] = cb + i;
-    pos += take[i] ? 1 : 0;
+    if (take && pos < a.kk) idx[pos] = cb + i;
+    pos += take ? 1 : 0;
   }
 }
 
@@ -1074,27 +1116,29 @@ kvc_status run_scores(const ScoreArgs& a, int KS, int B, hipStream_t st) {
   return pipe ? launch_pipe_any<2>(a, KS, B, st) : launch_score<T, 2>(a, KS, dim3((a.N + CH - 1) / CH, a.Hkv, B), st);
 }
 
+// Launch of pool_topk_lds_kernel<KPT> with its padded score row in dynamic LDS
+// (above the 64 KB default from KPT = 16 on).
+template <int KPT> kvc_status launch_topk_lds(const TopArgs& t, int B, hipStream_t st) {
+  constexpr size_t lds = static_cast<size_t>(KPT * kTopThreads + 2 * kMaxPoolHalf) * sizeof(float);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_topk_lds_kernel<KPT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) {
+      set_last_hip_error(e);
+      return KVC_ERR_HIP;
+    }
+  }
+  hipLaunchKernelGGL(pool_topk_lds_kernel<KPT>, dim3(t.Hkv, B), dim3(kTopThreads), lds, st, t);
+  return check_launch();
+}
+
 kvc_status run_topk(const TopArgs& t, int B, hipStream_t st) {
   if (chunked_topk(t.N)) return run_chunked_topk(t, B, st);
   // short rows: raw scores in LDS, keys in registers
   const int kpt = (t.N + kTopThreads - 1) / kTopThreads;
-  const size_t lds = static_cast<size_t>(t.N) * sizeof(float);
-  if (kpt <= 8) {
-    hipLaunchKernelGGL(pool_topk_lds_kernel<8>, dim3(t.Hkv, B), dim3(kTopThreads), lds, st, t);
-  } else if (kpt <= 16) {
-    hipLaunchKernelGGL(pool_topk_lds_kernel<16>, dim3(t.Hkv, B), dim3(kTopThreads), lds, st, t);
-  } else {
-    if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_topk_lds_kernel<32>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) {
-        set_last_hip_error(e);
-        return KVC_ERR_HIP;
-      }
-    }
-    hipLaunchKernelGGL(pool_topk_lds_kernel<32>, dim3(t.Hkv, B), dim3(kTopThreads), lds, st, t);
-  }
-  return check_launch();
+  if (kpt <= 8) return launch_topk_lds<8>(t, B, st);
+  if (kpt <= 16) return launch_topk_lds<16>(t, B, st);
+  return launch_topk_lds<32>(t, B, st);
 }
 
 // Position-only selection, the same for every (b, KV head): entry e of a row
