@@ -202,7 +202,10 @@ def test_window_scores_and_variance(dtype, B, G, Hkv, n, D, W):
 
 @pytest.mark.parametrize("B,Hkv,N,pool,budget", [
     (2, 3, 500, 7, 100), (1, 2, 40000, 7, 1500), (1, 1, 33000, 13, 700), (2, 2, 1000, 1, -1),
-    (1, 2, 300, 5, 0), (1, 1, 8160, 9, 512), (3, 1, 4096 * 9, 3, 1)])
+    (1, 2, 300, 5, 0), (1, 1, 8160, 9, 512), (3, 1, 4096 * 9, 3, 1),
+    # rows shorter than a pooling window and than one thread's candidates (the
+    # padded LDS row), and rows that end inside the last thread's candidates
+    (1, 1, 1, 7, 1), (2, 1, 5, 9, 2), (1, 2, 9, 3, 4), (1, 1, 8195, 7, 600), (1, 1, 16390, 5, 1000)])
 def test_topk_on_given_scores(B, Hkv, N, pool, budget):
     """kvc_topk on seeded scores on a coarse grid (many ties): the pooled scores
     are maxima of the inputs (exact) and idx is the oracle's top-k of them."""
