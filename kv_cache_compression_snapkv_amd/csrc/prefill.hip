@@ -149,7 +149,10 @@ template <typename T, int KS> struct PfGeom {
   static constexpr int STAGE = VOFF + D * VROW;
   static constexpr int PIECES = D * ES / 16;            // 16-byte pieces per key row
   static constexpr int KLOADS = (kKT * PIECES + kPfThreads - 1) / kPfThreads;
-  static constexpr int VITEMS = (kKT / 2) * PIECES;     // (key pair, piece) items
+  // (key pair, piece) items, key pair fastest: the transposed stores of one
+  // channel by the lanes of a wave then fall in distinct bank pairs (with the
+  // piece fastest, lanes 8 channel rows apart shared two bank groups)
+  static constexpr int VITEMS = (kKT / 2) * PIECES;
   static constexpr int VLOADS = (VITEMS + kPfThreads - 1) / kPfThreads;
 };
 
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
 #pragma unroll
     for (int u = 0; u < Gm::VLOADS; ++u) {
       const int e = tid + kPfThreads * u;
-      const int kp = e / Gm::PIECES, pc = e % Gm::PIECES;
+      const int kp = e % (kKT / 2), pc = e / (kKT / 2);  // key pair fastest
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         vst[u][w] = u32x4{0u, 0u, 0u, 0u};
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
     for (int u = 0; u < Gm::VLOADS; ++u) {
       const int e = tid + kPfThreads * u;
       if (e < Gm::VITEMS) {
-        const int kp = e / Gm::PIECES, pc = e % Gm::PIECES;
+        const int kp = e % (kKT / 2), pc = e / (kKT / 2);  // key pair fastest
         if constexpr (ES == 2) {
           // 8 channels of keys 2kp, 2kp+1: one dword (both keys) per channel
 #pragma unroll
