@@ -74,6 +74,18 @@ template <> struct Frag<float> {
   }
 };
 
+// Two transposing 8-byte LDS reads (ds_read_b64_tr_b16: within each quarter of
+// the wave, lane i receives element e of the read of lane 4e + i/4, element
+// i%4), joined into one 8-slot fragment.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 tr_pair(const unsigned char* p0, const unsigned char* p1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua.x, ua.y, ub.x, ub.y};
+}
+
 // acc[row 4*lq+i][col ln] += sum over the 8 k-slots of every lane quarter.
 __device__ __forceinline__ f32x4 mma(const Frag<uint16_t>& a, const Frag<uint16_t>& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v), __builtin_bit_cast(bf16x8, b.v),
@@ -144,9 +156,13 @@ template <typename T, int KS> struct PfGeom {
   static constexpr int D = 32 * KS;
   static constexpr int ES = sizeof(T);
   static constexpr int KROW = D * ES + 16;
-  static constexpr int VROW = kKT * ES + (ES == 2 ? 8 : 16);
+  // bf16 values are staged row-major like the keys (rows 32 bytes longer: the
+  // transposing reads of 4 rows x 32 bytes by 16 lanes then cover all banks);
+  // fp32 values transposed, channel-major
+  static constexpr bool VTR = ES == 2;
+  static constexpr int VROW = VTR ? D * ES + 32 : kKT * ES + 16;
   static constexpr int VOFF = kKT * KROW;
-  static constexpr int STAGE = VOFF + D * VROW;
+  static constexpr int STAGE = VOFF + (VTR ? kKT : D) * VROW;
   static constexpr int PIECES = D * ES / 16;            // 16-byte pieces per key row
   static constexpr int KLOADS = (kKT * PIECES + kPfThreads - 1) / kPfThreads;
   // (key pair, piece) items, key pair fastest: the transposed stores of one
@@ -203,7 +219,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
   }
 
   // staging of tile t into registers, then into LDS buffer `buf`
-  u32x4 kst[Gm::KLOADS], vst[Gm::VLOADS][2];
+  u32x4 kst[Gm::KLOADS], vst[Gm::VTR ? 1 : Gm::VLOADS][2], vrow[Gm::KLOADS];
   auto fetch = [&](int t) {
     const int kb = t * kKT;
 #pragma unroll
@@ -214,15 +230,26 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
       if (e < kKT * Gm::PIECES && kb + key < n)
         kst[u] = *reinterpret_cast<const u32x4*>(kg + (static_cast<size_t>(kb + key) * D * ES) + 16 * pc);
     }
+    if constexpr (Gm::VTR) {
 #pragma unroll
-    for (int u = 0; u < Gm::VLOADS; ++u) {
-      const int e = tid + kPfThreads * u;
-      const int kp = e % (kKT / 2), pc = e / (kKT / 2);  // key pair fastest
+      for (int u = 0; u < Gm::KLOADS; ++u) {
+        const int e = tid + kPfThreads * u;
+        const int key = e / Gm::PIECES, pc = e % Gm::PIECES;
+        vrow[u] = u32x4{0u, 0u, 0u, 0u};
+        if (e < kKT * Gm::PIECES && kb + key < n)
+          vrow[u] = *reinterpret_cast<const u32x4*>(vg + (static_cast<size_t>(kb + key) * D * ES) + 16 * pc);
+      }
+    } else {
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        vst[u][w] = u32x4{0u, 0u, 0u, 0u};
-        if (e < Gm::VITEMS && kb + 2 * kp + w < n)
-          vst[u][w] = *reinterpret_cast<const u32x4*>(vg + (static_cast<size_t>(kb + 2 * kp + w) * D * ES) + 16 * pc);
+      for (int u = 0; u < Gm::VLOADS; ++u) {
+        const int e = tid + kPfThreads * u;
+        const int kp = e % (kKT / 2), pc = e / (kKT / 2);  // key pair fastest
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          vst[u][w] = u32x4{0u, 0u, 0u, 0u};
+          if (e < Gm::VITEMS && kb + 2 * kp + w < n)
+            vst[u][w] = *reinterpret_cast<const u32x4*>(vg + (static_cast<size_t>(kb + 2 * kp + w) * D * ES) + 16 * pc);
+        }
       }
     }
   };
@@ -232,24 +259,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
 #pragma unroll
     for (int u = 0; u < Gm::KLOADS; ++u) {
       const int e = tid + kPfThreads * u;
-      if (e < kKT * Gm::PIECES)
+      if (e < kKT * Gm::PIECES) {
         *reinterpret_cast<u32x4*>(Ks + (e / Gm::PIECES) * Gm::KROW + 16 * (e % Gm::PIECES)) = kst[u];
+        if constexpr (Gm::VTR)
+          *reinterpret_cast<u32x4*>(Vt + (e / Gm::PIECES) * Gm::VROW + 16 * (e % Gm::PIECES)) = vrow[u];
+      }
     }
+    if constexpr (!Gm::VTR) {
 #pragma unroll
-    for (int u = 0; u < Gm::VLOADS; ++u) {
-      const int e = tid + kPfThreads * u;
-      if (e < Gm::VITEMS) {
-        const int kp = e % (kKT / 2), pc = e / (kKT / 2);  // key pair fastest
-        if constexpr (ES == 2) {
-          // 8 channels of keys 2kp, 2kp+1: one dword (both keys) per channel
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const uint32_t w0 = vst[u][0][c >> 1], w1 = vst[u][1][c >> 1];
-            const uint32_t lo = (c & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-            const uint32_t hi = (c & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16);
-            *reinterpret_cast<uint32_t*>(Vt + (8 * pc + c) * Gm::VROW + 4 * kp) = lo | hi;
-          }
-        } else {
+      for (int u = 0; u < Gm::VLOADS; ++u) {
+        const int e = tid + kPfThreads * u;
+        if (e < Gm::VITEMS) {
+          const int kp = e % (kKT / 2), pc = e / (kKT / 2);  // key pair fastest
           // 4 channels of keys 2kp, 2kp+1: two dwords per channel
 #pragma unroll
           for (int c = 0; c < 4; ++c)
@@ -325,8 +346,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       Frag<T> vf;
-      const unsigned char* vr = Vt + (16 * c + ln) * Gm::VROW;
-      vf.load4x2(vr + 4 * lq * ES, vr + (16 + 4 * lq) * ES);
+      if constexpr (Gm::VTR) {
+        // A = V^T: lane (ln, lq) takes channel 16c + ln of keys 4lq..4lq+3 and
+        // 16+4lq..16+4lq+3.  A transposing LDS read gives lane ln of a lane
+        // quarter element e of lane 4e + ln/4's 8-byte read, so lane j of the
+        // quarter reads channels 16c + 4(j%4) .. +3 of key 4lq + j/4 (+16).
+        const unsigned char* va = Vt + (4 * lq + (ln >> 2)) * Gm::VROW + (16 * c + 4 * (ln & 3)) * ES;
+        vf.v = tr_pair(va, va + 16 * Gm::VROW);
+      } else {
+        const unsigned char* vr = Vt + (16 * c + ln) * Gm::VROW;
+        vf.load4x2(vr + 4 * lq * ES, vr + (16 + 4 * lq) * ES);
+      }
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) {
         oacc[c][rs] = mma(vf, ph[rs], oacc[c][rs]);
