@@ -57,11 +57,36 @@ __device__ __forceinline__ float2 pair_f32(const uint16_t* p) {
 }
 __device__ __forceinline__ float2 pair_f32(const float* p) { return *reinterpret_cast<const float2*>(p); }
 
-// Code of x in a group (z, inv): a zero scale has inv = 0, so the product is 0
-// (or NaN for a non-finite operand, which the max below turns into 0): code 0.
-__device__ __forceinline__ uint32_t code_q(float x, float2 q, float qmax) {
+// Code of x in a group (z, inv), as a float bit pattern: t = (x - z) * inv is
+// clamped to [0, qmax] and 1.5 * 2^23 is added.  Floats in [2^23, 2^24) are
+// spaced 1 apart, so the sum is that constant plus rint(t), ties to even, and
+// the integer sits in the low mantissa bits; rounding commutes with a clamp to
+// integer bounds.  A zero scale has inv = 0, so t is 0 (or NaN for a non-finite
+// operand, which the clamp turns into 0): code 0.
+constexpr float kRoundAdd = 12582912.0f;  // 1.5 * 2^23
+constexpr uint32_t kRoundBits = 0x4B400000u;
+__device__ __forceinline__ uint32_t code_bits(float x, float2 q, float qmax) {
   const float t = __fmul_rn(__fsub_rn(x, q.x), q.y);
-  return static_cast<uint32_t>(fminf(fmaxf(__builtin_rintf(t), 0.0f), qmax));
+  return __float_as_uint(__fadd_rn(fminf(fmaxf(t, 0.0f), qmax), kRoundAdd));
+}
+// A word is the wrapping sum of code_bits(...) << (BITS * slot) over its 32/BITS
+// slots; subtracting the constant's share leaves the packed codes.
+template <int BITS> constexpr uint32_t code_bias() {
+  uint32_t c = 0;
+  for (int i = 0; i < 32 / BITS; ++i) c += kRoundBits << (BITS * i);
+  return c;
+}
+
+// Lane exchanges within a wave: dpp_f<0xB1> gives lane l the value of lane
+// l ^ 1, dpp_f<0x4E> that of l ^ 2 (quad permutes); from_upper<G> gives the
+// lanes whose index has bit G clear (G = 16 or 32) the value of lane l + G.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int G> __device__ __forceinline__ float from_upper(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (G == 32) return __uint_as_float(__builtin_amdgcn_permlane32_swap(u, u, false, false)[1]);
+  else return __uint_as_float(__builtin_amdgcn_permlane16_swap(u, u, false, false)[1]);
 }
 
 // Quantize the G tokens staged in L and write them at token offset q0 of the
@@ -91,13 +116,14 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
       lo1 = fminf(lo1, x.y);
       hi1 = fmaxf(hi1, x.y);
     }
-#pragma unroll
-    for (int o = 1; o <= 2; o <<= 1) {
-      lo0 = fminf(lo0, __shfl_xor(lo0, o));
-      hi0 = fmaxf(hi0, __shfl_xor(hi0, o));
-      lo1 = fminf(lo1, __shfl_xor(lo1, o));
-      hi1 = fmaxf(hi1, __shfl_xor(hi1, o));
-    }
+    lo0 = fminf(lo0, dpp_f<0xB1>(lo0));
+    hi0 = fmaxf(hi0, dpp_f<0xB1>(hi0));
+    lo1 = fminf(lo1, dpp_f<0xB1>(lo1));
+    hi1 = fmaxf(hi1, dpp_f<0xB1>(hi1));
+    lo0 = fminf(lo0, dpp_f<0x4E>(lo0));
+    hi0 = fmaxf(hi0, dpp_f<0x4E>(hi0));
+    lo1 = fminf(lo1, dpp_f<0x4E>(lo1));
+    hi1 = fmaxf(hi1, dpp_f<0x4E>(hi1));
     if (qt < 2) {
       const int c = 2 * p + qt;
       const GroupQ g = make_group(qt ? lo1 : lo0, qt ? hi1 : hi0, qmax);
@@ -106,7 +132,7 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
     }
   }
   // value groups: lane e walks half h of group j of token t (e = 2Gj + Gh + t);
-  // lanes e and e^G combine and the h = 0 lane makes the group
+  // the h = 0 lane takes lane e + G's extremes and makes the group
   for (int e = tid; e < 2 * G * ngv; e += kThreads) {
     const int t = e & (G - 1), j = e / (2 * G), h = (e / G) & 1;
     const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][j * G + (G / 2) * h]);
@@ -122,8 +148,8 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
         hi = fmaxf(hi, f[i]);
       }
     }
-    lo = fminf(lo, __shfl_xor(lo, G));
-    hi = fmaxf(hi, __shfl_xor(hi, G));
+    lo = fminf(lo, from_upper<G>(lo));
+    hi = fmaxf(hi, from_upper<G>(hi));
     if (h == 0) {
       const GroupQ g = make_group(lo, hi, qmax);
       L.vq[t][j] = make_float2(g.z, g.inv);
@@ -148,11 +174,12 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
       for (int i = 0; i < VEC; i += 2) {
         const uint4 qq = qs[(p * VEC + i) / 2];  // parameters of channels i, i+1 of this piece
         const int c = p * VEC + i;
-        word |= code_q(f[i], make_float2(__uint_as_float(qq.x), __uint_as_float(qq.y)), qmax) << (BITS * c);
-        word |= code_q(f[i + 1], make_float2(__uint_as_float(qq.z), __uint_as_float(qq.w)), qmax) << (BITS * (c + 1));
+        word += code_bits(f[i], make_float2(__uint_as_float(qq.x), __uint_as_float(qq.y)), qmax) << (BITS * c);
+        word += code_bits(f[i + 1], make_float2(__uint_as_float(qq.z), __uint_as_float(qq.w)), qmax)
+                << (BITS * (c + 1));
       }
     }
-    k_codes[static_cast<size_t>(q0 + t) * nw + w] = word;
+    k_codes[static_cast<size_t>(q0 + t) * nw + w] = word - code_bias<BITS>();
   }
   // value words: word row r of channel c holds tokens r*per..; a thread takes
   // the channel pair c, c+1 (same group, same parameters)
@@ -167,10 +194,11 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
       const int t = r * per + i;
       const float2 q = L.vq[t][j];
       const float2 x = pair_f32(&L.v[t][c]);
-      w0 |= code_q(x.x, q, qmax) << (BITS * i);
-      w1 |= code_q(x.y, q, qmax) << (BITS * i);
+      w0 += code_bits(x.x, q, qmax) << (BITS * i);
+      w1 += code_bits(x.y, q, qmax) << (BITS * i);
     }
-    *reinterpret_cast<uint2*>(&v_codes[(static_cast<size_t>(q0) / per + r) * D + c]) = make_uint2(w0, w1);
+    *reinterpret_cast<uint2*>(&v_codes[(static_cast<size_t>(q0) / per + r) * D + c]) =
+        make_uint2(w0 - code_bias<BITS>(), w1 - code_bias<BITS>());
   }
 }
 
@@ -202,10 +230,11 @@ __device__ __forceinline__ int kept_pos(const QuantArgs& a, int bj, int t) {
 // issued before the first LDS store: one memory round trip for the positions,
 // one for the data.
 template <typename T, int DM, int G>
-__device__ void stage_rows(QuantLds<T, DM, G>& L, const QuantArgs& a, int bj, int t_first, int count) {
+__device__ __forceinline__ void stage_rows(QuantLds<T, DM, G>& L, const QuantArgs& a, int D, int bj, int t_first,
+                                           int count) {
   constexpr int VEC = 16 / sizeof(T);                      // elements per 16 bytes
   constexpr int MAXV = (G * DM / VEC + kThreads - 1) / kThreads;  // pieces per thread at D = DM
-  const int D = a.D, ppr = D / VEC, total = G * ppr;       // pieces per row, per tensor
+  const int ppr = D / VEC, total = G * ppr;                // pieces per row, per tensor
   const T* k = static_cast<const T*>(a.k) + static_cast<size_t>(bj) * a.n * D;
   const T* v = static_cast<const T*>(a.v) + static_cast<size_t>(bj) * a.n * D;
   const int tid = threadIdx.x;
@@ -240,17 +269,17 @@ __device__ void stage_rows(QuantLds<T, DM, G>& L, const QuantArgs& a, int bj, in
   }
 }
 
+// One workgroup's block; D is the head dimension (the constant DM when they are
+// equal, so that the index arithmetic and loop bounds fold at compile time).
 template <typename T, int BITS, int DM, int G>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ __attribute__((aligned(16))) QuantLds<T, DM, G> L;
+__device__ __forceinline__ void quantize_body(QuantLds<T, DM, G>& L, const QuantArgs& a, int D) {
   const int blk = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int bj = b * a.Hkv + j;
-  const int D = a.D;
   const int tid = threadIdx.x;
   const int nqb = a.Q / G;
   if (blk < nqb) {
     const int t0 = blk * G;
-    stage_rows<T, DM, G>(L, a, bj, t0, G);
+    stage_rows<T, DM, G>(L, a, D, bj, t0, G);
     __syncthreads();
     const size_t qc = a.q_cap;
     quantize_block<BITS>(L, D, t0, a.k_codes + static_cast<size_t>(bj) * qc * (D * BITS / 32),
@@ -261,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     // residual: kept tokens [Q, T) -> bf16 ring rows 0..T-Q-1
     const int r0 = (blk - nqb) * G;
     const int nr = min(G, a.T - a.Q - r0);
-    stage_rows<T, DM, G>(L, a, bj, a.Q + r0, nr);
+    stage_rows<T, DM, G>(L, a, D, bj, a.Q + r0, nr);
     __syncthreads();
     uint16_t* kr = a.k_res + static_cast<size_t>(bj) * a.r_cap * D;  // [r_cap][D]
     uint16_t* vr = a.v_res + static_cast<size_t>(bj) * D * a.r_cap;  // [D][r_cap]
@@ -297,6 +326,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   }
 }
 
+template <typename T, int BITS, int DM, int G>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) QuantLds<T, DM, G> L;
+  if (a.D == DM) quantize_body<T, BITS>(L, a, DM);
+  else quantize_body<T, BITS>(L, a, a.D);
+}
+
 struct FlushArgs {
   const void* k_new;
   const void* v_new;
@@ -317,11 +353,9 @@ struct FlushArgs {
 // row loads, values with 16-byte loads of 8 consecutive ring rows of one channel
 // (r_start and r_cap are multiples of 8, so such a chunk never wraps).
 template <typename T, int BITS, int DM, int G>
-__global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
-  __shared__ __attribute__((aligned(16))) QuantLds<uint16_t, DM, G> L;  // the ring holds bf16
+__device__ __forceinline__ void flush_body(QuantLds<uint16_t, DM, G>& L, const FlushArgs& a, int D) {
   const int j = blockIdx.x, b = blockIdx.y, grp = blockIdx.z;
   const int bj = b * a.Hkv + j;
-  const int D = a.D;
   const int tid = threadIdx.x;
   const int t_first = grp * G;          // first residual token of this group
   const int r_new = a.r_old - t_first;  // the appended token's index inside this group's tokens
@@ -371,6 +405,13 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
                        a.k_meta + static_cast<size_t>(bj) * (qc / G) * D,
                        a.v_codes + static_cast<size_t>(bj) * (qc * BITS / 32) * D,
                        a.v_meta + static_cast<size_t>(bj) * qc * (D / G));
+}
+
+template <typename T, int BITS, int DM, int G>
+__global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
+  __shared__ __attribute__((aligned(16))) QuantLds<uint16_t, DM, G> L;  // the ring holds bf16
+  if (a.D == DM) flush_body<T, BITS>(L, a, DM);
+  else flush_body<T, BITS>(L, a, a.D);
 }
 
 // Head-dim bound of the LDS layout.
