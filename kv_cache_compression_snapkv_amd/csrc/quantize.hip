@@ -77,16 +77,10 @@ template <int BITS> constexpr uint32_t code_bias() {
   return c;
 }
 
-// Lane exchanges within a wave: dpp_f<0xB1> gives lane l the value of lane
-// l ^ 1, dpp_f<0x4E> that of l ^ 2 (quad permutes); from_upper<G> gives the
-// lanes whose index has bit G clear (G = 16 or 32) the value of lane l + G.
+// Lane exchange within a quad: dpp_f<0xB1> gives lane l the value of lane
+// l ^ 1, dpp_f<0x4E> that of l ^ 2.
 template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-template <int G> __device__ __forceinline__ float from_upper(float x) {
-  const uint32_t u = __float_as_uint(x);
-  if constexpr (G == 32) return __uint_as_float(__builtin_amdgcn_permlane32_swap(u, u, false, false)[1]);
-  else return __uint_as_float(__builtin_amdgcn_permlane16_swap(u, u, false, false)[1]);
 }
 
 // Quantize the G tokens staged in L and write them at token offset q0 of the
@@ -100,10 +94,14 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
   const float qmax = static_cast<float>((1 << BITS) - 1);
   const int ngv = D / G;
   // Extremes are exact in any order, so the groups' walks are split over lanes
-  // and combined with lane shuffles; both loops run over 2D items, a multiple of
-  // 64, so every wave in them is whole.
-  // key groups: lanes 4p..4p+3 walk channels 2p, 2p+1 over the tokens of one
-  // residue mod 4 each; lane 4p+k (k = 0, 1) then makes channel 2p+k's group
+  // and combined with quad-lane exchanges.  One pass over 2D items (a multiple
+  // of 64, so every wave in it is whole) walks both tensors; item e then makes
+  // one group: a key channel when bit 1 of e is clear, a value group when set.
+  //   keys: lanes 4p..4p+3 walk channels 2p, 2p+1 over the tokens of one
+  //   residue mod 4 each; lane 4p+k (k = 0, 1) makes channel 2p+k.
+  //   values: within each run of 2G items, item u walks half h = bit 1 of u of
+  //   group jv = e / 2G of token t = 2(u / 4) + (u & 1); lanes u and u ^ 2
+  //   combine, and the h = 1 lane makes the group.
   for (int e = tid; e < 2 * D; e += kThreads) {
     const int p = e >> 2, qt = e & 3;
     float2 x = pair_f32(&L.k[qt][2 * p]);
@@ -116,6 +114,21 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
       lo1 = fminf(lo1, x.y);
       hi1 = fmaxf(hi1, x.y);
     }
+    const int u = e & (2 * G - 1), jv = e / (2 * G), h = (u >> 1) & 1;
+    const int t = ((u >> 2) << 1) | (u & 1);
+    const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][jv * G + (G / 2) * h]);
+    float f[VEC];
+    unpack16(seg[0], f);
+    float vlo = f[0], vhi = f[0];
+#pragma unroll
+    for (int q = 0; q < (G / 2) / VEC; ++q) {
+      if (q) unpack16(seg[q], f);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        vlo = fminf(vlo, f[i]);
+        vhi = fmaxf(vhi, f[i]);
+      }
+    }
     lo0 = fminf(lo0, dpp_f<0xB1>(lo0));
     hi0 = fmaxf(hi0, dpp_f<0xB1>(hi0));
     lo1 = fminf(lo1, dpp_f<0xB1>(lo1));
@@ -124,36 +137,17 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
     hi0 = fmaxf(hi0, dpp_f<0x4E>(hi0));
     lo1 = fminf(lo1, dpp_f<0x4E>(lo1));
     hi1 = fmaxf(hi1, dpp_f<0x4E>(hi1));
-    if (qt < 2) {
+    vlo = fminf(vlo, dpp_f<0x4E>(vlo));
+    vhi = fmaxf(vhi, dpp_f<0x4E>(vhi));
+    const bool is_val = qt >= 2;
+    const GroupQ g = make_group(is_val ? vlo : (qt ? lo1 : lo0), is_val ? vhi : (qt ? hi1 : hi0), qmax);
+    if (is_val) {
+      L.vq[t][jv] = make_float2(g.z, g.inv);
+      v_meta[static_cast<size_t>(q0 + t) * ngv + jv] = g.meta;
+    } else {
       const int c = 2 * p + qt;
-      const GroupQ g = make_group(qt ? lo1 : lo0, qt ? hi1 : hi0, qmax);
       L.kq[c] = make_float2(g.z, g.inv);
       k_meta[static_cast<size_t>(q0 / G) * D + c] = g.meta;
-    }
-  }
-  // value groups: lane e walks half h of group j of token t (e = 2Gj + Gh + t);
-  // the h = 0 lane takes lane e + G's extremes and makes the group
-  for (int e = tid; e < 2 * G * ngv; e += kThreads) {
-    const int t = e & (G - 1), j = e / (2 * G), h = (e / G) & 1;
-    const uint4* seg = reinterpret_cast<const uint4*>(&L.v[t][j * G + (G / 2) * h]);
-    float f[VEC];
-    unpack16(seg[0], f);
-    float lo = f[0], hi = f[0];
-#pragma unroll
-    for (int p = 0; p < (G / 2) / VEC; ++p) {
-      if (p) unpack16(seg[p], f);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        lo = fminf(lo, f[i]);
-        hi = fmaxf(hi, f[i]);
-      }
-    }
-    lo = fminf(lo, from_upper<G>(lo));
-    hi = fmaxf(hi, from_upper<G>(hi));
-    if (h == 0) {
-      const GroupQ g = make_group(lo, hi, qmax);
-      L.vq[t][j] = make_float2(g.z, g.inv);
-      v_meta[static_cast<size_t>(q0 + t) * ngv + j] = g.meta;
     }
   }
   __syncthreads();
@@ -181,24 +175,31 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
     }
     k_codes[static_cast<size_t>(q0 + t) * nw + w] = word - code_bias<BITS>();
   }
-  // value words: word row r of channel c holds tokens r*per..; a thread takes
-  // the channel pair c, c+1 (same group, same parameters)
+  // value words: word row r of channel c holds tokens r*per..; lanes 2i and
+  // 2i+1 take the channel pair c, c+1 (same group, same parameters) over the
+  // first and the second half of the row's tokens, add their partial sums, and
+  // each stores one channel's word
   constexpr int rows = G / per;  // value word rows per block
-  const float rcp_pairs = __builtin_amdgcn_rcpf(static_cast<float>(D / 2));
-  for (int e = tid; e < rows * (D / 2); e += kThreads) {
-    const QR rc = small_divmod(e, D / 2, rcp_pairs);
-    const int r = rc.q, c = rc.r * 2, j = c / G;
+  constexpr int half = per / 2;
+  const float rcp_d = __builtin_amdgcn_rcpf(static_cast<float>(D));
+  for (int e = tid; e < rows * D; e += kThreads) {
+    const QR rc = small_divmod(e, D, rcp_d);
+    const int r = rc.q, hb = rc.r & 1, c = rc.r & ~1, j = c / G;
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int t = r * per + i;
+    for (int i = 0; i < half; ++i) {
+      const int t = r * per + hb * half + i;
       const float2 q = L.vq[t][j];
       const float2 x = pair_f32(&L.v[t][c]);
       w0 += code_bits(x.x, q, qmax) << (BITS * i);
       w1 += code_bits(x.y, q, qmax) << (BITS * i);
     }
-    *reinterpret_cast<uint2*>(&v_codes[(static_cast<size_t>(q0) / per + r) * D + c]) =
-        make_uint2(w0 - code_bias<BITS>(), w1 - code_bias<BITS>());
+    const uint32_t mine = hb ? w1 : w0, other = hb ? w0 : w1;  // this lane's channel, the partner's
+    const uint32_t from = static_cast<uint32_t>(
+        __builtin_amdgcn_mov_dpp(static_cast<int>(other), 0xB1, 0xF, 0xF, true));  // lane ^ 1's partial of it
+    const uint32_t lo_half = hb ? from : mine, hi_half = hb ? mine : from;
+    v_codes[(static_cast<size_t>(q0) / per + r) * D + c + hb] =
+        lo_half + (hi_half << (BITS * half)) - code_bias<BITS>();
   }
 }
 

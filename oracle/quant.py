@@ -35,8 +35,10 @@ def bf16_to_f32(bits):
 
 
 def f16_bits(x):
-    """float32 -> float16 bits, round to nearest even (numpy's cast)."""
-    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+    """float32 -> float16 bits, round to nearest even (numpy's cast; magnitudes
+    past the fp16 range become infinities, as IEEE rounding says)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
 def f16_to_f32(bits):

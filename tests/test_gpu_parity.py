@@ -58,6 +58,57 @@ def test_quantize_parity(dtype, bits, D, with_idx):
             gu.assert_cache_equal(gu.gpu_head_cache(cache, b, j), ref, f"b{b} j{j}")
 
 
+def _degenerate_case(dtype, n, D, group):
+    """Random keys and values with degenerate groups planted in the first key
+    group and in value tokens 5..9 (MiniKV Sec. 4.4 fp16 scale/zero): constant
+    groups (zero scale), ranges too wide for fp16 (infinite scale), ranges too
+    small for it (scale 0 after rounding), and groups near +-1e5 whose fp16 zero
+    overflows while the scale stays finite (t = +-inf, codes clamp)."""
+    g = torch.Generator().manual_seed(21)
+    k = torch.randn(1, 2, n, D, generator=g)
+    v = torch.randn(1, 2, n, D, generator=g)
+    r = torch.rand(group, generator=g)
+    k[:, :, :group, 0:4] = 0.75                                         # constant
+    k[:, :, :group, 4] = torch.where(torch.arange(group) % 2 == 0, 1e6, -1e6)  # inf scale, -inf zero
+    k[:, :, :group, 5] = 4e6 * r                                        # inf scale, finite zero
+    k[:, :, 0, 5] = 0.0
+    k[:, :, :group, 6] = 1e-30 * (r - 0.5)                              # scale and zero underflow
+    k[:, :, :group, 7] = -1e5 + 4000 * r                                 # -inf zero, finite scale
+    k[:, :, :group, 8] = 99000 + 4000 * r                                # +inf zero, finite scale
+    v[:, :, 5, :] = 2.5
+    v[:, :, 6, :] = torch.where(torch.arange(D) % 3 == 0, 1e6, -1e6)
+    v[:, :, 7, :] = 1e-30 * torch.randn(D, generator=g)
+    v[:, :, 8, :] = -1e5 + 4000 * torch.rand(D, generator=g)
+    v[:, :, 9, :] = 99000 + 4000 * torch.rand(D, generator=g)
+    if dtype == "bf16":
+        k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    return k.cuda(), v.cuda()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("group", [32, 16])
+def test_quantize_degenerate_groups(dtype, bits, group):
+    """Groups whose scale is zero, overflows or underflows fp16, or whose zero
+    overflows: codes and metadata bit-exact against the oracle (all-zero codes
+    where the scale is zero or not finite, clamped codes where t is infinite)."""
+    kvc = _kvc()
+    n, D, R = 160, 64, 16
+    k, v = _degenerate_case(dtype, n, D, group)
+    cache = kvc.Cache(1, 2, D, bits, R, q_cap=n + 64, device="cuda", group=group)
+    kvc.kvc_quantize(k, v, cache)
+    torch.cuda.synchronize()
+    kf, vf = gu.as_f32(k), gu.as_f32(v)
+    for j in range(2):
+        ref = oquant.build_head_cache(kf[0, j], vf[0, j], np.arange(n), R, bits, group)
+        gu.assert_cache_equal(gu.gpu_head_cache(cache, 0, j), ref, f"j{j}")
+        # the planted groups really are degenerate in the oracle
+        s_bits = (ref["k_meta"][0, :9] & 0xFFFF).astype(np.uint16).view(np.float16)
+        assert (s_bits[:4] == 0).all() and np.isinf(s_bits[4:6]).all() and s_bits[6] == 0
+        z_bits = (ref["k_meta"][0, 7:9] >> 16).astype(np.uint16).view(np.float16)
+        assert np.isinf(z_bits).all() and np.isfinite(s_bits[7:9]).all()
+
+
 @pytest.mark.parametrize("dtype,bits,G,D,R,n", [
     ("bf16", 2, 4, 128, 16, 300), ("bf16", 4, 1, 128, 16, 300), ("f32", 2, 1, 64, 16, 250),
     ("bf16", 2, 2, 64, 0, 200), ("bf16", 4, 8, 32, 40, 160), ("f32", 4, 3, 256, 24, 130),
