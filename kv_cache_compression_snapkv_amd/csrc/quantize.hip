@@ -212,20 +212,6 @@ struct QuantArgs {
   uint16_t *k_res, *v_res;
 };
 
-// Kept position t of (b, j): selected ascending, then the window; clamped into
-// the prompt so that a malformed idx cannot address outside k/v.
-__device__ __forceinline__ int kept_pos(const QuantArgs& a, int bj, int t) {
-  int p;
-  if (a.idx == nullptr) {
-    p = t;
-  } else if (t < a.k_sel) {
-    p = a.idx[static_cast<size_t>(bj) * a.k_sel + t];
-  } else {
-    p = a.n - a.W + (t - a.k_sel);
-  }
-  return min(max(p, 0), a.n - 1);
-}
-
 // Stage `count` kept tokens starting at kept index t_first (rows beyond count
 // are zero) as float32 rows of L.k / L.v.  Every 16-byte load of the G rows is
 // issued before the first LDS store: one memory round trip for the positions,
@@ -244,10 +230,32 @@ __device__ __forceinline__ void stage_rows(QuantLds<T, DM, G>& L, const QuantArg
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int e = tid + i * kThreads;
-    const QR rc = small_divmod(e, ppr, rcp_ppr);
+    constexpr unsigned kp = DM / VEC;
+    const QR rc = D == DM ? QR{static_cast<int>(static_cast<unsigned>(e) / kp),
+                               static_cast<int>(static_cast<unsigned>(e) % kp)}
+                          : small_divmod(e, ppr, rcp_ppr);
     tt[i] = rc.q;
     cc[i] = rc.r * VEC;
-    pos[i] = (e < total && tt[i] < count) ? kept_pos(a, bj, t_first + tt[i]) : 0;
+  }
+  // Kept token t is selected position idx[t] for t < k_sel, then the window;
+  // positions are clamped into the prompt so that a malformed idx cannot
+  // address outside k/v.  Every idx entry a thread needs is requested before
+  // any is used (the entry index is clamped into the selection, so each load is
+  // in bounds): one round trip.
+  int raw[MAXV];
+  const bool from_idx = a.idx != nullptr && a.k_sel > 0;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) raw[i] = 0;
+  if (from_idx) {
+    const int32_t* ib = a.idx + static_cast<size_t>(bj) * a.k_sel;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) raw[i] = ib[min(t_first + tt[i], a.k_sel - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = tid + i * kThreads, t = t_first + tt[i];
+    const int p = a.idx == nullptr ? t : (t < a.k_sel ? raw[i] : a.n - a.W + (t - a.k_sel));
+    pos[i] = (e < total && tt[i] < count) ? min(max(p, 0), a.n - 1) : 0;
   }
   uint4 kv[MAXV], vv[MAXV];
 #pragma unroll
