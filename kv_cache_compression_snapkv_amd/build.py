@@ -29,12 +29,14 @@ FLAGS = [
 ]
 
 
-# Per-source extras.  The decode sources (both group sizes), select.hip and
-# prefill.hip: their values are never NaN for finite inputs (logits, softmax
-# weights, -inf masks), so fmax needs no canonicalization and the 16-lane DPP max
-# folds into v_max_f32_dpp.
+# Per-source extras.  Every source's values are never NaN for finite inputs
+# (decode, selection and prefill: logits, softmax weights, -inf masks;
+# quantization: group extremes, and codes whose groups have a zero or infinite
+# scale use a zero-point of 0), so fmin/fmax need no canonicalization and the
+# DPP lane exchanges fold into v_min/v_max_f32_dpp.
 _NO_NANS = ["-fno-honor-nans"]
-EXTRA = {"decode.hip": _NO_NANS, "decode_g16.hip": _NO_NANS, "select.hip": _NO_NANS, "prefill.hip": _NO_NANS}
+EXTRA = {"decode.hip": _NO_NANS, "decode_g16.hip": _NO_NANS, "select.hip": _NO_NANS, "prefill.hip": _NO_NANS,
+         "quantize.hip": _NO_NANS}
 
 
 def _compile(src):

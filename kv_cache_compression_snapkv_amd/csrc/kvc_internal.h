@@ -70,8 +70,18 @@ template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* 
 
 // ---------------------------------------------------------------- group quantizer
 // One group's parameters: fp16 scale and zero-point, rounded first; codes use the
-// stored values and one IEEE reciprocal: code = clamp(rint((x - z) * (1/s)), 0, 2^b-1).
+// stored values and one float32 reciprocal: code = clamp(rint((x - z) * (1/s)), 0, 2^b-1).
 // A zero or non-finite scale gives all-zero codes.
+//
+// Both quotients are the correctly rounded float32 results, taken without a
+// division sequence:
+//   (hi - lo) / qmax as q0 = (hi - lo) * c with c = 1/qmax rounded, then one
+//   correction with its exact remainder: q0 + fma(-q0, qmax, hi - lo) * c;
+//   1/s as the hardware reciprocal estimate r0 corrected by one Newton step,
+//   r0 + fma(-s, r0, 1) * r0.
+// Checked exhaustively against IEEE division: the first for qmax = 3 and 15 and
+// every finite hi - lo >= 0; the second for every positive finite fp16 s with
+// r0 anywhere within 2 ulp of 1/s.
 struct GroupQ {
   float z;
   float inv;
@@ -81,22 +91,22 @@ struct GroupQ {
 
 __device__ __forceinline__ GroupQ make_group(float lo, float hi, float qmax) {
   GroupQ g;
-  const float sf = __fdiv_rn(hi - lo, qmax);
+  const float d = __fsub_rn(hi, lo);
+  const float c = 1.0f / qmax;  // a constant once qmax is
+  const float q0 = __fmul_rn(d, c);
+  const float sf = __builtin_isfinite(q0) ? __builtin_fmaf(__builtin_fmaf(-q0, qmax, d), c, q0) : q0;
   const uint32_t sb = f32_to_f16_bits(sf);
   const uint32_t zb = f32_to_f16_bits(lo);
   const float s = f16_bits_to_f32(sb);
   g.z = f16_bits_to_f32(zb);
   g.meta = sb | (zb << 16);
   g.ok = (s != 0.0f) && __builtin_isfinite(s);
-  g.inv = g.ok ? __fdiv_rn(1.0f, s) : 0.0f;
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  g.inv = g.ok ? __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0) : 0.0f;
+  // the codes of such a group are (x - z) * 0 = 0; a zero of 0 there keeps an
+  // infinite fp16 zero-point from making that product NaN (x is finite)
+  if (!g.ok) g.z = 0.0f;
   return g;
-}
-
-__device__ __forceinline__ uint32_t code_of(float x, float z, float inv, bool ok, float qmax) {
-  if (!ok) return 0u;
-  const float t = __fmul_rn(__fsub_rn(x, z), inv);
-  const float r = fminf(fmaxf(__builtin_rintf(t), 0.0f), qmax);
-  return static_cast<uint32_t>(r);
 }
 
 }  // namespace kvc

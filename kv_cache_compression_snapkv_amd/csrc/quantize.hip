@@ -61,8 +61,8 @@ __device__ __forceinline__ float2 pair_f32(const float* p) { return *reinterpret
 // clamped to [0, qmax] and 1.5 * 2^23 is added.  Floats in [2^23, 2^24) are
 // spaced 1 apart, so the sum is that constant plus rint(t), ties to even, and
 // the integer sits in the low mantissa bits; rounding commutes with a clamp to
-// integer bounds.  A zero scale has inv = 0, so t is 0 (or NaN for a non-finite
-// operand, which the clamp turns into 0): code 0.
+// integer bounds.  A zero or non-finite scale has inv = 0 and z = 0, so t is 0
+// for finite x: code 0.
 constexpr float kRoundAdd = 12582912.0f;  // 1.5 * 2^23
 constexpr uint32_t kRoundBits = 0x4B400000u;
 __device__ __forceinline__ uint32_t code_bits(float x, float2 q, float qmax) {
