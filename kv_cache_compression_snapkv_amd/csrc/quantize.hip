@@ -71,6 +71,13 @@ __device__ __forceinline__ uint32_t code_bits(float x, float2 q, float qmax) {
 }
 // A word is the wrapping sum of code_bits(...) << (BITS * slot) over its 32/BITS
 // slots; subtracting the constant's share leaves the packed codes.
+// acc + (bits << shift) as one v_lshl_add_u32: the empty asm keeps the running
+// sum opaque, so the compiler does not regroup the chain into shifts and adds.
+__device__ __forceinline__ uint32_t add_code(uint32_t acc, uint32_t bits, int shift) {
+  acc += bits << shift;
+  asm("" : "+v"(acc));
+  return acc;
+}
 template <int BITS> constexpr uint32_t code_bias() {
   uint32_t c = 0;
   for (int i = 0; i < 32 / BITS; ++i) c += kRoundBits << (BITS * i);
@@ -168,9 +175,10 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
       for (int i = 0; i < VEC; i += 2) {
         const uint4 qq = qs[(p * VEC + i) / 2];  // parameters of channels i, i+1 of this piece
         const int c = p * VEC + i;
-        word += code_bits(f[i], make_float2(__uint_as_float(qq.x), __uint_as_float(qq.y)), qmax) << (BITS * c);
-        word += code_bits(f[i + 1], make_float2(__uint_as_float(qq.z), __uint_as_float(qq.w)), qmax)
-                << (BITS * (c + 1));
+        word = add_code(word, code_bits(f[i], make_float2(__uint_as_float(qq.x), __uint_as_float(qq.y)), qmax),
+                        BITS * c);
+        word = add_code(word, code_bits(f[i + 1], make_float2(__uint_as_float(qq.z), __uint_as_float(qq.w)), qmax),
+                        BITS * (c + 1));
       }
     }
     k_codes[static_cast<size_t>(q0 + t) * nw + w] = word - code_bias<BITS>();
@@ -191,8 +199,8 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
       const int t = r * per + hb * half + i;
       const float2 q = L.vq[t][j];
       const float2 x = pair_f32(&L.v[t][c]);
-      w0 += code_bits(x.x, q, qmax) << (BITS * i);
-      w1 += code_bits(x.y, q, qmax) << (BITS * i);
+      w0 = add_code(w0, code_bits(x.x, q, qmax), BITS * i);
+      w1 = add_code(w1, code_bits(x.y, q, qmax), BITS * i);
     }
     const uint32_t mine = hb ? w1 : w0, other = hb ? w0 : w1;  // this lane's channel, the partner's
     const uint32_t from = static_cast<uint32_t>(
