@@ -33,7 +33,7 @@ def _case(seed, B, Hkv, n, D, dtype, outliers=True):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128, 224])   # 96, 224: head dims below the LDS layout's bound
 @pytest.mark.parametrize("with_idx", [True, False])
 def test_quantize_parity(dtype, bits, D, with_idx):
     kvc = _kvc()
@@ -115,7 +115,9 @@ def test_quantize_degenerate_groups(dtype, bits, group):
     ("bf16", 2, 16, 64, 16, 100),
     # histories long enough for the split runs (several workgroups per unit, merged)
     ("f32", 2, 1, 128, 16, 3000), ("f32", 4, 4, 128, 128, 2600), ("bf16", 2, 4, 128, 128, 4000),
-    ("bf16", 2, 4, 256, 16, 3000)])   # D = 256: four heads per workgroup in the split runs
+    ("bf16", 2, 4, 256, 16, 3000),   # D = 256: four heads per workgroup in the split runs
+    # odd multiples of 32 (three, five and seven key slices per lane group), short and split runs
+    ("bf16", 2, 2, 96, 16, 300), ("f32", 4, 1, 160, 24, 200), ("bf16", 2, 4, 224, 16, 2600)])
 def test_decode_parity_multi_step(dtype, bits, G, D, R, n):
     kvc = _kvc()
     B, Hkv = 2, 2
