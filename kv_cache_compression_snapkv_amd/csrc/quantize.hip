@@ -31,7 +31,7 @@ template <typename S, int DM, int G> struct QuantLds {
   static constexpr int LD = DM + 16 / sizeof(S);
   S k[G][LD];
   S v[G][LD];
-  float2 kq[DM];        // per key channel: (zero, 1/scale), 1/scale = 0 for a zero scale
+  float2 kq[DM];        // per key channel: (zero, 1/scale), both 0 for a zero or non-finite scale
   float2 vq[G][DM / G];  // per value token group
 };
 
@@ -70,9 +70,10 @@ __device__ __forceinline__ uint32_t code_bits(float x, float2 q, float qmax) {
   return __float_as_uint(__fadd_rn(fminf(fmaxf(t, 0.0f), qmax), kRoundAdd));
 }
 // A word is the wrapping sum of code_bits(...) << (BITS * slot) over its 32/BITS
-// slots; subtracting the constant's share leaves the packed codes.
-// acc + (bits << shift) as one v_lshl_add_u32: the empty asm keeps the running
-// sum opaque, so the compiler does not regroup the chain into shifts and adds.
+// slots; subtracting the constant's share, code_bias, leaves the packed codes.
+// add_code forms acc + (bits << shift) as one v_lshl_add_u32: the empty asm
+// keeps the running sum opaque, so the compiler does not regroup the chain into
+// separate shifts and three-way adds.
 __device__ __forceinline__ uint32_t add_code(uint32_t acc, uint32_t bits, int shift) {
   acc += bits << shift;
   asm("" : "+v"(acc));
@@ -160,8 +161,8 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
   __syncthreads();
   constexpr int per = 32 / BITS;
   const int nw = D / per;  // key words per token
-  // key words: word w of token t holds channels w*per.. of t; the lanes of a
-  // wave share w (their parameter reads are broadcasts)
+  // key words: word w of token t holds channels w*per.. of t; the G lanes of a
+  // token block share w (their parameter reads are broadcasts)
   for (int e = tid; e < G * nw; e += kThreads) {
     const int w = e / G, t = e % G;
     const uint4* xs = reinterpret_cast<const uint4*>(&L.k[t][w * per]);
@@ -191,7 +192,8 @@ __device__ __forceinline__ void quantize_block(QuantLds<S, DM, G>& L, int D, int
   constexpr int half = per / 2;
   const float rcp_d = __builtin_amdgcn_rcpf(static_cast<float>(D));
   for (int e = tid; e < rows * D; e += kThreads) {
-    const QR rc = small_divmod(e, D, rcp_d);
+    const QR rc = D == DM ? QR{static_cast<int>(static_cast<unsigned>(e) / DM), static_cast<int>(static_cast<unsigned>(e) % DM)}
+                          : small_divmod(e, D, rcp_d);
     const int r = rc.q, hb = rc.r & 1, c = rc.r & ~1, j = c / G;
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
