@@ -114,6 +114,13 @@ def counted_traffic(workload, bits, flush_all=False, group=32):
     return int(m.group(1))
 
 
+def _spread(xs):
+    """Median, 10th and 90th percentile (linear interpolation) of a list."""
+    import numpy as np
+    q = np.percentile(np.asarray(xs, dtype=np.float64), [50, 10, 90])
+    return {"median": float(q[0]), "p10": float(q[1]), "p90": float(q[2]), "n": len(xs)}
+
+
 def _timed(fn, share_s, max_reps):
     """Mean seconds per call of fn, repeated until share_s has passed (at least once)."""
     reps, t = 0, 0.0
@@ -412,6 +419,10 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
     step_ms = sum(e0.elapsed_time(e2) for e0, _, e2 in recs) / steps
     ncalls = len(call_bytes)
     achieved = sum(call_bytes) / (dec_ms * 1e-3) / 1e9
+    # spread over the timed steps (a graph replay is one step, so per-call times
+    # are per-step means): median, p10 and p90
+    call_us_steps = [e1.elapsed_time(e2) * 1e3 / ncalls for _, e1, e2 in recs]
+    pre_ms_steps = [e0.elapsed_time(e1) for e0, e1, _ in recs]
     attn = None
     if h2o:
         # the prefill attention alone (every layer), for its MFMA roofline
@@ -455,6 +466,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
         "desc": desc, "budgets": budgets, "footprint": fp,
         "tokens_per_s": B * cfg.decode_steps / (dec_ms * 1e-3),
         "step_ms": step_ms, "pre_ms": pre_ms, "dec_ms": dec_ms, "wall": wall, "prefill_attention": attn,
+        "pre_ms_over_steps": _spread(pre_ms_steps),
         "roofline": {
             "kernel": ((f"decode_kernel<GS={group}> (+ merge_kernel"
                         + (f"; flush_kernel of {cfg.residual // group} groups on 1 step in {cfg.residual})"
@@ -463,6 +475,7 @@ def run(cfg, bits, steps, warmup, graph=True, layers=None, policy="workload", se
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(cfg.name, bits, flush_all, group),
             "avg_call_us": dec_ms * 1e3 / ncalls, "algorithmic_bytes_per_call": sum(call_bytes) / ncalls,
+            "call_us_over_steps": _spread(call_us_steps),
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated), "
                             "profiles/decode_<workload>_<bits>bit[_g16]_hbm_counters.md; null if the decode sources changed since",
         },
@@ -490,8 +503,10 @@ def entry(r, cfg, bits, steps, warmup, selector, group=32):
     e = {"workload": r["desc"], "bits": bits, "selector": selector, "group": group,
          "decode_tokens_per_s": r["tokens_per_s"],
          "avg_call_us": r["roofline"]["avg_call_us"], "ms_per_step": r["step_ms"],
-         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch, "steps": steps, "warmup": warmup,
-         "roofline": r["roofline"]}
+         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
+         "select_quantize_ms_per_prompt_over_steps": {k: (v / cfg.batch if k != "n" else v)
+                                                      for k, v in r["pre_ms_over_steps"].items()},
+         "steps": steps, "warmup": warmup, "roofline": r["roofline"]}
     if r["prefill_attention"] is not None:
         e["prefill_attention"] = r["prefill_attention"]
     return e
@@ -528,6 +543,8 @@ def main():
                    "selector": args.selector, "group": args.group, "prefill_streams": args.streams,
                    "flush_all": args.flush_all},
         "select_quantize_ms_per_prompt": r["pre_ms"] / cfg.batch,
+        "select_quantize_ms_per_prompt_over_steps": {k: (v / cfg.batch if k != "n" else v)
+                                                     for k, v in r["pre_ms_over_steps"].items()},
         "decode_ms_per_token_all_layers": r["dec_ms"] / cfg.decode_steps,
         "decode_hbm_GBs": r["roofline"]["achieved"],
         "roofline": r["roofline"],
