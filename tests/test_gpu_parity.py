@@ -157,6 +157,9 @@ def test_decode_parity_multi_step(dtype, bits, G, D, R, n):
     ("bf16", 1, 4, 2, 300, 128, 20, 7, 0), ("bf16", 1, 4, 2, 300, 128, 20, 7, 5000),
     ("bf16", 1, 4, 2, 300, 128, 20, 7, -1), ("bf16", 1, 1, 1, 2000, 128, 150, 9, 333),
     ("bf16", 2, 2, 2, 600, 32, 24, 5, 80), ("bf16", 1, 16, 1, 900, 64, 16, 7, 100),
+    # odd numbers of 32-channel slices (the general scorer)
+    ("bf16", 1, 4, 2, 500, 96, 16, 7, 60), ("f32", 1, 2, 1, 400, 160, 12, 5, 50),
+    ("bf16", 1, 2, 1, 700, 224, 24, 7, 90),
     # rows of 9k-32k candidates (keys in registers, raw scores in LDS)
     ("bf16", 1, 2, 1, 12000, 64, 16, 7, 900), ("bf16", 1, 1, 1, 30000, 64, 8, 7, 2000),
     # rows above 32k candidates: 4096-candidate chunks over many workgroups
