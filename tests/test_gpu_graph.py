@@ -75,3 +75,82 @@ def test_graph_replays_equal_eager(group):
         torch.cuda.synchronize()
         for s in range(steps):
             assert torch.equal(outs0[s], ref[s]), f"eager rerun {rep}: step {s}"
+
+
+def test_graph_replays_long_rows_and_split_decode():
+    """The same check on the paths the small case does not reach: rows above
+    32k candidates (the chunked top-k's five launches, whose counters one launch
+    clears for the next), selection given the window rows' log-sum-exp, and a
+    history long enough for split decode runs merged by a second kernel
+    (1,792 packed tokens: 56 history tiles plus the residual's, more than six
+    per wave of an eight-wave workgroup)."""
+    gu.need_gpu()
+    import kv_cache_compression_snapkv_amd as kvc
+
+    B, Hkv, G, D, n, W, pool, budget, bits, R, steps = 1, 2, 2, 64, 40000, 16, 7, 1800, 2, 16, 12
+    Hq = Hkv * G
+    k, v = synth.random_case(41, B, Hkv, Hkv, D, n, "bf16", device="cuda")
+    q_win = synth.random_tensor(42, (B, Hq, W, D), "bf16", tag="qw").cuda()
+    # each window row's log-sum-exp of its causal scaled logits (float32 on the GPU)
+    kk = k.float().repeat_interleave(G, dim=1).contiguous()
+    lg = torch.matmul(q_win.float(), kk.transpose(-1, -2).contiguous()) / D ** 0.5
+    pos = torch.arange(n, device="cuda")
+    lim = n - W + torch.arange(W, device="cuda")
+    lse = torch.logsumexp(lg.masked_fill(pos[None, None, None, :] > lim[None, None, :, None], float("-inf")),
+                          dim=-1).contiguous()
+    del kk, lg
+    dec = [(synth.random_tensor(50 + s, (B, Hq, D), "bf16", tag="q").cuda(),
+            synth.random_tensor(150 + s, (B, Hkv, D), "bf16", tag="kn").cuda(),
+            synth.random_tensor(250 + s, (B, Hkv, D), "bf16", tag="vn").cuda()) for s in range(steps)]
+    T = budget + W
+    sel_ws = torch.empty(kvc.select_ws_bytes(1, B, Hq, Hkv, n, D, W, pool, budget), dtype=torch.uint8,
+                         device="cuda")
+
+    def make_cache():
+        return kvc.Cache(B, Hkv, D, bits, R, q_cap=T + steps + 32, device="cuda")
+
+    def run(cache, idx, idx_lse, dec_ws, outs):
+        cache.reset()
+        kvc.kvc_select_lse(q_win, k, lse, W, pool, budget, ws=sel_ws, idx=idx_lse)
+        kvc.kvc_select(q_win, k, W, pool, budget, ws=sel_ws, idx=idx)
+        kvc.kvc_quantize(k, v, cache, idx=idx, W=W)
+        for s, (q, kn, vn) in enumerate(dec):
+            kvc.kvc_decode_attn(cache, q, kn, vn, out=outs[s], ws=dec_ws)
+
+    c0 = make_cache()
+    idx0 = torch.empty(B, Hkv, budget, dtype=torch.int32, device="cuda")
+    idl0 = torch.empty_like(idx0)
+    ws0 = torch.zeros(kvc.decode_ws_bytes(c0, Hq), dtype=torch.uint8, device="cuda")
+    outs0 = [torch.empty(B, Hq, D, dtype=torch.float32, device="cuda") for _ in range(steps)]
+    run(c0, idx0, idl0, ws0, outs0)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs0]
+    ref_cache = {key: t.clone() for key, t in c0.views().items()}
+    ref_lse = idl0.clone()
+
+    c1 = make_cache()
+    idx1, idl1 = torch.empty_like(idx0), torch.empty_like(idx0)
+    ws1 = torch.zeros_like(ws0)
+    outs1 = [torch.empty_like(o) for o in outs0]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(c1, idx1, idl1, ws1, outs1)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs1:
+            o.fill_(float("nan"))
+        idx1.fill_(-1)
+        idl1.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx0), f"replay {rep}: idx"
+        assert torch.equal(idl1, ref_lse), f"replay {rep}: idx given lse"
+        for s in range(steps):
+            assert torch.equal(outs1[s], ref[s]), f"replay {rep}: step {s}"
+        for key, t in c1.views().items():
+            assert torch.equal(t, ref_cache[key]), f"replay {rep}: {key}"
+        run(c0, idx0, idl0, ws0, outs0)
+        torch.cuda.synchronize()
+        assert torch.equal(idl0, ref_lse), f"eager rerun {rep}: idx given lse"
+        for s in range(steps):
+            assert torch.equal(outs0[s], ref[s]), f"eager rerun {rep}: step {s}"
