@@ -154,3 +154,53 @@ def test_graph_replays_long_rows_and_split_decode():
         assert torch.equal(idl0, ref_lse), f"eager rerun {rep}: idx given lse"
         for s in range(steps):
             assert torch.equal(outs0[s], ref[s]), f"eager rerun {rep}: step {s}"
+
+
+def test_graph_replays_prefill_h2o_recent():
+    """The fused prefill (output, accumulated attention, its variance, row
+    log-sum-exp), H2O selection on it and position-only selection, captured and
+    replayed: every replay equal to the eager run bit for bit."""
+    gu.need_gpu()
+    import kv_cache_compression_snapkv_amd as kvc
+
+    B, Hkv, G, D, n, W, budget = 2, 2, 2, 64, 600, 16, 100
+    Hq = Hkv * G
+    k, v = synth.random_case(61, B, Hkv, Hkv, D, n, "bf16", device="cuda")
+    q = synth.random_tensor(62, (B, Hq, n, D), "bf16", tag="q").cuda()
+    pf_ws = torch.empty(kvc.prefill_ws_bytes(1, B, Hq, Hkv, n, D), dtype=torch.uint8, device="cuda")
+    h_ws = torch.empty(max(kvc.h2o_ws_bytes(B, Hkv, n, W, budget), 1), dtype=torch.uint8, device="cuda")
+
+    def buffers():
+        return {"out": torch.empty(B, Hq, n, D, dtype=torch.float32, device="cuda"),
+                "acc": torch.empty(B, Hkv, n, dtype=torch.float32, device="cuda"),
+                "var": torch.empty(B, Hkv, dtype=torch.float32, device="cuda"),
+                "lse": torch.empty(B, Hq, n, dtype=torch.float32, device="cuda"),
+                "idx_h": torch.empty(B, Hkv, budget, dtype=torch.int32, device="cuda"),
+                "idx_r": torch.empty(B, Hkv, budget, dtype=torch.int32, device="cuda")}
+
+    def run(bf):
+        kvc.kvc_prefill_attn(q, k, v, want_acc=True, want_var=True, ws=pf_ws, out=bf["out"], acc=bf["acc"],
+                             var=bf["var"], lse=bf["lse"])
+        kvc.kvc_select_h2o(bf["acc"], W, budget, ws=h_ws, idx=bf["idx_h"])
+        kvc.kvc_select_recent(B, Hkv, n, W, budget, 4, idx=bf["idx_r"])
+
+    b0 = buffers()
+    run(b0)
+    torch.cuda.synchronize()
+    ref = {key: t.clone() for key, t in b0.items()}
+    b1 = buffers()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(b1)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in b1.values():
+            t.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for key, t in b1.items():
+            assert torch.equal(t, ref[key]), f"replay {rep}: {key}"
+        run(b0)
+        torch.cuda.synchronize()
+        for key, t in b0.items():
+            assert torch.equal(t, ref[key]), f"eager rerun {rep}: {key}"
