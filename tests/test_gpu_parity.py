@@ -391,7 +391,7 @@ def test_recent_selection_end_to_end():
 # ---------------------------------------------------------------- group size 16
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("D,with_idx", [(64, True), (128, False), (256, True)])
+@pytest.mark.parametrize("D,with_idx", [(64, True), (128, False), (256, True), (96, True), (224, False)])
 def test_quantize_parity_group16(dtype, bits, D, with_idx):
     """MiniKV's group of 16 (keys per channel over 16 tokens, values per token
     over 16 channels): packed codes, metadata and residual bit-exact against the
@@ -425,7 +425,8 @@ def test_quantize_parity_group16(dtype, bits, D, with_idx):
     # odd number of 16-token groups (a half-full last tile)
     ("bf16", 2, 1, 128, 16, 4000), ("bf16", 4, 4, 128, 128, 2600), ("f32", 2, 1, 128, 16, 3000),
     ("bf16", 2, 1, 64, 16, 5000),
-    ("bf16", 2, 4, 256, 16, 3000)])   # D = 256: one head per workgroup (four would not fit a CU's LDS)
+    ("bf16", 2, 4, 256, 16, 3000),   # D = 256: one head per workgroup (four would not fit a CU's LDS)
+    ("bf16", 2, 2, 96, 16, 400), ("f32", 4, 1, 160, 32, 2600)])   # odd numbers of 32-channel slices
 def test_decode_parity_group16_multi_step(dtype, bits, G, D, R, n):
     """Decode over group-16 caches for 40 steps (several 16-token flushes, the
     residual ring wrapping): outputs within the decode tolerance and the cache
