@@ -310,7 +310,8 @@ kvc_status kvc_select_h2o(const float *acc, int32_t B, int32_t Hkv, int32_t n, i
  * (g*floor(T/g) with flush_all)
  * are quantized: per group of g values, lo/hi -> scale = fp16((hi-lo)/(2^b-1)),
  * zero = fp16(lo), code = clamp(rint((x - zero) * (1/scale)), 0, 2^b-1) in IEEE
- * float32 (scale 0 -> codes 0); the last T-Q go to the residual as bf16.
+ * float32 (a zero or non-finite scale gives codes 0; inputs must be finite);
+ * the last T-Q go to the residual as bf16.
  *   k, v [B][Hkv][n][D] dtype; idx [B][Hkv][k_sel] int32 (ascending, < n-W) or
  *   NULL; cache: batch/kv_heads/head_dim/bits/residual/capacities/pointers set,
  *   q_len == r_len == 0.  On success cache->q_len = Q, cache->r_len = T-Q,
