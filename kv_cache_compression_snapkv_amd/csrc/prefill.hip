@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kt = e >> 2, i = e & 3;
-        float x = s[kt][rs][i] * a.scale2;
+        float x = s[kt][rs][i];
         if (need_mask) {
           const int key = kb + 16 * kt + 4 * lq + i;
           if (key > row || key >= n) x = -INFINITY;
@@ -321,14 +321,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
         p[rs][e] = x;
         mt = fmaxf(mt, x);
       }
-      mt = max_q(mt);
+      mt = max_q(mt) * a.scale2;
       const float mnew = fmaxf(m_run[rs], mt);
       const float msafe = mnew == -INFINITY ? 0.0f : mnew;
       alpha[rs] = __builtin_amdgcn_exp2f(m_run[rs] - msafe);
       float ls = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[rs][e] = __builtin_amdgcn_exp2f(p[rs][e] - msafe);
+        p[rs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[rs][e], a.scale2, -msafe));
         ls += p[rs][e];
       }
       l_part[rs] = l_part[rs] * alpha[rs] + ls;
