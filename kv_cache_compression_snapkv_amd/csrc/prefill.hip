@@ -38,7 +38,7 @@ namespace {
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kKT = 32;       // keys per staged tile (forward pass)
-constexpr int kColKeys = 64;  // keys per workgroup (column-sum pass)
+constexpr int kColKeys = 64;  // keys per wave (column-sum pass; kPfWaves blocks per workgroup)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -399,26 +399,41 @@ __global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
   }
 }
 
-// Column sums.  Workgroup: 64 keys key0.. of one (b, KV head), held by every wave
-// as MFMA A operands; the (head, 16-row tile) items with rows >= key0 are dealt
-// to the waves in turn; each lane adds 2^(x - lse_row) for its keys, then the
-// 16 lanes of a key row and the 4 waves are summed in a fixed order.  Grid
+// Column sums.  Workgroup: kPfWaves x 64 keys of one (b, KV head); wave w holds
+// keys key0 + 64w .. +63 as MFMA A operands.  The (16-row tile, head) items with
+// rows >= key0 are taken in stages of kPfWaves / WPI items: each wave (or pair
+// of waves for fp32) copies one item's query tile and row lse values into LDS,
+// double-buffered with one barrier per stage, and all four waves read every
+// staged tile, so the query rows are fetched once per 256 keys rather than once
+// per 64.  A wave skips the items whose rows all lie above its keys, and only
+// items that reach past one of its keys (or past n) take the masked path.  Each
+// lane adds 2^(x - lse_row) for its keys over the items in order, then the 16
+// lanes of a key are summed in a fixed order: deterministic, no atomics.  Grid
 // (B*Hkv, key blocks) as in the forward pass.
 template <typename T, int KS>
 __global__ __launch_bounds__(kPfThreads, 2) void colsum_kernel(PfArgs a) {
   constexpr int D = 32 * KS, ES = sizeof(T);
-  __shared__ float red[kPfWaves][kColKeys];
+  constexpr int WPI = ES == 2 ? 1 : 2;          // waves copying one item
+  constexpr int NI = kPfWaves / WPI;            // items per stage
+  constexpr int ROW = D * ES + 16;              // padded LDS row pitch, bytes
+  constexpr int ITEM = 16 * ROW;
+  constexpr int PIECES = D * ES / 16;           // 16-byte pieces per row
+  constexpr int LOADS = 16 * PIECES / (64 * WPI);  // = KS copies per lane
+  static_assert(LOADS * 64 * WPI == 16 * PIECES, "item copy split");
+  __shared__ __attribute__((aligned(16))) unsigned char qs[2][NI * ITEM];
+  __shared__ float ls[2][NI * 16];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ln = lane & 15, lq = lane >> 4;
-  const int bj = blockIdx.x, kbk = blockIdx.y;
+  const int bj = blockIdx.x;
   const int b = bj / a.Hkv, j = bj % a.Hkv;
   const int n = a.n, G = a.G;
-  const int key0 = kbk * kColKeys;
+  const int key0 = blockIdx.y * (kColKeys * kPfWaves);
+  const int kw0 = key0 + kColKeys * wave;  // this wave's first key
   const unsigned char* kg = static_cast<const unsigned char*>(a.k) + static_cast<size_t>(bj) * n * D * ES;
   Frag<T> kf[4][KS];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    const int key = key0 + 16 * kt + ln;
+    const int key = kw0 + 16 * kt + ln;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (key < n) kf[kt][s].load8(kg + (static_cast<size_t>(key) * D + 32 * s + 8 * lq) * ES);
@@ -432,18 +447,48 @@ __global__ __launch_bounds__(kPfThreads, 2) void colsum_kernel(PfArgs a) {
     for (int i = 0; i < 4; ++i) cs[kt][i] = 0.0f;
   const int rt0 = key0 / 16, nrt = (n + 15) / 16;
   const int items = G * (nrt - rt0);
-  for (int it = wave; it < items; it += kPfWaves) {
+  const int nst = (items + NI - 1) / NI;
+  const unsigned char* qg = static_cast<const unsigned char*>(a.q);
+  const size_t hrow0 = (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(j) * G) * n;  // head j*G, row 0
+
+  // this wave's share of one item's copy: item wave / WPI of the stage,
+  // 16-byte pieces (wave % WPI) * 64 * LOADS + lane + 64u of the 16-row tile
+  const int my_item = wave / WPI, my_part = wave % WPI;
+  u32x4 stg[LOADS];
+  float lst = INFINITY;
+  auto fetch = [&](int st) {
+    const int it = st * NI + my_item;  // wave-uniform
     const int rt = rt0 + it / G, g = it % G;
-    const int h = j * G + g;
-    const size_t qrow0 = (static_cast<size_t>(b) * a.Hq + h) * n;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = my_part * 64 * LOADS + lane + 64 * u;
+      const int r = c / PIECES, pc = c % PIECES;
+      const int row = rt * 16 + r;
+      if (it < items && row < n)
+        stg[u] = *reinterpret_cast<const u32x4*>(qg + ((hrow0 + static_cast<size_t>(g) * n + row) * D) * ES + 16 * pc);
+      else
+        stg[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (my_part == 0 && lane < 16) {
+      const int row = rt * 16 + lane;
+      lst = it < items && row < n ? a.lse[hrow0 + static_cast<size_t>(g) * n + row] : INFINITY;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = my_part * 64 * LOADS + lane + 64 * u;
+      *reinterpret_cast<u32x4*>(&qs[buf][my_item * ITEM + (c / PIECES) * ROW + 16 * (c % PIECES)]) = stg[u];
+    }
+    if (my_part == 0 && lane < 16) ls[buf][my_item * 16 + lane] = lst;
+  };
+  auto item = [&](int buf, int ii, int rt, auto masked) {
     const int row = rt * 16 + ln;
+    const unsigned char* qt = &qs[buf][ii * ITEM + ln * ROW];
     Frag<T> qf[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (row < n) qf[s].load8(static_cast<const unsigned char*>(a.q) + ((qrow0 + row) * D + 32 * s + 8 * lq) * ES);
-      else qf[s].zero();
-    }
-    const float lr = row < n ? a.lse[qrow0 + row] : INFINITY;
+    for (int s = 0; s < KS; ++s) qf[s].load8(qt + (32 * s + 8 * lq) * ES);
+    const float lr = ls[buf][ii * 16 + ln];
     f32x4 s4[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -451,33 +496,48 @@ __global__ __launch_bounds__(kPfThreads, 2) void colsum_kernel(PfArgs a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) s4[kt] = mma(kf[kt][s], qf[s], s4[kt]);
     }
-    const bool need_mask = key0 + kColKeys - 1 > rt * 16 || key0 + kColKeys > n;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s4[kt][i], a.scale2, -lr));
-        if (need_mask) {
-          const int key = key0 + 16 * kt + 4 * lq + i;
+        if constexpr (decltype(masked)::value) {
+          const int key = kw0 + 16 * kt + 4 * lq + i;
           if (key > row || key >= n) pv = 0.0f;
         }
         cs[kt][i] += pv;
       }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) fetch(st + 1);
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int it = st * NI + ii;
+      const int rt = rt0 + it / G;
+      // rows rt*16..rt*16+15 against keys kw0..kw0+63: skip when every key lies
+      // past every row; mask when some key does, or when keys reach n
+      if (it < items && kw0 < n && rt * 16 + 15 >= kw0) {
+        if (kw0 + kColKeys - 1 > rt * 16 || kw0 + kColKeys > n) item(buf, ii, rt, std::true_type{});
+        else item(buf, ii, rt, std::false_type{});
+      }
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float t = sum16(cs[kt][i]);
-      if (ln == 0) red[wave][16 * kt + 4 * lq + i] = t;
+      const int key = kw0 + 16 * kt + 4 * lq + i;
+      if (ln == 0 && key < n) a.acc[static_cast<size_t>(bj) * n + key] = t;
     }
-  __syncthreads();
-  if (tid < kColKeys && key0 + tid < n) {
-    float t = red[0][tid];
-#pragma unroll
-    for (int w = 1; w < kPfWaves; ++w) t += red[w][tid];
-    a.acc[static_cast<size_t>(bj) * n + key0 + tid] = t;
-  }
 }
 
 template <typename T, int KS>
@@ -495,7 +555,7 @@ kvc_status launch_prefill_t(const PfArgs& a, bool colsums, hipStream_t st) {
   hipLaunchKernelGGL((fa_fwd_kernel<T, KS>), dim3(a.units, a.nrb), dim3(kPfThreads), bytes, st, a);
   kvc_status s = check_launch();
   if (s != KVC_OK || !colsums) return s;
-  const int nkb = (a.n + kColKeys - 1) / kColKeys;
+  const int nkb = (a.n + kColKeys * kPfWaves - 1) / (kColKeys * kPfWaves);
   hipLaunchKernelGGL((colsum_kernel<T, KS>), dim3(a.B * a.Hkv, nkb), dim3(kPfThreads), 0, st, a);
   return check_launch();
 }
