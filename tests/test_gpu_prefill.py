@@ -74,7 +74,9 @@ def check_prefill(q, k, v, out, acc, var, heads=None, where="", lse=None):
     ("bf16", 1, 4, 1, 77, 32),
     ("f32", 1, 2, 2, 130, 128),     # G = 1
     ("bf16", 2, 4, 2, 1, 64),       # a single position
-    ("f32", 1, 4, 2, 33, 32)])
+    ("f32", 1, 4, 2, 33, 32),
+    ("bf16", 1, 16, 2, 700, 128),   # G = 8 over three 256-key blocks, ragged
+    ("f32", 2, 6, 2, 530, 64)])     # fp32 stages of two items, G = 3, three blocks
 def test_prefill_parity(dtype, B, Hq, Hkv, n, D):
     kvc = _kvc()
     q, k, v = _inputs(1, B, Hq, Hkv, n, D, dtype)
