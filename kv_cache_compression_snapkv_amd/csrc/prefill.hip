@@ -178,8 +178,11 @@ template <typename T, int KS> struct PfGeom {
 // consecutive workgroups are different units (KV head, head group), so with 8
 // units per sequence each accelerator die's L2 serves one KV head; the row
 // blocks run last-first (the longest causal ranges start first).
+// Three workgroups per CU for 16-bit inputs (168 VGPRs, no spill at D = 128): a
+// third wave per SIMD overlaps more of the others' softmax with products.  fp32
+// inputs keep two (their D = 128 fragments would spill).
 template <typename T, int KS>
-__global__ __launch_bounds__(kPfThreads, 2) void fa_fwd_kernel(PfArgs a) {
+__global__ __launch_bounds__(kPfThreads, sizeof(T) == 2 ? 3 : 2) void fa_fwd_kernel(PfArgs a) {
   using Gm = PfGeom<T, KS>;
   constexpr int D = Gm::D, ES = Gm::ES;
   constexpr int NCT = D / 16;  // channel tiles of the output
